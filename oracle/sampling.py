@@ -1,0 +1,178 @@
+"""Draft selection, verification and the counter-based RNG.
+
+Verification follows the pages: greedy match at temperature 0 (lossless),
+and at T > 0 rejection sampling as in Leviathan et al. 2023, which the paper
+inherits to keep the target distribution (pith.science review, "Assumptions",
+section 3.5 entry). For a draft d ~ q and target distribution p:
+    accept d iff u * q(d) < p(d),  u ~ U(0,1)          (so P(accept) = min(1, p/q))
+    else  y ~ r,  r(x) = max(0, p(x) - q(x)) / sum_x max(0, p(x) - q(x)).
+Sampling from a distribution is done by the Gumbel-max rule:
+    argmax_i (log w_i + G_i),  G_i = -log(-log u_i),
+which draws i with probability w_i / sum(w) (Gumbel 1954; Maddison et al. 2014).
+
+Readings (the pages are silent):
+  * argmax ties go to the lowest token id;
+  * top-p: sort by probability (ties: lower id first), keep the shortest prefix
+    whose sum reaches top_p, including the token that crosses; top_p >= 1 keeps all;
+  * the RNG is counter based, so every draw is a pure function of
+    (seed, stream, position, index): u = ((x >> 41) + 0.5) * 2^-23 with
+    x = mix(mix(mix(seed) ^ (stream << 32 | pos)) + index * 0x9E3779B97F4A7C15),
+    where mix is the SplitMix64 output function (Steele, Lea & Flood 2014);
+  * forced mode (acceptance sweep): the draft at position x becomes the
+    reference greedy token r[x] when u_FORCE(x) < p_force, else (r[x] + 1) mod V.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+import numpy as np
+
+GOLDEN = 0x9E3779B97F4A7C15
+MASK64 = 0xFFFFFFFFFFFFFFFF
+
+STREAM_DRAFT = 1
+STREAM_ACC = 2
+STREAM_RES = 3
+STREAM_FORCE = 4
+STREAM_FIRST = 5
+
+NEAR_TIE = 1e-3
+
+
+def mix64(z) -> np.ndarray:
+    """SplitMix64 output function on uint64 values (wrapping arithmetic)."""
+    z = np.asarray(z, dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        z = (z ^ (z >> np.uint64(30))) * np.uint64(0xBF58476D1CE4E5B9)
+        z = (z ^ (z >> np.uint64(27))) * np.uint64(0x94D049BB133111EB)
+        return z ^ (z >> np.uint64(31))
+
+
+def splitmix64_sequence(seed: int, count: int) -> np.ndarray:
+    """The SplitMix64 generator itself: state += golden; output mix(state)."""
+    with np.errstate(over="ignore"):
+        states = (np.uint64(seed) + np.uint64(GOLDEN) * np.arange(1, count + 1, dtype=np.uint64))
+    return mix64(states)
+
+
+def uniform(seed: int, stream: int, pos: int, idx) -> np.ndarray:
+    """u(seed, stream, pos, idx) in (0, 1); exact in float32 and float64."""
+    idx = np.asarray(idx, dtype=np.uint64)
+    k0 = mix64(np.uint64(seed & MASK64))
+    key = np.uint64(((stream & 0xFFFFFFFF) << 32) | (pos & 0xFFFFFFFF))
+    k1 = mix64(k0 ^ key)
+    with np.errstate(over="ignore"):
+        x = mix64(k1 + idx * np.uint64(GOLDEN))
+    return ((x >> np.uint64(41)).astype(np.float64) + 0.5) * 2.0 ** -23
+
+
+def gumbel(u: np.ndarray) -> np.ndarray:
+    return -np.log(-np.log(u))
+
+
+def top2_gap(scores: np.ndarray) -> float:
+    finite = scores[np.isfinite(scores)]
+    if finite.size < 2:
+        return np.inf
+    top = np.partition(finite, -2)[-2:]
+    return float(top[1] - top[0])
+
+
+def argmax_lowest(scores: np.ndarray) -> int:
+    return int(np.argmax(scores))          # numpy returns the first (lowest) index
+
+
+def nucleus(p: np.ndarray, top_p: float) -> np.ndarray:
+    """Boolean mask of the top-p nucleus of distribution p."""
+    if top_p >= 1.0:
+        return np.ones(p.shape, dtype=bool)
+    ids = np.arange(p.size)
+    order = np.lexsort((ids, -p))
+    cum = np.cumsum(p[order])
+    r = int(np.searchsorted(cum, top_p, side="left"))
+    r = min(r, p.size - 1)
+    keep = np.zeros(p.shape, dtype=bool)
+    keep[order[: r + 1]] = True
+    return keep
+
+
+def distribution(z: np.ndarray, T: float, top_p: float) -> np.ndarray:
+    """softmax(z / T) restricted to its top-p nucleus and renormalised."""
+    p = np.exp(z / T - np.max(z / T))
+    p = p / p.sum()
+    keep = nucleus(p, top_p)
+    p = np.where(keep, p, 0.0)
+    return p / p.sum()
+
+
+def gumbel_max(w: np.ndarray, seed: int, stream: int, pos: int) -> Tuple[int, bool]:
+    """Sample i ~ w / sum(w) by Gumbel-max; returns (i, near-tie flag)."""
+    G = gumbel(uniform(seed, stream, pos, np.arange(w.size)))
+    with np.errstate(divide="ignore"):
+        s = np.where(w > 0, np.log(w) + G, -np.inf)
+    return argmax_lowest(s), top2_gap(s) < NEAR_TIE
+
+
+@dataclass
+class Sampling:
+    temperature: float = 0.0
+    top_p: float = 1.0
+    seed: int = 0
+    forced_p: Optional[float] = None       # forced mode when not None (T = 0 only)
+    forced_ref: Optional[np.ndarray] = None  # reference tokens for positions P0, P0+1, ...
+    forced_base: int = 0                   # position of forced_ref[0]
+
+
+def first_token(z: np.ndarray, s: Sampling, pos: int) -> Tuple[int, bool]:
+    if s.temperature == 0.0:
+        return argmax_lowest(z), top2_gap(z) < NEAR_TIE
+    return gumbel_max(distribution(z, s.temperature, s.top_p), s.seed, STREAM_FIRST, pos)
+
+
+def select_draft(z_q: np.ndarray, s: Sampling, pos: int):
+    """The PDM's draft for position pos: (d, q or None, near-tie flag)."""
+    V = z_q.size
+    if s.temperature == 0.0:
+        d, flag, q = argmax_lowest(z_q), top2_gap(z_q) < NEAR_TIE, None
+    else:
+        q = distribution(z_q, s.temperature, s.top_p)
+        d, flag = gumbel_max(q, s.seed, STREAM_DRAFT, pos)
+    if s.forced_p is not None and s.forced_ref is not None:
+        j = pos - s.forced_base
+        if 0 <= j < len(s.forced_ref):
+            ref = int(s.forced_ref[j])
+            # p_force crosses the C boundary as a float32; u is exact in both types.
+            hit = uniform(s.seed, STREAM_FORCE, pos, 0)[()] < float(np.float32(s.forced_p))
+            d, flag = (ref if hit else (ref + 1) % V), False
+    return int(d), q, bool(flag)
+
+
+def verify(z_t: np.ndarray, d: int, q: Optional[np.ndarray], s: Sampling, v: int):
+    """Verify draft d at position v against target logits z_t.
+
+    Returns (y, accepted, near-tie flag): y is the committed token.
+    """
+    if s.temperature == 0.0:
+        y = argmax_lowest(z_t)
+        return y, y == d, top2_gap(z_t) < NEAR_TIE
+    p = distribution(z_t, s.temperature, s.top_p)
+    u = uniform(s.seed, STREAM_ACC, v, 0)[()]
+    lhs, rhs = u * q[d], p[d]
+    flag = abs(lhs - rhs) < NEAR_TIE * q[d]
+    if lhs < rhs:
+        return int(d), True, bool(flag)
+    y, rflag = gumbel_max(np.maximum(p - q, 0.0), s.seed, STREAM_RES, v)
+    return int(y), False, bool(flag or rflag)
+
+
+def accept_probability(p: np.ndarray, q: np.ndarray) -> np.ndarray:
+    """P(accept | draft x) = min(1, p(x)/q(x)) for x with q(x) > 0."""
+    with np.errstate(divide="ignore", invalid="ignore"):
+        return np.where(q > 0, np.minimum(1.0, p / np.where(q > 0, q, 1.0)), 0.0)
+
+
+def residual_distribution(p: np.ndarray, q: np.ndarray) -> np.ndarray:
+    r = np.maximum(p - q, 0.0)
+    tot = r.sum()
+    return r / tot if tot > 0 else r

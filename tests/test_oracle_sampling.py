@@ -1,0 +1,140 @@
+"""Pins for the sampling rules and the counter-based RNG.
+
+Rejection sampling must reproduce the target distribution exactly (Leviathan
+et al. 2023, the paper's section 3.5 assumption on the pith.science review
+page); Gumbel-max must draw from softmax; SplitMix64 must reproduce its
+published output sequence.
+"""
+import numpy as np
+import pytest
+from scipy import stats
+
+from oracle import sampling as S
+
+
+def test_splitmix64_published_sequence():
+    # Seed 0 output sequence of the SplitMix64 reference generator (Vigna's splitmix64.c,
+    # Steele, Lea & Flood 2014).
+    want = [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F, 0xF88BB8A8724C81EC]
+    assert [int(x) for x in S.splitmix64_sequence(0, 4)] == want
+
+
+def test_uniform_exact_in_float32_and_open_interval():
+    u = S.uniform(123, S.STREAM_DRAFT, 77, np.arange(200000))
+    assert u.min() > 0.0 and u.max() < 1.0
+    np.testing.assert_array_equal(u.astype(np.float32).astype(np.float64), u)
+    assert abs(u.mean() - 0.5) < 3e-3
+    # different streams / positions / seeds give different draws
+    assert not np.array_equal(u[:100], S.uniform(123, S.STREAM_RES, 77, np.arange(100)))
+    assert not np.array_equal(u[:100], S.uniform(123, S.STREAM_DRAFT, 78, np.arange(100)))
+    assert not np.array_equal(u[:100], S.uniform(124, S.STREAM_DRAFT, 77, np.arange(100)))
+    # a pure function of its counter
+    np.testing.assert_array_equal(S.uniform(123, S.STREAM_DRAFT, 77, [5, 9]), u[[5, 9]])
+
+
+def test_top_p_closed_cases():
+    p = np.array([0.1, 0.4, 0.2, 0.3])
+    assert S.nucleus(p, 0.5).tolist() == [False, True, False, True]
+    assert S.nucleus(p, 0.4).tolist() == [False, True, False, False]    # reaches exactly
+    assert S.nucleus(p, 0.95).tolist() == [True, True, True, True]
+    assert S.nucleus(p, 1.0).all()
+    ties = np.full(4, 0.25)
+    assert S.nucleus(ties, 0.5).tolist() == [True, True, False, False]  # ties by lower id
+    assert S.nucleus(ties, 0.6).tolist() == [True, True, True, False]
+    d = S.distribution(np.log(p), 1.0, 0.5)
+    np.testing.assert_allclose(d, [0, 0.4 / 0.7, 0, 0.3 / 0.7])
+
+
+def _rand_dist(rng, V, zeros=0):
+    w = rng.gamma(0.5, size=V)
+    if zeros:
+        w[rng.choice(V, zeros, replace=False)] = 0.0
+    return w / w.sum()
+
+
+@pytest.mark.parametrize("V", [2, 3, 5, 8])
+def test_rejection_sampling_exact_enumeration(V):
+    """sum_d q(d) a(d) [d = x] + (1 - sum_d q(d) a(d)) r(x) == p(x) for every x."""
+    rng = np.random.default_rng(V)
+    cases = []
+    for _ in range(30):
+        cases.append((_rand_dist(rng, V), _rand_dist(rng, V)))
+    cases.append((_rand_dist(rng, V, zeros=V // 2), _rand_dist(rng, V)))
+    cases.append((_rand_dist(rng, V), _rand_dist(rng, V, zeros=V // 2)))
+    same = _rand_dist(rng, V)
+    cases.append((same, same.copy()))
+    for p, q in cases:
+        a = S.accept_probability(p, q)
+        acc = q * a
+        out = acc + (1.0 - acc.sum()) * S.residual_distribution(p, q)
+        np.testing.assert_allclose(out, p, rtol=0, atol=1e-12)
+
+
+def test_gumbel_max_draws_from_its_weights():
+    w = np.array([0.05, 0.4, 0.0, 0.25, 0.3])
+    n = 40000
+    draws = np.array([S.gumbel_max(w, 9, S.STREAM_DRAFT, pos)[0] for pos in range(n)])
+    assert not np.any(draws == 2)
+    counts = np.bincount(draws, minlength=5)
+    keep = w > 0
+    chi = stats.chisquare(counts[keep], n * w[keep])
+    assert chi.pvalue > 1e-3
+
+
+def test_rejection_sampling_monte_carlo_through_verify():
+    """Draft with select_draft, verify with verify(): committed tokens are distributed as p."""
+    rng = np.random.default_rng(11)
+    V = 6
+    z_t = rng.standard_normal(V) * 1.5
+    z_q = rng.standard_normal(V) * 1.5
+    s = S.Sampling(temperature=1.0, seed=5)
+    p = S.distribution(z_t, 1.0, 1.0)
+    n = 30000
+    out = np.empty(n, dtype=np.int64)
+    acc = 0
+    for pos in range(n):
+        d, q, _ = S.select_draft(z_q, s, pos)
+        y, a, _ = S.verify(z_t, d, q, s, pos)
+        out[pos] = y
+        acc += a
+    chi = stats.chisquare(np.bincount(out, minlength=V), n * p)
+    assert chi.pvalue > 1e-3
+    q = S.distribution(z_q, 1.0, 1.0)
+    # acceptance rate is sum_x min(p, q)
+    assert abs(acc / n - np.minimum(p, q).sum()) < 4 * np.sqrt(0.25 / n)
+
+
+def test_rejection_sampling_monte_carlo_with_top_p():
+    rng = np.random.default_rng(12)
+    V = 7
+    z_t = rng.standard_normal(V) * 2
+    z_q = rng.standard_normal(V) * 2
+    s = S.Sampling(temperature=0.8, top_p=0.7, seed=6)
+    p = S.distribution(z_t, 0.8, 0.7)
+    n = 30000
+    out = np.array([S.verify(z_t, *S.select_draft(z_q, s, pos)[:2], s, pos)[0] for pos in range(n)])
+    counts = np.bincount(out, minlength=V)
+    assert counts[p == 0].sum() == 0
+    chi = stats.chisquare(counts[p > 0], n * p[p > 0])
+    assert chi.pvalue > 1e-3
+
+
+def test_greedy_verify_and_ties():
+    z = np.array([0.5, 2.0, 2.0, -1.0])
+    y, acc, flag = S.verify(z, 2, None, S.Sampling(), 10)
+    assert y == 1 and not acc and flag        # tie -> lowest id, flagged as near-tie
+    y, acc, flag = S.verify(np.array([0.0, 3.0, 1.0]), 1, None, S.Sampling(), 10)
+    assert y == 1 and acc and not flag
+
+
+def test_forced_mode_replaces_the_draft():
+    ref = np.array([7, 3, 9, 1] * 50)
+    s = S.Sampling(seed=2, forced_p=0.6, forced_ref=ref, forced_base=100)
+    z = np.zeros(16)
+    hits = 0
+    for x in range(100, 300):
+        d, _, _ = S.select_draft(z, s, x)
+        r = ref[x - 100]
+        assert d in (r, (r + 1) % 16)
+        hits += d == r
+    assert 0.45 < hits / 200 < 0.75
