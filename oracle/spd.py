@@ -37,7 +37,6 @@ import numpy as np
 
 from spd_inputs.configs import ModelConfig
 from .model import Model
-from .numerics import round_to_bf16
 from .sampling import Sampling, first_token, select_draft, verify, argmax_lowest
 
 
@@ -126,7 +125,7 @@ class SPD:
         t0, flag = first_token(z, self.s, P0)
         self.prefill_logits, self.prefill_flag = z, flag
         # PDM over the verified prefix, features at full depth
-        X = np.concatenate([m.pdm.gemm_in(A[i]) for i in range(len(B))], axis=1)
+        X = np.concatenate([A[i] for i in range(len(B))], axis=1)
         Z = X @ m.W("pdm.proj").T
         for r in range(self.Ls):
             Z = m.pdm.prefill_layer(r, Z, 0)

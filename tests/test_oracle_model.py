@@ -54,7 +54,7 @@ def _linear_closed_form(q, k, v, gam):
     return torch.einsum("tjh,jhd->thd", s, v)
 
 
-def torch_forward(cfg, W, tokens, round_gemm):
+def torch_forward(cfg, W, tokens, round_gemm=False):
     """Whole-prompt forward; returns (final residual rows, logits of the last row)."""
     bf16 = cfg.dtype == "bf16"
     store = _bf if bf16 else _f32
@@ -87,9 +87,9 @@ def torch_forward(cfg, W, tokens, round_gemm):
     return H.numpy(), z.numpy()
 
 
-@pytest.mark.parametrize("name,plen,tol", [("tiny", 32, 1e-11), ("mid_bf16_L6_d384_n3", 40, 1e-6),
-                                           ("mid_bf16_L4_d512_hd128_n4", 20, 1e-6),
-                                           ("mid_hybrid_bf16_L8_d256_n4", 24, 1e-6)])
+@pytest.mark.parametrize("name,plen,tol", [("tiny", 32, 1e-11), ("mid_bf16_L6_d384_n3", 40, 1e-9),
+                                           ("mid_bf16_L4_d512_hd128_n4", 20, 1e-9),
+                                           ("mid_hybrid_bf16_L8_d256_n4", 24, 1e-9)])
 def test_prefill_matches_library_reference(name, plen, tol):
     cfg, W, prompt = workload(name)
     toks = prompt[:plen]
@@ -97,14 +97,14 @@ def test_prefill_matches_library_reference(name, plen, tol):
     H = m.embed_many(toks)
     for l in range(cfg.n_layers):
         H = m.target.prefill_layer(l, H, 0)
-    Href, zref = torch_forward(cfg, W, toks, round_gemm=True)
+    Href, zref = torch_forward(cfg, W, toks)
     np.testing.assert_allclose(H, Href, rtol=0, atol=tol * max(1.0, np.abs(Href).max()))
     np.testing.assert_allclose(m.logits(H[-1]), zref, rtol=0, atol=tol)
 
 
 @pytest.mark.parametrize("name", ["tiny", "mid_bf16_L7_d256_n3_uneven", "mid_hybrid_bf16_L8_d256_n4"])
 def test_decode_one_position_at_a_time_matches_reference(name):
-    """Decode (no GEMM-input rounding) equals the library forward without that rounding."""
+    """Decode, one position at a time, equals the library forward over the whole prompt."""
     cfg, W, prompt = workload(name)
     toks = prompt[:20]
     m = Model(cfg, W)
@@ -117,9 +117,11 @@ def test_decode_one_position_at_a_time_matches_reference(name):
     np.testing.assert_allclose(m.logits(h), zref, rtol=0, atol=1e-9)
 
 
-def test_decode_equals_prefill_on_f32_weights():
-    """Without bf16 roundings, the batched causal prefill and per-position decode agree."""
-    cfg, W, prompt = workload("tiny")
+@pytest.mark.parametrize("name", ["tiny", "mid_bf16_L6_d384_n3"])
+def test_decode_equals_prefill(name):
+    """The batched causal prefill and per-position decode agree (same roundings: the KV store)."""
+    cfg, W, prompt = workload(name)
+    prompt = prompt[:40]
     a, b = Model(cfg, W), Model(cfg, W)
     H = a.embed_many(prompt)
     for l in range(cfg.n_layers):
@@ -128,9 +130,9 @@ def test_decode_equals_prefill_on_f32_weights():
         h = b.embed(t)
         for l in range(cfg.n_layers):
             h = b.target.decode_layer(l, h, pos)
-        np.testing.assert_allclose(h, H[pos], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(h, H[pos], rtol=0, atol=1e-9)
     for l in range(cfg.n_layers):
-        np.testing.assert_allclose(a.target.K[l], b.target.K[l], atol=1e-12)
+        np.testing.assert_allclose(a.target.K[l], b.target.K[l], atol=1e-9)
 
 
 def test_gqa_head_mapping():
