@@ -1,0 +1,238 @@
+/*
+ * spd.h - C ABI of the single-GPU Speculative Pipeline Decoding (SPD) hot path.
+ *
+ * The method (arXiv 2605.30852, as summarised on the pith.science review
+ * page, "What carries the argument" and "Core claim"; aiqbench abstract):
+ * the target LLM is cut into n pipeline stages so that n tokens of ONE
+ * sequence advance at once, each in a different stage; a Pipeline Draft
+ * Module (PDM) reads the pipeline's input states, concatenates hidden states
+ * at anchor depths B, projects k*d -> d, and runs Ls decoder layers plus the
+ * LM head to draft the next token while the step runs; the token leaving the
+ * last stage verifies the next position (greedy match, or rejection sampling
+ * as in Leviathan et al. 2023 at temperature > 0), and a rejection truncates
+ * the KV cache, flushes the pipeline and reseeds it. On one GPU every step
+ * runs all n stage slices as grouped launches (the "depth staircase").
+ *
+ * Conventions
+ *   - Every call returns SPD_OK or a negative SPD_E_* code; no exception ever
+ *     crosses this boundary. spd_last_error() then holds a message.
+ *   - Ownership: the caller owns the weights (device memory), the workspace
+ *     (device memory of spd_workspace_bytes() bytes) and the HIP stream; the
+ *     library borrows them until spd_destroy(). The library owns the handle
+ *     and a few pinned host staging buffers that it allocates in spd_init().
+ *     No step call allocates memory.
+ *   - Call order: spd_init -> spd_prefill -> (spd_step -> spd_verify_commit)*.
+ *     Any other order returns SPD_E_STATE and changes nothing.
+ *   - A handle is used from one host thread and one stream.
+ *   - Host pointers are marked [host]; all others are device pointers.
+ */
+#ifndef SPD_H
+#define SPD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct spd_handle spd_handle;   /* opaque, library-owned */
+
+enum {
+  SPD_OK = 0,
+  SPD_E_ARG = -1,       /* null or out-of-range argument */
+  SPD_E_CONFIG = -2,    /* configuration the library does not support */
+  SPD_E_STATE = -3,     /* call out of order */
+  SPD_E_CAPACITY = -4,  /* a position would reach max_ctx, or workspace too small */
+  SPD_E_DEVICE = -5     /* a HIP runtime call failed */
+};
+
+enum { SPD_F32 = 0, SPD_BF16 = 1 };                 /* weight (and KV cache) storage */
+enum { SPD_FILL_CLAMP = 0, SPD_FILL_ZERO = 1 };      /* anchors not computed yet */
+enum { SPD_LAYER_SOFTMAX = 0, SPD_LAYER_LINEAR = 1 };
+
+/*
+ * Model and SPD configuration. Free parameters in the pages' notation
+ * (pith.science review, "Assumptions & free parameters"): anchors B, pipeline
+ * width n, speculation layers Ls, temperature T.
+ *   n_layers = L; n_stages = n (1 <= n <= L);
+ *   stage_layers [host, n entries, sum = L] or NULL for the default split
+ *     (the first L mod n stages get ceil(L/n) layers);
+ *   anchors [host, k entries]: depths b in [0, L], strictly ascending, anchors[0] == 0;
+ *     anchor b is the residual stream after b target layers (b = 0: embedding);
+ *   pdm_layers = Ls >= 1 (Ls > L/n is allowed: the PDM is then simply not
+ *     latency-masked, which the pages state as the condition Ls <= L/n);
+ *   layer_kind [host, L entries] SPD_LAYER_* or NULL for all softmax;
+ *   anchor_fill: how a PDM row fills anchors deeper than its current depth:
+ *     SPD_FILL_CLAMP repeats the deepest computed anchor (default), SPD_FILL_ZERO uses 0;
+ *   max_ctx: KV capacity in positions; every in-flight position must stay below it.
+ * Limits: d_model, d_ffn, n_q_heads*head_dim multiples of 8; head_dim even and
+ * <= 128; n_q_heads a multiple of n_kv_heads with at most 16 query heads per
+ * KV head; n <= 16; k <= 8; Ls <= 16.
+ */
+typedef struct {
+  int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, d_ffn, vocab;
+  int32_t dtype;                  /* SPD_F32 | SPD_BF16 */
+  float rope_theta, rms_eps;
+  const uint8_t* layer_kind;      /* [host] */
+  int32_t n_stages;
+  const int32_t* stage_layers;    /* [host] */
+  int32_t n_anchors;
+  const int32_t* anchors;         /* [host] */
+  int32_t pdm_layers;
+  int32_t anchor_fill;
+  int32_t max_ctx;
+} spd_model_config;
+
+/*
+ * Weights: device pointers owned by the caller, row-major, K (input) dimension
+ * contiguous. Matrices are stored in cfg.dtype; RMSNorm gains are float32.
+ *   embed   [V][d]        lm_head [V][d]   (tied: the PDM uses the same head)
+ *   final_norm [d] f32    pdm_final_norm [d] f32
+ *   pdm_proj [d][k*d]     input order: anchor 0's d values, then anchor 1's, ...
+ *   layers  [host] array of 7*L device pointers, per layer in this order:
+ *     attn_norm [d] f32,
+ *     w_qkv  softmax layer: [(hq + 2 hkv) hd][d], q rows then k rows then v rows;
+ *            linear layer:  [3 hq hd][d]
+ *     w_o [d][hq hd], ffn_norm [d] f32, w_gate [F][d], w_up [F][d], w_down [d][F]
+ *   pdm_layers [host] array of 7*Ls pointers, same order (softmax layers).
+ */
+typedef struct {
+  const void* embed;
+  const void* lm_head;
+  const float* final_norm;
+  const void* const* layers;
+  const void* pdm_proj;
+  const void* const* pdm_layers;
+  const float* pdm_final_norm;
+} spd_weights;
+
+/*
+ * Sampling. temperature == 0: greedy drafts and greedy verification
+ * (lossless: the committed stream is the target's greedy stream).
+ * temperature > 0: drafts d ~ q = softmax(z_pdm/T), target p = softmax(z/T);
+ * accept iff u*q(d) < p(d), else commit y ~ max(0, p - q) (normalised).
+ * top_p >= 1 disables nucleus filtering (top_p < 1 is SPD_E_CONFIG in this
+ * version). Random numbers are a pure function of (seed, stream, position,
+ * index): SplitMix64 output function, u = ((x >> 41) + 0.5) * 2^-23.
+ * forced_mode = 1 (temperature 0 only) replaces each draft at position x by
+ * forced_ref[x - P0] with probability forced_p, else by (forced_ref[x - P0] + 1) mod V,
+ * where P0 is the prompt length given to spd_prefill; positions past the end
+ * of forced_ref keep the PDM's draft. forced_ref [host] is copied at spd_prefill.
+ */
+typedef struct {
+  float temperature;
+  float top_p;
+  uint64_t seed;
+  int32_t forced_mode;
+  float forced_p;
+  const int32_t* forced_ref;      /* [host] */
+  int32_t forced_ref_len;
+} spd_sampling;
+
+/* Bytes of device workspace spd_init needs for this configuration (0 on invalid config). */
+size_t spd_workspace_bytes(const spd_model_config* cfg);
+
+/*
+ * Validate the configuration, carve the caller's workspace, bind the weight
+ * pointers, and precompute the RoPE table. hip_stream is a hipStream_t (NULL:
+ * the null stream). The workspace must stay valid and unused by the caller
+ * until spd_destroy. Errors: SPD_E_ARG, SPD_E_CONFIG, SPD_E_CAPACITY (ws_bytes
+ * too small), SPD_E_DEVICE.
+ */
+int spd_init(const spd_model_config* cfg, const spd_weights* w, const spd_sampling* s,
+             void* d_workspace, size_t ws_bytes, void* hip_stream, spd_handle** out);
+
+/*
+ * Run the target over the prompt [host, len token ids in [0, V)] in chunks,
+ * writing the target KV cache, the anchor states of every prompt position, the
+ * PDM KV cache over the verified prefix (its depth-maximised features: all
+ * anchors), and the first generated token (greedy, or sampled at T > 0).
+ * Blocking. Afterwards the pipeline holds one token (position len, stage 0).
+ * Errors: SPD_E_ARG (bad ids, len < 1), SPD_E_CAPACITY (len >= max_ctx),
+ * SPD_E_STATE (already prefilled: call spd_reset first), SPD_E_DEVICE.
+ */
+int spd_prefill(spd_handle* h, const int32_t* prompt, int32_t len, int32_t* first_token);
+
+/*
+ * Enqueue one pipeline step on the stream and return at once: embed the
+ * stage-0 token; the PDM drafts the next token from the step's input states;
+ * every in-flight token runs its stage's layers; if the oldest token leaves the
+ * last stage, its logits verify the following position. Nothing is committed
+ * until spd_verify_commit. Errors: SPD_E_STATE (a step is pending or no
+ * prefill), SPD_E_CAPACITY (the newest position reached max_ctx), SPD_E_DEVICE.
+ */
+int spd_step(spd_handle* h);
+
+/*
+ * Wait for the pending step and apply its verdict: on accept the ring shifts
+ * and the draft enters stage 0; on reject every layer's KV length becomes the
+ * verified position v, the pipeline is flushed and reseeded with the
+ * corrected token at v. This is the only per-step device-to-host wait.
+ *   verified: 1 if a token left the last stage this step (else a refill step)
+ *   position: v, the position whose token was committed (verified == 1)
+ *   token: the committed token y; accepted: 1 if y is the draft
+ *   draft_token: the draft that stood at v before verification
+ *   new_draft: the token drafted this step, for position newest + 1
+ *   newest: position of this step's stage-0 token
+ *   flags: bit 0 near-tie in the verify decision (top-2 gap < 1e-3, or
+ *     |u q(d) - p(d)| < 1e-3 q(d)); bit 1 near-tie in the draft selection
+ *   committed_total: N after this step; inflight: tokens in flight now
+ */
+typedef struct {
+  int32_t verified, position, token, accepted, draft_token, flags;
+  int32_t committed_total, inflight, new_draft, newest;
+} spd_commit;
+int spd_verify_commit(spd_handle* h, spd_commit* out);
+
+/* Counters of Eq. (9): K steps, N committed tokens (the prefill's first token
+ * excluded), alpha = N/K, s0 = alpha * n. */
+typedef struct { int64_t K, N, accepted, rejected; double alpha, s0; } spd_stats;
+int spd_get_stats(const spd_handle* h, spd_stats* out);
+
+/* Current KV lengths: per_layer [host, L] for the target, *pdm_len for the
+ * PDM's permanent rows (positions with full depth). Either may be NULL. */
+int spd_get_kv_lens(const spd_handle* h, int32_t* per_layer, int32_t* pdm_len);
+
+/* Copy one internal buffer to host memory for parity checks; bytes must equal
+ * the buffer's size (spd_debug_size). Synchronises the stream. Not for the hot loop. */
+enum {
+  SPD_DBG_TARGET_LOGITS = 1,   /* f32 [V]: last target head output (prefill row or exit) */
+  SPD_DBG_DRAFT_LOGITS = 2,    /* f32 [V]: last PDM head output (raw logits) */
+  SPD_DBG_H_RING = 3,          /* f32 [n+1][d]: residual of position p in slot p mod (n+1) */
+  SPD_DBG_ANCHORS = 4,         /* f32 [n+1][k][d]: anchors of position p in slot p mod (n+1) */
+  SPD_DBG_PDM_ROWS = 5,        /* f32 [n+1][d]: PDM residual rows of the last step */
+  SPD_DBG_TARGET_KV = 6,       /* dtype [softmax layers][2][hkv][max_ctx][hd] */
+  SPD_DBG_PDM_KV = 7,          /* dtype [Ls][2][hkv][max_ctx][hd] */
+  SPD_DBG_TOKENS = 8           /* i32 [n+1]: token of position p in slot p mod (n+1) */
+};
+size_t spd_debug_size(const spd_handle* h, int32_t what);
+int spd_debug_copy(const spd_handle* h, int32_t what, void* host_dst, size_t bytes);
+
+/*
+ * Measurement. When enabled, every launch of a step is bracketed by HIP events
+ * on the handle's stream, and spd_verify_commit accumulates per launch kind:
+ * the number of launches, their total duration and their algorithmic HBM
+ * bytes (weights read once, KV rows read once). Kinds, in order: 0 embed,
+ * 1 PDM projection GEMV, 2 QKV GEMV, 3 attention, 4 linear attention, 5 O GEMV,
+ * 6 gate/up GEMV, 7 down GEMV, 8 LM-head GEMV, 9 vocabulary stats, 10 verify,
+ * 11 residual sample. Enabling or disabling clears the totals; a pending step
+ * gives SPD_E_STATE.
+ */
+int spd_timing_enable(spd_handle* h, int on);
+int spd_timing_read(const spd_handle* h, int32_t kind, int64_t* count, double* total_ms,
+                    double* bytes);
+
+/* Return to the post-init state (no prefill); device buffers are reused. */
+int spd_reset(spd_handle* h);
+/* Message of the last failed call on this handle ("" if none); valid until the next call. */
+const char* spd_last_error(const spd_handle* h);
+/* Message of the last spd_init failure (no handle exists then). */
+const char* spd_init_error(void);
+/* Release the handle and its pinned buffers; the caller's buffers are untouched. NULL is a no-op. */
+void spd_destroy(spd_handle* h);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPD_H */

@@ -1,0 +1,956 @@
+// Host side of the SPD library: configuration, workspace plan, the pipeline
+// state machine (in-flight ring, stage plan, commit / rollback bookkeeping),
+// and the per-step launch plan. Step semantics follow arXiv 2605.30852 as
+// summarised on the pith.science review page ("What carries the argument"):
+// n stages, n tokens in flight, the PDM on the step's input states, streaming
+// verification, truncate / flush / reseed on rejection.
+//
+// Device rings are indexed by position mod (n + 1): the residual and anchor
+// states of in-flight positions, their tokens, and the draft distributions.
+// A rejection therefore needs no device work: KV lengths are host state, and
+// every ring slot of a discarded position is rewritten before it is read.
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <deque>
+#include <string>
+#include <vector>
+
+#include "spd.h"
+#include "spd_internal.h"
+
+using namespace spd;
+
+namespace spd {
+int attn_max_split();
+}
+
+namespace {
+
+thread_local std::string g_init_error;
+
+constexpr int kPrefillChunk = 512;
+constexpr int kVocabBlocks = 256;
+constexpr size_t kDescBytes = 512 * 1024;
+constexpr int kTensorsPerLayer = 7;
+enum { T_ATTN_NORM = 0, T_QKV, T_O, T_FFN_NORM, T_GATE, T_UP, T_DOWN };
+
+size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
+
+// Distance in floats between two float arrays that may live in different allocations.
+long long float_gap(const float* to, const float* from) {
+  return ((long long)(intptr_t)to - (long long)(intptr_t)from) / (long long)sizeof(float);
+}
+
+struct Inflight {
+  int pos;
+  int stage;
+};
+
+// Launch kinds of a step (and their timing buckets).
+enum OpKind { OP_EMBED = 0, OP_GEMV_PROJ, OP_GEMV_QKV, OP_ATTN, OP_LIN, OP_GEMV_O, OP_GEMV_GU,
+              OP_GEMV_DOWN, OP_GEMV_HEAD, OP_VOCAB, OP_FINAL, OP_RESID, OP_NKINDS };
+
+struct Op {
+  int kind;
+  size_t off;      // descriptor offset in the step's descriptor block
+  int count;       // problems
+  int ntiles;      // workgroups
+  int split;       // attention split length
+  double bytes;    // algorithmic HBM bytes (weights + KV) for the timing report
+};
+
+struct Plan {
+  int L, d, hq, hkv, hd, F, V, n, k, Ls, max_ctx, ring, qrows, linrows, qo;
+  bool bf16;
+  int esz;
+  float theta, eps;
+  int fill;
+  std::vector<int> kind, sizes, starts, anchors, ord;   // ord: index among softmax / linear layers
+  int nsoft = 0, nlin = 0;
+  int R = 0;   // sub-layer launches per step
+  // workspace offsets
+  size_t o_kv, o_pkv, o_lin, o_h, o_anch, o_tok, o_qring, o_qlse, o_X, o_hp, o_qbuf, o_attn,
+      o_act, o_lqkv, o_logits, o_part, o_verdict, o_rcnt, o_desc, o_apart, o_acnt, o_rope,
+      o_forced, o_ptok, o_pH, o_pA, o_pQKV, o_pO, o_pG, o_pU, o_pZ, o_panch, total;
+  size_t kv_layer_bytes;     // K and V of one layer
+  size_t lin_state_bytes;    // one state [hq][hd][hd] f32
+  int maxprob;               // problems per launch
+};
+
+bool plan_config(const spd_model_config* c, Plan& p, std::string& err) {
+  auto bad = [&](const char* m) { err = m; return false; };
+  if (!c) return bad("null config");
+  p.L = c->n_layers; p.d = c->d_model; p.hq = c->n_q_heads; p.hkv = c->n_kv_heads;
+  p.hd = c->head_dim; p.F = c->d_ffn; p.V = c->vocab; p.n = c->n_stages; p.k = c->n_anchors;
+  p.Ls = c->pdm_layers; p.max_ctx = c->max_ctx; p.theta = c->rope_theta; p.eps = c->rms_eps;
+  p.fill = c->anchor_fill;
+  if (c->dtype != SPD_F32 && c->dtype != SPD_BF16) return bad("dtype must be SPD_F32 or SPD_BF16");
+  p.bf16 = c->dtype == SPD_BF16;
+  p.esz = p.bf16 ? 2 : 4;
+  if (p.L < 1 || p.d < 8 || p.hq < 1 || p.hkv < 1 || p.hd < 2 || p.F < 8 || p.V < 2)
+    return bad("model dimensions out of range");
+  if (p.d % 8 || p.F % 8 || (p.hq * p.hd) % 8) return bad("d_model, d_ffn, n_q_heads*head_dim must be multiples of 8");
+  if (p.hd % 2 || p.hd > 128) return bad("head_dim must be even and <= 128");
+  if (p.hq % p.hkv || p.hq / p.hkv > 16) return bad("n_q_heads must be a multiple of n_kv_heads, group <= 16");
+  if (p.n < 1 || p.n > kMaxStages || p.n > p.L) return bad("n_stages must be in [1, min(L, 16)]");
+  if (p.k < 1 || p.k > kMaxAnchors || !c->anchors) return bad("need 1..8 anchors");
+  if (p.Ls < 1 || p.Ls > 16) return bad("pdm_layers must be in [1, 16]");
+  if (p.fill != SPD_FILL_CLAMP && p.fill != SPD_FILL_ZERO) return bad("bad anchor_fill");
+  if (p.max_ctx < 2) return bad("max_ctx too small");
+  if (!(p.eps > 0.f) || !(p.theta > 0.f)) return bad("rms_eps and rope_theta must be positive");
+  p.anchors.assign(c->anchors, c->anchors + p.k);
+  if (p.anchors[0] != 0) return bad("anchors[0] must be 0 (the embedding)");
+  for (int i = 1; i < p.k; ++i)
+    if (p.anchors[i] <= p.anchors[i - 1]) return bad("anchors must be strictly ascending");
+  if (p.anchors.back() > p.L) return bad("anchor depth beyond n_layers");
+  p.kind.assign(p.L, SPD_LAYER_SOFTMAX);
+  if (c->layer_kind)
+    for (int l = 0; l < p.L; ++l) p.kind[l] = c->layer_kind[l];
+  for (int l = 0; l < p.L; ++l) {
+    if (p.kind[l] == SPD_LAYER_LINEAR) return bad("linear-attention layers are not supported yet");
+    if (p.kind[l] != SPD_LAYER_SOFTMAX) return bad("bad layer_kind");
+  }
+  p.sizes.resize(p.n);
+  if (c->stage_layers) {
+    int s = 0;
+    for (int i = 0; i < p.n; ++i) {
+      p.sizes[i] = c->stage_layers[i];
+      if (p.sizes[i] < 1) return bad("stage sizes must be >= 1");
+      s += p.sizes[i];
+    }
+    if (s != p.L) return bad("stage sizes must sum to n_layers");
+  } else {
+    for (int i = 0; i < p.n; ++i) p.sizes[i] = p.L / p.n + (i < p.L % p.n ? 1 : 0);
+  }
+  p.starts.resize(p.n);
+  for (int i = 0, s = 0; i < p.n; ++i) { p.starts[i] = s; s += p.sizes[i]; }
+  p.ord.assign(p.L, 0);
+  for (int l = 0; l < p.L; ++l) p.ord[l] = p.kind[l] == SPD_LAYER_SOFTMAX ? p.nsoft++ : p.nlin++;
+  p.ring = p.n + 1;
+  p.qrows = (p.hq + 2 * p.hkv) * p.hd;
+  p.linrows = 3 * p.hq * p.hd;
+  p.qo = p.hq * p.hd;
+  p.R = std::max(*std::max_element(p.sizes.begin(), p.sizes.end()), p.Ls);
+  p.maxprob = p.n + 1;
+  // workspace plan
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes); return at; };
+  const size_t ctx = p.max_ctx;
+  p.kv_layer_bytes = 2 * (size_t)p.hkv * ctx * p.hd * p.esz;
+  p.lin_state_bytes = (size_t)p.hq * p.hd * p.hd * 4;
+  p.o_kv = take(p.nsoft * p.kv_layer_bytes);
+  p.o_pkv = take((size_t)p.Ls * p.kv_layer_bytes);
+  p.o_lin = take((size_t)p.nlin * p.ring * p.lin_state_bytes);
+  p.o_h = take((size_t)p.ring * p.d * 4);
+  p.o_anch = take((size_t)p.ring * p.k * p.d * 4);
+  p.o_tok = take((size_t)p.ring * 4);
+  p.o_qring = take((size_t)p.ring * p.V * 4);
+  p.o_qlse = take((size_t)p.ring * 4);
+  const int T = p.n + p.ring;   // decode rows: target tokens + PDM rows
+  p.o_X = take((size_t)p.ring * p.k * p.d * 4);
+  p.o_hp = take((size_t)p.ring * p.d * 4);
+  p.o_qbuf = take((size_t)T * p.qo * 4);
+  p.o_attn = take((size_t)T * p.qo * 4);
+  p.o_act = take((size_t)T * p.F * 4);
+  p.o_lqkv = take((size_t)p.n * p.linrows * 4);
+  p.o_logits = take((size_t)p.V * 4);
+  p.o_part = take((size_t)3 * kVocabBlocks * sizeof(VocabPartial));
+  p.o_verdict = take(sizeof(Verdict));
+  p.o_rcnt = take(64);
+  p.o_desc = take(kDescBytes);
+  const int G = p.hq / p.hkv;
+  p.o_apart = take((size_t)T * p.hkv * attn_max_split() * G * (p.hd + 2) * 4);
+  p.o_acnt = take((size_t)T * p.hkv * 4);
+  p.o_rope = take((size_t)ctx * (p.hd / 2) * sizeof(float2));
+  p.o_forced = take(ctx * 4);
+  const size_t CH = kPrefillChunk;
+  const size_t widest = std::max({(size_t)p.d, (size_t)p.qo, (size_t)p.F, (size_t)p.k * p.d});
+  p.o_ptok = take(ctx * 4);
+  p.o_pH = take(CH * p.d * 4);
+  p.o_pA = take(CH * widest * 4);
+  p.o_pQKV = take(CH * std::max(p.qrows, p.linrows) * 4);
+  p.o_pO = take(CH * p.qo * 4);
+  p.o_pG = take(CH * p.F * 4);
+  p.o_pU = take(CH * p.F * 4);
+  p.o_pZ = take(CH * p.d * 4);
+  p.o_panch = take((size_t)p.k * CH * p.d * 4);
+  p.total = o;
+  return true;
+}
+
+}  // namespace
+
+struct spd_handle {
+  Plan p;
+  // weights
+  const void* embed;
+  const void* head;
+  const float* final_norm;
+  const void* proj;
+  const float* pdm_final_norm;
+  std::vector<const void*> lw;   // [L][7]
+  std::vector<const void*> pw;   // [Ls][7]
+  // sampling
+  float temp, top_p, forced_p;
+  unsigned long long seed;
+  int forced_mode;
+  std::vector<int> forced_ref;
+  // device
+  char* ws;
+  hipStream_t st;
+  // pinned host staging
+  char* h_desc = nullptr;
+  Verdict* h_verdict = nullptr;
+  // state machine
+  enum { S_INIT, S_READY, S_PENDING } state = S_INIT;
+  int P0 = 0;
+  std::deque<Inflight> F;
+  int pdm_len = 0;
+  std::vector<int> kv_len;
+  long long N = 0, K = 0, acc = 0, rej = 0;
+  // the pending step
+  bool pend_exit = false;
+  int pend_v = 0, pend_dpos = 0, pend_newest = 0;
+  std::vector<std::pair<int, int>> pend_layers;   // (layer, pos) processed
+  std::vector<Op> ops;
+  // timing
+  bool timing = false;
+  std::vector<hipEvent_t> ev;
+  std::vector<int> ev_kind;
+  std::vector<double> ev_bytes;
+  double kt_ms[OP_NKINDS] = {};
+  double kt_bytes[OP_NKINDS] = {};
+  long long kt_count[OP_NKINDS] = {};
+  std::string err;
+
+  template <typename T> T* at(size_t off) const { return reinterpret_cast<T*>(ws + off); }
+  int slot(int pos) const { return pos % p.ring; }
+  const void* W(int l, int t) const { return lw[(size_t)l * kTensorsPerLayer + t]; }
+  const void* PW(int r, int t) const { return pw[(size_t)r * kTensorsPerLayer + t]; }
+  void* kvK(int l) const { return ws + p.o_kv + (size_t)p.ord[l] * p.kv_layer_bytes; }
+  void* kvV(int l) const { return (char*)kvK(l) + p.kv_layer_bytes / 2; }
+  void* pK(int r) const { return ws + p.o_pkv + (size_t)r * p.kv_layer_bytes; }
+  void* pV(int r) const { return (char*)pK(r) + p.kv_layer_bytes / 2; }
+};
+
+namespace {
+
+int fail(spd_handle* h, int code, const std::string& m) {
+  if (h) h->err = m;
+  return code;
+}
+
+#define HIPCHK(h, call)                                                                  \
+  do {                                                                                   \
+    hipError_t e_ = (call);                                                              \
+    if (e_ != hipSuccess)                                                                \
+      return fail(h, SPD_E_DEVICE, std::string(#call) + ": " + hipGetErrorString(e_));   \
+  } while (0)
+
+// ---- descriptor block builder -------------------------------------------------
+struct DescWriter {
+  char* base;
+  size_t used = 0;
+  template <typename T> size_t put(const T* items, int count) {
+    used = align_up(used, 64);
+    const size_t at = used;
+    std::memcpy(base + at, items, sizeof(T) * count);
+    used += sizeof(T) * count;
+    return at;
+  }
+};
+
+int units_per_tile(const GemvProb& g) {
+  const bool paired = g.epi == EPI_QKV || g.epi == EPI_SWIGLU;
+  const int rw = g.nvec == 1 ? kRowsSingle : kRowsMulti;
+  return kWaves * (paired ? rw / 2 : rw);
+}
+
+int finish_tiles(std::vector<GemvProb>& v) {
+  int t = 0;
+  for (auto& g : v) {
+    const int units = g.epi == EPI_QKV ? g.rows / 2 : g.rows;
+    g.tile0 = t;
+    g.ntiles = (units + units_per_tile(g) - 1) / units_per_tile(g);
+    t += g.ntiles;
+  }
+  return t;
+}
+
+GemvProb gemv(const void* W, int rows, int K, const float* x, long long xs, int nvec, int epi,
+              float* y, long long ys, const float* gain, long long gs, float eps) {
+  GemvProb g{};
+  g.W = W; g.rows = rows; g.K = K; g.x = x; g.x_stride = xs; g.nvec = nvec; g.epi = epi;
+  g.y = y; g.y_stride = ys; g.gain = gain; g.gain_stride = gs; g.eps = eps;
+  return g;
+}
+
+double gemv_bytes(const std::vector<GemvProb>& v, int esz) {
+  double b = 0;
+  for (auto& g : v) b += (double)g.rows * g.K * esz * (g.epi == EPI_SWIGLU ? 2 : 1);
+  return b;
+}
+
+int attn_split(const Plan& p, const std::vector<AttnProb>& v) {
+  long long keys = 0;
+  int maxlen = 1;
+  for (auto& a : v) { keys += a.len; maxlen = std::max(maxlen, a.len); }
+  const long long target = 2 * 256;   // workgroups to fill 256 CUs twice
+  long long s = (keys * p.hkv + target - 1) / target;
+  s = std::max<long long>(kAttnTile, (s + kAttnTile - 1) / kAttnTile * kAttnTile);
+  while ((maxlen + s - 1) / s > attn_max_split()) s += kAttnTile;
+  return (int)s;
+}
+
+int finish_attn(const Plan& p, std::vector<AttnProb>& v, int split) {
+  int t = 0;
+  for (size_t i = 0; i < v.size(); ++i) {
+    v[i].nsplit = (v[i].len + split - 1) / split;
+    v[i].tile0 = t;
+    v[i].slot = (int)i;
+    t += p.hkv * v[i].nsplit;
+  }
+  return t;
+}
+
+void fill_rope(const Plan& p, std::vector<float2>& tab) {
+  const int half = p.hd / 2;
+  tab.resize((size_t)p.max_ctx * half);
+  for (int pos = 0; pos < p.max_ctx; ++pos)
+    for (int i = 0; i < half; ++i) {
+      const double inv = std::pow((double)p.theta, -2.0 * i / p.hd);
+      const double a = (double)pos * inv;
+      tab[(size_t)pos * half + i] = make_float2((float)std::cos(a), (float)std::sin(a));
+    }
+}
+
+// Launch one op of the plan.
+hipError_t run_op(spd_handle* h, const Op& op) {
+  const Plan& p = h->p;
+  char* d = h->ws + p.o_desc;
+  const float2* rope = h->at<float2>(p.o_rope);
+  switch (op.kind) {
+    case OP_EMBED:
+      return launch_embed_gather(reinterpret_cast<const EmbedGather*>(d + op.off), op.count, p.k,
+                                 p.d, p.bf16, h->st);
+    case OP_GEMV_PROJ: case OP_GEMV_QKV: case OP_GEMV_O: case OP_GEMV_GU: case OP_GEMV_DOWN:
+    case OP_GEMV_HEAD:
+      return launch_gemv(reinterpret_cast<const GemvProb*>(d + op.off), op.count, op.ntiles,
+                         p.bf16, rope, h->st);
+    case OP_ATTN:
+      return launch_attention(reinterpret_cast<const AttnProb*>(d + op.off), op.count, op.ntiles,
+                              p.bf16, p.hq, p.hkv, p.hd, p.max_ctx, op.split,
+                              h->at<float>(p.o_apart), h->at<int>(p.o_acnt), h->st);
+    case OP_VOCAB:
+      return launch_vocab_stats(reinterpret_cast<const VocabDesc*>(d + op.off), kVocabBlocks,
+                                h->at<VocabPartial>(p.o_part), h->st);
+    case OP_FINAL:
+      return launch_finalize(reinterpret_cast<const FinalizeDesc*>(d + op.off), h->st);
+    case OP_RESID:
+      return launch_residual_impl(reinterpret_cast<const FinalizeDesc*>(d + op.off),
+                                  h->at<VocabPartial>(p.o_part), kVocabBlocks, h->at<int>(p.o_rcnt),
+                                  h->st);
+  }
+  return hipErrorInvalidValue;
+}
+
+int run_ops(spd_handle* h) {
+  for (const Op& op : h->ops) {
+    if (h->timing) {
+      hipEvent_t a, b;
+      HIPCHK(h, hipEventCreate(&a));
+      HIPCHK(h, hipEventCreate(&b));
+      HIPCHK(h, hipEventRecord(a, h->st));
+      HIPCHK(h, run_op(h, op));
+      HIPCHK(h, hipEventRecord(b, h->st));
+      h->ev.push_back(a);
+      h->ev.push_back(b);
+      h->ev_kind.push_back(op.kind);
+      h->ev_bytes.push_back(op.bytes);
+    } else {
+      HIPCHK(h, run_op(h, op));
+    }
+  }
+  return SPD_OK;
+}
+
+int collect_timing(spd_handle* h) {
+  for (size_t i = 0; i < h->ev_kind.size(); ++i) {
+    float ms = 0.f;
+    HIPCHK(h, hipEventElapsedTime(&ms, h->ev[2 * i], h->ev[2 * i + 1]));
+    h->kt_ms[h->ev_kind[i]] += ms;
+    h->kt_bytes[h->ev_kind[i]] += h->ev_bytes[i];
+    h->kt_count[h->ev_kind[i]] += 1;
+    (void)hipEventDestroy(h->ev[2 * i]);
+    (void)hipEventDestroy(h->ev[2 * i + 1]);
+  }
+  h->ev.clear();
+  h->ev_kind.clear();
+  h->ev_bytes.clear();
+  return SPD_OK;
+}
+
+// ---- the per-step plan -----------------------------------------------------------
+int build_step(spd_handle* h, DescWriter& dw) {
+  const Plan& p = h->p;
+  h->ops.clear();
+  h->pend_layers.clear();
+  const int newest = h->F.back().pos;
+  const int first = h->F.front().pos;
+  const int dpos = newest + 1;
+  const bool exited = h->F.front().stage == p.n - 1;
+  const int ex_pos = first;
+  const int v = ex_pos + 1;
+  const int M = newest - h->pdm_len + 1;
+  if (M < 1 || M > p.ring) return fail(h, SPD_E_STATE, "internal: PDM window out of range");
+  float* hring = h->at<float>(p.o_h);
+  float* anch = h->at<float>(p.o_anch);
+  float* hp = h->at<float>(p.o_hp);
+  float* X = h->at<float>(p.o_X);
+  float* qbuf = h->at<float>(p.o_qbuf);
+  float* attn = h->at<float>(p.o_attn);
+  float* act = h->at<float>(p.o_act);
+  float* logits = h->at<float>(p.o_logits);
+  float* qring = h->at<float>(p.o_qring);
+  float* qlse = h->at<float>(p.o_qlse);
+  const int kd = p.k * p.d;
+
+  // 1. embedding + PDM feature gather
+  EmbedGather eg{};
+  eg.embed = h->embed;
+  eg.tok_ring = h->at<int>(p.o_tok);
+  eg.h_ring = hring;
+  eg.anchors = anch;
+  eg.X = X;
+  eg.newest_slot = h->slot(newest);
+  eg.d = p.d; eg.k = p.k; eg.M = M;
+  for (int r = 0; r < M; ++r) {
+    const int x = h->pdm_len + r;
+    eg.row_slot[r] = h->slot(x);
+    int depth = p.L;
+    if (x >= first) depth = p.starts[h->F[x - first].stage];
+    int deepest = 0;
+    for (int i = 0; i < p.k; ++i)
+      if (p.anchors[i] <= depth) deepest = i;
+    for (int i = 0; i < p.k; ++i) {
+      int src;
+      if (p.anchors[i] <= depth) src = i;
+      else src = p.fill == SPD_FILL_CLAMP ? deepest : -1;
+      if (x == newest && src == 0) src = -2;   // the newest g0 is embedded in this launch
+      eg.src[r][i] = (signed char)src;
+    }
+  }
+  h->ops.push_back({OP_EMBED, dw.put(&eg, 1), M, 0, 0, 0.0});
+
+  // 2. PDM projection of the gathered features
+  {
+    std::vector<GemvProb> g{gemv(h->proj, p.d, kd, X, kd, M, EPI_STORE, hp, p.d, nullptr, 0, 0.f)};
+    const int nt = finish_tiles(g);
+    h->ops.push_back({OP_GEMV_PROJ, dw.put(g.data(), 1), 1, nt, 0, gemv_bytes(g, p.esz)});
+  }
+
+  // 3. sub-layers: every in-flight token at layer start(stage)+r, the PDM at layer r
+  const int n_inf = (int)h->F.size();
+  for (int r = 0; r < p.R; ++r) {
+    std::vector<GemvProb> qkv, o, gu, down;
+    std::vector<AttnProb> at;
+    const bool pdm_on = r < p.Ls;
+    const bool pdm_last = r == p.Ls - 1;
+    double kvb = 0;
+    for (int j = 0; j < n_inf; ++j) {
+      const Inflight f = h->F[j];
+      if (p.sizes[f.stage] <= r) continue;
+      const int l = p.starts[f.stage] + r;
+      const int s = h->slot(f.pos);
+      float* hv = hring + (size_t)s * p.d;
+      GemvProb q = gemv(h->W(l, T_QKV), p.qrows, p.d, hv, 0, 1, EPI_QKV, nullptr, 0,
+                        (const float*)h->W(l, T_ATTN_NORM), 0, p.eps);
+      q.aux = qbuf + (size_t)j * p.qo;
+      q.kv_k = h->kvK(l); q.kv_v = h->kvV(l);
+      q.pos0 = f.pos; q.hq = p.hq; q.hkv = p.hkv; q.hd = p.hd; q.max_ctx = p.max_ctx;
+      qkv.push_back(q);
+      AttnProb a{};
+      a.q = qbuf + (size_t)j * p.qo; a.out = attn + (size_t)j * p.qo;
+      a.K = h->kvK(l); a.V = h->kvV(l); a.len = f.pos + 1;
+      at.push_back(a);
+      kvb += 2.0 * (f.pos + 1) * p.hkv * p.hd * p.esz;
+      o.push_back(gemv(h->W(l, T_O), p.d, p.qo, attn + (size_t)j * p.qo, 0, 1, EPI_ADD, hv, 0,
+                       nullptr, 0, 0.f));
+      GemvProb g = gemv(h->W(l, T_GATE), p.F, p.d, hv, 0, 1, EPI_SWIGLU, act + (size_t)j * p.F, 0,
+                        (const float*)h->W(l, T_FFN_NORM), 0, p.eps);
+      g.W2 = h->W(l, T_UP);
+      gu.push_back(g);
+      GemvProb dn = gemv(h->W(l, T_DOWN), p.d, p.F, act + (size_t)j * p.F, 0, 1, EPI_ADD, hv, 0,
+                         nullptr, 0, 0.f);
+      for (int i = 0; i < p.k; ++i)
+        if (p.anchors[i] == l + 1) dn.aux = anch + ((size_t)s * p.k + i) * p.d;
+      down.push_back(dn);
+      h->pend_layers.push_back({l, f.pos});
+    }
+    if (pdm_on) {
+      const int base = p.n;   // PDM rows use decode rows n .. n + M - 1
+      GemvProb q = gemv(h->PW(r, T_QKV), p.qrows, p.d, hp, p.d, M, EPI_QKV, nullptr, 0,
+                        (const float*)h->PW(r, T_ATTN_NORM), 0, p.eps);
+      q.aux = qbuf + (size_t)base * p.qo; q.aux_stride = p.qo;
+      q.kv_k = h->pK(r); q.kv_v = h->pV(r);
+      q.pos0 = h->pdm_len; q.hq = p.hq; q.hkv = p.hkv; q.hd = p.hd; q.max_ctx = p.max_ctx;
+      qkv.push_back(q);
+      for (int m = 0; m < M; ++m) {
+        AttnProb a{};
+        a.q = qbuf + (size_t)(base + m) * p.qo; a.out = attn + (size_t)(base + m) * p.qo;
+        a.K = h->pK(r); a.V = h->pV(r); a.len = h->pdm_len + m + 1;
+        at.push_back(a);
+      }
+      kvb += 2.0 * (h->pdm_len + M) * p.hkv * p.hd * p.esz;
+      // the last PDM layer only feeds the LM head: its O / FFN run on the newest row alone
+      const int r0 = pdm_last ? M - 1 : 0, nr = pdm_last ? 1 : M;
+      float* hrow = hp + (size_t)r0 * p.d;
+      o.push_back(gemv(h->PW(r, T_O), p.d, p.qo, attn + (size_t)(base + r0) * p.qo, p.qo, nr,
+                       EPI_ADD, hrow, p.d, nullptr, 0, 0.f));
+      GemvProb g = gemv(h->PW(r, T_GATE), p.F, p.d, hrow, p.d, nr, EPI_SWIGLU,
+                        act + (size_t)(base + r0) * p.F, p.F, (const float*)h->PW(r, T_FFN_NORM),
+                        0, p.eps);
+      g.W2 = h->PW(r, T_UP);
+      gu.push_back(g);
+      down.push_back(gemv(h->PW(r, T_DOWN), p.d, p.F, act + (size_t)(base + r0) * p.F, p.F, nr,
+                          EPI_ADD, hrow, p.d, nullptr, 0, 0.f));
+    }
+    if (qkv.empty()) continue;
+    int nt = finish_tiles(qkv);
+    h->ops.push_back({OP_GEMV_QKV, dw.put(qkv.data(), (int)qkv.size()), (int)qkv.size(), nt, 0,
+                      gemv_bytes(qkv, p.esz)});
+    const int split = attn_split(p, at);
+    nt = finish_attn(p, at, split);
+    h->ops.push_back({OP_ATTN, dw.put(at.data(), (int)at.size()), (int)at.size(), nt, split, kvb});
+    nt = finish_tiles(o);
+    h->ops.push_back({OP_GEMV_O, dw.put(o.data(), (int)o.size()), (int)o.size(), nt, 0,
+                      gemv_bytes(o, p.esz)});
+    nt = finish_tiles(gu);
+    h->ops.push_back({OP_GEMV_GU, dw.put(gu.data(), (int)gu.size()), (int)gu.size(), nt, 0,
+                      gemv_bytes(gu, p.esz)});
+    nt = finish_tiles(down);
+    h->ops.push_back({OP_GEMV_DOWN, dw.put(down.data(), (int)down.size()), (int)down.size(), nt,
+                      0, gemv_bytes(down, p.esz)});
+  }
+
+  // 4. one sweep of the tied LM head: the exiting token's row and the PDM's newest row
+  float* qnew = qring + (size_t)h->slot(dpos) * p.V;
+  float* hnew = hp + (size_t)(M - 1) * p.d;
+  {
+    GemvProb g;
+    if (exited) {
+      float* hx = hring + (size_t)h->slot(ex_pos) * p.d;
+      g = gemv(h->head, p.V, p.d, hx, float_gap(hnew, hx), 2, EPI_STORE, logits,
+               float_gap(qnew, logits), h->final_norm, float_gap(h->pdm_final_norm, h->final_norm),
+               p.eps);
+    } else {
+      g = gemv(h->head, p.V, p.d, hnew, 0, 1, EPI_STORE, qnew, 0, h->pdm_final_norm, 0, p.eps);
+    }
+    std::vector<GemvProb> gv{g};
+    const int nt = finish_tiles(gv);
+    h->ops.push_back({OP_GEMV_HEAD, dw.put(gv.data(), 1), 1, nt, 0, gemv_bytes(gv, p.esz)});
+  }
+  const bool sampled = h->temp > 0.f;
+  const float inv_t = sampled ? 1.f / h->temp : 1.f;
+  VocabDesc vd{};
+  vd.logits[0] = logits; vd.logits[1] = qnew;
+  vd.active[0] = exited ? 1 : 0; vd.active[1] = 1;
+  vd.gumbel_stream[1] = sampled ? RNG_DRAFT : 0;
+  vd.gumbel_pos[1] = dpos;
+  vd.V = p.V; vd.nblocks = kVocabBlocks; vd.inv_temp = inv_t; vd.sampled = sampled;
+  vd.seed = h->seed;
+  h->ops.push_back({OP_VOCAB, dw.put(&vd, 1), 1, kVocabBlocks, 0, 0.0});
+  FinalizeDesc fd{};
+  fd.mode = 0; fd.exited = exited; fd.single = n_inf == 1; fd.v = v; fd.dpos = dpos;
+  fd.ring = p.ring; fd.V = p.V; fd.nblocks = kVocabBlocks; fd.temp = h->temp; fd.inv_temp = inv_t;
+  fd.seed = h->seed; fd.forced_mode = h->forced_mode; fd.forced_p = h->forced_p;
+  fd.forced_base = h->P0; fd.forced_len = (int)h->forced_ref.size();
+  fd.forced_ref = h->at<int>(p.o_forced);
+  fd.zt = logits;
+  fd.zq_v = qring + (size_t)h->slot(v) * p.V;
+  fd.lse_q_v = qlse + h->slot(v);
+  fd.lse_q_new = qlse + h->slot(dpos);
+  fd.tok_ring = h->at<int>(p.o_tok);
+  fd.verdict = h->at<Verdict>(p.o_verdict);
+  fd.part = h->at<VocabPartial>(p.o_part);
+  const size_t foff = dw.put(&fd, 1);
+  h->ops.push_back({OP_FINAL, foff, 1, 1, 0, 0.0});
+  if (sampled && exited) h->ops.push_back({OP_RESID, foff, 1, kVocabBlocks, 0, 0.0});
+  h->pend_exit = exited;
+  h->pend_v = v;
+  h->pend_dpos = dpos;
+  h->pend_newest = newest;
+  return SPD_OK;
+}
+
+}  // namespace
+
+// ======================================================================================
+extern "C" {
+
+size_t spd_workspace_bytes(const spd_model_config* cfg) {
+  Plan p;
+  std::string err;
+  if (!plan_config(cfg, p, err)) return 0;
+  return p.total;
+}
+
+const char* spd_init_error(void) { return g_init_error.c_str(); }
+
+int spd_init(const spd_model_config* cfg, const spd_weights* w, const spd_sampling* s,
+             void* d_workspace, size_t ws_bytes, void* hip_stream, spd_handle** out) {
+  g_init_error.clear();
+  if (!out) { g_init_error = "null out"; return SPD_E_ARG; }
+  *out = nullptr;
+  Plan p;
+  std::string err;
+  if (!cfg || !w || !s || !d_workspace) { g_init_error = "null argument"; return SPD_E_ARG; }
+  if (!plan_config(cfg, p, err)) { g_init_error = err; return SPD_E_CONFIG; }
+  if (ws_bytes < p.total) {
+    g_init_error = "workspace too small: need " + std::to_string(p.total) + " bytes";
+    return SPD_E_CAPACITY;
+  }
+  if (!(s->temperature >= 0.f)) { g_init_error = "temperature must be >= 0"; return SPD_E_ARG; }
+  if (s->top_p < 1.f) { g_init_error = "top_p < 1 is not supported by the GPU path"; return SPD_E_CONFIG; }
+  if (s->forced_mode && s->temperature != 0.f) {
+    g_init_error = "forced mode needs temperature 0";
+    return SPD_E_CONFIG;
+  }
+  if (s->forced_mode && (s->forced_ref_len < 0 || (s->forced_ref_len > 0 && !s->forced_ref))) {
+    g_init_error = "forced mode needs forced_ref";
+    return SPD_E_ARG;
+  }
+  if (!w->embed || !w->lm_head || !w->final_norm || !w->layers || !w->pdm_proj ||
+      !w->pdm_layers || !w->pdm_final_norm) {
+    g_init_error = "null weight pointer";
+    return SPD_E_ARG;
+  }
+  spd_handle* h = new spd_handle();
+  h->p = p;
+  h->embed = w->embed; h->head = w->lm_head; h->final_norm = w->final_norm;
+  h->proj = w->pdm_proj; h->pdm_final_norm = w->pdm_final_norm;
+  h->lw.assign(w->layers, w->layers + (size_t)p.L * kTensorsPerLayer);
+  h->pw.assign(w->pdm_layers, w->pdm_layers + (size_t)p.Ls * kTensorsPerLayer);
+  for (auto ptr : h->lw)
+    if (!ptr) { g_init_error = "null layer weight"; delete h; return SPD_E_ARG; }
+  for (auto ptr : h->pw)
+    if (!ptr) { g_init_error = "null PDM layer weight"; delete h; return SPD_E_ARG; }
+  h->temp = s->temperature; h->top_p = s->top_p; h->seed = s->seed;
+  h->forced_mode = s->forced_mode; h->forced_p = s->forced_p;
+  if (s->forced_mode && s->forced_ref_len > 0)
+    h->forced_ref.assign(s->forced_ref, s->forced_ref + s->forced_ref_len);
+  if ((int)h->forced_ref.size() > p.max_ctx) h->forced_ref.resize(p.max_ctx);
+  h->ws = static_cast<char*>(d_workspace);
+  h->st = static_cast<hipStream_t>(hip_stream);
+  h->kv_len.assign(p.L, 0);
+  auto dev_fail = [&](hipError_t e, const char* what) {
+    g_init_error = std::string(what) + ": " + hipGetErrorString(e);
+    if (h->h_desc) (void)hipHostFree(h->h_desc);
+    if (h->h_verdict) (void)hipHostFree(h->h_verdict);
+    delete h;
+    return SPD_E_DEVICE;
+  };
+  hipError_t e;
+  if ((e = hipHostMalloc((void**)&h->h_desc, kDescBytes, hipHostMallocDefault)) != hipSuccess)
+    return dev_fail(e, "hipHostMalloc");
+  if ((e = hipHostMalloc((void**)&h->h_verdict, sizeof(Verdict), hipHostMallocDefault)) != hipSuccess)
+    return dev_fail(e, "hipHostMalloc");
+  std::vector<float2> rope;
+  fill_rope(p, rope);
+  if ((e = hipMemcpyAsync(h->ws + p.o_rope, rope.data(), rope.size() * sizeof(float2),
+                          hipMemcpyHostToDevice, h->st)) != hipSuccess)
+    return dev_fail(e, "hipMemcpyAsync(rope)");
+  // arrival counters start at zero and are reset by their last user
+  if ((e = hipMemsetAsync(h->ws + p.o_acnt, 0, (size_t)(p.n + p.ring) * p.hkv * 4, h->st)) != hipSuccess)
+    return dev_fail(e, "hipMemsetAsync");
+  if ((e = hipMemsetAsync(h->ws + p.o_rcnt, 0, 64, h->st)) != hipSuccess)
+    return dev_fail(e, "hipMemsetAsync");
+  if ((e = hipStreamSynchronize(h->st)) != hipSuccess) return dev_fail(e, "hipStreamSynchronize");
+  *out = h;
+  return SPD_OK;
+}
+
+int spd_prefill(spd_handle* h, const int32_t* prompt, int32_t len, int32_t* first_token) {
+  if (!h) return SPD_E_ARG;
+  h->err.clear();
+  if (h->state != spd_handle::S_INIT) return fail(h, SPD_E_STATE, "already prefilled (spd_reset first)");
+  if (!prompt || len < 1) return fail(h, SPD_E_ARG, "empty prompt");
+  const Plan& p = h->p;
+  if (len >= p.max_ctx) return fail(h, SPD_E_CAPACITY, "prompt does not fit max_ctx");
+  for (int i = 0; i < len; ++i)
+    if (prompt[i] < 0 || prompt[i] >= p.V) return fail(h, SPD_E_ARG, "token id out of range");
+  hipStream_t st = h->st;
+  int* toks = h->at<int>(p.o_ptok);
+  // prompt and forced reference share one staging copy
+  std::memcpy(h->h_desc, prompt, (size_t)len * 4);
+  HIPCHK(h, hipMemcpyAsync(toks, h->h_desc, (size_t)len * 4, hipMemcpyHostToDevice, st));
+  HIPCHK(h, hipStreamSynchronize(st));
+  if (!h->forced_ref.empty()) {
+    std::memcpy(h->h_desc, h->forced_ref.data(), h->forced_ref.size() * 4);
+    HIPCHK(h, hipMemcpyAsync(h->ws + p.o_forced, h->h_desc, h->forced_ref.size() * 4,
+                             hipMemcpyHostToDevice, st));
+    HIPCHK(h, hipStreamSynchronize(st));
+  }
+  const bool bf = p.bf16;
+  float* H = h->at<float>(p.o_pH);
+  float* A = h->at<float>(p.o_pA);
+  float* QKV = h->at<float>(p.o_pQKV);
+  float* O = h->at<float>(p.o_pO);
+  float* Gb = h->at<float>(p.o_pG);
+  float* Ub = h->at<float>(p.o_pU);
+  float* Z = h->at<float>(p.o_pZ);
+  float* AN = h->at<float>(p.o_panch);
+  const float2* rope = h->at<float2>(p.o_rope);
+  const int CH = kPrefillChunk;
+  const int kd = p.k * p.d;
+  // one decoder layer over P rows of the residual Rb (fp32 activations throughout)
+  auto layer = [&](float* Rb, int P, int pos0, const void* const* wt, void* Kc, void* Vc) -> int {
+    HIPCHK(h, launch_rmsnorm_rows(Rb, p.d, (const float*)wt[T_ATTN_NORM], A, p.d, P, p.d, p.eps, false, st));
+    HIPCHK(h, launch_gemm(A, p.d, wt[T_QKV], QKV, p.qrows, P, p.qrows, p.d, false, bf, st));
+    HIPCHK(h, launch_rope_kv(QKV, p.qrows, Kc, Vc, rope, pos0, P, p.hq, p.hkv, p.hd, p.max_ctx, bf, st));
+    HIPCHK(h, launch_attention_prefill(QKV, p.qrows, O, p.qo, Kc, Vc, pos0, P, bf, p.hq, p.hkv,
+                                       p.hd, p.max_ctx, st));
+    HIPCHK(h, launch_gemm(O, p.qo, wt[T_O], Rb, p.d, P, p.d, p.qo, true, bf, st));
+    HIPCHK(h, launch_rmsnorm_rows(Rb, p.d, (const float*)wt[T_FFN_NORM], A, p.d, P, p.d, p.eps, false, st));
+    HIPCHK(h, launch_gemm(A, p.d, wt[T_GATE], Gb, p.F, P, p.F, p.d, false, bf, st));
+    HIPCHK(h, launch_gemm(A, p.d, wt[T_UP], Ub, p.F, P, p.F, p.d, false, bf, st));
+    HIPCHK(h, launch_swiglu_rows(Gb, Ub, p.F, A, p.F, P, p.F, false, st));
+    HIPCHK(h, launch_gemm(A, p.F, wt[T_DOWN], Rb, p.d, P, p.d, p.F, true, bf, st));
+    return SPD_OK;
+  };
+  for (int c0 = 0; c0 < len; c0 += CH) {
+    const int P = std::min(CH, len - c0);
+    HIPCHK(h, launch_embed_rows(h->embed, toks + c0, H, P, p.d, bf, st));
+    HIPCHK(h, launch_copy_rows(H, p.d, AN, p.d, P, p.d, st));   // anchor 0: the embedding
+    for (int l = 0; l < p.L; ++l) {
+      const int rc = layer(H, P, c0, &h->lw[(size_t)l * kTensorsPerLayer], h->kvK(l), h->kvV(l));
+      if (rc != SPD_OK) return rc;
+      for (int i = 1; i < p.k; ++i)
+        if (p.anchors[i] == l + 1)
+          HIPCHK(h, launch_copy_rows(H, p.d, AN + (size_t)i * CH * p.d, p.d, P, p.d, st));
+    }
+    // the verified prefix's depth-maximised PDM features: every anchor, concatenated
+    for (int i = 0; i < p.k; ++i)
+      HIPCHK(h, launch_copy_rows(AN + (size_t)i * CH * p.d, p.d, A + (size_t)i * p.d, kd, P, p.d, st));
+    HIPCHK(h, launch_gemm(A, kd, h->proj, Z, p.d, P, p.d, kd, false, bf, st));
+    for (int r = 0; r < p.Ls; ++r) {
+      const int rc = layer(Z, P, c0, &h->pw[(size_t)r * kTensorsPerLayer], h->pK(r), h->pV(r));
+      if (rc != SPD_OK) return rc;
+    }
+    if (c0 + P == len) {
+      // first token from the last prompt row (fp32 input to the head, as in decode)
+      DescWriter dw{h->h_desc};
+      std::vector<GemvProb> g{gemv(h->head, p.V, p.d, H + (size_t)(P - 1) * p.d, 0, 1, EPI_STORE,
+                                   h->at<float>(p.o_logits), 0, h->final_norm, 0, p.eps)};
+      const int nt = finish_tiles(g);
+      const size_t go = dw.put(g.data(), 1);
+      const bool sampled = h->temp > 0.f;
+      VocabDesc vd{};
+      vd.logits[0] = h->at<float>(p.o_logits); vd.logits[1] = nullptr;
+      vd.active[0] = 1; vd.active[1] = 0;
+      vd.gumbel_stream[0] = sampled ? RNG_FIRST : 0; vd.gumbel_pos[0] = len;
+      vd.V = p.V; vd.nblocks = kVocabBlocks; vd.inv_temp = sampled ? 1.f / h->temp : 1.f;
+      vd.sampled = sampled; vd.seed = h->seed;
+      const size_t vo = dw.put(&vd, 1);
+      FinalizeDesc fd{};
+      fd.mode = 1; fd.dpos = len; fd.ring = p.ring; fd.V = p.V; fd.nblocks = kVocabBlocks;
+      fd.temp = h->temp; fd.inv_temp = vd.inv_temp; fd.seed = h->seed;
+      fd.tok_ring = h->at<int>(p.o_tok); fd.verdict = h->at<Verdict>(p.o_verdict);
+      fd.part = h->at<VocabPartial>(p.o_part);
+      const size_t fo = dw.put(&fd, 1);
+      char* d = h->ws + p.o_desc;
+      HIPCHK(h, hipMemcpyAsync(d, h->h_desc, dw.used, hipMemcpyHostToDevice, st));
+      HIPCHK(h, launch_gemv(reinterpret_cast<const GemvProb*>(d + go), 1, nt, bf, rope, st));
+      HIPCHK(h, launch_vocab_stats(reinterpret_cast<const VocabDesc*>(d + vo), kVocabBlocks,
+                                   h->at<VocabPartial>(p.o_part), st));
+      HIPCHK(h, launch_finalize(reinterpret_cast<const FinalizeDesc*>(d + fo), st));
+      HIPCHK(h, hipMemcpyAsync(h->h_verdict, h->at<Verdict>(p.o_verdict), sizeof(Verdict),
+                               hipMemcpyDeviceToHost, st));
+      // the exiting-row residual of the last prompt position (debug view)
+      HIPCHK(h, launch_copy_rows(H + (size_t)(P - 1) * p.d, p.d, h->at<float>(p.o_h) +
+                                 (size_t)h->slot(len - 1) * p.d, p.d, 1, p.d, st));
+    }
+  }
+  HIPCHK(h, hipStreamSynchronize(st));
+  const int t0 = h->h_verdict->first_token;
+  if (first_token) *first_token = t0;
+  h->P0 = len;
+  h->F.clear();
+  h->F.push_back({len, 0});
+  h->pdm_len = len;
+  std::fill(h->kv_len.begin(), h->kv_len.end(), len);
+  h->N = h->K = h->acc = h->rej = 0;
+  h->state = spd_handle::S_READY;
+  return SPD_OK;
+}
+
+int spd_step(spd_handle* h) {
+  if (!h) return SPD_E_ARG;
+  h->err.clear();
+  if (h->state != spd_handle::S_READY)
+    return fail(h, SPD_E_STATE, h->state == spd_handle::S_INIT ? "no prefill" : "a step is pending");
+  const int newest = h->F.back().pos;
+  if (newest >= h->p.max_ctx) return fail(h, SPD_E_CAPACITY, "newest position reached max_ctx");
+  DescWriter dw{h->h_desc};
+  int rc = build_step(h, dw);
+  if (rc != SPD_OK) return rc;
+  if (dw.used > kDescBytes) return fail(h, SPD_E_CAPACITY, "internal: descriptor block overflow");
+  HIPCHK(h, hipMemcpyAsync(h->ws + h->p.o_desc, h->h_desc, dw.used, hipMemcpyHostToDevice, h->st));
+  rc = run_ops(h);
+  if (rc != SPD_OK) return rc;
+  HIPCHK(h, hipMemcpyAsync(h->h_verdict, h->at<Verdict>(h->p.o_verdict), sizeof(Verdict),
+                           hipMemcpyDeviceToHost, h->st));
+  h->state = spd_handle::S_PENDING;
+  return SPD_OK;
+}
+
+int spd_verify_commit(spd_handle* h, spd_commit* out) {
+  if (!h) return SPD_E_ARG;
+  h->err.clear();
+  if (h->state != spd_handle::S_PENDING) return fail(h, SPD_E_STATE, "no pending step");
+  HIPCHK(h, hipStreamSynchronize(h->st));
+  if (h->timing) {
+    const int rc = collect_timing(h);
+    if (rc != SPD_OK) return rc;
+  }
+  const Verdict vd = *h->h_verdict;
+  const Plan& p = h->p;
+  h->K += 1;
+  for (auto& lp : h->pend_layers) h->kv_len[lp.first] = lp.second + 1;
+  h->pdm_len = std::max(h->pdm_len, h->F.front().pos);
+  for (auto& f : h->F) f.stage += 1;
+  spd_commit c{};
+  c.newest = h->pend_newest;
+  c.new_draft = vd.draft;
+  c.flags = vd.flags;
+  if (h->pend_exit) {
+    const int v = h->pend_v;
+    h->N += 1;
+    c.verified = 1;
+    c.position = v;
+    c.token = vd.committed;
+    c.accepted = vd.accepted;
+    c.draft_token = vd.verified_draft;
+    if (vd.accepted) {
+      h->acc += 1;
+      h->F.pop_front();
+      h->F.push_back({h->pend_dpos, 0});
+    } else {
+      h->rej += 1;
+      for (auto& k : h->kv_len) k = std::min(k, v);
+      h->F.clear();
+      h->F.push_back({v, 0});
+    }
+  } else {
+    h->F.push_back({h->pend_dpos, 0});
+  }
+  (void)p;
+  c.committed_total = (int)h->N;
+  c.inflight = (int)h->F.size();
+  if (out) *out = c;
+  h->state = spd_handle::S_READY;
+  return SPD_OK;
+}
+
+int spd_get_stats(const spd_handle* h, spd_stats* out) {
+  if (!h || !out) return SPD_E_ARG;
+  out->K = h->K; out->N = h->N; out->accepted = h->acc; out->rejected = h->rej;
+  out->alpha = h->K ? (double)h->N / (double)h->K : 0.0;
+  out->s0 = out->alpha * h->p.n;
+  return SPD_OK;
+}
+
+int spd_get_kv_lens(const spd_handle* h, int32_t* per_layer, int32_t* pdm_len) {
+  if (!h) return SPD_E_ARG;
+  if (per_layer)
+    for (int l = 0; l < h->p.L; ++l) per_layer[l] = h->kv_len[l];
+  if (pdm_len) *pdm_len = h->pdm_len;
+  return SPD_OK;
+}
+
+size_t spd_debug_size(const spd_handle* h, int32_t what) {
+  if (!h) return 0;
+  const Plan& p = h->p;
+  switch (what) {
+    case SPD_DBG_TARGET_LOGITS: case SPD_DBG_DRAFT_LOGITS: return (size_t)p.V * 4;
+    case SPD_DBG_H_RING: case SPD_DBG_PDM_ROWS: return (size_t)p.ring * p.d * 4;
+    case SPD_DBG_ANCHORS: return (size_t)p.ring * p.k * p.d * 4;
+    case SPD_DBG_TARGET_KV: return (size_t)p.nsoft * p.kv_layer_bytes;
+    case SPD_DBG_PDM_KV: return (size_t)p.Ls * p.kv_layer_bytes;
+    case SPD_DBG_TOKENS: return (size_t)p.ring * 4;
+  }
+  return 0;
+}
+
+int spd_debug_copy(const spd_handle* hc, int32_t what, void* dst, size_t bytes) {
+  spd_handle* h = const_cast<spd_handle*>(hc);
+  if (!h || !dst) return SPD_E_ARG;
+  const Plan& p = h->p;
+  const size_t need = spd_debug_size(h, what);
+  if (need == 0 || bytes != need) return fail(h, SPD_E_ARG, "bad debug buffer or size");
+  const char* src = nullptr;
+  switch (what) {
+    case SPD_DBG_TARGET_LOGITS: src = h->ws + p.o_logits; break;
+    case SPD_DBG_DRAFT_LOGITS: {
+      // the most recent draft: position newest + 1 of the last step
+      const int dpos = h->state == spd_handle::S_INIT ? 0 : h->pend_dpos;
+      src = h->ws + p.o_qring + (size_t)h->slot(dpos) * p.V * 4;
+      break;
+    }
+    case SPD_DBG_H_RING: src = h->ws + p.o_h; break;
+    case SPD_DBG_PDM_ROWS: src = h->ws + p.o_hp; break;
+    case SPD_DBG_ANCHORS: src = h->ws + p.o_anch; break;
+    case SPD_DBG_TARGET_KV: src = h->ws + p.o_kv; break;
+    case SPD_DBG_PDM_KV: src = h->ws + p.o_pkv; break;
+    case SPD_DBG_TOKENS: src = h->ws + p.o_tok; break;
+  }
+  HIPCHK(h, hipStreamSynchronize(h->st));
+  HIPCHK(h, hipMemcpy(dst, src, bytes, hipMemcpyDeviceToHost));
+  return SPD_OK;
+}
+
+int spd_reset(spd_handle* h) {
+  if (!h) return SPD_E_ARG;
+  if (h->state == spd_handle::S_PENDING) HIPCHK(h, hipStreamSynchronize(h->st));
+  h->state = spd_handle::S_INIT;
+  h->F.clear();
+  h->pdm_len = 0;
+  std::fill(h->kv_len.begin(), h->kv_len.end(), 0);
+  h->N = h->K = h->acc = h->rej = 0;
+  h->P0 = 0;
+  h->pend_dpos = 0;
+  return SPD_OK;
+}
+
+const char* spd_last_error(const spd_handle* h) { return h ? h->err.c_str() : "null handle"; }
+
+void spd_destroy(spd_handle* h) {
+  if (!h) return;
+  (void)hipStreamSynchronize(h->st);
+  for (auto e : h->ev) (void)hipEventDestroy(e);
+  if (h->h_desc) (void)hipHostFree(h->h_desc);
+  if (h->h_verdict) (void)hipHostFree(h->h_verdict);
+  delete h;
+}
+
+// ---- measurement -------------------------------------------------------------------
+int spd_timing_enable(spd_handle* h, int on) {
+  if (!h) return SPD_E_ARG;
+  if (h->state == spd_handle::S_PENDING) return fail(h, SPD_E_STATE, "a step is pending");
+  h->timing = on != 0;
+  for (int i = 0; i < OP_NKINDS; ++i) { h->kt_ms[i] = 0; h->kt_bytes[i] = 0; h->kt_count[i] = 0; }
+  return SPD_OK;
+}
+
+int spd_timing_read(const spd_handle* h, int32_t kind, int64_t* count, double* total_ms,
+                    double* bytes) {
+  if (!h || kind < 0 || kind >= OP_NKINDS) return SPD_E_ARG;
+  if (count) *count = h->kt_count[kind];
+  if (total_ms) *total_ms = h->kt_ms[kind];
+  if (bytes) *bytes = h->kt_bytes[kind];
+  return SPD_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,223 @@
+// Internal declarations shared by the host scheduler and the CDNA4 kernels.
+// Descriptor structs live in device memory (uploaded once per step) and are
+// read by every workgroup of a grouped launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace spd {
+
+constexpr int kMaxStages = 16;          // n
+constexpr int kMaxRows = kMaxStages + 1;  // PDM rows per step: n + 1
+constexpr int kMaxAnchors = 8;          // k
+constexpr int kWaves = 4;               // waves per GEMV workgroup
+constexpr int kRowsSingle = 8;          // weight rows per wave, one input vector
+constexpr int kRowsMulti = 4;           // weight rows per wave, several input vectors
+constexpr int kMaxVec = kMaxRows;       // input vectors of one GEMV problem
+constexpr int kAttnTile = 64;           // keys per attention tile
+constexpr int kVocabBlock = 1024;       // threads of the vocabulary reduction blocks
+constexpr float kNearTie = 1e-3f;
+
+// GEMV epilogues.
+enum Epi : int {
+  EPI_STORE = 0,   // y[v][row] = acc
+  EPI_ADD = 1,     // y[v][row] += acc; aux (if set): aux[v][row] = new y (anchor capture)
+  EPI_SWIGLU = 2,  // y[v][row] = silu(W row) * (W2 row)
+  EPI_QKV = 3,     // rotate q,k pairs (RoPE at pos0 + v); q -> aux, k,v -> KV cache
+};
+
+// One matrix times nvec vectors, y = epilogue(W * (x ⊙ gain) * rms_scale(x)).
+struct GemvProb {
+  const void* W;       // [rows][K] in the weight dtype
+  const void* W2;      // SWIGLU: the up matrix (W is the gate)
+  const float* x;      // vector v at x + v * x_stride
+  const float* gain;   // RMSNorm gain of vector v at gain + v * gain_stride; null: no norm
+  float* y;            // output of vector v at y + v * y_stride
+  float* aux;          // EPI_QKV: rotated q; EPI_ADD: optional copy of the new residual
+  void* kv_k;          // EPI_QKV: K cache of this layer [hkv][max_ctx][hd]
+  void* kv_v;          // EPI_QKV: V cache of this layer
+  long long x_stride, gain_stride, y_stride, aux_stride;
+  float eps;
+  int rows;            // matrix rows (SWIGLU: rows of each of W and W2)
+  int K;
+  int nvec;
+  int epi;
+  int pos0;            // EPI_QKV: position of vector 0
+  int tile0;           // first workgroup of this problem in the launch
+  int ntiles;
+  int hq, hkv, hd, max_ctx;
+  int pad[2];
+};
+
+// Attention over one layer's KV cache for a group of query rows.
+// Decode mode: one query per problem, keys 0..len-1.
+struct AttnProb {
+  const float* q;      // [hq][hd], rotated
+  float* out;          // [hq][hd]
+  const void* K;       // [hkv][max_ctx][hd]
+  const void* V;
+  int len;             // keys 0..len-1
+  int tile0;           // first workgroup: tile0 + g * nsplit + s
+  int nsplit;
+  int slot;            // index of this problem's partial/counter area
+};
+
+// Linear-attention (recurrent) step for one token at one layer.
+struct LinProb {
+  const float* qkv;    // [3][H][hd]: q, k, v of this token
+  float* out;          // [H][hd]
+  const float* s_prev; // state after the previous position [H][hd][hd]
+  float* s_next;       // state after this position
+};
+
+// The embedding of the stage-0 token and the PDM feature gather (anchor clamp).
+struct EmbedGather {
+  const void* embed;          // [V][d]
+  const int* tok_ring;        // token of position p at tok_ring[p % ring]
+  float* h_ring;              // [ring][d]
+  float* anchors;             // [ring][k][d]
+  float* X;                   // [M][k * d] gathered PDM features
+  int newest_slot;
+  int d, k, M;
+  int row_slot[kMaxRows];     // ring slot of PDM row r
+  signed char src[kMaxRows][kMaxAnchors];  // anchor index feeding segment i; -1: zeros; -2: newest g0
+};
+
+// The vocabulary pass: statistics of up to two logit rows (target, draft).
+struct VocabDesc {
+  const float* logits[2];     // row 0: target head output, row 1: draft (PDM) head output
+  int active[2];
+  int gumbel_stream[2];       // 0: none
+  int gumbel_pos[2];
+  int V;
+  int nblocks;
+  float inv_temp;             // 1/T (T > 0) else 1
+  int sampled;                // T > 0
+  unsigned long long seed;
+};
+
+struct VocabPartial {
+  float max, second;          // raw logit max and runner-up
+  int arg;
+  float sum;                  // sum exp(z/T - max/T)
+  float gmax, gsecond;        // Gumbel-perturbed z/T + G
+  int garg;
+  int pad;
+};
+
+// Device-side verdict of one step, copied to pinned host memory at its end.
+struct Verdict {
+  int draft;            // this step's draft (position newest + 1)
+  int committed;        // y
+  int accepted;
+  int flags;            // bit 0 verify near-tie, bit 1 draft near-tie
+  int verified_draft;
+  int exited;
+  int need_residual;
+  int first_token;      // prefill: first generated token
+  float lse_t, lse_q, p_d, q_d;
+};
+
+struct FinalizeDesc {
+  int mode;             // 0: step, 1: prefill (first token)
+  int exited;
+  int single;           // the exiting token is the only one in flight (v = newest + 1)
+  int v;                // verified position
+  int dpos;             // position of this step's draft
+  int ring;             // n + 1
+  int V;
+  int nblocks;
+  float temp;
+  float inv_temp;
+  unsigned long long seed;
+  int forced_mode;
+  float forced_p;
+  int forced_base;      // position of forced_ref[0]
+  int forced_len;
+  const int* forced_ref;
+  const float* zt;      // target logits (row 0)
+  const float* zq_v;    // stored draft logits of the draft at v
+  const float* lse_q_v; // its log-sum-exp (of z/T)
+  float* lse_q_new;     // where to store this draft's log-sum-exp
+  int* tok_ring;
+  Verdict* verdict;
+  const VocabPartial* part;  // [2][nblocks]
+};
+
+enum RngStream : int { RNG_DRAFT = 1, RNG_ACC = 2, RNG_RES = 3, RNG_FORCE = 4, RNG_FIRST = 5 };
+
+// ---- small device helpers ------------------------------------------------
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float -> bfloat16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// SplitMix64 output function (Steele, Lea & Flood 2014).
+__device__ __forceinline__ unsigned long long mix64(unsigned long long z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// Counter-based uniform in (0,1): a pure function of (seed, stream, pos, idx).
+__device__ __forceinline__ float rng_uniform(unsigned long long seed, int stream, int pos,
+                                             unsigned long long idx) {
+  unsigned long long k0 = mix64(seed);
+  unsigned long long key = ((unsigned long long)(unsigned)stream << 32) | (unsigned)pos;
+  unsigned long long k1 = mix64(k0 ^ key);
+  unsigned long long x = mix64(k1 + idx * 0x9E3779B97F4A7C15ull);
+  return ((float)(x >> 41) + 0.5f) * (1.0f / 8388608.0f);
+}
+
+__device__ __forceinline__ float gumbel_of(float u) { return -logf(-logf(u)); }
+
+}  // namespace spd
+
+// ---- kernel launchers (one per .hip file) -----------------------------------
+namespace spd {
+hipError_t launch_gemv(const GemvProb* d_probs, int nprob, int ntiles, bool bf16,
+                       const float2* rope, hipStream_t st);
+hipError_t launch_attention(const AttnProb* d_probs, int nprob, int ntiles, bool bf16,
+                            int hq, int hkv, int hd, int max_ctx, int split_len,
+                            float* partials, int* counters, hipStream_t st);
+hipError_t launch_attention_prefill(const float* q, int q_stride, float* out, int out_stride,
+                                    const void* K, const void* V, int pos0, int P, bool bf16,
+                                    int hq, int hkv, int hd, int max_ctx, hipStream_t st);
+hipError_t launch_linear_step(const LinProb* d_probs, int nprob, int H, int hd, float eps,
+                              hipStream_t st);
+hipError_t launch_linear_scan(const float* qkv, int qkv_stride, float* out, int out_stride,
+                              const float* s_in, float* s_out, int P, int H, int hd, float eps,
+                              hipStream_t st);
+hipError_t launch_embed_gather(const EmbedGather* d_desc, int M, int k, int d, bool bf16,
+                               hipStream_t st);
+hipError_t launch_vocab_stats(const VocabDesc* d_desc, int nblocks, VocabPartial* part,
+                              hipStream_t st);
+hipError_t launch_finalize(const FinalizeDesc* d_desc, hipStream_t st);
+hipError_t launch_residual_impl(const FinalizeDesc* d_desc, VocabPartial* part, int nblocks,
+                                int* counter, hipStream_t st);
+// prefill helpers
+hipError_t launch_embed_rows(const void* embed, const int* toks, float* H, int P, int d,
+                             bool bf16, hipStream_t st);
+hipError_t launch_rmsnorm_rows(const float* H, int h_stride, const float* gain, void* out,
+                               int out_stride, int P, int d, float eps, bool out_bf16,
+                               hipStream_t st);
+hipError_t launch_round_rows(const float* X, int x_stride, void* out, int out_stride, int P,
+                             int n, bool out_bf16, hipStream_t st);
+hipError_t launch_rope_kv(float* QKV, int stride, void* Kc, void* Vc, const float2* rope,
+                          int pos0, int P, int hq, int hkv, int hd, int max_ctx, bool bf16,
+                          hipStream_t st);
+hipError_t launch_swiglu_rows(const float* G, const float* U, int stride, void* out,
+                              int out_stride, int P, int F, bool out_bf16, hipStream_t st);
+hipError_t launch_copy_rows(const float* src, int src_stride, float* dst, int dst_stride,
+                            int P, int n, hipStream_t st);
+// C[P][N] (=|+=) A[P][K] * W[N][K]^T, A and C float32, W in the weight dtype.
+hipError_t launch_gemm(const float* A, int lda, const void* W, float* C, int ldc, int P, int N,
+                       int K, bool accumulate, bool bf16, hipStream_t st);
+}  // namespace spd

@@ -1,0 +1,106 @@
+"""Lockstep comparison of the HIP path (through the C ABI) with the CPU oracle.
+
+Comparison rule:
+  * integers bit-exact: first token, every step's draft, verified position,
+    committed token, accept flag, KV length of every layer, PDM length;
+  * floats: logits max-abs <= 1e-4 (f32 weights) / 5e-2 (bf16 weights);
+    residual and anchor states relative L2 <= 1e-5 (f32) / 2e-2 (bf16);
+  * a token decision may differ only where the oracle flags a near-tie
+    (top-2 gap < 1e-3, or |u q(d) - p(d)| < 1e-3 q(d)); the comparison stops there.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from oracle.sampling import Sampling
+from oracle.spd import SPD as OracleSPD
+
+
+def tolerances(cfg):
+    if cfg.dtype == "bf16":
+        return 5e-2, 2e-2
+    return 1e-4, 1e-5
+
+
+def rel(a, b):
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-30))
+
+
+def run_parity(cfg, W, dW, prompt, G=None, T=0.0, seed=0, n=None, fill="clamp",
+               forced_p=None, forced_ref=None, check_states=True, max_steps=None):
+    from speculative_pipeline_decoding_amd import SPD
+    G = cfg.gen_len if G is None else G
+    tol_l, tol_h = tolerances(cfg)
+    s = Sampling(temperature=T, seed=seed)
+    kw = {}
+    if forced_p is not None:
+        s.forced_p, s.forced_ref, s.forced_base = forced_p, np.asarray(forced_ref), len(prompt)
+        kw = dict(forced_p=forced_p, forced_ref=list(forced_ref))
+    gpu = SPD(cfg, dW, temperature=T, seed=seed, n=n, fill=fill, **kw)
+    orc = OracleSPD(cfg, W, s, n=n, fill=fill)
+    rep = {"steps": 0, "max_logit_err": 0.0, "max_state_rel": 0.0, "stopped_at_near_tie": None,
+           "flagged": 0}
+    t0o = orc.prefill(prompt)
+    t0g = gpu.prefill(prompt)
+    zt = gpu.debug("target_logits")
+    err = float(np.abs(zt - orc.prefill_logits).max())
+    rep["max_logit_err"] = err
+    assert err <= tol_l, f"prefill logits err {err}"
+    if t0g != t0o:
+        assert orc.prefill_flag, f"first token {t0g} != {t0o} without a near tie"
+        rep["stopped_at_near_tie"] = 0
+        gpu.close()
+        return rep
+    ring = gpu.n + 1
+    while 1 + orc.N < G and (max_steps is None or rep["steps"] < max_steps):
+        rec = orc.step()
+        gpu.step()
+        c = gpu.verify_commit()
+        rep["steps"] += 1
+        k = rep["steps"]
+        assert c.newest == rec.newest, (k, c.newest, rec.newest)
+        zq = gpu.debug("draft_logits")
+        e = float(np.abs(zq - rec.draft_logits).max())
+        rep["max_logit_err"] = max(rep["max_logit_err"], e)
+        assert e <= tol_l, f"step {k}: draft logits err {e}"
+        rep["flagged"] += int(rec.draft_flag) + int(rec.verify_flag)
+        if c.new_draft != rec.draft:
+            assert rec.draft_flag, f"step {k}: draft {c.new_draft} != {rec.draft} without a near tie"
+            rep["stopped_at_near_tie"] = k
+            break
+        assert bool(c.verified) == rec.exited, (k, c.verified, rec.exited)
+        if rec.exited:
+            zt = gpu.debug("target_logits")
+            e = float(np.abs(zt - rec.target_logits).max())
+            rep["max_logit_err"] = max(rep["max_logit_err"], e)
+            assert e <= tol_l, f"step {k}: target logits err {e}"
+            assert c.position == rec.verified_pos
+            assert c.draft_token == rec.verified_draft, (k, c.draft_token, rec.verified_draft)
+            if c.token != rec.committed or bool(c.accepted) != rec.accepted:
+                assert rec.verify_flag, (f"step {k}: commit ({c.token}, {c.accepted}) != "
+                                         f"({rec.committed}, {rec.accepted}) without a near tie")
+                rep["stopped_at_near_tie"] = k
+                break
+        kv, pl = gpu.kv_lens()
+        assert kv == rec.kv_len, (k, kv, rec.kv_len)
+        assert pl == rec.pdm_len, (k, pl, rec.pdm_len)
+        assert c.committed_total == orc.N and c.inflight == len(orc.F)
+        if check_states:
+            hr = gpu.debug("h_ring").reshape(ring, cfg.d_model)
+            an = gpu.debug("anchors").reshape(ring, len(orc.B), cfg.d_model)
+            for x, hv in orc.h.items():
+                r = rel(hr[x % ring], hv)
+                rep["max_state_rel"] = max(rep["max_state_rel"], r)
+                assert r <= tol_h, f"step {k}: residual of position {x} rel err {r}"
+            for x, amap in orc.anch.items():
+                for i, av in amap.items():
+                    r = rel(an[x % ring, i], av)
+                    rep["max_state_rel"] = max(rep["max_state_rel"], r)
+                    assert r <= tol_h, f"step {k}: anchor {i} of position {x} rel err {r}"
+    st = gpu.stats()
+    if rep["stopped_at_near_tie"] is None:
+        assert (st.N, st.K, st.accepted, st.rejected) == (orc.N, orc.K, orc.accepted, orc.rejected)
+        assert abs(st.s0 - orc.s0) < 1e-12
+    rep.update(N=st.N, K=st.K, alpha=st.alpha, s0=st.s0, tokens_match=orc.committed)
+    gpu.close()
+    return rep

@@ -1,0 +1,123 @@
+"""HIP path vs oracle, step by step, through the C ABI (needs an MI355X)."""
+import numpy as np
+import pytest
+
+from conftest import workload
+from parity import run_parity
+
+pytestmark = pytest.mark.gpu
+
+_dev = {}
+
+
+def dev_weights(name):
+    if name not in _dev:
+        import torch
+        from speculative_pipeline_decoding_amd import upload_weights
+        cfg, W, _ = workload(name)
+        _dev.clear()
+        torch.cuda.empty_cache()
+        _dev[name] = upload_weights(cfg, W)
+    return _dev[name]
+
+
+def _run(name, **kw):
+    cfg, W, prompt = workload(name)
+    print(f"[parity] {name} {kw}", flush=True)
+    rep = run_parity(cfg, W, dev_weights(name), prompt, **kw)
+    print(f"[parity] {name} {kw} -> {rep}", flush=True)
+    return rep
+
+
+def test_tiny_greedy_full_length():
+    rep = _run("tiny")
+    assert rep["stopped_at_near_tie"] is None and rep["N"] == 63
+
+
+def test_tiny_sampled():
+    rep = _run("tiny", T=1.0, seed=3)
+    assert rep["steps"] > 0
+
+
+@pytest.mark.parametrize("n", [1, 3, 4])
+def test_tiny_other_widths(n):
+    rep = _run("tiny", n=n, G=30)
+    assert rep["steps"] > 0
+
+
+def test_tiny_forced_and_zero_fill():
+    from oracle.spd import ar_decode
+    cfg, W, prompt = workload("tiny")
+    ref = ar_decode(cfg, W, prompt, G=cfg.gen_len + 8)
+    rep = _run("tiny", forced_p=0.7, forced_ref=ref, seed=5, fill="zero")
+    assert rep["stopped_at_near_tie"] is None
+
+
+@pytest.mark.parametrize("name", ["mid_bf16_L6_d384_n3", "mid_bf16_L7_d256_n3_uneven",
+                                  "mid_f32_L4_d128_n1", "mid_bf16_L4_d512_hd128_n4"])
+def test_mid_greedy(name):
+    rep = _run(name)
+    assert rep["steps"] > 0
+
+
+@pytest.mark.parametrize("name", ["mid_bf16_L6_d384_n3", "mid_bf16_L4_d512_hd128_n4"])
+def test_mid_sampled(name):
+    rep = _run(name, T=1.0, seed=7)
+    assert rep["steps"] > 0
+
+
+def test_mid_forced_acceptance():
+    from oracle.spd import ar_decode
+    cfg, W, prompt = workload("mid_bf16_L6_d384_n3")
+    ref = ar_decode(cfg, W, prompt, G=cfg.gen_len + 8)
+    rep = _run("mid_bf16_L6_d384_n3", forced_p=0.8, forced_ref=ref, seed=2)
+    assert rep["stopped_at_near_tie"] is None
+
+
+def test_determinism_same_seed_same_bits():
+    from speculative_pipeline_decoding_amd import SPD
+    cfg, W, prompt = workload("mid_bf16_L6_d384_n3")
+    outs = []
+    for _ in range(2):
+        g = SPD(cfg, dev_weights("mid_bf16_L6_d384_n3"), temperature=1.0, seed=11)
+        toks, recs = g.generate(prompt, 16)
+        outs.append((toks, g.debug("target_logits").tobytes(), g.debug("anchors").tobytes()))
+        g.close()
+    assert outs[0] == outs[1]
+
+
+def test_call_order_and_capacity_errors():
+    from speculative_pipeline_decoding_amd import SPD, SpdError
+    from speculative_pipeline_decoding_amd.binding import SPD_E_STATE, SPD_E_CAPACITY, SPD_E_ARG
+    cfg, W, prompt = workload("tiny")
+    g = SPD(cfg, dev_weights("tiny"))
+    with pytest.raises(SpdError) as e:
+        g.step()
+    assert e.value.code == SPD_E_STATE
+    with pytest.raises(SpdError) as e:
+        g.prefill([cfg.vocab])
+    assert e.value.code == SPD_E_ARG
+    with pytest.raises(SpdError) as e:
+        g.prefill([1] * cfg.max_ctx)
+    assert e.value.code == SPD_E_CAPACITY
+    g.prefill(prompt)
+    with pytest.raises(SpdError) as e:
+        g.prefill(prompt)
+    assert e.value.code == SPD_E_STATE
+    with pytest.raises(SpdError) as e:
+        g.verify_commit()
+    assert e.value.code == SPD_E_STATE
+    g.step()
+    with pytest.raises(SpdError) as e:
+        g.step()
+    assert e.value.code == SPD_E_STATE
+    g.verify_commit()
+    # run until the newest position reaches max_ctx
+    with pytest.raises(SpdError) as e:
+        for _ in range(4 * cfg.max_ctx):
+            g.step()
+            g.verify_commit()
+    assert e.value.code == SPD_E_CAPACITY
+    g.reset()
+    assert g.prefill(prompt) >= 0
+    g.close()
