@@ -1,0 +1,251 @@
+#!/usr/bin/env python3
+"""Committed tokens/s of Speculative Pipeline Decoding on one MI355X.
+
+A bench "step" is one SPD pipeline step (spd_step + spd_verify_commit): the
+stage-0 embedding, the PDM (anchor gather, k*d -> d projection, Ls layers,
+LM head, draft), every in-flight token's stage slice (QKV + RoPE + KV write,
+staircase attention, O, SwiGLU FFN, residual + anchor capture), and the
+streaming verification with commit / truncate / flush / reseed.
+
+Default workload: dense 32-layer bf16 decoder, d=2560, 32 q / 8 kv heads x 80,
+SwiGLU 9728, vocab 151936, SPD n=8, Ls=4, anchors {0,8,16,24,31}, context 2048
+(1792-token prompt + 256 generated), T=1 with rejection-sampling verification
+and top-p 1.0 (--t0-run adds the greedy, lossless T=0 run).
+Weights are seeded random N(0, 0.02) and the prompt is uniform random ids:
+synthetic data of the workload's shape.
+
+Timed region: W warm-up steps, then exactly K steps between two device
+synchronisations, with inputs resident in HBM. value = committed tokens / s.
+Per-launch timing for the roofline comes from HIP events recorded by the
+library on its own stream over a second region of K steps right after it.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "committed tokens/s (1 seq, 1 GPU) + step µs + % HBM roofline, n=8"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def pct(xs, q):
+    xs = sorted(xs)
+    if not xs:
+        return None
+    i = min(len(xs) - 1, max(0, int(round(q * (len(xs) - 1)))))
+    return xs[i]
+
+
+def run_spd(cfg, dW, prompt, T, seed, warmup, steps, instrument):
+    import torch
+    from speculative_pipeline_decoding_amd import SPD
+    stream = torch.cuda.current_stream()
+    spd = SPD(cfg, dW, temperature=T, seed=seed, stream=stream)
+    t = time.perf_counter()
+    spd.prefill(prompt)
+    torch.cuda.synchronize()
+    prefill_s = time.perf_counter() - t
+    for _ in range(warmup):
+        spd.step()
+        spd.verify_commit()
+    out = {"prefill_s": prefill_s}
+
+    def region(with_kernel_events):
+        if with_kernel_events:
+            spd.timing(True)
+        s0 = spd.stats()
+        evs, kinds = [], []
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            spd.step()
+            b.record(stream)
+            c = spd.verify_commit()
+            evs.append((a, b))
+            kinds.append(bool(c.verified))
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        s1 = spd.stats()
+        step_ms = [a.elapsed_time(b) for a, b in evs]
+        res = {"wall_s": wall, "N": s1.N - s0.N, "K": s1.K - s0.K, "step_ms": step_ms,
+               "full": [m for m, k in zip(step_ms, kinds) if k],
+               "refill": [m for m, k in zip(step_ms, kinds) if not k]}
+        if with_kernel_events:
+            res["kernels"] = spd.timing_read()
+            spd.timing(False)
+        return res
+
+    out["timed"] = region(False)
+    if instrument:
+        # the same steps again from a fresh prefill, each launch bracketed by HIP events
+        spd.reset()
+        spd.prefill(prompt)
+        for _ in range(warmup):
+            spd.step()
+            spd.verify_commit()
+        out["instrumented"] = region(True)
+    st = spd.stats()
+    out["alpha_total"], out["s0_total"] = st.alpha, st.s0
+    spd.close()
+    return out
+
+
+def cpu_baseline(cfg, W, T, seed, alpha, budget_s):
+    """The oracle as it stands, on the host cores, over a bounded sample of the same model."""
+    import numpy as np
+    from oracle.spd import SPD as OracleSPD
+    from oracle.sampling import Sampling
+    from spd_inputs import make_prompt
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    plen = 16
+    o = OracleSPD(cfg, W, Sampling(temperature=T, seed=seed))
+    t = time.perf_counter()
+    o.prefill(make_prompt(cfg, length=plen))
+    setup = time.perf_counter() - t
+    log(f"cpu baseline: oracle set up in {setup:.1f}s (weights upcast to float64, untimed)")
+    t0 = time.perf_counter()
+    k = 0
+    while k < 2 or (time.perf_counter() - t0 < budget_s and k < 64):
+        o.step()
+        k += 1
+        log(f"cpu baseline: oracle step {k} at {time.perf_counter() - t0:.1f}s")
+    dt = time.perf_counter() - t0
+    steps_per_s = k / dt
+    return {"value": alpha * steps_per_s, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": (f"{k} SPD steps ({dt:.1f} s) of the same n={o.n} model after a {plen}-token "
+                       f"prompt (float64 numpy oracle, weights upcast once before timing); "
+                       f"oracle steps/s {steps_per_s:.4f} scaled by the GPU run's committed "
+                       f"tokens per step alpha={alpha:.4f}"),
+            "steps_per_s": steps_per_s}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--workload", default="cfg3")
+    ap.add_argument("--temperature", type=float, default=1.0)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--t0-run", action="store_true",
+                    help="also time the same steps at T=0 (greedy, lossless) and report them")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this build runs the "
+              "SPD hot path on a single MI355X, with no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from spd_inputs import get, make_prompt, make_weights, weight_bytes
+    from speculative_pipeline_decoding_amd import upload_weights
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    cfg = get(args.workload)
+    if args.warmup + args.steps > cfg.gen_len:
+        print(f"warmup + steps must be <= {cfg.gen_len} (the workload generates {cfg.gen_len} "
+              "tokens; each step commits at most one)", file=sys.stderr)
+        sys.exit(2)
+    t = time.perf_counter()
+    W = make_weights(cfg)
+    log(f"weights drawn in {time.perf_counter() - t:.1f}s ({weight_bytes(cfg) / 1e9:.2f} GB)")
+    dW = upload_weights(cfg, W)
+    torch.cuda.synchronize()
+    prompt = make_prompt(cfg)
+    log(f"weights resident on {torch.cuda.get_device_name(0)}")
+
+    main_run = run_spd(cfg, dW, prompt, args.temperature, args.seed, args.warmup, args.steps, True)
+    tm = main_run["timed"]
+    log(f"T={args.temperature}: prefill {main_run['prefill_s']:.2f}s, timed {tm['K']} steps in "
+        f"{tm['wall_s'] * 1e3:.1f} ms, N={tm['N']}")
+    t0_run = None
+    if args.t0_run and args.temperature != 0.0:
+        r = run_spd(cfg, dW, prompt, 0.0, args.seed, args.warmup, args.steps, False)
+        rt = r["timed"]
+        t0_run = {"temperature": 0.0, "tokens_per_s": rt["N"] / rt["wall_s"], "N": rt["N"],
+                  "K": rt["K"], "alpha": rt["N"] / rt["K"], "s0": rt["N"] / rt["K"] * cfg.n_stages,
+                  "ms_per_step": rt["wall_s"] * 1e3 / rt["K"],
+                  "step_us_median": 1e3 * statistics.median(rt["step_ms"])}
+        log(f"T=0: timed {rt['K']} steps, N={rt['N']}")
+
+    value = tm["N"] / tm["wall_s"]
+    ms_per_step = tm["wall_s"] * 1e3 / tm["K"]
+    alpha = tm["N"] / tm["K"]
+    kern = main_run["instrumented"]["kernels"]
+    ik = main_run["instrumented"]["K"]
+    step_bytes = sum(v["bytes"] for v in kern.values()) / ik
+    gpu_step_ms = statistics.mean(tm["step_ms"])
+    dominant = max((k for k in kern if k.startswith("gemv")), key=lambda k: kern[k]["ms"])
+    d = kern[dominant]
+    achieved = (d["bytes"] / d["count"]) / (d["ms"] / d["count"] * 1e-3) / 1e9
+    kernels = {k: {"launches": v["count"], "avg_us": 1e3 * v["ms"] / v["count"],
+                   "GBps": (v["bytes"] / (v["ms"] * 1e-3) / 1e9) if v["bytes"] else None,
+                   "bytes_per_launch": v["bytes"] / v["count"]}
+               for k, v in kern.items() if v["count"]}
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "n": cfg.n_stages, "Ls": cfg.pdm_layers,
+                   "anchors": list(cfg.anchors), "context": cfg.prompt_len + cfg.gen_len,
+                   "prompt": cfg.prompt_len, "temperature": args.temperature, "top_p": 1.0,
+                   "weights": "bf16 N(0,0.02) seeded", "kv_cache": "bf16",
+                   "prompt_ids": "uniform random"},
+        "roofline": {"bound": "hbm", "kernel": dominant,
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+        "step_us": {"median": 1e3 * statistics.median(tm["step_ms"]),
+                    "p10": 1e3 * pct(tm["step_ms"], 0.1), "p90": 1e3 * pct(tm["step_ms"], 0.9),
+                    "full_median": 1e3 * statistics.median(tm["full"]) if tm["full"] else None,
+                    "refill_median": 1e3 * statistics.median(tm["refill"]) if tm["refill"] else None,
+                    "full_steps": len(tm["full"]), "refill_steps": len(tm["refill"])},
+        "alpha": alpha,
+        "s0": alpha * cfg.n_stages,
+        "step_hbm_roofline": {"algorithmic_bytes_per_step": step_bytes,
+                              "frac": step_bytes / (gpu_step_ms * 1e-3) / (HBM_PEAK_GBS * 1e9)},
+        "kernels": kernels,
+        "t0_run": t0_run,
+        "prefill_s": main_run["prefill_s"],
+        "device": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        del dW
+        torch.cuda.empty_cache()
+        res["cpu_baseline"] = cpu_baseline(cfg, W, args.temperature, args.seed, alpha,
+                                           args.cpu_budget)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
