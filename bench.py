@@ -150,6 +150,9 @@ def main():
                     help="also time the same steps at T=0 (greedy, lossless) and report them")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="first run one device-to-device copy of this many MiB: a kernel of "
+                         "known traffic, to scale hardware byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this build runs the "
@@ -173,6 +176,15 @@ def main():
     torch.cuda.synchronize()
     prompt = make_prompt(cfg)
     log(f"weights resident on {torch.cuda.get_device_name(0)}")
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {args.calib_copy_mib} MiB read + {args.calib_copy_mib} MiB written")
+        del src, dst
 
     main_run = run_spd(cfg, dW, prompt, args.temperature, args.seed, args.warmup, args.steps, True)
     tm = main_run["timed"]

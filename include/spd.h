@@ -66,9 +66,9 @@ enum { SPD_LAYER_SOFTMAX = 0, SPD_LAYER_LINEAR = 1 };
  *   anchor_fill: how a PDM row fills anchors deeper than its current depth:
  *     SPD_FILL_CLAMP repeats the deepest computed anchor (default), SPD_FILL_ZERO uses 0;
  *   max_ctx: KV capacity in positions; every in-flight position must stay below it.
- * Limits: d_model, d_ffn, n_q_heads*head_dim multiples of 8; head_dim even and
- * <= 128; n_q_heads a multiple of n_kv_heads with at most 16 query heads per
- * KV head; n <= 16; k <= 8; Ls <= 16.
+ * Limits: d_model, d_ffn, n_q_heads*head_dim multiples of 8; head_dim in
+ * {16, 32, 64, 80, 128} (bf16) or {16, 32, 64} (f32); n_q_heads a multiple of
+ * n_kv_heads with at most 16 query heads per KV head; n <= 16; k <= 8; Ls <= 16.
  */
 typedef struct {
   int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, d_ffn, vocab;

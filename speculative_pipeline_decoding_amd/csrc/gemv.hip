@@ -288,13 +288,12 @@ __device__ void gemv_multi(const GemvProb& p, int tile, float* xs, float* red,
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void gemv_kernel(const GemvProb* __restrict__ probs, int nprob,
-                                                   const float2* __restrict__ rope) {
+__device__ __forceinline__ void gemv_body(const GemvProb* __restrict__ probs, int nprob,
+                                          const float2* __restrict__ rope) {
   __shared__ __attribute__((aligned(16))) float xs[kMaxVec * 64 * Elt<T>::N];
   __shared__ float red[kWaves][kRed];
   const int b = blockIdx.x;
-  int pi = 0;
-  while (pi + 1 < nprob && probs[pi + 1].tile0 <= b) ++pi;
+  const int pi = find_problem(probs, nprob, b);
   const GemvProb& p = probs[pi];
   const int tile = b - p.tile0;
   float* r = red[threadIdx.x >> 6];
@@ -302,18 +301,43 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvProb* __restrict__ 
   else gemv_multi<T, kRowsMulti>(p, tile, xs, r, rope);
 }
 
+// One kernel symbol per role in the step, so profiles separate them.
+#define SPD_GEMV_KERNEL(name)                                                              \
+  template <typename T>                                                                    \
+  __global__ __launch_bounds__(256) void name(const GemvProb* __restrict__ probs, int nprob, \
+                                              const float2* __restrict__ rope) {           \
+    gemv_body<T>(probs, nprob, rope);                                                      \
+  }
+SPD_GEMV_KERNEL(gemv_proj)
+SPD_GEMV_KERNEL(gemv_qkv)
+SPD_GEMV_KERNEL(gemv_o)
+SPD_GEMV_KERNEL(gemv_gate_up)
+SPD_GEMV_KERNEL(gemv_down)
+SPD_GEMV_KERNEL(gemv_head)
+#undef SPD_GEMV_KERNEL
+
+template <typename T>
+hipError_t launch_role(int role, const GemvProb* d_probs, int nprob, int ntiles,
+                       const float2* rope, hipStream_t st) {
+  const dim3 grid(ntiles), block(kWaves * 64);
+  switch (role) {
+    case GEMV_PROJ: hipLaunchKernelGGL(gemv_proj<T>, grid, block, 0, st, d_probs, nprob, rope); break;
+    case GEMV_QKV: hipLaunchKernelGGL(gemv_qkv<T>, grid, block, 0, st, d_probs, nprob, rope); break;
+    case GEMV_O: hipLaunchKernelGGL(gemv_o<T>, grid, block, 0, st, d_probs, nprob, rope); break;
+    case GEMV_GATE_UP: hipLaunchKernelGGL(gemv_gate_up<T>, grid, block, 0, st, d_probs, nprob, rope); break;
+    case GEMV_DOWN: hipLaunchKernelGGL(gemv_down<T>, grid, block, 0, st, d_probs, nprob, rope); break;
+    default: hipLaunchKernelGGL(gemv_head<T>, grid, block, 0, st, d_probs, nprob, rope); break;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
-hipError_t launch_gemv(const GemvProb* d_probs, int nprob, int ntiles, bool bf16,
+hipError_t launch_gemv(int role, const GemvProb* d_probs, int nprob, int ntiles, bool bf16,
                        const float2* rope, hipStream_t st) {
   if (ntiles <= 0 || nprob <= 0) return hipSuccess;
-  if (bf16)
-    hipLaunchKernelGGL(gemv_kernel<uint16_t>, dim3(ntiles), dim3(kWaves * 64), 0, st, d_probs,
-                       nprob, rope);
-  else
-    hipLaunchKernelGGL(gemv_kernel<float>, dim3(ntiles), dim3(kWaves * 64), 0, st, d_probs,
-                       nprob, rope);
-  return hipGetLastError();
+  return bf16 ? launch_role<uint16_t>(role, d_probs, nprob, ntiles, rope, st)
+              : launch_role<float>(role, d_probs, nprob, ntiles, rope, st);
 }
 
 }  // namespace spd

@@ -17,19 +17,19 @@ __device__ __forceinline__ void st(T* p, size_t i, float v) {
 }
 
 // Block 0 embeds the stage-0 token into its residual slot and anchor 0 (depth 0).
-// Block 1 + r builds PDM row r's feature: anchor segments in ascending depth; a
-// segment deeper than the row's current depth repeats its deepest computed
-// anchor (clamp) or is zero, as the host encoded in src.
+// Block 1 + r * k + s copies segment s of PDM row r's feature: anchor segments in
+// ascending depth; a segment deeper than the row's current depth repeats its
+// deepest computed anchor (clamp) or is zero, as the host encoded in src.
 template <typename T>
 __global__ __launch_bounds__(256) void embed_gather_kernel(const EmbedGather* __restrict__ dd) {
   const EmbedGather& e = *dd;
   const int d = e.d;
-  const T* E = static_cast<const T*>(e.embed);
+  const T* __restrict__ E = static_cast<const T*>(e.embed);
   const int tok = e.tok_ring[e.newest_slot];
-  const T* erow = E + (size_t)tok * d;
+  const T* __restrict__ erow = E + (size_t)tok * d;
   if (blockIdx.x == 0) {
-    float* h = e.h_ring + (size_t)e.newest_slot * d;
-    float* a0 = e.anchors + (size_t)e.newest_slot * e.k * d;
+    float* __restrict__ h = e.h_ring + (size_t)e.newest_slot * d;
+    float* __restrict__ a0 = e.anchors + (size_t)e.newest_slot * e.k * d;
     for (int i = threadIdx.x; i < d; i += blockDim.x) {
       const float v = ld(erow, i);
       h[i] = v;
@@ -37,17 +37,18 @@ __global__ __launch_bounds__(256) void embed_gather_kernel(const EmbedGather* __
     }
     return;
   }
-  const int r = blockIdx.x - 1;
-  const float* arow = e.anchors + (size_t)e.row_slot[r] * e.k * d;
-  float* X = e.X + (size_t)r * e.k * d;
-  for (int s = 0; s < e.k; ++s) {
-    const int src = e.src[r][s];
-    for (int i = threadIdx.x; i < d; i += blockDim.x) {
-      float v = 0.f;
-      if (src == -2) v = ld(erow, i);
-      else if (src >= 0) v = arow[(size_t)src * d + i];
-      X[(size_t)s * d + i] = v;
-    }
+  const int r = (blockIdx.x - 1) / e.k, sg = (blockIdx.x - 1) % e.k;
+  const int src = e.src[r][sg];
+  float4* __restrict__ X = reinterpret_cast<float4*>(e.X + ((size_t)r * e.k + sg) * d);
+  if (src >= 0) {
+    const float4* __restrict__ a =
+        reinterpret_cast<const float4*>(e.anchors + ((size_t)e.row_slot[r] * e.k + src) * d);
+    for (int i = threadIdx.x; i < d / 4; i += blockDim.x) X[i] = a[i];
+  } else if (src == -1) {
+    for (int i = threadIdx.x; i < d / 4; i += blockDim.x) X[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  } else {
+    for (int i = threadIdx.x; i < d / 4; i += blockDim.x)
+      X[i] = make_float4(ld(erow, 4 * i), ld(erow, 4 * i + 1), ld(erow, 4 * i + 2), ld(erow, 4 * i + 3));
   }
 }
 
@@ -145,9 +146,10 @@ __global__ void copy_rows_kernel(const float* __restrict__ s, int ss, float* __r
 
 hipError_t launch_embed_gather(const EmbedGather* d_desc, int M, int k, int d, bool bf16,
                                hipStream_t s) {
-  (void)k; (void)d;
-  if (bf16) hipLaunchKernelGGL(embed_gather_kernel<uint16_t>, dim3(M + 1), dim3(256), 0, s, d_desc);
-  else hipLaunchKernelGGL(embed_gather_kernel<float>, dim3(M + 1), dim3(256), 0, s, d_desc);
+  (void)d;
+  const dim3 grid(1 + M * k);
+  if (bf16) hipLaunchKernelGGL(embed_gather_kernel<uint16_t>, grid, dim3(256), 0, s, d_desc);
+  else hipLaunchKernelGGL(embed_gather_kernel<float>, grid, dim3(256), 0, s, d_desc);
   return hipGetLastError();
 }
 

@@ -24,6 +24,7 @@ using namespace spd;
 
 namespace spd {
 int attn_max_split();
+bool attn_supported_head_dim(int hd, bool bf16);
 }
 
 namespace {
@@ -72,7 +73,7 @@ struct Plan {
   int R = 0;   // sub-layer launches per step
   // workspace offsets
   size_t o_kv, o_pkv, o_lin, o_h, o_anch, o_tok, o_qring, o_qlse, o_X, o_hp, o_qbuf, o_attn,
-      o_act, o_lqkv, o_logits, o_part, o_verdict, o_rcnt, o_desc, o_apart, o_acnt, o_rope,
+      o_act, o_lqkv, o_logits, o_part, o_verdict, o_desc, o_apart, o_rope,
       o_forced, o_ptok, o_pH, o_pA, o_pQKV, o_pO, o_pG, o_pU, o_pZ, o_panch, total;
   size_t kv_layer_bytes;     // K and V of one layer
   size_t lin_state_bytes;    // one state [hq][hd][hd] f32
@@ -92,7 +93,8 @@ bool plan_config(const spd_model_config* c, Plan& p, std::string& err) {
   if (p.L < 1 || p.d < 8 || p.hq < 1 || p.hkv < 1 || p.hd < 2 || p.F < 8 || p.V < 2)
     return bad("model dimensions out of range");
   if (p.d % 8 || p.F % 8 || (p.hq * p.hd) % 8) return bad("d_model, d_ffn, n_q_heads*head_dim must be multiples of 8");
-  if (p.hd % 2 || p.hd > 128) return bad("head_dim must be even and <= 128");
+  if (!attn_supported_head_dim(p.hd, p.bf16))
+    return bad("head_dim must be 16, 32 or 64 (f32), or 16, 32, 64, 80 or 128 (bf16)");
   if (p.hq % p.hkv || p.hq / p.hkv > 16) return bad("n_q_heads must be a multiple of n_kv_heads, group <= 16");
   if (p.n < 1 || p.n > kMaxStages || p.n > p.L) return bad("n_stages must be in [1, min(L, 16)]");
   if (p.k < 1 || p.k > kMaxAnchors || !c->anchors) return bad("need 1..8 anchors");
@@ -158,11 +160,9 @@ bool plan_config(const spd_model_config* c, Plan& p, std::string& err) {
   p.o_logits = take((size_t)p.V * 4);
   p.o_part = take((size_t)3 * kVocabBlocks * sizeof(VocabPartial));
   p.o_verdict = take(sizeof(Verdict));
-  p.o_rcnt = take(64);
   p.o_desc = take(kDescBytes);
   const int G = p.hq / p.hkv;
   p.o_apart = take((size_t)T * p.hkv * attn_max_split() * G * (p.hd + 2) * 4);
-  p.o_acnt = take((size_t)T * p.hkv * 4);
   p.o_rope = take((size_t)ctx * (p.hd / 2) * sizeof(float2));
   p.o_forced = take(ctx * 4);
   const size_t CH = kPrefillChunk;
@@ -336,13 +336,17 @@ hipError_t run_op(spd_handle* h, const Op& op) {
       return launch_embed_gather(reinterpret_cast<const EmbedGather*>(d + op.off), op.count, p.k,
                                  p.d, p.bf16, h->st);
     case OP_GEMV_PROJ: case OP_GEMV_QKV: case OP_GEMV_O: case OP_GEMV_GU: case OP_GEMV_DOWN:
-    case OP_GEMV_HEAD:
-      return launch_gemv(reinterpret_cast<const GemvProb*>(d + op.off), op.count, op.ntiles,
-                         p.bf16, rope, h->st);
+    case OP_GEMV_HEAD: {
+      const int role = op.kind == OP_GEMV_PROJ ? GEMV_PROJ : op.kind == OP_GEMV_QKV ? GEMV_QKV
+                     : op.kind == OP_GEMV_O ? GEMV_O : op.kind == OP_GEMV_GU ? GEMV_GATE_UP
+                     : op.kind == OP_GEMV_DOWN ? GEMV_DOWN : GEMV_HEAD;
+      return launch_gemv(role, reinterpret_cast<const GemvProb*>(d + op.off), op.count,
+                         op.ntiles, p.bf16, rope, h->st);
+    }
     case OP_ATTN:
       return launch_attention(reinterpret_cast<const AttnProb*>(d + op.off), op.count, op.ntiles,
                               p.bf16, p.hq, p.hkv, p.hd, p.max_ctx, op.split,
-                              h->at<float>(p.o_apart), h->at<int>(p.o_acnt), h->st);
+                              op.ntiles > op.count * p.hkv, h->at<float>(p.o_apart), h->st);
     case OP_VOCAB:
       return launch_vocab_stats(reinterpret_cast<const VocabDesc*>(d + op.off), kVocabBlocks,
                                 h->at<VocabPartial>(p.o_part), h->st);
@@ -350,8 +354,7 @@ hipError_t run_op(spd_handle* h, const Op& op) {
       return launch_finalize(reinterpret_cast<const FinalizeDesc*>(d + op.off), h->st);
     case OP_RESID:
       return launch_residual_impl(reinterpret_cast<const FinalizeDesc*>(d + op.off),
-                                  h->at<VocabPartial>(p.o_part), kVocabBlocks, h->at<int>(p.o_rcnt),
-                                  h->st);
+                                  h->at<VocabPartial>(p.o_part), kVocabBlocks, h->st);
   }
   return hipErrorInvalidValue;
 }
@@ -662,11 +665,6 @@ int spd_init(const spd_model_config* cfg, const spd_weights* w, const spd_sampli
   if ((e = hipMemcpyAsync(h->ws + p.o_rope, rope.data(), rope.size() * sizeof(float2),
                           hipMemcpyHostToDevice, h->st)) != hipSuccess)
     return dev_fail(e, "hipMemcpyAsync(rope)");
-  // arrival counters start at zero and are reset by their last user
-  if ((e = hipMemsetAsync(h->ws + p.o_acnt, 0, (size_t)(p.n + p.ring) * p.hkv * 4, h->st)) != hipSuccess)
-    return dev_fail(e, "hipMemsetAsync");
-  if ((e = hipMemsetAsync(h->ws + p.o_rcnt, 0, 64, h->st)) != hipSuccess)
-    return dev_fail(e, "hipMemsetAsync");
   if ((e = hipStreamSynchronize(h->st)) != hipSuccess) return dev_fail(e, "hipStreamSynchronize");
   *out = h;
   return SPD_OK;
@@ -762,7 +760,7 @@ int spd_prefill(spd_handle* h, const int32_t* prompt, int32_t len, int32_t* firs
       const size_t fo = dw.put(&fd, 1);
       char* d = h->ws + p.o_desc;
       HIPCHK(h, hipMemcpyAsync(d, h->h_desc, dw.used, hipMemcpyHostToDevice, st));
-      HIPCHK(h, launch_gemv(reinterpret_cast<const GemvProb*>(d + go), 1, nt, bf, rope, st));
+      HIPCHK(h, launch_gemv(GEMV_HEAD, reinterpret_cast<const GemvProb*>(d + go), 1, nt, bf, rope, st));
       HIPCHK(h, launch_vocab_stats(reinterpret_cast<const VocabDesc*>(d + vo), kVocabBlocks,
                                    h->at<VocabPartial>(p.o_part), st));
       HIPCHK(h, launch_finalize(reinterpret_cast<const FinalizeDesc*>(d + fo), st));

@@ -60,7 +60,7 @@ struct AttnProb {
   int len;             // keys 0..len-1
   int tile0;           // first workgroup: tile0 + g * nsplit + s
   int nsplit;
-  int slot;            // index of this problem's partial/counter area
+  int slot;            // index of this problem's partial area
 };
 
 // Linear-attention (recurrent) step for one token at one layer.
@@ -178,15 +178,27 @@ __device__ __forceinline__ float rng_uniform(unsigned long long seed, int stream
 
 __device__ __forceinline__ float gumbel_of(float u) { return -logf(-logf(u)); }
 
+// Index of the problem that owns workgroup b in a grouped launch whose problems
+// start at ascending workgroups tile0 (nprob <= 64). Each lane reads one start,
+// so the search costs one memory round trip instead of a chain of dependent loads.
+template <typename P>
+__device__ __forceinline__ int find_problem(const P* __restrict__ probs, int nprob, int b) {
+  const int lane = threadIdx.x & 63;
+  const bool owns = lane < nprob && probs[lane < nprob ? lane : 0].tile0 <= b;
+  const unsigned long long mask = __ballot(owns);
+  return __popcll(mask) - 1;
+}
+
 }  // namespace spd
 
 // ---- kernel launchers (one per .hip file) -----------------------------------
 namespace spd {
-hipError_t launch_gemv(const GemvProb* d_probs, int nprob, int ntiles, bool bf16,
+enum GemvRole : int { GEMV_PROJ = 0, GEMV_QKV, GEMV_O, GEMV_GATE_UP, GEMV_DOWN, GEMV_HEAD };
+hipError_t launch_gemv(int role, const GemvProb* d_probs, int nprob, int ntiles, bool bf16,
                        const float2* rope, hipStream_t st);
 hipError_t launch_attention(const AttnProb* d_probs, int nprob, int ntiles, bool bf16,
-                            int hq, int hkv, int hd, int max_ctx, int split_len,
-                            float* partials, int* counters, hipStream_t st);
+                            int hq, int hkv, int hd, int max_ctx, int split_len, bool any_split,
+                            float* partials, hipStream_t st);
 hipError_t launch_attention_prefill(const float* q, int q_stride, float* out, int out_stride,
                                     const void* K, const void* V, int pos0, int P, bool bf16,
                                     int hq, int hkv, int hd, int max_ctx, hipStream_t st);
@@ -201,7 +213,7 @@ hipError_t launch_vocab_stats(const VocabDesc* d_desc, int nblocks, VocabPartial
                               hipStream_t st);
 hipError_t launch_finalize(const FinalizeDesc* d_desc, hipStream_t st);
 hipError_t launch_residual_impl(const FinalizeDesc* d_desc, VocabPartial* part, int nblocks,
-                                int* counter, hipStream_t st);
+                                hipStream_t st);
 // prefill helpers
 hipError_t launch_embed_rows(const void* embed, const int* toks, float* H, int P, int d,
                              bool bf16, hipStream_t st);

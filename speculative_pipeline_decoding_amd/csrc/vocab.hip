@@ -8,8 +8,8 @@
 //   draft, and verifies the position after the exiting token: greedy match at
 //   T = 0; at T > 0 rejection sampling (accept iff u q(d) < p(d), Leviathan et
 //   al. 2023, the paper's section 3.5 assumption on the pith.science review).
-// residual (grid, rejections at T > 0 only): y = argmax over {p > q} of
-//   log(p - q) + G, merged by the last block to finish.
+// residual (rejections at T > 0 only): y = argmax over {p > q} of
+//   log(p - q) + G, per-block partials merged by a one-block kernel.
 #include <climits>
 
 #include "spd_internal.h"
@@ -177,13 +177,11 @@ __global__ __launch_bounds__(kVocabBlock) void finalize_kernel(const FinalizeDes
   *f.verdict = v;
 }
 
-// Residual sample after a rejection at T > 0. Partials go to part[2 * nblocks + b];
-// the last block to arrive merges them (its arrival counter sits after the verdict).
+// Residual sample after a rejection at T > 0: every block writes the Gumbel
+// top-2 of its slice of log(p - q) + G to part[2 * nblocks + b] ...
 __global__ __launch_bounds__(kVocabBlock) void residual_kernel(const FinalizeDesc* __restrict__ fd,
-                                                                VocabPartial* __restrict__ part,
-                                                                int* __restrict__ counter) {
+                                                                VocabPartial* __restrict__ part) {
   __shared__ Stat sh[kVocabBlock];
-  __shared__ int last;
   const FinalizeDesc& f = *fd;
   if (!f.verdict->need_residual) return;
   const float lse_t = f.verdict->lse_t;
@@ -204,18 +202,19 @@ __global__ __launch_bounds__(kVocabBlock) void residual_kernel(const FinalizeDes
   }
   const Stat b = block_reduce(s, 1.f, sh);
   if (threadIdx.x == 0) part[2 * f.nblocks + blockIdx.x] = to_partial(b);
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) last = (atomicAdd(counter, 1) == (int)gridDim.x - 1);
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
+}
+
+// ... and one block merges them in block order and commits the sample.
+__global__ __launch_bounds__(kVocabBlock) void residual_final_kernel(
+    const FinalizeDesc* __restrict__ fd, const VocabPartial* __restrict__ part) {
+  __shared__ Stat sh[kVocabBlock];
+  const FinalizeDesc& f = *fd;
+  if (!f.verdict->need_residual) return;
   Stat m = stat_empty();
   for (int i = threadIdx.x; i < f.nblocks; i += blockDim.x)
     m = merge(m, from_partial(part[2 * f.nblocks + i]), 1.f);
   m = block_reduce(m, 1.f, sh);
   if (threadIdx.x == 0) {
-    *counter = 0;
     Verdict* v = f.verdict;
     v->committed = m.garg;
     if ((m.gmax - m.gsecond) < kNearTie) v->flags |= 1;
@@ -237,9 +236,9 @@ hipError_t launch_finalize(const FinalizeDesc* d_desc, hipStream_t st) {
 }
 
 hipError_t launch_residual_impl(const FinalizeDesc* d_desc, VocabPartial* part, int nblocks,
-                                int* counter, hipStream_t st) {
-  hipLaunchKernelGGL(residual_kernel, dim3(nblocks), dim3(kVocabBlock), 0, st, d_desc, part,
-                     counter);
+                                hipStream_t st) {
+  hipLaunchKernelGGL(residual_kernel, dim3(nblocks), dim3(kVocabBlock), 0, st, d_desc, part);
+  hipLaunchKernelGGL(residual_final_kernel, dim3(1), dim3(kVocabBlock), 0, st, d_desc, part);
   return hipGetLastError();
 }
 
