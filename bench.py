@@ -207,7 +207,8 @@ def main():
     ik = main_run["instrumented"]["K"]
     step_bytes = sum(v["bytes"] for v in kern.values()) / ik
     gpu_step_ms = statistics.mean(tm["step_ms"])
-    dominant = max((k for k in kern if k.startswith("gemv")), key=lambda k: kern[k]["ms"])
+    dominant = max((k for k in kern if k.startswith("gemv") and kern[k]["count"]),
+                   key=lambda k: kern[k]["ms"])
     d = kern[dominant]
     achieved = (d["bytes"] / d["count"]) / (d["ms"] / d["count"] * 1e-3) / 1e9
     kernels = {k: {"launches": v["count"], "avg_us": 1e3 * v["ms"] / v["count"],

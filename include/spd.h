@@ -216,8 +216,11 @@ int spd_debug_copy(const spd_handle* h, int32_t what, void* host_dst, size_t byt
  * bytes (weights read once, KV rows read once). Kinds, in order: 0 embed,
  * 1 PDM projection GEMV, 2 QKV GEMV, 3 attention, 4 linear attention, 5 O GEMV,
  * 6 gate/up GEMV, 7 down GEMV, 8 LM-head GEMV, 9 vocabulary stats, 10 verify,
- * 11 residual sample. Enabling or disabling clears the totals; a pending step
- * gives SPD_E_STATE.
+ * 11 residual sample, then the PDM's own launches: 12 QKV GEMV, 13 attention,
+ * 14 O GEMV, 15 gate/up GEMV, 16 down GEMV. Kinds 0-11 except 1 run on the
+ * caller's stream; the PDM's run on a second, library-owned stream that forks
+ * after the embedding and joins before the LM head, so their durations overlap.
+ * Enabling or disabling clears the totals; a pending step gives SPD_E_STATE.
  */
 int spd_timing_enable(spd_handle* h, int on);
 int spd_timing_read(const spd_handle* h, int32_t kind, int64_t* count, double* total_ms,

@@ -22,7 +22,8 @@ DBG = {"target_logits": 1, "draft_logits": 2, "h_ring": 3, "anchors": 4, "pdm_ro
        "target_kv": 6, "pdm_kv": 7, "tokens": 8}
 # launch kinds reported by spd_timing_read
 OP_NAMES = ["embed", "gemv_proj", "gemv_qkv", "attention", "linear", "gemv_o", "gemv_gate_up",
-            "gemv_down", "gemv_head", "vocab", "finalize", "residual"]
+            "gemv_down", "gemv_head", "vocab", "finalize", "residual", "pdm_qkv", "pdm_attention",
+            "pdm_o", "pdm_gate_up", "pdm_down"]
 TENSORS = ("attn_norm", "w_qkv", "w_o", "ffn_norm", "w_gate", "w_up", "w_down")
 
 

@@ -21,16 +21,6 @@ namespace {
 constexpr int kMaxSplit = 64;
 constexpr int kAttnWaves = 4;
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
 
 template <typename T, int HD>
 __device__ __forceinline__ void unpack(const uint4& u, float* f) {

@@ -1,19 +1,28 @@
 // Grouped stage-sliced GEMV for the depth staircase.
 //
-// One launch runs a list of problems: each in-flight token's matrix at its own
-// layer (one input vector), and the PDM's matrix with its n+1 rows (several
-// input vectors). Batch-1 decode is HBM bound, so the kernel streams each
-// weight row once with 16-byte loads, keeps fp32 activations, and reduces
-// dot products with cross-lane shuffles inside a wavefront (64 lanes).
+// One launch runs a list of problems, y = epilogue(W (g ⊙ x) / rms(x)):
+//   * the in-flight tokens, each at its own layer with one input vector, and the
+//     LM head with one or two vectors (the exiting token and the PDM's newest
+//     row share one sweep of the tied head): the "rows" kernel, in which a wave
+//     owns four weight rows and walks all of K;
+//   * the PDM's matrix with its n+1 rows: the "split-K" kernel, in which the four
+//     waves of a workgroup share four weight rows and take alternate chunks of K,
+//     so a short, wide PDM problem still keeps many loads in flight.
+// Batch-1 decode is HBM bound: weights are streamed once with 16-byte
+// nontemporal loads, activations stay fp32, dot products are reduced with DPP
+// moves inside a wavefront.
 //
 // RMSNorm is fused without a prologue: W (g ⊙ x) / rms(x) is linear in the
-// scale, so every wave accumulates sum(x^2) next to the dot products (all
-// waves use the same lane partition, so they agree bit for bit) and scales
-// the reduced result once.
+// scale, so the kernel accumulates sum(x^2) next to the dot products (every
+// wave uses the same lane partition, so all agree bit for bit) and scales the
+// reduced result once.
 #include "spd_internal.h"
 
 namespace spd {
 namespace {
+
+constexpr int RW = 4;         // weight rows per wave (rows kernel) / per workgroup (split-K)
+constexpr int kSplit = 4;     // waves sharing the rows of a split-K workgroup
 
 template <typename T> struct Elt;
 template <> struct Elt<uint16_t> { static constexpr int N = 8; };   // bf16 per 16 bytes
@@ -32,15 +41,9 @@ template <int N>
 __device__ __forceinline__ void load_f32(const float* p, float* f) {
 #pragma unroll
   for (int i = 0; i < N; i += 4) {
-    float4 t = *reinterpret_cast<const float4*>(p + i);
+    const float4 t = *reinterpret_cast<const float4*>(p + i);
     f[i] = t.x; f[i + 1] = t.y; f[i + 2] = t.z; f[i + 3] = t.w;
   }
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
 }
 
 __device__ __forceinline__ int units_of(const GemvProb& p) {
@@ -50,10 +53,10 @@ __device__ __forceinline__ bool paired(const GemvProb& p) {
   return p.epi == EPI_QKV || p.epi == EPI_SWIGLU;
 }
 
-// Weight row feeding slot j of a wave whose first unit is u0.
+// Weight row feeding slot j of a group of RW rows whose first unit is u0.
 // Plain: slot j -> row u0 + j. SWIGLU: slots [0, RW/2) gate rows, [RW/2, RW) up rows.
 // QKV: slots (2t, 2t+1) -> the RoPE pair (i, i + hd/2) of unit u0 + t.
-template <typename T, int RW>
+template <typename T>
 __device__ __forceinline__ const T* row_ptr(const GemvProb& p, int u0, int j, int nunits) {
   int row;
   const T* M = static_cast<const T*>(p.W);
@@ -68,6 +71,13 @@ __device__ __forceinline__ const T* row_ptr(const GemvProb& p, int u0, int j, in
     row = min(u0 + j, nunits - 1);
   }
   return M + (size_t)row * p.K;
+}
+
+// Slots holding the two values of unit ut: (a, b) = gate/up, RoPE pair, or (a, a).
+__device__ __forceinline__ void unit_slots(const GemvProb& p, int ut, int& ja, int& jb) {
+  ja = ut; jb = ut;
+  if (p.epi == EPI_SWIGLU) jb = ut + RW / 2;
+  else if (p.epi == EPI_QKV) { ja = 2 * ut; jb = 2 * ut + 1; }
 }
 
 template <typename T>
@@ -118,100 +128,101 @@ __device__ void epilogue(const GemvProb& p, int v, int unit, float a, float b,
   }
 }
 
-// Reduced sums of one wave live in LDS: red[j * kMaxVec + v] for slot j, vector v;
-// red[kRowsSingle * kMaxVec + v] holds the RMSNorm scale of vector v.
-constexpr int kRed = kRowsSingle * kMaxVec + kMaxVec;
-
-template <typename T, int RW>
-__device__ void finish(const GemvProb& p, int u0, int nunits, int nv, float* red,
-                       const float2* __restrict__ rope) {
-  const int lane = threadIdx.x & 63;
-  const bool pr = paired(p);
-  const int upw = pr ? RW / 2 : RW;
-  for (int t = lane; t < upw * nv; t += 64) {
-    const int ut = t % upw, v = t / upw;
-    const int unit = u0 + ut;
-    if (unit >= nunits) continue;
-    int ja = ut, jb = ut;
-    if (p.epi == EPI_SWIGLU) jb = ut + RW / 2;
-    else if (p.epi == EPI_QKV) { ja = 2 * ut; jb = 2 * ut + 1; }
-    const float sc = red[kRowsSingle * kMaxVec + v];
-    epilogue<T>(p, v, unit, red[ja * kMaxVec + v] * sc, red[jb * kMaxVec + v] * sc, rope);
-  }
-}
-
-// One input vector: x is read straight from L1/L2 (it is shared by every wave).
-template <typename T, int RW>
-__device__ void gemv_single(const GemvProb& p, int tile, float* red,
-                            const float2* __restrict__ rope) {
+// ---- rows kernel: one wave = RW weight rows over all of K, NV <= 2 vectors ------------
+template <typename T, int NV>
+__device__ void rows_body(const GemvProb& p, int tile, const float2* __restrict__ rope) {
   constexpr int E = Elt<T>::N;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int upw = paired(p) ? RW / 2 : RW;
   const int nunits = units_of(p);
   const int u0 = (tile * kWaves + wave) * upw;
   if (u0 >= nunits) return;
+  const int nv = p.nvec;
   const T* rp[RW];
 #pragma unroll
-  for (int j = 0; j < RW; ++j) rp[j] = row_ptr<T, RW>(p, u0, j, nunits);
-  float acc[RW];
+  for (int j = 0; j < RW; ++j) rp[j] = row_ptr<T>(p, u0, j, nunits);
+  float acc[RW][NV], ss[NV];
 #pragma unroll
-  for (int j = 0; j < RW; ++j) acc[j] = 0.f;
-  float ss = 0.f;
+  for (int v = 0; v < NV; ++v) {
+    ss[v] = 0.f;
+#pragma unroll
+    for (int j = 0; j < RW; ++j) acc[j][v] = 0.f;
+  }
   const int K = p.K;
-  const float* __restrict__ x = p.x;
   const float* __restrict__ g = p.gain;
   for (int k0 = lane * E; k0 < K; k0 += 64 * E) {
     uint4 w[RW];
 #pragma unroll
-    for (int j = 0; j < RW; ++j) w[j] = *reinterpret_cast<const uint4*>(rp[j] + k0);
-    float xv[E];
-    load_f32<E>(x + k0, xv);
-    if (g) {
-      float gv[E];
-      load_f32<E>(g + k0, gv);
+    for (int j = 0; j < RW; ++j) w[j] = load_stream(rp[j] + k0);
+    float xv[NV][E];
 #pragma unroll
-      for (int e = 0; e < E; ++e) { ss += xv[e] * xv[e]; xv[e] *= gv[e]; }
+    for (int v = 0; v < NV; ++v) {
+      if (v < nv) {
+        load_f32<E>(p.x + v * p.x_stride + k0, xv[v]);
+        if (g) {
+          float gv[E];
+          load_f32<E>(g + v * p.gain_stride + k0, gv);
+#pragma unroll
+          for (int e = 0; e < E; ++e) { ss[v] += xv[v][e] * xv[v][e]; xv[v][e] *= gv[e]; }
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) xv[v][e] = 0.f;
+      }
     }
 #pragma unroll
     for (int j = 0; j < RW; ++j) {
       float wf[E];
       to_f32(w[j], wf, (const T*)nullptr);
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[j] += wf[e] * xv[e];
+      for (int v = 0; v < NV; ++v)
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[j][v] += wf[e] * xv[v][e];
     }
   }
 #pragma unroll
-  for (int j = 0; j < RW; ++j) acc[j] = wave_sum(acc[j]);
-  float sc = 1.f;
-  if (g) sc = rsqrtf(wave_sum(ss) / (float)K + p.eps);
-  if (lane == 0) {
+  for (int v = 0; v < NV; ++v) {
 #pragma unroll
-    for (int j = 0; j < RW; ++j) red[j * kMaxVec] = acc[j];
-    red[kRowsSingle * kMaxVec] = sc;
+    for (int j = 0; j < RW; ++j) acc[j][v] = wave_sum(acc[j][v]);
+    ss[v] = g ? rsqrtf(wave_sum(ss[v]) / (float)K + p.eps) : 1.f;
   }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  finish<T, RW>(p, u0, nunits, 1, red, rope);
+  // every lane holds every reduced sum; lane t finishes (unit t % upw, vector t / upw)
+  if (lane < upw * nv) {
+    const int ut = lane % upw, v = lane / upw;
+    int ja, jb;
+    unit_slots(p, ut, ja, jb);
+    float a = 0.f, b = 0.f, sc = 1.f;
+#pragma unroll
+    for (int vv = 0; vv < NV; ++vv) {
+      if (vv == v) {
+        sc = ss[vv];
+#pragma unroll
+        for (int j = 0; j < RW; ++j) {
+          if (j == ja) a = acc[j][vv];
+          if (j == jb) b = acc[j][vv];
+        }
+      }
+    }
+    if (u0 + ut < nunits) epilogue<T>(p, v, u0 + ut, a * sc, b * sc, rope);
+  }
 }
 
-// Several input vectors (the PDM rows, or the two LM-head rows): each chunk of
-// x is staged in LDS once per workgroup and read by all four waves.
-template <typename T, int RW>
-__device__ void gemv_multi(const GemvProb& p, int tile, float* xs, float* red,
-                           const float2* __restrict__ rope) {
+// ---- split-K kernel: a workgroup = RW weight rows, waves take alternate K chunks -------
+template <typename T>
+__device__ void splitk_body(const GemvProb& p, int tile, float* red,
+                            const float2* __restrict__ rope) {
   constexpr int E = Elt<T>::N;
-  constexpr int C = 64 * E;  // chunk of K per iteration
+  constexpr int C = 64 * E;          // elements of K per chunk
+  constexpr int RS = RW * kMaxVec + kMaxVec;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int upw = paired(p) ? RW / 2 : RW;
   const int nunits = units_of(p);
-  const int u0 = (tile * kWaves + wave) * upw;
-  const bool idle = u0 >= nunits;
+  const int u0 = tile * upw;
   const int nv = p.nvec;
   const T* rp[RW];
 #pragma unroll
-  for (int j = 0; j < RW; ++j) rp[j] = row_ptr<T, RW>(p, idle ? 0 : u0, j, nunits);
-  float acc[RW][kMaxVec];
-  float ss[kMaxVec];
+  for (int j = 0; j < RW; ++j) rp[j] = row_ptr<T>(p, u0, j, nunits);
+  float acc[RW][kMaxVec], ss[kMaxVec];
 #pragma unroll
   for (int v = 0; v < kMaxVec; ++v) {
     ss[v] = 0.f;
@@ -221,22 +232,10 @@ __device__ void gemv_multi(const GemvProb& p, int tile, float* xs, float* red,
   const int K = p.K;
   const float* __restrict__ g = p.gain;
   const bool shared_gain = p.gain_stride == 0;
-  for (int c0 = 0; c0 < K; c0 += C) {
-    const int k0 = c0 + lane * E;
-    const bool kin = k0 < K && !idle;
+  for (int k0 = wave * C + lane * E; k0 < K; k0 += kSplit * C) {
     uint4 w[RW];
 #pragma unroll
-    for (int j = 0; j < RW; ++j)
-      w[j] = kin ? *reinterpret_cast<const uint4*>(rp[j] + k0) : make_uint4(0, 0, 0, 0);
-    __syncthreads();
-    for (int i = threadIdx.x; i < nv * (C / 4); i += blockDim.x) {
-      const int v = i / (C / 4), c = i % (C / 4), k = c0 + c * 4;
-      float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (k < K) t = *reinterpret_cast<const float4*>(p.x + v * p.x_stride + k);
-      reinterpret_cast<float4*>(xs)[v * (C / 4) + c] = t;
-    }
-    __syncthreads();
-    if (!kin) continue;
+    for (int j = 0; j < RW; ++j) w[j] = load_stream(rp[j] + k0);
     float wf[RW][E];
 #pragma unroll
     for (int j = 0; j < RW; ++j) to_f32(w[j], wf[j], (const T*)nullptr);
@@ -246,11 +245,7 @@ __device__ void gemv_multi(const GemvProb& p, int tile, float* xs, float* red,
     for (int v = 0; v < kMaxVec; ++v) {
       if (v < nv) {
         float xv[E];
-#pragma unroll
-        for (int e = 0; e < E; e += 4) {
-          float4 t = reinterpret_cast<const float4*>(xs + v * C + lane * E)[e / 4];
-          xv[e] = t.x; xv[e + 1] = t.y; xv[e + 2] = t.z; xv[e + 3] = t.w;
-        }
+        load_f32<E>(p.x + v * p.x_stride + k0, xv);
         if (g) {
           if (!shared_gain) load_f32<E>(g + v * p.gain_stride + k0, gv);
 #pragma unroll
@@ -263,50 +258,63 @@ __device__ void gemv_multi(const GemvProb& p, int tile, float* xs, float* red,
       }
     }
   }
-  if (idle) return;
+  // per-wave sums -> LDS, then wave 0 adds the four waves in order and finishes
+  float* mine = red + wave * RS;
 #pragma unroll
   for (int v = 0; v < kMaxVec; ++v) {
     if (v < nv) {
 #pragma unroll
-      for (int j = 0; j < RW; ++j) acc[j][v] = wave_sum(acc[j][v]);
-      ss[v] = g ? rsqrtf(wave_sum(ss[v]) / (float)K + p.eps) : 1.f;
-    }
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int v = 0; v < kMaxVec; ++v) {
-      if (v < nv) {
-#pragma unroll
-        for (int j = 0; j < RW; ++j) red[j * kMaxVec + v] = acc[j][v];
-        red[kRowsSingle * kMaxVec + v] = ss[v];
+      for (int j = 0; j < RW; ++j) {
+        const float s = wave_sum(acc[j][v]);
+        if (lane == 0) mine[j * kMaxVec + v] = s;
       }
+      const float t = wave_sum(ss[v]);
+      if (lane == 0) mine[RW * kMaxVec + v] = t;
     }
   }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  finish<T, RW>(p, u0, nunits, nv, red, rope);
+  __syncthreads();
+  if (wave != 0) return;
+  for (int t = lane; t < upw * nv; t += 64) {
+    const int ut = t % upw, v = t / upw;
+    if (u0 + ut >= nunits) continue;
+    int ja, jb;
+    unit_slots(p, ut, ja, jb);
+    float a = 0.f, b = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int u = 0; u < kSplit; ++u) {
+      a += red[u * RS + ja * kMaxVec + v];
+      b += red[u * RS + jb * kMaxVec + v];
+      s2 += red[u * RS + RW * kMaxVec + v];
+    }
+    const float sc = g ? rsqrtf(s2 / (float)K + p.eps) : 1.f;
+    epilogue<T>(p, v, u0 + ut, a * sc, b * sc, rope);
+  }
 }
 
-template <typename T>
+// Kernel kinds: 1 or 2 vectors (rows kernel) or up to kMaxVec (split-K).
+enum Kind { K_ROWS1 = 0, K_ROWS2 = 1, K_SPLITK = 2 };
+
+template <typename T, int KIND>
 __device__ __forceinline__ void gemv_body(const GemvProb* __restrict__ probs, int nprob,
                                           const float2* __restrict__ rope) {
-  __shared__ __attribute__((aligned(16))) float xs[kMaxVec * 64 * Elt<T>::N];
-  __shared__ float red[kWaves][kRed];
   const int b = blockIdx.x;
   const int pi = find_problem(probs, nprob, b);
   const GemvProb& p = probs[pi];
   const int tile = b - p.tile0;
-  float* r = red[threadIdx.x >> 6];
-  if (p.nvec == 1) gemv_single<T, kRowsSingle>(p, tile, r, rope);
-  else gemv_multi<T, kRowsMulti>(p, tile, xs, r, rope);
+  if constexpr (KIND == K_SPLITK) {
+    __shared__ float red[kSplit * (RW * kMaxVec + kMaxVec)];
+    splitk_body<T>(p, tile, red, rope);
+  } else {
+    rows_body<T, KIND == K_ROWS1 ? 1 : 2>(p, tile, rope);
+  }
 }
 
 // One kernel symbol per role in the step, so profiles separate them.
 #define SPD_GEMV_KERNEL(name)                                                              \
-  template <typename T>                                                                    \
+  template <typename T, int KIND>                                                          \
   __global__ __launch_bounds__(256) void name(const GemvProb* __restrict__ probs, int nprob, \
                                               const float2* __restrict__ rope) {           \
-    gemv_body<T>(probs, nprob, rope);                                                      \
+    gemv_body<T, KIND>(probs, nprob, rope);                                                \
   }
 SPD_GEMV_KERNEL(gemv_proj)
 SPD_GEMV_KERNEL(gemv_qkv)
@@ -316,28 +324,42 @@ SPD_GEMV_KERNEL(gemv_down)
 SPD_GEMV_KERNEL(gemv_head)
 #undef SPD_GEMV_KERNEL
 
-template <typename T>
-hipError_t launch_role(int role, const GemvProb* d_probs, int nprob, int ntiles,
-                       const float2* rope, hipStream_t st) {
-  const dim3 grid(ntiles), block(kWaves * 64);
+template <typename T, int KIND>
+void launch_kind(int role, dim3 grid, const GemvProb* d_probs, int nprob, const float2* rope,
+                 hipStream_t st) {
+  const dim3 block(kWaves * 64);
   switch (role) {
-    case GEMV_PROJ: hipLaunchKernelGGL(gemv_proj<T>, grid, block, 0, st, d_probs, nprob, rope); break;
-    case GEMV_QKV: hipLaunchKernelGGL(gemv_qkv<T>, grid, block, 0, st, d_probs, nprob, rope); break;
-    case GEMV_O: hipLaunchKernelGGL(gemv_o<T>, grid, block, 0, st, d_probs, nprob, rope); break;
-    case GEMV_GATE_UP: hipLaunchKernelGGL(gemv_gate_up<T>, grid, block, 0, st, d_probs, nprob, rope); break;
-    case GEMV_DOWN: hipLaunchKernelGGL(gemv_down<T>, grid, block, 0, st, d_probs, nprob, rope); break;
-    default: hipLaunchKernelGGL(gemv_head<T>, grid, block, 0, st, d_probs, nprob, rope); break;
+    case GEMV_PROJ: hipLaunchKernelGGL((gemv_proj<T, KIND>), grid, block, 0, st, d_probs, nprob, rope); break;
+    case GEMV_QKV: hipLaunchKernelGGL((gemv_qkv<T, KIND>), grid, block, 0, st, d_probs, nprob, rope); break;
+    case GEMV_O: hipLaunchKernelGGL((gemv_o<T, KIND>), grid, block, 0, st, d_probs, nprob, rope); break;
+    case GEMV_GATE_UP: hipLaunchKernelGGL((gemv_gate_up<T, KIND>), grid, block, 0, st, d_probs, nprob, rope); break;
+    case GEMV_DOWN: hipLaunchKernelGGL((gemv_down<T, KIND>), grid, block, 0, st, d_probs, nprob, rope); break;
+    default: hipLaunchKernelGGL((gemv_head<T, KIND>), grid, block, 0, st, d_probs, nprob, rope); break;
   }
-  return hipGetLastError();
+}
+
+template <typename T>
+void launch_t(int role, int maxvec, dim3 grid, const GemvProb* d_probs, int nprob,
+              const float2* rope, hipStream_t st) {
+  if (maxvec <= 1) launch_kind<T, K_ROWS1>(role, grid, d_probs, nprob, rope, st);
+  else if (maxvec == 2) launch_kind<T, K_ROWS2>(role, grid, d_probs, nprob, rope, st);
+  else launch_kind<T, K_SPLITK>(role, grid, d_probs, nprob, rope, st);
 }
 
 }  // namespace
 
-hipError_t launch_gemv(int role, const GemvProb* d_probs, int nprob, int ntiles, bool bf16,
-                       const float2* rope, hipStream_t st) {
+int gemv_units_per_tile(int nvec_max, bool is_paired) {
+  const int upw = is_paired ? RW / 2 : RW;
+  return nvec_max <= 2 ? kWaves * upw : upw;
+}
+
+hipError_t launch_gemv(int role, const GemvProb* d_probs, int nprob, int ntiles, int maxvec,
+                       bool bf16, const float2* rope, hipStream_t st) {
   if (ntiles <= 0 || nprob <= 0) return hipSuccess;
-  return bf16 ? launch_role<uint16_t>(role, d_probs, nprob, ntiles, rope, st)
-              : launch_role<float>(role, d_probs, nprob, ntiles, rope, st);
+  if (maxvec > kMaxVec) return hipErrorInvalidValue;
+  if (bf16) launch_t<uint16_t>(role, maxvec, dim3(ntiles), d_probs, nprob, rope, st);
+  else launch_t<float>(role, maxvec, dim3(ntiles), d_probs, nprob, rope, st);
+  return hipGetLastError();
 }
 
 }  // namespace spd

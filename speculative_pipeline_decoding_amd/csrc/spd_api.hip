@@ -49,9 +49,12 @@ struct Inflight {
   int stage;
 };
 
-// Launch kinds of a step (and their timing buckets).
+// Launch kinds of a step (and their timing buckets). The PDM's launches run on a
+// second stream, concurrently with the target's sub-layers (fork after the embed,
+// join before the LM head).
 enum OpKind { OP_EMBED = 0, OP_GEMV_PROJ, OP_GEMV_QKV, OP_ATTN, OP_LIN, OP_GEMV_O, OP_GEMV_GU,
-              OP_GEMV_DOWN, OP_GEMV_HEAD, OP_VOCAB, OP_FINAL, OP_RESID, OP_NKINDS };
+              OP_GEMV_DOWN, OP_GEMV_HEAD, OP_VOCAB, OP_FINAL, OP_RESID, OP_PDM_QKV, OP_PDM_ATTN,
+              OP_PDM_O, OP_PDM_GU, OP_PDM_DOWN, OP_NKINDS, OP_FORK = 100, OP_JOIN = 101 };
 
 struct Op {
   int kind;
@@ -60,6 +63,8 @@ struct Op {
   int ntiles;      // workgroups
   int split;       // attention split length
   double bytes;    // algorithmic HBM bytes (weights + KV) for the timing report
+  int stream = 0;  // 0: the caller's stream, 1: the PDM stream
+  int maxvec = 1;  // GEMV: largest vector count in the launch
 };
 
 struct Plan {
@@ -199,7 +204,9 @@ struct spd_handle {
   std::vector<int> forced_ref;
   // device
   char* ws;
-  hipStream_t st;
+  hipStream_t st;                 // the caller's stream: target chain, head, verify
+  hipStream_t st2 = nullptr;      // library-owned stream for the PDM chain
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   // pinned host staging
   char* h_desc = nullptr;
   Verdict* h_verdict = nullptr;
@@ -262,18 +269,20 @@ struct DescWriter {
   }
 };
 
-int units_per_tile(const GemvProb& g) {
-  const bool paired = g.epi == EPI_QKV || g.epi == EPI_SWIGLU;
-  const int rw = g.nvec == 1 ? kRowsSingle : kRowsMulti;
-  return kWaves * (paired ? rw / 2 : rw);
+int max_vec(const std::vector<GemvProb>& v) {
+  int m = 1;
+  for (auto& g : v) m = std::max(m, g.nvec);
+  return m;
 }
 
 int finish_tiles(std::vector<GemvProb>& v) {
+  const int mv = max_vec(v);
   int t = 0;
   for (auto& g : v) {
     const int units = g.epi == EPI_QKV ? g.rows / 2 : g.rows;
+    const int upt = gemv_units_per_tile(mv, g.epi == EPI_QKV || g.epi == EPI_SWIGLU);
     g.tile0 = t;
-    g.ntiles = (units + units_per_tile(g) - 1) / units_per_tile(g);
+    g.ntiles = (units + upt - 1) / upt;
     t += g.ntiles;
   }
   return t;
@@ -304,12 +313,12 @@ int attn_split(const Plan& p, const std::vector<AttnProb>& v) {
   return (int)s;
 }
 
-int finish_attn(const Plan& p, std::vector<AttnProb>& v, int split) {
+int finish_attn(const Plan& p, std::vector<AttnProb>& v, int split, int slot0) {
   int t = 0;
   for (size_t i = 0; i < v.size(); ++i) {
     v[i].nsplit = (v[i].len + split - 1) / split;
     v[i].tile0 = t;
-    v[i].slot = (int)i;
+    v[i].slot = slot0 + (int)i;
     t += p.hkv * v[i].nsplit;
   }
   return t;
@@ -326,48 +335,66 @@ void fill_rope(const Plan& p, std::vector<float2>& tab) {
     }
 }
 
+hipStream_t op_stream(const spd_handle* h, const Op& op) { return op.stream ? h->st2 : h->st; }
+
+int gemv_role(int kind) {
+  switch (kind) {
+    case OP_GEMV_PROJ: return GEMV_PROJ;
+    case OP_GEMV_QKV: case OP_PDM_QKV: return GEMV_QKV;
+    case OP_GEMV_O: case OP_PDM_O: return GEMV_O;
+    case OP_GEMV_GU: case OP_PDM_GU: return GEMV_GATE_UP;
+    case OP_GEMV_DOWN: case OP_PDM_DOWN: return GEMV_DOWN;
+  }
+  return GEMV_HEAD;
+}
+
 // Launch one op of the plan.
 hipError_t run_op(spd_handle* h, const Op& op) {
   const Plan& p = h->p;
   char* d = h->ws + p.o_desc;
   const float2* rope = h->at<float2>(p.o_rope);
+  hipStream_t st = op_stream(h, op);
   switch (op.kind) {
+    case OP_FORK: {
+      hipError_t e = hipEventRecord(h->ev_fork, h->st);
+      return e != hipSuccess ? e : hipStreamWaitEvent(h->st2, h->ev_fork, 0);
+    }
+    case OP_JOIN: {
+      hipError_t e = hipEventRecord(h->ev_join, h->st2);
+      return e != hipSuccess ? e : hipStreamWaitEvent(h->st, h->ev_join, 0);
+    }
     case OP_EMBED:
       return launch_embed_gather(reinterpret_cast<const EmbedGather*>(d + op.off), op.count, p.k,
-                                 p.d, p.bf16, h->st);
+                                 p.d, p.bf16, st);
     case OP_GEMV_PROJ: case OP_GEMV_QKV: case OP_GEMV_O: case OP_GEMV_GU: case OP_GEMV_DOWN:
-    case OP_GEMV_HEAD: {
-      const int role = op.kind == OP_GEMV_PROJ ? GEMV_PROJ : op.kind == OP_GEMV_QKV ? GEMV_QKV
-                     : op.kind == OP_GEMV_O ? GEMV_O : op.kind == OP_GEMV_GU ? GEMV_GATE_UP
-                     : op.kind == OP_GEMV_DOWN ? GEMV_DOWN : GEMV_HEAD;
-      return launch_gemv(role, reinterpret_cast<const GemvProb*>(d + op.off), op.count,
-                         op.ntiles, p.bf16, rope, h->st);
-    }
-    case OP_ATTN:
+    case OP_GEMV_HEAD: case OP_PDM_QKV: case OP_PDM_O: case OP_PDM_GU: case OP_PDM_DOWN:
+      return launch_gemv(gemv_role(op.kind), reinterpret_cast<const GemvProb*>(d + op.off),
+                         op.count, op.ntiles, op.maxvec, p.bf16, rope, st);
+    case OP_ATTN: case OP_PDM_ATTN:
       return launch_attention(reinterpret_cast<const AttnProb*>(d + op.off), op.count, op.ntiles,
                               p.bf16, p.hq, p.hkv, p.hd, p.max_ctx, op.split,
-                              op.ntiles > op.count * p.hkv, h->at<float>(p.o_apart), h->st);
+                              op.ntiles > op.count * p.hkv, h->at<float>(p.o_apart), st);
     case OP_VOCAB:
       return launch_vocab_stats(reinterpret_cast<const VocabDesc*>(d + op.off), kVocabBlocks,
-                                h->at<VocabPartial>(p.o_part), h->st);
+                                h->at<VocabPartial>(p.o_part), st);
     case OP_FINAL:
-      return launch_finalize(reinterpret_cast<const FinalizeDesc*>(d + op.off), h->st);
+      return launch_finalize(reinterpret_cast<const FinalizeDesc*>(d + op.off), st);
     case OP_RESID:
       return launch_residual_impl(reinterpret_cast<const FinalizeDesc*>(d + op.off),
-                                  h->at<VocabPartial>(p.o_part), kVocabBlocks, h->st);
+                                  h->at<VocabPartial>(p.o_part), kVocabBlocks, st);
   }
   return hipErrorInvalidValue;
 }
 
 int run_ops(spd_handle* h) {
   for (const Op& op : h->ops) {
-    if (h->timing) {
+    if (h->timing && op.kind < OP_NKINDS) {
       hipEvent_t a, b;
       HIPCHK(h, hipEventCreate(&a));
       HIPCHK(h, hipEventCreate(&b));
-      HIPCHK(h, hipEventRecord(a, h->st));
+      HIPCHK(h, hipEventRecord(a, op_stream(h, op)));
       HIPCHK(h, run_op(h, op));
-      HIPCHK(h, hipEventRecord(b, h->st));
+      HIPCHK(h, hipEventRecord(b, op_stream(h, op)));
       h->ev.push_back(a);
       h->ev.push_back(b);
       h->ev_kind.push_back(op.kind);
@@ -419,8 +446,25 @@ int build_step(spd_handle* h, DescWriter& dw) {
   float* qring = h->at<float>(p.o_qring);
   float* qlse = h->at<float>(p.o_qlse);
   const int kd = p.k * p.d;
+  auto push_gemv = [&](int kind, std::vector<GemvProb>& g, int stream) {
+    if (g.empty()) return;
+    const int nt = finish_tiles(g);
+    Op op{kind, dw.put(g.data(), (int)g.size()), (int)g.size(), nt, 0, gemv_bytes(g, p.esz)};
+    op.stream = stream;
+    op.maxvec = max_vec(g);
+    h->ops.push_back(op);
+  };
+  auto push_attn = [&](int kind, std::vector<AttnProb>& a, int stream, int slot0, double kvb) {
+    if (a.empty()) return;
+    const int split = attn_split(p, a);
+    const int nt = finish_attn(p, a, split, slot0);
+    Op op{kind, dw.put(a.data(), (int)a.size()), (int)a.size(), nt, split, kvb};
+    op.stream = stream;
+    h->ops.push_back(op);
+  };
 
-  // 1. embedding + PDM feature gather
+  // 1. embedding + PDM feature gather, on the caller's stream (it must precede the
+  //    target's first writes to the residual and anchor rings)
   EmbedGather eg{};
   eg.embed = h->embed;
   eg.tok_ring = h->at<int>(p.o_tok);
@@ -446,21 +490,58 @@ int build_step(spd_handle* h, DescWriter& dw) {
     }
   }
   h->ops.push_back({OP_EMBED, dw.put(&eg, 1), M, 0, 0, 0.0});
+  h->ops.push_back({OP_FORK, 0, 0, 0, 0, 0.0});
 
-  // 2. PDM projection of the gathered features
+  // 2. the PDM chain on its own stream: projection of the gathered features, then Ls
+  //    decoder layers over the M window rows (decode rows n .. n + M - 1)
   {
     std::vector<GemvProb> g{gemv(h->proj, p.d, kd, X, kd, M, EPI_STORE, hp, p.d, nullptr, 0, 0.f)};
-    const int nt = finish_tiles(g);
-    h->ops.push_back({OP_GEMV_PROJ, dw.put(g.data(), 1), 1, nt, 0, gemv_bytes(g, p.esz)});
+    push_gemv(OP_GEMV_PROJ, g, 1);
   }
-
-  // 3. sub-layers: every in-flight token at layer start(stage)+r, the PDM at layer r
-  const int n_inf = (int)h->F.size();
-  for (int r = 0; r < p.R; ++r) {
+  const int base = p.n;
+  for (int r = 0; r < p.Ls; ++r) {
+    const bool last = r == p.Ls - 1;
     std::vector<GemvProb> qkv, o, gu, down;
     std::vector<AttnProb> at;
-    const bool pdm_on = r < p.Ls;
-    const bool pdm_last = r == p.Ls - 1;
+    GemvProb q = gemv(h->PW(r, T_QKV), p.qrows, p.d, hp, p.d, M, EPI_QKV, nullptr, 0,
+                      (const float*)h->PW(r, T_ATTN_NORM), 0, p.eps);
+    q.aux = qbuf + (size_t)base * p.qo; q.aux_stride = p.qo;
+    q.kv_k = h->pK(r); q.kv_v = h->pV(r);
+    q.pos0 = h->pdm_len; q.hq = p.hq; q.hkv = p.hkv; q.hd = p.hd; q.max_ctx = p.max_ctx;
+    qkv.push_back(q);
+    for (int m = 0; m < M; ++m) {
+      AttnProb a{};
+      a.q = qbuf + (size_t)(base + m) * p.qo; a.out = attn + (size_t)(base + m) * p.qo;
+      a.K = h->pK(r); a.V = h->pV(r); a.len = h->pdm_len + m + 1;
+      at.push_back(a);
+    }
+    const double kvb = 2.0 * (h->pdm_len + M) * p.hkv * p.hd * p.esz;
+    // the last PDM layer only feeds the LM head: its O / FFN run on the newest row alone
+    const int r0 = last ? M - 1 : 0, nr = last ? 1 : M;
+    float* hrow = hp + (size_t)r0 * p.d;
+    o.push_back(gemv(h->PW(r, T_O), p.d, p.qo, attn + (size_t)(base + r0) * p.qo, p.qo, nr,
+                     EPI_ADD, hrow, p.d, nullptr, 0, 0.f));
+    GemvProb g = gemv(h->PW(r, T_GATE), p.F, p.d, hrow, p.d, nr, EPI_SWIGLU,
+                      act + (size_t)(base + r0) * p.F, p.F, (const float*)h->PW(r, T_FFN_NORM), 0,
+                      p.eps);
+    g.W2 = h->PW(r, T_UP);
+    gu.push_back(g);
+    down.push_back(gemv(h->PW(r, T_DOWN), p.d, p.F, act + (size_t)(base + r0) * p.F, p.F, nr,
+                        EPI_ADD, hrow, p.d, nullptr, 0, 0.f));
+    push_gemv(OP_PDM_QKV, qkv, 1);
+    push_attn(OP_PDM_ATTN, at, 1, p.n, kvb);
+    push_gemv(OP_PDM_O, o, 1);
+    push_gemv(OP_PDM_GU, gu, 1);
+    push_gemv(OP_PDM_DOWN, down, 1);
+  }
+
+  // 3. target sub-layers on the caller's stream: every in-flight token at layer
+  //    start(stage) + r, all stages in one launch per sub-layer op
+  const int n_inf = (int)h->F.size();
+  const int R = *std::max_element(p.sizes.begin(), p.sizes.end());
+  for (int r = 0; r < R; ++r) {
+    std::vector<GemvProb> qkv, o, gu, down;
+    std::vector<AttnProb> at;
     double kvb = 0;
     for (int j = 0; j < n_inf; ++j) {
       const Inflight f = h->F[j];
@@ -492,51 +573,13 @@ int build_step(spd_handle* h, DescWriter& dw) {
       down.push_back(dn);
       h->pend_layers.push_back({l, f.pos});
     }
-    if (pdm_on) {
-      const int base = p.n;   // PDM rows use decode rows n .. n + M - 1
-      GemvProb q = gemv(h->PW(r, T_QKV), p.qrows, p.d, hp, p.d, M, EPI_QKV, nullptr, 0,
-                        (const float*)h->PW(r, T_ATTN_NORM), 0, p.eps);
-      q.aux = qbuf + (size_t)base * p.qo; q.aux_stride = p.qo;
-      q.kv_k = h->pK(r); q.kv_v = h->pV(r);
-      q.pos0 = h->pdm_len; q.hq = p.hq; q.hkv = p.hkv; q.hd = p.hd; q.max_ctx = p.max_ctx;
-      qkv.push_back(q);
-      for (int m = 0; m < M; ++m) {
-        AttnProb a{};
-        a.q = qbuf + (size_t)(base + m) * p.qo; a.out = attn + (size_t)(base + m) * p.qo;
-        a.K = h->pK(r); a.V = h->pV(r); a.len = h->pdm_len + m + 1;
-        at.push_back(a);
-      }
-      kvb += 2.0 * (h->pdm_len + M) * p.hkv * p.hd * p.esz;
-      // the last PDM layer only feeds the LM head: its O / FFN run on the newest row alone
-      const int r0 = pdm_last ? M - 1 : 0, nr = pdm_last ? 1 : M;
-      float* hrow = hp + (size_t)r0 * p.d;
-      o.push_back(gemv(h->PW(r, T_O), p.d, p.qo, attn + (size_t)(base + r0) * p.qo, p.qo, nr,
-                       EPI_ADD, hrow, p.d, nullptr, 0, 0.f));
-      GemvProb g = gemv(h->PW(r, T_GATE), p.F, p.d, hrow, p.d, nr, EPI_SWIGLU,
-                        act + (size_t)(base + r0) * p.F, p.F, (const float*)h->PW(r, T_FFN_NORM),
-                        0, p.eps);
-      g.W2 = h->PW(r, T_UP);
-      gu.push_back(g);
-      down.push_back(gemv(h->PW(r, T_DOWN), p.d, p.F, act + (size_t)(base + r0) * p.F, p.F, nr,
-                          EPI_ADD, hrow, p.d, nullptr, 0, 0.f));
-    }
-    if (qkv.empty()) continue;
-    int nt = finish_tiles(qkv);
-    h->ops.push_back({OP_GEMV_QKV, dw.put(qkv.data(), (int)qkv.size()), (int)qkv.size(), nt, 0,
-                      gemv_bytes(qkv, p.esz)});
-    const int split = attn_split(p, at);
-    nt = finish_attn(p, at, split);
-    h->ops.push_back({OP_ATTN, dw.put(at.data(), (int)at.size()), (int)at.size(), nt, split, kvb});
-    nt = finish_tiles(o);
-    h->ops.push_back({OP_GEMV_O, dw.put(o.data(), (int)o.size()), (int)o.size(), nt, 0,
-                      gemv_bytes(o, p.esz)});
-    nt = finish_tiles(gu);
-    h->ops.push_back({OP_GEMV_GU, dw.put(gu.data(), (int)gu.size()), (int)gu.size(), nt, 0,
-                      gemv_bytes(gu, p.esz)});
-    nt = finish_tiles(down);
-    h->ops.push_back({OP_GEMV_DOWN, dw.put(down.data(), (int)down.size()), (int)down.size(), nt,
-                      0, gemv_bytes(down, p.esz)});
+    push_gemv(OP_GEMV_QKV, qkv, 0);
+    push_attn(OP_ATTN, at, 0, 0, kvb);
+    push_gemv(OP_GEMV_O, o, 0);
+    push_gemv(OP_GEMV_GU, gu, 0);
+    push_gemv(OP_GEMV_DOWN, down, 0);
   }
+  h->ops.push_back({OP_JOIN, 0, 0, 0, 0, 0.0});
 
   // 4. one sweep of the tied LM head: the exiting token's row and the PDM's newest row
   float* qnew = qring + (size_t)h->slot(dpos) * p.V;
@@ -552,8 +595,7 @@ int build_step(spd_handle* h, DescWriter& dw) {
       g = gemv(h->head, p.V, p.d, hnew, 0, 1, EPI_STORE, qnew, 0, h->pdm_final_norm, 0, p.eps);
     }
     std::vector<GemvProb> gv{g};
-    const int nt = finish_tiles(gv);
-    h->ops.push_back({OP_GEMV_HEAD, dw.put(gv.data(), 1), 1, nt, 0, gemv_bytes(gv, p.esz)});
+    push_gemv(OP_GEMV_HEAD, gv, 0);
   }
   const bool sampled = h->temp > 0.f;
   const float inv_t = sampled ? 1.f / h->temp : 1.f;
@@ -652,6 +694,9 @@ int spd_init(const spd_model_config* cfg, const spd_weights* w, const spd_sampli
     g_init_error = std::string(what) + ": " + hipGetErrorString(e);
     if (h->h_desc) (void)hipHostFree(h->h_desc);
     if (h->h_verdict) (void)hipHostFree(h->h_verdict);
+    if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
+    if (h->ev_join) (void)hipEventDestroy(h->ev_join);
+    if (h->st2) (void)hipStreamDestroy(h->st2);
     delete h;
     return SPD_E_DEVICE;
   };
@@ -660,6 +705,13 @@ int spd_init(const spd_model_config* cfg, const spd_weights* w, const spd_sampli
     return dev_fail(e, "hipHostMalloc");
   if ((e = hipHostMalloc((void**)&h->h_verdict, sizeof(Verdict), hipHostMallocDefault)) != hipSuccess)
     return dev_fail(e, "hipHostMalloc");
+  // the PDM stream (default priority) and the events that fork and join it each step
+  if ((e = hipStreamCreateWithFlags(&h->st2, hipStreamNonBlocking)) != hipSuccess)
+    return dev_fail(e, "hipStreamCreateWithFlags");
+  if ((e = hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming)) != hipSuccess)
+    return dev_fail(e, "hipEventCreateWithFlags");
+  if ((e = hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming)) != hipSuccess)
+    return dev_fail(e, "hipEventCreateWithFlags");
   std::vector<float2> rope;
   fill_rope(p, rope);
   if ((e = hipMemcpyAsync(h->ws + p.o_rope, rope.data(), rope.size() * sizeof(float2),
@@ -760,7 +812,7 @@ int spd_prefill(spd_handle* h, const int32_t* prompt, int32_t len, int32_t* firs
       const size_t fo = dw.put(&fd, 1);
       char* d = h->ws + p.o_desc;
       HIPCHK(h, hipMemcpyAsync(d, h->h_desc, dw.used, hipMemcpyHostToDevice, st));
-      HIPCHK(h, launch_gemv(GEMV_HEAD, reinterpret_cast<const GemvProb*>(d + go), 1, nt, bf, rope, st));
+      HIPCHK(h, launch_gemv(GEMV_HEAD, reinterpret_cast<const GemvProb*>(d + go), 1, nt, 1, bf, rope, st));
       HIPCHK(h, launch_vocab_stats(reinterpret_cast<const VocabDesc*>(d + vo), kVocabBlocks,
                                    h->at<VocabPartial>(p.o_part), st));
       HIPCHK(h, launch_finalize(reinterpret_cast<const FinalizeDesc*>(d + fo), st));
@@ -928,8 +980,12 @@ void spd_destroy(spd_handle* h) {
   if (!h) return;
   (void)hipStreamSynchronize(h->st);
   for (auto e : h->ev) (void)hipEventDestroy(e);
+  if (h->st2) (void)hipStreamSynchronize(h->st2);
   if (h->h_desc) (void)hipHostFree(h->h_desc);
   if (h->h_verdict) (void)hipHostFree(h->h_verdict);
+  if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
+  if (h->ev_join) (void)hipEventDestroy(h->ev_join);
+  if (h->st2) (void)hipStreamDestroy(h->st2);
   delete h;
 }
 

@@ -12,8 +12,6 @@ constexpr int kMaxStages = 16;          // n
 constexpr int kMaxRows = kMaxStages + 1;  // PDM rows per step: n + 1
 constexpr int kMaxAnchors = 8;          // k
 constexpr int kWaves = 4;               // waves per GEMV workgroup
-constexpr int kRowsSingle = 8;          // weight rows per wave, one input vector
-constexpr int kRowsMulti = 4;           // weight rows per wave, several input vectors
 constexpr int kMaxVec = kMaxRows;       // input vectors of one GEMV problem
 constexpr int kAttnTile = 64;           // keys per attention tile
 constexpr int kVocabBlock = 1024;       // threads of the vocabulary reduction blocks
@@ -178,6 +176,40 @@ __device__ __forceinline__ float rng_uniform(unsigned long long seed, int stream
 
 __device__ __forceinline__ float gumbel_of(float u) { return -logf(-logf(u)); }
 
+// ---- wavefront (64-lane) reductions with DPP moves --------------------------
+// Within each row of 16 lanes: xor 1 and xor 2 by quad permutes, then the
+// half-row and row mirrors; across the four rows: readlane of lanes 0, 16, 32,
+// 48. Every lane gets the same result, in the same order in every wave.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_mov<0xB1>(v);    // quad_perm [1,0,3,2]
+  v += dpp_mov<0x4E>(v);    // quad_perm [2,3,0,1]
+  v += dpp_mov<0x141>(v);   // row_half_mirror
+  v += dpp_mov<0x140>(v);   // row_mirror
+  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_mov<0xB1>(v));
+  v = fmaxf(v, dpp_mov<0x4E>(v));
+  v = fmaxf(v, dpp_mov<0x141>(v));
+  v = fmaxf(v, dpp_mov<0x140>(v));
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
+}
+
+// 16 bytes of weights, streamed once: a nontemporal load keeps them from
+// displacing reusable lines (activations, KV rows) in the caches.
+__device__ __forceinline__ uint4 load_stream(const void* p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Index of the problem that owns workgroup b in a grouped launch whose problems
 // start at ascending workgroups tile0 (nprob <= 64). Each lane reads one start,
 // so the search costs one memory round trip instead of a chain of dependent loads.
@@ -194,8 +226,10 @@ __device__ __forceinline__ int find_problem(const P* __restrict__ probs, int npr
 // ---- kernel launchers (one per .hip file) -----------------------------------
 namespace spd {
 enum GemvRole : int { GEMV_PROJ = 0, GEMV_QKV, GEMV_O, GEMV_GATE_UP, GEMV_DOWN, GEMV_HEAD };
-hipError_t launch_gemv(int role, const GemvProb* d_probs, int nprob, int ntiles, bool bf16,
-                       const float2* rope, hipStream_t st);
+// maxvec: the largest nvec in the launch (1, 2: rows kernel; more: split-K kernel)
+hipError_t launch_gemv(int role, const GemvProb* d_probs, int nprob, int ntiles, int maxvec,
+                       bool bf16, const float2* rope, hipStream_t st);
+int gemv_units_per_tile(int nvec_max, bool is_paired);
 hipError_t launch_attention(const AttnProb* d_probs, int nprob, int ntiles, bool bf16,
                             int hq, int hkv, int hd, int max_ctx, int split_len, bool any_split,
                             float* partials, hipStream_t st);
