@@ -16,8 +16,11 @@ synthetic data of the workload's shape.
 
 Timed region: W warm-up steps, then exactly K steps between two device
 synchronisations, with inputs resident in HBM. value = committed tokens / s.
-Per-launch timing for the roofline comes from HIP events recorded by the
-library on its own stream over a second region of K steps right after it.
+Per-launch durations for the roofline come from HIP start/stop events that the
+library binds to each launch's dispatch packet (hipExtLaunchKernel), on the
+stream the launch runs on, over a second pass of the same warm-up and timed
+steps replayed from a fresh prefill (the events cost ~15% of step time, so the
+headline region runs without them).
 """
 from __future__ import annotations
 
@@ -47,7 +50,7 @@ def pct(xs, q):
     return xs[i]
 
 
-def run_spd(cfg, dW, prompt, T, seed, warmup, steps, instrument):
+def run_spd(cfg, dW, prompt, T, seed, warmup, steps, kernel_timing):
     import torch
     from speculative_pipeline_decoding_amd import SPD
     stream = torch.cuda.current_stream()
@@ -56,14 +59,12 @@ def run_spd(cfg, dW, prompt, T, seed, warmup, steps, instrument):
     spd.prefill(prompt)
     torch.cuda.synchronize()
     prefill_s = time.perf_counter() - t
+    out = {"prefill_s": prefill_s}
     for _ in range(warmup):
         spd.step()
         spd.verify_commit()
-    out = {"prefill_s": prefill_s}
 
-    def region(with_kernel_events):
-        if with_kernel_events:
-            spd.timing(True)
+    def region():
         s0 = spd.stats()
         evs, kinds = [], []
         torch.cuda.synchronize()
@@ -81,27 +82,46 @@ def run_spd(cfg, dW, prompt, T, seed, warmup, steps, instrument):
         wall = time.perf_counter() - t0
         s1 = spd.stats()
         step_ms = [a.elapsed_time(b) for a, b in evs]
-        res = {"wall_s": wall, "N": s1.N - s0.N, "K": s1.K - s0.K, "step_ms": step_ms,
-               "full": [m for m, k in zip(step_ms, kinds) if k],
-               "refill": [m for m, k in zip(step_ms, kinds) if not k]}
-        if with_kernel_events:
-            res["kernels"] = spd.timing_read()
-            spd.timing(False)
-        return res
+        return s1, {"wall_s": wall, "N": s1.N - s0.N, "K": s1.K - s0.K, "step_ms": step_ms,
+                    "full": [m for m, k in zip(step_ms, kinds) if k],
+                    "refill": [m for m, k in zip(step_ms, kinds) if not k]}
 
-    out["timed"] = region(False)
-    if instrument:
-        # the same steps again from a fresh prefill, each launch bracketed by HIP events
+    s1, out["timed"] = region()
+    if kernel_timing:
+        # The same steps again from a fresh prefill, with start/stop events bound to each
+        # launch's dispatch packet (kernel durations without the command processor's gaps).
+        # They are kept out of the headline region, which runs without them.
         spd.reset()
         spd.prefill(prompt)
+        spd.timing(True)
         for _ in range(warmup):
             spd.step()
             spd.verify_commit()
-        out["instrumented"] = region(True)
-    st = spd.stats()
-    out["alpha_total"], out["s0_total"] = st.alpha, st.s0
+        _, kt = region()
+        out["kernels"] = spd.timing_read()
+        out["kernel_steps"] = warmup + steps
+        spd.timing(False)
+    out["alpha_total"], out["s0_total"] = s1.alpha, s1.s0
     spd.close()
     return out
+
+
+def traffic_from_profile(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary, or None
+    when there is none or it was taken on a different GEMV source than the current one."""
+    from speculative_pipeline_decoding_amd.profile_summary import source_hash
+    path = os.path.join(ROOT, "profiles", f"{kernel}_traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    digest, value = None, None
+    for line in open(path):
+        if line.startswith("gemv source sha256[:16]:"):
+            digest = line.split(":", 1)[1].strip()
+        if line.startswith("traffic_bytes_per_launch"):
+            value = float(line.split()[-1])
+    if digest != source_hash() or value is None:
+        return None
+    return value
 
 
 def cpu_baseline(cfg, W, T, seed, alpha, budget_s):
@@ -203,8 +223,8 @@ def main():
     value = tm["N"] / tm["wall_s"]
     ms_per_step = tm["wall_s"] * 1e3 / tm["K"]
     alpha = tm["N"] / tm["K"]
-    kern = main_run["instrumented"]["kernels"]
-    ik = main_run["instrumented"]["K"]
+    kern = main_run["kernels"]
+    ik = main_run["kernel_steps"]
     step_bytes = sum(v["bytes"] for v in kern.values()) / ik
     gpu_step_ms = statistics.mean(tm["step_ms"])
     dominant = max((k for k in kern if k.startswith("gemv") and kern[k]["count"]),
@@ -235,7 +255,10 @@ def main():
                    "prompt_ids": "uniform random"},
         "roofline": {"bound": "hbm", "kernel": dominant,
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic_from_profile(cfg.name, dominant),
+                     "algorithmic_bytes_per_launch": d["bytes"] / d["count"],
+                     "avg_launch_us": 1e3 * d["ms"] / d["count"]},
         "step_us": {"median": 1e3 * statistics.median(tm["step_ms"]),
                     "p10": 1e3 * pct(tm["step_ms"], 0.1), "p90": 1e3 * pct(tm["step_ms"], 0.9),
                     "full_median": 1e3 * statistics.median(tm["full"]) if tm["full"] else None,

@@ -255,28 +255,30 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_merge_kernel(
 template <typename T, int HD, int GMAX>
 void launch_one(dim3 grid, hipStream_t st, const AttnProb* probs, int nprob, const float* pq,
                 int q_stride, float* pout, int out_stride, const void* pK, const void* pV,
-                int pos0, int G, int hkv, int max_ctx, int split, float* part, bool merge) {
-  hipLaunchKernelGGL((attn_kernel<T, HD, GMAX>), grid, dim3(kAttnWaves * 64), 0, st, probs, nprob,
-                     pq, q_stride, pout, out_stride, pK, pV, pos0, G, hkv, max_ctx, split, part);
+                int pos0, int G, int hkv, int max_ctx, int split, float* part, bool merge,
+                LaunchEv ev) {
+  LaunchEv e1{ev.start, merge ? nullptr : ev.stop}, e2{nullptr, ev.stop};
+  SPD_LAUNCH(e1, (attn_kernel<T, HD, GMAX>), grid, dim3(kAttnWaves * 64), 0, st, probs, nprob,
+             pq, q_stride, pout, out_stride, pK, pV, pos0, G, hkv, max_ctx, split, part);
   if (merge)
-    hipLaunchKernelGGL((attn_merge_kernel<HD>), dim3(nprob * hkv), dim3(kAttnWaves * 64), 0, st,
-                       probs, G, hkv, part);
+    SPD_LAUNCH(e2, (attn_merge_kernel<HD>), dim3(nprob * hkv), dim3(kAttnWaves * 64), 0, st,
+               probs, G, hkv, part);
 }
 
 template <typename T>
 hipError_t dispatch(dim3 grid, hipStream_t st, const AttnProb* probs, int nprob, const float* pq,
                     int q_stride, float* pout, int out_stride, const void* pK, const void* pV,
                     int pos0, int hq, int hkv, int hd, int max_ctx, int split, float* part,
-                    bool merge) {
+                    bool merge, LaunchEv ev = {}) {
   const int G = hq / hkv;
 #define SPD_ATTN_CASE(HDV)                                                                   \
   if (hd == HDV) {                                                                           \
     if (G <= 4)                                                                              \
       launch_one<T, HDV, 4>(grid, st, probs, nprob, pq, q_stride, pout, out_stride, pK, pV,  \
-                            pos0, G, hkv, max_ctx, split, part, merge);                        \
+                            pos0, G, hkv, max_ctx, split, part, merge, ev);                        \
     else                                                                                     \
       launch_one<T, HDV, 16>(grid, st, probs, nprob, pq, q_stride, pout, out_stride, pK, pV, \
-                             pos0, G, hkv, max_ctx, split, part, merge);                       \
+                             pos0, G, hkv, max_ctx, split, part, merge, ev);                       \
     return hipGetLastError();                                                                \
   }
   SPD_ATTN_CASE(16)
@@ -298,13 +300,13 @@ bool attn_supported_head_dim(int hd, bool bf16) {
 
 hipError_t launch_attention(const AttnProb* d_probs, int nprob, int ntiles, bool bf16, int hq,
                             int hkv, int hd, int max_ctx, int split_len, bool any_split,
-                            float* partials, hipStream_t st) {
+                            float* partials, hipStream_t st, LaunchEv ev) {
   if (ntiles <= 0) return hipSuccess;
   if (bf16)
     return dispatch<uint16_t>(dim3(ntiles), st, d_probs, nprob, nullptr, 0, nullptr, 0, nullptr,
-                              nullptr, 0, hq, hkv, hd, max_ctx, split_len, partials, any_split);
+                              nullptr, 0, hq, hkv, hd, max_ctx, split_len, partials, any_split, ev);
   return dispatch<float>(dim3(ntiles), st, d_probs, nprob, nullptr, 0, nullptr, 0, nullptr,
-                         nullptr, 0, hq, hkv, hd, max_ctx, split_len, partials, any_split);
+                         nullptr, 0, hq, hkv, hd, max_ctx, split_len, partials, any_split, ev);
 }
 
 hipError_t launch_attention_prefill(const float* q, int q_stride, float* out, int out_stride,

@@ -322,28 +322,36 @@ SPD_GEMV_KERNEL(gemv_o)
 SPD_GEMV_KERNEL(gemv_gate_up)
 SPD_GEMV_KERNEL(gemv_down)
 SPD_GEMV_KERNEL(gemv_head)
+SPD_GEMV_KERNEL(pdm_gemv_qkv)
+SPD_GEMV_KERNEL(pdm_gemv_o)
+SPD_GEMV_KERNEL(pdm_gemv_gate_up)
+SPD_GEMV_KERNEL(pdm_gemv_down)
 #undef SPD_GEMV_KERNEL
 
 template <typename T, int KIND>
 void launch_kind(int role, dim3 grid, const GemvProb* d_probs, int nprob, const float2* rope,
-                 hipStream_t st) {
+                 hipStream_t st, LaunchEv ev) {
   const dim3 block(kWaves * 64);
   switch (role) {
-    case GEMV_PROJ: hipLaunchKernelGGL((gemv_proj<T, KIND>), grid, block, 0, st, d_probs, nprob, rope); break;
-    case GEMV_QKV: hipLaunchKernelGGL((gemv_qkv<T, KIND>), grid, block, 0, st, d_probs, nprob, rope); break;
-    case GEMV_O: hipLaunchKernelGGL((gemv_o<T, KIND>), grid, block, 0, st, d_probs, nprob, rope); break;
-    case GEMV_GATE_UP: hipLaunchKernelGGL((gemv_gate_up<T, KIND>), grid, block, 0, st, d_probs, nprob, rope); break;
-    case GEMV_DOWN: hipLaunchKernelGGL((gemv_down<T, KIND>), grid, block, 0, st, d_probs, nprob, rope); break;
-    default: hipLaunchKernelGGL((gemv_head<T, KIND>), grid, block, 0, st, d_probs, nprob, rope); break;
+    case GEMV_PROJ: SPD_LAUNCH(ev, (gemv_proj<T, KIND>), grid, block, 0, st, d_probs, nprob, rope); break;
+    case GEMV_QKV: SPD_LAUNCH(ev, (gemv_qkv<T, KIND>), grid, block, 0, st, d_probs, nprob, rope); break;
+    case GEMV_O: SPD_LAUNCH(ev, (gemv_o<T, KIND>), grid, block, 0, st, d_probs, nprob, rope); break;
+    case GEMV_GATE_UP: SPD_LAUNCH(ev, (gemv_gate_up<T, KIND>), grid, block, 0, st, d_probs, nprob, rope); break;
+    case GEMV_DOWN: SPD_LAUNCH(ev, (gemv_down<T, KIND>), grid, block, 0, st, d_probs, nprob, rope); break;
+    case GEMV_PDM_QKV: SPD_LAUNCH(ev, (pdm_gemv_qkv<T, KIND>), grid, block, 0, st, d_probs, nprob, rope); break;
+    case GEMV_PDM_O: SPD_LAUNCH(ev, (pdm_gemv_o<T, KIND>), grid, block, 0, st, d_probs, nprob, rope); break;
+    case GEMV_PDM_GATE_UP: SPD_LAUNCH(ev, (pdm_gemv_gate_up<T, KIND>), grid, block, 0, st, d_probs, nprob, rope); break;
+    case GEMV_PDM_DOWN: SPD_LAUNCH(ev, (pdm_gemv_down<T, KIND>), grid, block, 0, st, d_probs, nprob, rope); break;
+    default: SPD_LAUNCH(ev, (gemv_head<T, KIND>), grid, block, 0, st, d_probs, nprob, rope); break;
   }
 }
 
 template <typename T>
 void launch_t(int role, int maxvec, dim3 grid, const GemvProb* d_probs, int nprob,
-              const float2* rope, hipStream_t st) {
-  if (maxvec <= 1) launch_kind<T, K_ROWS1>(role, grid, d_probs, nprob, rope, st);
-  else if (maxvec == 2) launch_kind<T, K_ROWS2>(role, grid, d_probs, nprob, rope, st);
-  else launch_kind<T, K_SPLITK>(role, grid, d_probs, nprob, rope, st);
+              const float2* rope, hipStream_t st, LaunchEv ev) {
+  if (maxvec <= 1) launch_kind<T, K_ROWS1>(role, grid, d_probs, nprob, rope, st, ev);
+  else if (maxvec == 2) launch_kind<T, K_ROWS2>(role, grid, d_probs, nprob, rope, st, ev);
+  else launch_kind<T, K_SPLITK>(role, grid, d_probs, nprob, rope, st, ev);
 }
 
 }  // namespace
@@ -354,11 +362,11 @@ int gemv_units_per_tile(int nvec_max, bool is_paired) {
 }
 
 hipError_t launch_gemv(int role, const GemvProb* d_probs, int nprob, int ntiles, int maxvec,
-                       bool bf16, const float2* rope, hipStream_t st) {
+                       bool bf16, const float2* rope, hipStream_t st, LaunchEv ev) {
   if (ntiles <= 0 || nprob <= 0) return hipSuccess;
   if (maxvec > kMaxVec) return hipErrorInvalidValue;
-  if (bf16) launch_t<uint16_t>(role, maxvec, dim3(ntiles), d_probs, nprob, rope, st);
-  else launch_t<float>(role, maxvec, dim3(ntiles), d_probs, nprob, rope, st);
+  if (bf16) launch_t<uint16_t>(role, maxvec, dim3(ntiles), d_probs, nprob, rope, st, ev);
+  else launch_t<float>(role, maxvec, dim3(ntiles), d_probs, nprob, rope, st, ev);
   return hipGetLastError();
 }
 

@@ -145,11 +145,11 @@ __global__ void copy_rows_kernel(const float* __restrict__ s, int ss, float* __r
 }  // namespace
 
 hipError_t launch_embed_gather(const EmbedGather* d_desc, int M, int k, int d, bool bf16,
-                               hipStream_t s) {
+                               hipStream_t s, LaunchEv ev) {
   (void)d;
   const dim3 grid(1 + M * k);
-  if (bf16) hipLaunchKernelGGL(embed_gather_kernel<uint16_t>, grid, dim3(256), 0, s, d_desc);
-  else hipLaunchKernelGGL(embed_gather_kernel<float>, grid, dim3(256), 0, s, d_desc);
+  if (bf16) SPD_LAUNCH(ev, embed_gather_kernel<uint16_t>, grid, dim3(256), 0, s, d_desc);
+  else SPD_LAUNCH(ev, embed_gather_kernel<float>, grid, dim3(256), 0, s, d_desc);
   return hipGetLastError();
 }
 

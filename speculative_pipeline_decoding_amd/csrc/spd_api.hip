@@ -340,16 +340,20 @@ hipStream_t op_stream(const spd_handle* h, const Op& op) { return op.stream ? h-
 int gemv_role(int kind) {
   switch (kind) {
     case OP_GEMV_PROJ: return GEMV_PROJ;
-    case OP_GEMV_QKV: case OP_PDM_QKV: return GEMV_QKV;
-    case OP_GEMV_O: case OP_PDM_O: return GEMV_O;
-    case OP_GEMV_GU: case OP_PDM_GU: return GEMV_GATE_UP;
-    case OP_GEMV_DOWN: case OP_PDM_DOWN: return GEMV_DOWN;
+    case OP_GEMV_QKV: return GEMV_QKV;
+    case OP_GEMV_O: return GEMV_O;
+    case OP_GEMV_GU: return GEMV_GATE_UP;
+    case OP_GEMV_DOWN: return GEMV_DOWN;
+    case OP_PDM_QKV: return GEMV_PDM_QKV;
+    case OP_PDM_O: return GEMV_PDM_O;
+    case OP_PDM_GU: return GEMV_PDM_GATE_UP;
+    case OP_PDM_DOWN: return GEMV_PDM_DOWN;
   }
   return GEMV_HEAD;
 }
 
-// Launch one op of the plan.
-hipError_t run_op(spd_handle* h, const Op& op) {
+// Launch one op of the plan (with packet-bound timing events when ev is set).
+hipError_t run_op(spd_handle* h, const Op& op, LaunchEv ev = {}) {
   const Plan& p = h->p;
   char* d = h->ws + p.o_desc;
   const float2* rope = h->at<float2>(p.o_rope);
@@ -365,40 +369,37 @@ hipError_t run_op(spd_handle* h, const Op& op) {
     }
     case OP_EMBED:
       return launch_embed_gather(reinterpret_cast<const EmbedGather*>(d + op.off), op.count, p.k,
-                                 p.d, p.bf16, st);
+                                 p.d, p.bf16, st, ev);
     case OP_GEMV_PROJ: case OP_GEMV_QKV: case OP_GEMV_O: case OP_GEMV_GU: case OP_GEMV_DOWN:
     case OP_GEMV_HEAD: case OP_PDM_QKV: case OP_PDM_O: case OP_PDM_GU: case OP_PDM_DOWN:
       return launch_gemv(gemv_role(op.kind), reinterpret_cast<const GemvProb*>(d + op.off),
-                         op.count, op.ntiles, op.maxvec, p.bf16, rope, st);
+                         op.count, op.ntiles, op.maxvec, p.bf16, rope, st, ev);
     case OP_ATTN: case OP_PDM_ATTN:
       return launch_attention(reinterpret_cast<const AttnProb*>(d + op.off), op.count, op.ntiles,
                               p.bf16, p.hq, p.hkv, p.hd, p.max_ctx, op.split,
-                              op.ntiles > op.count * p.hkv, h->at<float>(p.o_apart), st);
+                              op.ntiles > op.count * p.hkv, h->at<float>(p.o_apart), st, ev);
     case OP_VOCAB:
       return launch_vocab_stats(reinterpret_cast<const VocabDesc*>(d + op.off), kVocabBlocks,
-                                h->at<VocabPartial>(p.o_part), st);
+                                h->at<VocabPartial>(p.o_part), st, ev);
     case OP_FINAL:
-      return launch_finalize(reinterpret_cast<const FinalizeDesc*>(d + op.off), st);
+      return launch_finalize(reinterpret_cast<const FinalizeDesc*>(d + op.off), st, ev);
     case OP_RESID:
       return launch_residual_impl(reinterpret_cast<const FinalizeDesc*>(d + op.off),
-                                  h->at<VocabPartial>(p.o_part), kVocabBlocks, st);
+                                  h->at<VocabPartial>(p.o_part), kVocabBlocks, st, ev);
   }
   return hipErrorInvalidValue;
 }
 
 int run_ops(spd_handle* h) {
+  size_t k = 0;
   for (const Op& op : h->ops) {
     if (h->timing && op.kind < OP_NKINDS) {
-      hipEvent_t a, b;
-      HIPCHK(h, hipEventCreate(&a));
-      HIPCHK(h, hipEventCreate(&b));
-      HIPCHK(h, hipEventRecord(a, op_stream(h, op)));
-      HIPCHK(h, run_op(h, op));
-      HIPCHK(h, hipEventRecord(b, op_stream(h, op)));
-      h->ev.push_back(a);
-      h->ev.push_back(b);
+      if (2 * k + 1 >= h->ev.size()) return fail(h, SPD_E_CAPACITY, "internal: timing event pool");
+      const LaunchEv ev{h->ev[2 * k], h->ev[2 * k + 1]};
+      HIPCHK(h, run_op(h, op, ev));
       h->ev_kind.push_back(op.kind);
       h->ev_bytes.push_back(op.bytes);
+      ++k;
     } else {
       HIPCHK(h, run_op(h, op));
     }
@@ -413,10 +414,7 @@ int collect_timing(spd_handle* h) {
     h->kt_ms[h->ev_kind[i]] += ms;
     h->kt_bytes[h->ev_kind[i]] += h->ev_bytes[i];
     h->kt_count[h->ev_kind[i]] += 1;
-    (void)hipEventDestroy(h->ev[2 * i]);
-    (void)hipEventDestroy(h->ev[2 * i + 1]);
   }
-  h->ev.clear();
   h->ev_kind.clear();
   h->ev_bytes.clear();
   return SPD_OK;
@@ -995,6 +993,13 @@ int spd_timing_enable(spd_handle* h, int on) {
   if (h->state == spd_handle::S_PENDING) return fail(h, SPD_E_STATE, "a step is pending");
   h->timing = on != 0;
   for (int i = 0; i < OP_NKINDS; ++i) { h->kt_ms[i] = 0; h->kt_bytes[i] = 0; h->kt_count[i] = 0; }
+  // two events per timed launch of a step, created once and reused every step
+  const size_t want = 2 * (size_t)(8 + 5 * (h->p.L + h->p.Ls));
+  while (h->timing && h->ev.size() < want) {
+    hipEvent_t e;
+    HIPCHK(h, hipEventCreate(&e));
+    h->ev.push_back(e);
+  }
   return SPD_OK;
 }
 

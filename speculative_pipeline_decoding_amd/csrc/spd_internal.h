@@ -3,6 +3,7 @@
 // read by every workgroup of a grouped launch.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -225,14 +226,30 @@ __device__ __forceinline__ int find_problem(const P* __restrict__ probs, int npr
 
 // ---- kernel launchers (one per .hip file) -----------------------------------
 namespace spd {
-enum GemvRole : int { GEMV_PROJ = 0, GEMV_QKV, GEMV_O, GEMV_GATE_UP, GEMV_DOWN, GEMV_HEAD };
+// Optional timing events bound to the dispatch packets themselves (start: when the
+// first launch of an op begins, stop: when its last one ends), so a measured
+// duration is the kernels' own and excludes the command processor's gaps.
+struct LaunchEv {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+#define SPD_LAUNCH(ev, kernel, grid, block, shm, st, ...)                                     \
+  do {                                                                                       \
+    if ((ev).start || (ev).stop)                                                             \
+      hipExtLaunchKernelGGL(kernel, grid, block, shm, st, (ev).start, (ev).stop, 0, __VA_ARGS__); \
+    else                                                                                     \
+      hipLaunchKernelGGL(kernel, grid, block, shm, st, __VA_ARGS__);                         \
+  } while (0)
+
+enum GemvRole : int { GEMV_PROJ = 0, GEMV_QKV, GEMV_O, GEMV_GATE_UP, GEMV_DOWN, GEMV_HEAD,
+                      GEMV_PDM_QKV, GEMV_PDM_O, GEMV_PDM_GATE_UP, GEMV_PDM_DOWN };
 // maxvec: the largest nvec in the launch (1, 2: rows kernel; more: split-K kernel)
 hipError_t launch_gemv(int role, const GemvProb* d_probs, int nprob, int ntiles, int maxvec,
-                       bool bf16, const float2* rope, hipStream_t st);
+                       bool bf16, const float2* rope, hipStream_t st, LaunchEv ev = {});
 int gemv_units_per_tile(int nvec_max, bool is_paired);
 hipError_t launch_attention(const AttnProb* d_probs, int nprob, int ntiles, bool bf16,
                             int hq, int hkv, int hd, int max_ctx, int split_len, bool any_split,
-                            float* partials, hipStream_t st);
+                            float* partials, hipStream_t st, LaunchEv ev = {});
 hipError_t launch_attention_prefill(const float* q, int q_stride, float* out, int out_stride,
                                     const void* K, const void* V, int pos0, int P, bool bf16,
                                     int hq, int hkv, int hd, int max_ctx, hipStream_t st);
@@ -242,12 +259,12 @@ hipError_t launch_linear_scan(const float* qkv, int qkv_stride, float* out, int 
                               const float* s_in, float* s_out, int P, int H, int hd, float eps,
                               hipStream_t st);
 hipError_t launch_embed_gather(const EmbedGather* d_desc, int M, int k, int d, bool bf16,
-                               hipStream_t st);
+                               hipStream_t st, LaunchEv ev = {});
 hipError_t launch_vocab_stats(const VocabDesc* d_desc, int nblocks, VocabPartial* part,
-                              hipStream_t st);
-hipError_t launch_finalize(const FinalizeDesc* d_desc, hipStream_t st);
+                              hipStream_t st, LaunchEv ev = {});
+hipError_t launch_finalize(const FinalizeDesc* d_desc, hipStream_t st, LaunchEv ev = {});
 hipError_t launch_residual_impl(const FinalizeDesc* d_desc, VocabPartial* part, int nblocks,
-                                hipStream_t st);
+                                hipStream_t st, LaunchEv ev = {});
 // prefill helpers
 hipError_t launch_embed_rows(const void* embed, const int* toks, float* H, int P, int d,
                              bool bf16, hipStream_t st);

@@ -225,20 +225,21 @@ __global__ __launch_bounds__(kVocabBlock) void residual_final_kernel(
 }  // namespace
 
 hipError_t launch_vocab_stats(const VocabDesc* d_desc, int nblocks, VocabPartial* part,
-                              hipStream_t st) {
-  hipLaunchKernelGGL(vocab_stats_kernel, dim3(nblocks), dim3(kVocabBlock), 0, st, d_desc, part);
+                              hipStream_t st, LaunchEv ev) {
+  SPD_LAUNCH(ev, vocab_stats_kernel, dim3(nblocks), dim3(kVocabBlock), 0, st, d_desc, part);
   return hipGetLastError();
 }
 
-hipError_t launch_finalize(const FinalizeDesc* d_desc, hipStream_t st) {
-  hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(kVocabBlock), 0, st, d_desc);
+hipError_t launch_finalize(const FinalizeDesc* d_desc, hipStream_t st, LaunchEv ev) {
+  SPD_LAUNCH(ev, finalize_kernel, dim3(1), dim3(kVocabBlock), 0, st, d_desc);
   return hipGetLastError();
 }
 
 hipError_t launch_residual_impl(const FinalizeDesc* d_desc, VocabPartial* part, int nblocks,
-                                hipStream_t st) {
-  hipLaunchKernelGGL(residual_kernel, dim3(nblocks), dim3(kVocabBlock), 0, st, d_desc, part);
-  hipLaunchKernelGGL(residual_final_kernel, dim3(1), dim3(kVocabBlock), 0, st, d_desc, part);
+                                hipStream_t st, LaunchEv ev) {
+  const LaunchEv e1{ev.start, nullptr}, e2{nullptr, ev.stop};
+  SPD_LAUNCH(e1, residual_kernel, dim3(nblocks), dim3(kVocabBlock), 0, st, d_desc, part);
+  SPD_LAUNCH(e2, residual_final_kernel, dim3(1), dim3(kVocabBlock), 0, st, d_desc, part);
   return hipGetLastError();
 }
 

@@ -1,0 +1,116 @@
+"""Summarise rocprofv3 CSV output into the short text kept under profiles/.
+
+  python -m speculative_pipeline_decoding_amd.profile_summary stats DIR
+      per-kernel dispatch count, total and average duration (kernel trace)
+  python -m speculative_pipeline_decoding_amd.profile_summary traffic FETCH_DIR WRITE_DIR \
+         --calib-mib 1024 [--kernel gemv_gate_up]
+      FETCH_SIZE and WRITE_SIZE per dispatch (KiB), each scaled by what the same
+      counter reads for a plain device-to-device copy of known size (the largest
+      copy dispatch in the run, of --calib-mib MiB), as HBM bytes per launch.
+
+Every summary records the SHA-256 of the GEMV source it measured, so a later
+reader can tell whether the numbers still describe the current kernel.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import glob
+import hashlib
+import os
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+GEMV_SOURCE = os.path.join(HERE, "csrc", "gemv.hip")
+
+
+def source_hash(path: str = GEMV_SOURCE) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def short_name(n: str) -> str:
+    n = n.replace("spd::(anonymous namespace)::", "").replace("void ", "")
+    n = n.replace("unsigned short", "bf16")
+    base = n.split("(")[0]
+    return base[:60]
+
+
+def _find(d: str, suffix: str) -> str:
+    hits = sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
+    if not hits:
+        raise SystemExit(f"no *{suffix} under {d}")
+    return hits[0]
+
+
+def kernel_durations(trace_dir: str):
+    rows = list(csv.DictReader(open(_find(trace_dir, "kernel_trace.csv"))))
+    agg = collections.defaultdict(list)
+    for r in rows:
+        agg[short_name(r["Kernel_Name"])].append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    return agg
+
+
+def counter_values(d: str, counter: str):
+    rows = list(csv.DictReader(open(_find(d, "counter_collection.csv"))))
+    agg = collections.defaultdict(list)
+    for r in rows:
+        if r["Counter_Name"] == counter:
+            agg[short_name(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+    return agg
+
+
+def cmd_stats(a):
+    agg = kernel_durations(a.dir)
+    tot = sum(sum(v) for v in agg.values())
+    print(f"gemv source sha256[:16]: {source_hash()}")
+    print(f"{'kernel':62s} {'calls':>7s} {'total_ms':>10s} {'avg_us':>9s} {'share':>6s}")
+    for k, v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+        print(f"{k:62s} {len(v):7d} {sum(v) / 1e3:10.3f} {sum(v) / len(v):9.2f} {100 * sum(v) / tot:5.1f}%")
+
+
+def cmd_traffic(a):
+    f = counter_values(a.fetch_dir, "FETCH_SIZE")
+    w = counter_values(a.write_dir, "WRITE_SIZE")
+    copy_name = next((k for k in f if "copyBuffer" in k), None)
+    if copy_name is None:
+        raise SystemExit("no copy dispatch in the FETCH_SIZE run (pass --calib-copy-mib to bench.py)")
+    known = a.calib_mib * 1024.0           # KiB moved each way by the calibration copy
+    fscale = known / max(f[copy_name])
+    wscale = known / max(w[copy_name])
+    print(f"gemv source sha256[:16]: {source_hash()}")
+    print(f"calibration copy {a.calib_mib} MiB: FETCH_SIZE reads {max(f[copy_name]):.1f} KiB "
+          f"(scale {fscale:.4f}), WRITE_SIZE reads {max(w[copy_name]):.1f} KiB (scale {wscale:.4f})")
+    print(f"{'kernel':62s} {'calls':>6s} {'fetch_MB':>10s} {'write_MB':>9s} (per dispatch, scaled)")
+    for k in sorted(f, key=lambda k: -sum(f[k])):
+        fv, wv = f[k], w.get(k, [0.0])
+        fb = sum(fv) / len(fv) * 1024 * fscale
+        wb = sum(wv) / len(wv) * 1024 * wscale
+        print(f"{k:62s} {len(fv):6d} {fb / 1e6:10.2f} {wb / 1e6:9.2f}")
+    if a.kernel:
+        keys = [k for k in f if k.startswith(a.kernel)]
+        if keys:
+            k = max(keys, key=lambda k: sum(f[k]))
+            fv, wv = f[k], w.get(k, [0.0])
+            tb = (sum(fv) / len(fv)) * 1024 * fscale + (sum(wv) / len(wv)) * 1024 * wscale
+            print(f"traffic_bytes_per_launch {k} {tb:.0f}")
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("dir")
+    t = sub.add_parser("traffic")
+    t.add_argument("fetch_dir")
+    t.add_argument("write_dir")
+    t.add_argument("--calib-mib", type=int, required=True)
+    t.add_argument("--kernel", default="gemv_gate_up")
+    a = ap.parse_args(argv)
+    {"stats": cmd_stats, "traffic": cmd_traffic}[a.cmd](a)
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])
