@@ -5,9 +5,9 @@
 //     LM head with one or two vectors (the exiting token and the PDM's newest
 //     row share one sweep of the tied head): the "rows" kernel, in which a wave
 //     owns four weight rows and walks all of K;
-//   * the PDM's matrix with its n+1 rows: the "split-K" kernel, in which the four
-//     waves of a workgroup share four weight rows and take alternate chunks of K,
-//     so a short, wide PDM problem still keeps many loads in flight.
+//   * the PDM's matrix with its n+1 rows: with bf16 weights the matrix-core
+//     kernel (below); with fp32 weights the "split-K" kernel, in which the four
+//     waves of a workgroup share four weight rows and take alternate chunks of K.
 // Batch-1 decode is HBM bound: weights are streamed once with 16-byte
 // nontemporal loads, activations stay fp32, dot products are reduced with DPP
 // moves inside a wavefront.
@@ -17,6 +17,8 @@
 // wave uses the same lane partition, so all agree bit for bit) and scales the
 // reduced result once.
 #include "spd_internal.h"
+
+#include <algorithm>
 
 namespace spd {
 namespace {
@@ -291,8 +293,191 @@ __device__ void splitk_body(const GemvProb& p, int tile, float* red,
   }
 }
 
-// Kernel kinds: 1 or 2 vectors (rows kernel) or up to kMaxVec (split-K).
-enum Kind { K_ROWS1 = 0, K_ROWS2 = 1, K_SPLITK = 2 };
+// ---- matrix-core kernel: bf16 weights times 3..16 vectors ------------------------------
+// With n+1 vectors every weight element feeds n+1 products, which on the vector ALU
+// costs more than streaming the element. Here a wave owns tiles of 16 weight rows and
+// runs v_mfma_f32_16x16x32_bf16 with the rows as A and the vectors as B (columns).
+// The weights are exact bf16; the fp32 input g ⊙ x is split into three bf16 terms
+// (split3), so the three products summed in fp32 reproduce an fp32 GEMV to fp32
+// rounding.
+//
+// A workgroup first stages the whole input, every vector over all of K, in LDS as
+// three bf16 planes (one pass over x; each thread keeps per-vector sums of x^2 for
+// its columns, added in a fixed order afterwards). After that single barrier the
+// waves only stream weights: each keeps a ring of kMcRing 64-column blocks of loads
+// in flight (the B fragments come from LDS, on their own counter, so they never wait
+// behind the weight stream). Within a block, lane group q = l / 16 takes 16
+// consecutive columns (two 16-byte loads); a dot product does not care which k sits
+// in which MFMA slot, so the B fragments are read with the same permutation.
+//
+// Slots: plain, slot s = row u0 + s; SWIGLU, slots 0-7 gate rows u0.., 8-15 the up
+// rows of the same units; QKV, slots 0-7 the first halves of RoPE pairs u0.., 8-15
+// their partners. The partner of slot s sits in lane l ^ 32 of the accumulator.
+constexpr int kMcRing = 8;                   // 64-column blocks in flight per wave
+constexpr int kMcWaves = 8;                  // waves per workgroup (one workgroup per CU)
+constexpr int kMcLdsElems = 76800;           // bf16 elements of staged planes (150 KiB)
+constexpr int kMcMaxVec = 16;
+
+__device__ __forceinline__ int mc_units(const GemvProb& p) { return paired(p) ? 8 : 16; }
+// LDS row stride: whole 64-column blocks (zero past K) plus 16 bytes, so the 16 rows read
+// by one lane group start in distinct banks
+__host__ __device__ __forceinline__ int mc_ldk(int K) { return (K + 63) / 64 * 64 + 8; }
+
+__device__ __forceinline__ const uint16_t* mc_row(const GemvProb& p, int u0, int slot, int nunits) {
+  const uint16_t* M = static_cast<const uint16_t*>(p.W);
+  int row;
+  if (p.epi == EPI_SWIGLU) {
+    row = min(u0 + (slot & 7), nunits - 1);
+    if (slot >= 8) M = static_cast<const uint16_t*>(p.W2);
+  } else if (p.epi == EPI_QKV) {
+    const int half = p.hd >> 1;
+    const int unit = min(u0 + (slot & 7), nunits - 1);
+    row = (unit / half) * p.hd + unit % half + (slot >= 8 ? half : 0);
+  } else {
+    row = min(u0 + slot, nunits - 1);
+  }
+  return M + (size_t)row * p.K;
+}
+
+__device__ void mfma_body(const GemvProb& p, int tile, const float2* __restrict__ rope,
+                          uint16_t* planes, float* red) {
+  constexpr int NW = kMcWaves;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int upt = mc_units(p);
+  const int nunits = units_of(p);
+  const int KS = p.ksplit, RT = NW / KS;
+  const int rt = wave / KS, ks = wave % KS;
+  const int slot = lane & 15, grp = lane >> 4;
+  const int K = p.K, nv = p.nvec, LDK = mc_ldk(K);
+  const size_t PL = (size_t)nv * LDK;        // plane stride
+  const int nblk = (K + 63) / 64;
+  const int b_lo = nblk * ks / KS, b_hi = nblk * (ks + 1) / KS;
+  const int u0 = (tile * RT + rt) * upt;
+
+  // weight stream: block b of this lane's row. Pieces past K or past the range load the
+  // row's first 8 columns instead (finite weights, met by zero planes or a skipped
+  // block), so every load is issued and none is followed by a select: the compiler's
+  // count of loads in flight stays exact and each wait is for the oldest block only.
+  const uint16_t* arow = mc_row(p, u0, slot, nunits);
+  uint4 ra[kMcRing][2];
+  auto load = [&](int j, int b) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int k = 64 * b + 16 * grp + 8 * h;
+      ra[j][h] = load_stream(arow + (b < b_hi && k < K ? k : 0));
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < kMcRing; ++j) load(j, b_lo + j);
+
+  // stage g ⊙ x as three bf16 planes [3][nv][LDK]: float4 pieces idx = t + 512 i over
+  // nv rows of LDK / 4 (zero past K); the last round repeats a piece instead of
+  // branching, so every load is issued unconditionally
+  {
+    const int q4 = LDK / 4, total = nv * q4;
+    constexpr int U = 4;
+    for (int i0 = threadIdx.x; i0 < total; i0 += U * 64 * NW) {
+      float4 xv[U], gv[U];
+      int id[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        id[u] = min(i0 + u * 64 * NW, total - 1);
+        const int m = id[u] / q4, c = 4 * (id[u] - m * q4);
+        const int cc = min(c, K - 4);
+        xv[u] = load_g4(p.x + (size_t)m * p.x_stride + cc);
+        gv[u] = p.gain ? load_g4(p.gain + cc) : make_float4(1.f, 1.f, 1.f, 1.f);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int m = id[u] / q4, c = 4 * (id[u] - m * q4);
+        const float4 x = c < K ? xv[u] : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 g = gv[u];
+        uint32_t h0, m0, l0, h1, m1, l1, h2, m2, l2, h3, m3, l3;
+        split3(x.x * g.x, h0, m0, l0);
+        split3(x.y * g.y, h1, m1, l1);
+        split3(x.z * g.z, h2, m2, l2);
+        split3(x.w * g.w, h3, m3, l3);
+        uint16_t* o = planes + (size_t)m * LDK + c;
+        lds_store8(o, h0 | h1 << 16, h2 | h3 << 16);
+        lds_store8(o + PL, m0 | m1 << 16, m2 | m3 << 16);
+        lds_store8(o + 2 * PL, l0 | l1 << 16, l2 | l3 << 16);
+      }
+    }
+  }
+  // sum(x^2) of vector m by wave m % NW: lanes over K in order, then a wave reduction
+  if (p.gain) {
+    for (int m = wave; m < nv; m += NW) {
+      const float* xr = p.x + (size_t)m * p.x_stride;
+      float t = 0.f;
+#pragma unroll 4
+      for (int c = 4 * lane; c < K; c += 256) {
+        const float4 x = load_g4(xr + c);
+        t += x.x * x.x; t += x.y * x.y; t += x.z * x.z; t += x.w * x.w;
+      }
+      t = wave_sum(t);
+      if (lane == 0) red[m] = t;
+    }
+  }
+  __syncthreads();
+  const int vb = min(slot, nv - 1);          // B row of this lane (columns >= nv are ignored)
+  const float sc = p.gain ? rsqrtf(red[vb] / (float)K + p.eps) : 1.f;
+  const uint16_t* bp = planes + (size_t)vb * LDK + 16 * grp;
+
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int b0 = b_lo; b0 < b_hi; b0 += kMcRing) {
+#pragma unroll
+    for (int j = 0; j < kMcRing; ++j) {
+      const int b = b0 + j;
+      if (b < b_hi) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint16_t* q = bp + 64 * b + 8 * h;
+          const uint4 x0 = lds_load16(q);
+          const uint4 x1 = lds_load16(q + PL);
+          const uint4 x2 = lds_load16(q + 2 * PL);
+          acc = mfma_bf16(ra[j][h], x2, acc);
+          acc = mfma_bf16(ra[j][h], x1, acc);
+          acc = mfma_bf16(ra[j][h], x0, acc);
+        }
+      }
+      load(j, b + kMcRing);
+    }
+  }
+
+  // K-ranges: waves ks > 0 hand their accumulators to wave ks = 0 of their row tile
+  float* part = reinterpret_cast<float*>(planes);
+  if (KS > 1) {
+    __syncthreads();                         // every wave is done reading the planes
+    if (ks > 0) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) part[(wave * 4 + e) * 64 + lane] = acc[e];
+    }
+    __syncthreads();
+    if (ks != 0) return;
+    for (int o = 1; o < KS; ++o)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += part[((wave + o) * 4 + e) * 64 + lane];
+  }
+
+  const bool pr = paired(p);
+  const int v = slot;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int s4 = 4 * grp + e;
+    const float a = acc[e] * sc;
+    const float b = pr ? __shfl_xor(a, 32) : 0.f;
+    if (v >= nv) continue;
+    if (pr) {
+      if (grp < 2 && u0 + s4 < nunits) epilogue<uint16_t>(p, v, u0 + s4, a, b, rope);
+    } else if (u0 + s4 < nunits) {
+      epilogue<uint16_t>(p, v, u0 + s4, a, 0.f, rope);
+    }
+  }
+}
+
+// Kernel kinds: 1 or 2 vectors (rows kernel), 3..16 vectors on the matrix cores (bf16
+// weights, input staged whole in LDS), else up to kMaxVec (split-K).
+enum Kind { K_ROWS1 = 0, K_ROWS2 = 1, K_SPLITK = 2, K_MFMA = 3 };
 
 template <typename T, int KIND>
 __device__ __forceinline__ void gemv_body(const GemvProb* __restrict__ probs, int nprob,
@@ -304,6 +489,11 @@ __device__ __forceinline__ void gemv_body(const GemvProb* __restrict__ probs, in
   if constexpr (KIND == K_SPLITK) {
     __shared__ float red[kSplit * (RW * kMaxVec + kMaxVec)];
     splitk_body<T>(p, tile, red, rope);
+  } else if constexpr (KIND == K_MFMA) {
+    static_assert(sizeof(T) == 2, "matrix-core GEMV takes bf16 weights");
+    __shared__ __attribute__((aligned(16))) uint16_t planes[kMcLdsElems];
+    __shared__ float red[kMcMaxVec];
+    mfma_body(p, tile, rope, planes, red);
   } else {
     rows_body<T, KIND == K_ROWS1 ? 1 : 2>(p, tile, rope);
   }
@@ -312,7 +502,8 @@ __device__ __forceinline__ void gemv_body(const GemvProb* __restrict__ probs, in
 // One kernel symbol per role in the step, so profiles separate them.
 #define SPD_GEMV_KERNEL(name)                                                              \
   template <typename T, int KIND>                                                          \
-  __global__ __launch_bounds__(256) void name(const GemvProb* __restrict__ probs, int nprob, \
+  __global__ __launch_bounds__(KIND == 3 ? 512 : 256) void name(                           \
+      const GemvProb* __restrict__ probs, int nprob,                                       \
                                               const float2* __restrict__ rope) {           \
     gemv_body<T, KIND>(probs, nprob, rope);                                                \
   }
@@ -331,7 +522,7 @@ SPD_GEMV_KERNEL(pdm_gemv_down)
 template <typename T, int KIND>
 void launch_kind(int role, dim3 grid, const GemvProb* d_probs, int nprob, const float2* rope,
                  hipStream_t st, LaunchEv ev) {
-  const dim3 block(kWaves * 64);
+  const dim3 block((KIND == K_MFMA ? kMcWaves : kWaves) * 64);
   switch (role) {
     case GEMV_PROJ: SPD_LAUNCH(ev, (gemv_proj<T, KIND>), grid, block, 0, st, d_probs, nprob, rope); break;
     case GEMV_QKV: SPD_LAUNCH(ev, (gemv_qkv<T, KIND>), grid, block, 0, st, d_probs, nprob, rope); break;
@@ -346,27 +537,66 @@ void launch_kind(int role, dim3 grid, const GemvProb* d_probs, int nprob, const 
   }
 }
 
-template <typename T>
-void launch_t(int role, int maxvec, dim3 grid, const GemvProb* d_probs, int nprob,
-              const float2* rope, hipStream_t st, LaunchEv ev) {
-  if (maxvec <= 1) launch_kind<T, K_ROWS1>(role, grid, d_probs, nprob, rope, st, ev);
-  else if (maxvec == 2) launch_kind<T, K_ROWS2>(role, grid, d_probs, nprob, rope, st, ev);
-  else launch_kind<T, K_SPLITK>(role, grid, d_probs, nprob, rope, st, ev);
-}
-
 }  // namespace
 
-int gemv_units_per_tile(int nvec_max, bool is_paired) {
-  const int upw = is_paired ? RW / 2 : RW;
-  return nvec_max <= 2 ? kWaves * upw : upw;
+int gemv_plan(GemvProb* v, int n, bool bf16) {
+  int mv = 1;
+  bool mc = bf16 && n == 1;   // the matrix-core kernel takes one problem per launch
+  auto a16 = [](const void* q) { return q == nullptr || ((uintptr_t)q & 15) == 0; };
+  for (int i = 0; i < n; ++i) {
+    const GemvProb& g = v[i];
+    mv = std::max(mv, g.nvec);
+    // 16-byte pieces of weights and inputs; the whole input fits the LDS planes
+    mc = mc && g.K % 8 == 0 && g.x_stride % 4 == 0 && g.gain_stride == 0 && a16(g.W) &&
+         a16(g.W2) && a16(g.x) && a16(g.gain) && g.nvec <= kMcMaxVec &&
+         (size_t)3 * g.nvec * mc_ldk(g.K) <= (size_t)kMcLdsElems;
+  }
+  int kind = mv <= 1 ? K_ROWS1 : mv == 2 ? K_ROWS2 : K_SPLITK;
+  if (mc && mv > 2) kind = K_MFMA;
+  int t = 0;
+  for (int i = 0; i < n; ++i) {
+    GemvProb& g = v[i];
+    const bool pr = g.epi == EPI_QKV || g.epi == EPI_SWIGLU;
+    const int units = g.epi == EPI_QKV ? g.rows / 2 : g.rows;
+    g.ksplit = 1;
+    if (kind == K_MFMA) {
+      // one workgroup per CU (LDS); its waves split K when row tiles alone fill < 128 CUs
+      const int wt = (units + (pr ? 8 : 16) - 1) / (pr ? 8 : 16);
+      while (g.ksplit < kMcWaves && (wt + kMcWaves / g.ksplit - 1) / (kMcWaves / g.ksplit) < 128)
+        g.ksplit *= 2;
+      g.ntiles = (wt + kMcWaves / g.ksplit - 1) / (kMcWaves / g.ksplit);
+    } else {
+      const int upw = pr ? RW / 2 : RW;
+      const int upt = kind == K_SPLITK ? upw : kWaves * upw;
+      g.ntiles = (units + upt - 1) / upt;
+    }
+    g.tile0 = t;
+    t += g.ntiles;
+  }
+  return kind * (1 << 24) + t;
 }
 
-hipError_t launch_gemv(int role, const GemvProb* d_probs, int nprob, int ntiles, int maxvec,
-                       bool bf16, const float2* rope, hipStream_t st, LaunchEv ev) {
+hipError_t launch_gemv(int role, const GemvProb* d_probs, int nprob, int plan, bool bf16,
+                       const float2* rope, hipStream_t st, LaunchEv ev) {
+  const int kind = plan >> 24, ntiles = plan & ((1 << 24) - 1);
   if (ntiles <= 0 || nprob <= 0) return hipSuccess;
-  if (maxvec > kMaxVec) return hipErrorInvalidValue;
-  if (bf16) launch_t<uint16_t>(role, maxvec, dim3(ntiles), d_probs, nprob, rope, st, ev);
-  else launch_t<float>(role, maxvec, dim3(ntiles), d_probs, nprob, rope, st, ev);
+  const dim3 grid(ntiles);
+  if (bf16) {
+    switch (kind) {
+      case K_ROWS1: launch_kind<uint16_t, K_ROWS1>(role, grid, d_probs, nprob, rope, st, ev); break;
+      case K_ROWS2: launch_kind<uint16_t, K_ROWS2>(role, grid, d_probs, nprob, rope, st, ev); break;
+      case K_SPLITK: launch_kind<uint16_t, K_SPLITK>(role, grid, d_probs, nprob, rope, st, ev); break;
+      case K_MFMA: launch_kind<uint16_t, K_MFMA>(role, grid, d_probs, nprob, rope, st, ev); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (kind) {
+      case K_ROWS1: launch_kind<float, K_ROWS1>(role, grid, d_probs, nprob, rope, st, ev); break;
+      case K_ROWS2: launch_kind<float, K_ROWS2>(role, grid, d_probs, nprob, rope, st, ev); break;
+      case K_SPLITK: launch_kind<float, K_SPLITK>(role, grid, d_probs, nprob, rope, st, ev); break;
+      default: return hipErrorInvalidValue;
+    }
+  }
   return hipGetLastError();
 }
 

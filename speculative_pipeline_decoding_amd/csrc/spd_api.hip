@@ -64,7 +64,7 @@ struct Op {
   int split;       // attention split length
   double bytes;    // algorithmic HBM bytes (weights + KV) for the timing report
   int stream = 0;  // 0: the caller's stream, 1: the PDM stream
-  int maxvec = 1;  // GEMV: largest vector count in the launch
+  int plan = 0;    // GEMV: kernel kind and workgroups (gemv_plan)
 };
 
 struct Plan {
@@ -269,23 +269,8 @@ struct DescWriter {
   }
 };
 
-int max_vec(const std::vector<GemvProb>& v) {
-  int m = 1;
-  for (auto& g : v) m = std::max(m, g.nvec);
-  return m;
-}
-
-int finish_tiles(std::vector<GemvProb>& v) {
-  const int mv = max_vec(v);
-  int t = 0;
-  for (auto& g : v) {
-    const int units = g.epi == EPI_QKV ? g.rows / 2 : g.rows;
-    const int upt = gemv_units_per_tile(mv, g.epi == EPI_QKV || g.epi == EPI_SWIGLU);
-    g.tile0 = t;
-    g.ntiles = (units + upt - 1) / upt;
-    t += g.ntiles;
-  }
-  return t;
+int finish_tiles(const Plan& p, std::vector<GemvProb>& v) {
+  return gemv_plan(v.data(), (int)v.size(), p.bf16);
 }
 
 GemvProb gemv(const void* W, int rows, int K, const float* x, long long xs, int nvec, int epi,
@@ -373,7 +358,7 @@ hipError_t run_op(spd_handle* h, const Op& op, LaunchEv ev = {}) {
     case OP_GEMV_PROJ: case OP_GEMV_QKV: case OP_GEMV_O: case OP_GEMV_GU: case OP_GEMV_DOWN:
     case OP_GEMV_HEAD: case OP_PDM_QKV: case OP_PDM_O: case OP_PDM_GU: case OP_PDM_DOWN:
       return launch_gemv(gemv_role(op.kind), reinterpret_cast<const GemvProb*>(d + op.off),
-                         op.count, op.ntiles, op.maxvec, p.bf16, rope, st, ev);
+                         op.count, op.plan, p.bf16, rope, st, ev);
     case OP_ATTN: case OP_PDM_ATTN:
       return launch_attention(reinterpret_cast<const AttnProb*>(d + op.off), op.count, op.ntiles,
                               p.bf16, p.hq, p.hkv, p.hd, p.max_ctx, op.split,
@@ -446,10 +431,11 @@ int build_step(spd_handle* h, DescWriter& dw) {
   const int kd = p.k * p.d;
   auto push_gemv = [&](int kind, std::vector<GemvProb>& g, int stream) {
     if (g.empty()) return;
-    const int nt = finish_tiles(g);
-    Op op{kind, dw.put(g.data(), (int)g.size()), (int)g.size(), nt, 0, gemv_bytes(g, p.esz)};
+    const int plan = finish_tiles(p, g);
+    Op op{kind, dw.put(g.data(), (int)g.size()), (int)g.size(), plan & 0xffffff, 0,
+          gemv_bytes(g, p.esz)};
     op.stream = stream;
-    op.maxvec = max_vec(g);
+    op.plan = plan;
     h->ops.push_back(op);
   };
   auto push_attn = [&](int kind, std::vector<AttnProb>& a, int stream, int slot0, double kvb) {
@@ -792,7 +778,7 @@ int spd_prefill(spd_handle* h, const int32_t* prompt, int32_t len, int32_t* firs
       DescWriter dw{h->h_desc};
       std::vector<GemvProb> g{gemv(h->head, p.V, p.d, H + (size_t)(P - 1) * p.d, 0, 1, EPI_STORE,
                                    h->at<float>(p.o_logits), 0, h->final_norm, 0, p.eps)};
-      const int nt = finish_tiles(g);
+      const int plan = finish_tiles(p, g);
       const size_t go = dw.put(g.data(), 1);
       const bool sampled = h->temp > 0.f;
       VocabDesc vd{};
@@ -810,7 +796,7 @@ int spd_prefill(spd_handle* h, const int32_t* prompt, int32_t len, int32_t* firs
       const size_t fo = dw.put(&fd, 1);
       char* d = h->ws + p.o_desc;
       HIPCHK(h, hipMemcpyAsync(d, h->h_desc, dw.used, hipMemcpyHostToDevice, st));
-      HIPCHK(h, launch_gemv(GEMV_HEAD, reinterpret_cast<const GemvProb*>(d + go), 1, nt, 1, bf, rope, st));
+      HIPCHK(h, launch_gemv(GEMV_HEAD, reinterpret_cast<const GemvProb*>(d + go), 1, plan, bf, rope, st));
       HIPCHK(h, launch_vocab_stats(reinterpret_cast<const VocabDesc*>(d + vo), kVocabBlocks,
                                    h->at<VocabPartial>(p.o_part), st));
       HIPCHK(h, launch_finalize(reinterpret_cast<const FinalizeDesc*>(d + fo), st));

@@ -46,7 +46,8 @@ struct GemvProb {
   int tile0;           // first workgroup of this problem in the launch
   int ntiles;
   int hq, hkv, hd, max_ctx;
-  int pad[2];
+  int ksplit;          // matrix-core kernel: row tiles per wave (1 or 2)
+  int pad;
 };
 
 // Attention over one layer's KV cache for a group of query rows.
@@ -188,6 +189,39 @@ __device__ __forceinline__ float dpp_mov(float v) {
 __device__ __forceinline__ float lane_f(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
+// Sum over the 16 lanes of a DPP row (every lane of the row gets it); LANES = 8 stops at
+// half rows.
+template <int LANES>
+__device__ __forceinline__ float row_sum(float v) {
+  v += dpp_mov<0xB1>(v);
+  v += dpp_mov<0x4E>(v);
+  v += dpp_mov<0x141>(v);
+  if constexpr (LANES == 16) v += dpp_mov<0x140>(v);
+  return v;
+}
+
+// Operand and accumulator types of the CDNA4 bf16 matrix instruction
+// v_mfma_f32_16x16x32_bf16: lane l holds A[l % 16][8 (l / 16) + e] and
+// B[8 (l / 16) + e][l % 16] (e = 0..7) and D[4 (l / 16) + r][l % 16] (r = 0..3).
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4_t mfma_bf16(const uint4& a, const uint4& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// x = hi + mid + lo with each term a bfloat16 (round to nearest even at every step);
+// the residual left out is below 2^-24 |x|, so three bf16 products summed in fp32 give
+// an fp32-accurate product with an exact bf16 operand.
+__device__ __forceinline__ void split3(float x, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  hi = f2bf(x);
+  const float r1 = x - __uint_as_float(hi << 16);
+  mid = f2bf(r1);
+  const float r2 = r1 - __uint_as_float(mid << 16);
+  lo = f2bf(r2);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
   v += dpp_mov<0xB1>(v);    // quad_perm [1,0,3,2]
   v += dpp_mov<0x4E>(v);    // quad_perm [2,3,0,1]
@@ -205,9 +239,29 @@ __device__ __forceinline__ float wave_max(float v) {
 
 // 16 bytes of weights, streamed once: a nontemporal load keeps them from
 // displacing reusable lines (activations, KV rows) in the caches.
+// The pointer is taken as a global-memory one: a generic (flat) load would count on the
+// LDS counter too, and every wait for it would also drain pending LDS traffic.
+#define SPD_GLOBAL __attribute__((address_space(1)))
 __device__ __forceinline__ uint4 load_stream(const void* p) {
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  const u32x4 v = __builtin_nontemporal_load((const SPD_GLOBAL u32x4*)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+// Ordinary 16-byte load through a global-memory pointer.
+__device__ __forceinline__ float4 load_g4(const float* p) {
+  const f32x4_t v = *(const SPD_GLOBAL f32x4_t*)p;
+  return make_float4(v[0], v[1], v[2], v[3]);
+}
+#define SPD_LOCAL __attribute__((address_space(3)))
+// 8-byte LDS store through a local-memory pointer.
+__device__ __forceinline__ void lds_store8(void* p, uint32_t a, uint32_t b) {
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  *(SPD_LOCAL u32x2*)p = u32x2{a, b};
+}
+// 16-byte read of LDS through a local-memory pointer (ds_read_b128, LDS counter only).
+__device__ __forceinline__ uint4 lds_load16(const void* p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = *(const SPD_LOCAL u32x4*)p;
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
@@ -243,10 +297,11 @@ struct LaunchEv {
 
 enum GemvRole : int { GEMV_PROJ = 0, GEMV_QKV, GEMV_O, GEMV_GATE_UP, GEMV_DOWN, GEMV_HEAD,
                       GEMV_PDM_QKV, GEMV_PDM_O, GEMV_PDM_GATE_UP, GEMV_PDM_DOWN };
-// maxvec: the largest nvec in the launch (1, 2: rows kernel; more: split-K kernel)
-hipError_t launch_gemv(int role, const GemvProb* d_probs, int nprob, int ntiles, int maxvec,
-                       bool bf16, const float2* rope, hipStream_t st, LaunchEv ev = {});
-int gemv_units_per_tile(int nvec_max, bool is_paired);
+// Chooses the kernel kind for a grouped launch, fills tile0 / ntiles / ksplit of every
+// problem, and returns the launch plan (kind << 24 | workgroups) for launch_gemv.
+int gemv_plan(GemvProb* probs, int nprob, bool bf16);
+hipError_t launch_gemv(int role, const GemvProb* d_probs, int nprob, int plan, bool bf16,
+                       const float2* rope, hipStream_t st, LaunchEv ev = {});
 hipError_t launch_attention(const AttnProb* d_probs, int nprob, int ntiles, bool bf16,
                             int hq, int hkv, int hd, int max_ctx, int split_len, bool any_split,
                             float* partials, hipStream_t st, LaunchEv ev = {});
