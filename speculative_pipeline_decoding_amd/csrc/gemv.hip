@@ -314,7 +314,7 @@ __device__ void splitk_body(const GemvProb& p, int tile, float* red,
 // rows of the same units; QKV, slots 0-7 the first halves of RoPE pairs u0.., 8-15
 // their partners. The partner of slot s sits in lane l ^ 32 of the accumulator.
 constexpr int kMcRing = 8;                   // 64-column blocks in flight per wave
-constexpr int kMcWaves = 8;                  // waves per workgroup (one workgroup per CU)
+constexpr int kMcMaxWaves = 8;               // waves per workgroup (one workgroup per CU)
 constexpr int kMcLdsElems = 76800;           // bf16 elements of staged planes (150 KiB)
 constexpr int kMcMaxVec = 16;
 
@@ -341,7 +341,7 @@ __device__ __forceinline__ const uint16_t* mc_row(const GemvProb& p, int u0, int
 
 __device__ void mfma_body(const GemvProb& p, int tile, const float2* __restrict__ rope,
                           uint16_t* planes, float* red) {
-  constexpr int NW = kMcWaves;
+  const int NW = blockDim.x >> 6;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int upt = mc_units(p);
   const int nunits = units_of(p);
@@ -370,28 +370,35 @@ __device__ void mfma_body(const GemvProb& p, int tile, const float2* __restrict_
 #pragma unroll
   for (int j = 0; j < kMcRing; ++j) load(j, b_lo + j);
 
-  // stage g ⊙ x as three bf16 planes [3][nv][LDK]: float4 pieces idx = t + 512 i over
-  // nv rows of LDK / 4 (zero past K); the last round repeats a piece instead of
-  // branching, so every load is issued unconditionally
-  {
-    const int q4 = LDK / 4, total = nv * q4;
-    constexpr int U = 4;
-    for (int i0 = threadIdx.x; i0 < total; i0 += U * 64 * NW) {
-      float4 xv[U], gv[U];
-      int id[U];
+  // stage g ⊙ x as three bf16 planes [3][nv][LDK] (zero past K): thread t takes the
+  // float4 column c = 4 t, 4 (t + 64 NW), ... of every vector, so the gain is read once
+  // and the per-vector sums of x^2 stay in registers (added across threads in a fixed
+  // order below)
+  float ss[kMcMaxVec];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        id[u] = min(i0 + u * 64 * NW, total - 1);
-        const int m = id[u] / q4, c = 4 * (id[u] - m * q4);
-        const int cc = min(c, K - 4);
-        xv[u] = load_g4(p.x + (size_t)m * p.x_stride + cc);
-        gv[u] = p.gain ? load_g4(p.gain + cc) : make_float4(1.f, 1.f, 1.f, 1.f);
-      }
+  for (int m = 0; m < kMcMaxVec; ++m) ss[m] = 0.f;
+  // two columns per thread per round: a 2560-wide input is staged in one round trip
+  for (int c0 = 4 * threadIdx.x; c0 < LDK; c0 += 2 * 4 * 64 * NW) {
+    float4 xv[2][kMcMaxVec], gv[2];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int m = id[u] / q4, c = 4 * (id[u] - m * q4);
-        const float4 x = c < K ? xv[u] : make_float4(0.f, 0.f, 0.f, 0.f);
-        const float4 g = gv[u];
+    for (int u = 0; u < 2; ++u) {
+      const int cc = min(c0 + u * 4 * 64 * NW, K - 4);
+#pragma unroll
+      for (int m = 0; m < kMcMaxVec; ++m)
+        if (m < nv) xv[u][m] = load_g4(p.x + (size_t)m * p.x_stride + cc);
+      gv[u] = p.gain ? load_g4(p.gain + cc) : make_float4(1.f, 1.f, 1.f, 1.f);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+    const int c = c0 + u * 4 * 64 * NW;
+    if (c >= LDK) break;
+    const float4 g = gv[u];
+    const bool in = c < K;
+#pragma unroll
+    for (int m = 0; m < kMcMaxVec; ++m) {
+      if (m < nv) {
+        const float4 x = in ? xv[u][m] : make_float4(0.f, 0.f, 0.f, 0.f);
+        ss[m] += x.x * x.x; ss[m] += x.y * x.y; ss[m] += x.z * x.z; ss[m] += x.w * x.w;
         uint32_t h0, m0, l0, h1, m1, l1, h2, m2, l2, h3, m3, l3;
         split3(x.x * g.x, h0, m0, l0);
         split3(x.y * g.y, h1, m1, l1);
@@ -403,24 +410,26 @@ __device__ void mfma_body(const GemvProb& p, int tile, const float2* __restrict_
         lds_store8(o + 2 * PL, l0 | l1 << 16, l2 | l3 << 16);
       }
     }
+    }
   }
-  // sum(x^2) of vector m by wave m % NW: lanes over K in order, then a wave reduction
+  // sum(x^2) per vector: lanes, then the waves in order
   if (p.gain) {
-    for (int m = wave; m < nv; m += NW) {
-      const float* xr = p.x + (size_t)m * p.x_stride;
-      float t = 0.f;
-#pragma unroll 4
-      for (int c = 4 * lane; c < K; c += 256) {
-        const float4 x = load_g4(xr + c);
-        t += x.x * x.x; t += x.y * x.y; t += x.z * x.z; t += x.w * x.w;
+#pragma unroll
+    for (int m = 0; m < kMcMaxVec; ++m) {
+      if (m < nv) {
+        const float t = wave_sum(ss[m]);
+        if (lane == 0) red[wave * kMcMaxVec + m] = t;
       }
-      t = wave_sum(t);
-      if (lane == 0) red[m] = t;
     }
   }
   __syncthreads();
   const int vb = min(slot, nv - 1);          // B row of this lane (columns >= nv are ignored)
-  const float sc = p.gain ? rsqrtf(red[vb] / (float)K + p.eps) : 1.f;
+  float sc = 1.f;
+  if (p.gain) {
+    float t = 0.f;
+    for (int w = 0; w < NW; ++w) t += red[w * kMcMaxVec + vb];
+    sc = rsqrtf(t / (float)K + p.eps);
+  }
   const uint16_t* bp = planes + (size_t)vb * LDK + 16 * grp;
 
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -492,7 +501,7 @@ __device__ __forceinline__ void gemv_body(const GemvProb* __restrict__ probs, in
   } else if constexpr (KIND == K_MFMA) {
     static_assert(sizeof(T) == 2, "matrix-core GEMV takes bf16 weights");
     __shared__ __attribute__((aligned(16))) uint16_t planes[kMcLdsElems];
-    __shared__ float red[kMcMaxVec];
+    __shared__ float red[kMcMaxWaves * kMcMaxVec];
     mfma_body(p, tile, rope, planes, red);
   } else {
     rows_body<T, KIND == K_ROWS1 ? 1 : 2>(p, tile, rope);
@@ -521,8 +530,8 @@ SPD_GEMV_KERNEL(pdm_gemv_down)
 
 template <typename T, int KIND>
 void launch_kind(int role, dim3 grid, const GemvProb* d_probs, int nprob, const float2* rope,
-                 hipStream_t st, LaunchEv ev) {
-  const dim3 block((KIND == K_MFMA ? kMcWaves : kWaves) * 64);
+                 hipStream_t st, LaunchEv ev, int waves = kWaves) {
+  const dim3 block(waves * 64);
   switch (role) {
     case GEMV_PROJ: SPD_LAUNCH(ev, (gemv_proj<T, KIND>), grid, block, 0, st, d_probs, nprob, rope); break;
     case GEMV_QKV: SPD_LAUNCH(ev, (gemv_qkv<T, KIND>), grid, block, 0, st, d_probs, nprob, rope); break;
@@ -560,11 +569,14 @@ int gemv_plan(GemvProb* v, int n, bool bf16) {
     const int units = g.epi == EPI_QKV ? g.rows / 2 : g.rows;
     g.ksplit = 1;
     if (kind == K_MFMA) {
-      // one workgroup per CU (LDS); its waves split K when row tiles alone fill < 128 CUs
+      // One workgroup per CU (the LDS planes), and a CU streams only so fast: spread the
+      // row tiles over all 256 CUs (RT per workgroup), then let KS waves share each row
+      // tile's K so a workgroup has up to 8 waves of loads in flight.
       const int wt = (units + (pr ? 8 : 16) - 1) / (pr ? 8 : 16);
-      while (g.ksplit < kMcWaves && (wt + kMcWaves / g.ksplit - 1) / (kMcWaves / g.ksplit) < 128)
-        g.ksplit *= 2;
-      g.ntiles = (wt + kMcWaves / g.ksplit - 1) / (kMcWaves / g.ksplit);
+      const int rt = std::min(kMcMaxWaves, (wt + 255) / 256);
+      g.ksplit = std::max(1, kMcMaxWaves / rt);
+      g.pad = rt;
+      g.ntiles = (wt + rt - 1) / rt;
     } else {
       const int upw = pr ? RW / 2 : RW;
       const int upt = kind == K_SPLITK ? upw : kWaves * upw;
@@ -573,12 +585,13 @@ int gemv_plan(GemvProb* v, int n, bool bf16) {
     g.tile0 = t;
     t += g.ntiles;
   }
-  return kind * (1 << 24) + t;
+  const int waves = kind == K_MFMA ? v[0].pad * v[0].ksplit : kWaves;
+  return kind << 28 | waves << 20 | t;
 }
 
 hipError_t launch_gemv(int role, const GemvProb* d_probs, int nprob, int plan, bool bf16,
                        const float2* rope, hipStream_t st, LaunchEv ev) {
-  const int kind = plan >> 24, ntiles = plan & ((1 << 24) - 1);
+  const int kind = plan >> 28, waves = (plan >> 20) & 255, ntiles = plan & ((1 << 20) - 1);
   if (ntiles <= 0 || nprob <= 0) return hipSuccess;
   const dim3 grid(ntiles);
   if (bf16) {
@@ -586,7 +599,7 @@ hipError_t launch_gemv(int role, const GemvProb* d_probs, int nprob, int plan, b
       case K_ROWS1: launch_kind<uint16_t, K_ROWS1>(role, grid, d_probs, nprob, rope, st, ev); break;
       case K_ROWS2: launch_kind<uint16_t, K_ROWS2>(role, grid, d_probs, nprob, rope, st, ev); break;
       case K_SPLITK: launch_kind<uint16_t, K_SPLITK>(role, grid, d_probs, nprob, rope, st, ev); break;
-      case K_MFMA: launch_kind<uint16_t, K_MFMA>(role, grid, d_probs, nprob, rope, st, ev); break;
+      case K_MFMA: launch_kind<uint16_t, K_MFMA>(role, grid, d_probs, nprob, rope, st, ev, waves); break;
       default: return hipErrorInvalidValue;
     }
   } else {

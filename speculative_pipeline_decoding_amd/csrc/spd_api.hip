@@ -432,7 +432,7 @@ int build_step(spd_handle* h, DescWriter& dw) {
   auto push_gemv = [&](int kind, std::vector<GemvProb>& g, int stream) {
     if (g.empty()) return;
     const int plan = finish_tiles(p, g);
-    Op op{kind, dw.put(g.data(), (int)g.size()), (int)g.size(), plan & 0xffffff, 0,
+    Op op{kind, dw.put(g.data(), (int)g.size()), (int)g.size(), plan & 0xfffff, 0,
           gemv_bytes(g, p.esz)};
     op.stream = stream;
     op.plan = plan;

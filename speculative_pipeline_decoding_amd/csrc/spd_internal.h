@@ -46,8 +46,8 @@ struct GemvProb {
   int tile0;           // first workgroup of this problem in the launch
   int ntiles;
   int hq, hkv, hd, max_ctx;
-  int ksplit;          // matrix-core kernel: row tiles per wave (1 or 2)
-  int pad;
+  int ksplit;          // matrix-core kernel: waves sharing one row tile's K
+  int pad;             // matrix-core kernel: row tiles per workgroup
 };
 
 // Attention over one layer's KV cache for a group of query rows.
@@ -298,7 +298,8 @@ struct LaunchEv {
 enum GemvRole : int { GEMV_PROJ = 0, GEMV_QKV, GEMV_O, GEMV_GATE_UP, GEMV_DOWN, GEMV_HEAD,
                       GEMV_PDM_QKV, GEMV_PDM_O, GEMV_PDM_GATE_UP, GEMV_PDM_DOWN };
 // Chooses the kernel kind for a grouped launch, fills tile0 / ntiles / ksplit of every
-// problem, and returns the launch plan (kind << 24 | workgroups) for launch_gemv.
+// problem, and returns the launch plan (kind << 28 | waves per workgroup << 20 |
+// workgroups) for launch_gemv.
 int gemv_plan(GemvProb* probs, int nprob, bool bf16);
 hipError_t launch_gemv(int role, const GemvProb* d_probs, int nprob, int plan, bool bf16,
                        const float2* rope, hipStream_t st, LaunchEv ev = {});
