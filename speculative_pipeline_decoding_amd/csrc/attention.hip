@@ -12,7 +12,10 @@
 // of one (problem, kv head) are merged by a second small kernel (the kernel
 // boundary orders the partials; no device-wide fence in the hot loop).
 //
-// Prefill uses the same kernel with one problem per prompt row and no split.
+// That kernel serves fp32 caches. bf16 caches take the matrix-core kernel below, which
+// also groups query rows that share a cache (the PDM window, prompt rows).
+//
+// Prefill uses the same kernels with the prompt rows as problems and no split.
 #include "spd_internal.h"
 
 namespace spd {
@@ -221,73 +224,328 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_kernel(
 }
 
 // Merge the key splits of every (problem, kv head) whose keys were split:
-// out = sum_s acc_s e^(m_s - M) / sum_s l_s e^(m_s - M), in split order.
+// out = sum_s acc_s e^(m_s - M) / sum_s l_s e^(m_s - M), in split order. A record holds
+// CW query columns (column c = row c / G, head g G + c % G). The split weights are found
+// once per column (every record's m and l read in one round), then each output element
+// sums its splits with the loads of eight splits in flight at a time.
 template <int HD>
 __global__ __launch_bounds__(kAttnWaves * 64) void attn_merge_kernel(
-    const AttnProb* __restrict__ probs, int G, int hkv, const float* __restrict__ partials) {
-  constexpr int HALF = HD / 2;
+    const AttnProb* __restrict__ probs, int G, int hkv, int CW, const float* __restrict__ partials) {
+  constexpr int PW = HD + 2;
+  __shared__ float wgt[kMaxSplit][16];      // e^(m_s - M) / L per split and column
+  __shared__ float ml[kMaxSplit][16][2];
   const AttnProb& P = probs[blockIdx.x / hkv];
   const int g = blockIdx.x % hkv;
   const int nsplit = P.nsplit;
   if (nsplit == 1) return;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const size_t pstride = HD + 2;
-  const float* base = partials + (((size_t)P.slot * hkv + g) * kMaxSplit) * G * pstride;
-  for (int h = w; h < G; h += kAttnWaves) {
+  const int ncol = P.nrows * G;
+  const float* base = partials + ((size_t)P.slot * hkv + g) * kMaxSplit * CW * PW;
+  for (int t = threadIdx.x; t < nsplit * ncol; t += blockDim.x) {
+    const int u = t / ncol, c = t % ncol;
+    const float2 v = *reinterpret_cast<const float2*>(base + ((size_t)u * CW + c) * PW);
+    ml[u][c][0] = v.x;
+    ml[u][c][1] = v.y;
+  }
+  __syncthreads();
+  if (threadIdx.x < ncol) {
+    const int c = threadIdx.x;
     float M = -INFINITY;
-    for (int t = 0; t < nsplit; ++t) M = fmaxf(M, base[((size_t)t * G + h) * pstride]);
+    for (int u = 0; u < nsplit; ++u) M = fmaxf(M, ml[u][c][0]);
     float L = 0.f;
-    float2 a = make_float2(0.f, 0.f);
-    for (int t = 0; t < nsplit; ++t) {
-      const float* pp = base + ((size_t)t * G + h) * pstride;
-      const float f = expf(pp[0] - M);
-      L += pp[1] * f;
-      if (lane < HALF) { a.x += pp[2 + 2 * lane] * f; a.y += pp[3 + 2 * lane] * f; }
+    for (int u = 0; u < nsplit; ++u) {
+      const float f = ml[u][c][0] == -INFINITY ? 0.f : expf(ml[u][c][0] - M);
+      wgt[u][c] = f;
+      L += ml[u][c][1] * f;
     }
-    const int head = g * G + h;
-    if (lane < HALF) {
-      P.out[head * HD + 2 * lane] = a.x / L;
-      P.out[head * HD + 2 * lane + 1] = a.y / L;
+    const float inv = 1.f / L;
+    for (int u = 0; u < nsplit; ++u) wgt[u][c] *= inv;
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < ncol * HD; t += blockDim.x) {
+    const int c = t / HD, d = t % HD;
+    const float* rec = base + (size_t)c * PW + 2 + d;
+    float a = 0.f;
+    for (int u0 = 0; u0 < nsplit; u0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = u0 + i < nsplit ? rec[(size_t)(u0 + i) * CW * PW] : 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (u0 + i < nsplit) a += v[i] * wgt[u0 + i][c];
+    }
+    P.out[(size_t)(c / G) * P.out_stride + (size_t)(g * G + c % G) * HD + d] = a;
+  }
+}
+
+// ---- matrix-core kernel (bf16 caches) ------------------------------------------------
+// One workgroup = (problem, kv head, key split); its four waves take contiguous runs of
+// 32-key blocks. The up-to-16 query columns of the problem (its rows x the G heads of
+// the kv head) are the B operand of v_mfma_f32_16x16x32_bf16 throughout:
+//   scores  S[key][col] = K[key][:] . q[col][:]   (A = K rows; q split into three bf16
+//                                                   terms, so q.k is fp32-accurate)
+//   output  O[dim][col] += V[key][dim] p[col][key] (A = the key-blocked V; p split into
+//                                                   two bf16 terms)
+// The score tile leaves lane (col = l % 16, q = l / 16) holding keys 4q..4q+3 of each
+// 16-key half; the PV step takes exactly those keys as its k slots, so p goes from
+// the softmax to the next MFMA without leaving the lane. The softmax is the usual
+// running max / sum per column, reduced over the four lane groups with shuffles.
+template <int HD>
+__global__ __launch_bounds__(kAttnWaves * 64) void attn_mfma_kernel(
+    const AttnProb* __restrict__ probs, int nprob,
+    // prefill mode (probs == nullptr): workgroup b covers prompt rows R (b / hkv) .. of kv
+    // head b % hkv, R = 16 / G, row r at position pos0 + r
+    const float* __restrict__ pq, int pq_stride, float* __restrict__ pout, int pout_stride,
+    const void* pK, const void* pV, int pos0, int prows,
+    int G, int hkv, int max_ctx, int split_len, float* __restrict__ partials) {
+  constexpr int KST = (HD + 31) / 32;     // 32-dim steps of q.k
+  constexpr int DT = HD / 16;             // 16-dim output tiles
+  constexpr int PW = HD + 2;              // record: m, l, o[HD]
+  __shared__ float mg[kAttnWaves][16][PW];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = lane & 15, gq = lane >> 4;
+  const float* q;
+  float* out;
+  const uint16_t* Kb;
+  const uint16_t* Vb;
+  int len, nrows, qs, os, nsplit, s, g, slot;
+  if (probs) {
+    const int pi = find_problem(probs, nprob, blockIdx.x);
+    const AttnProb& P = probs[pi];
+    const int t = blockIdx.x - P.tile0;
+    g = t / P.nsplit; s = t % P.nsplit; nsplit = P.nsplit; slot = P.slot;
+    q = P.q; out = P.out; len = P.len; nrows = P.nrows; qs = P.q_stride; os = P.out_stride;
+    Kb = static_cast<const uint16_t*>(P.K);
+    Vb = static_cast<const uint16_t*>(P.V);
+  } else {
+    const int R = 16 / G;
+    const int r0 = (blockIdx.x / hkv) * R;
+    g = blockIdx.x % hkv; s = 0; nsplit = 1; slot = 0;
+    nrows = min(R, prows - r0); len = pos0 + r0 + 1;
+    q = pq + (size_t)r0 * pq_stride; out = pout + (size_t)r0 * pout_stride;
+    qs = pq_stride; os = pout_stride;
+    Kb = static_cast<const uint16_t*>(pK);
+    Vb = static_cast<const uint16_t*>(pV);
+  }
+  const int ncol = nrows * G;
+  const bool cvalid = c < ncol;
+  const int crow = cvalid ? c / G : 0, chead = g * G + c % G;
+  const int clen = cvalid ? len + crow : 0;          // keys visible to this column
+  const int k_lo = s * split_len, k_hi = min(len + nrows - 1, k_lo + split_len);
+  const float scale = rsqrtf((float)HD);
+
+  const int nb = (k_hi - k_lo + 31) / 32;
+  const int j_lo = nb * w / kAttnWaves, j_hi = nb * (w + 1) / kAttnWaves;
+  const uint16_t* Kg = Kb + (size_t)g * max_ctx * HD;
+  const uint16_t* Vg = Vb + (size_t)g * (kv_ctx(max_ctx) / 32) * HD * 32;
+
+  // K and V pieces of block j; rows past the cache end are clamped (their scores are
+  // masked, and the cache is zero-filled at set-up, so every value is finite)
+  uint4 kf[2][2][KST], vf[2][DT];
+  auto load = [&](int buf, int j) {
+    const int kb = k_lo + 32 * min(j, j_hi - 1);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int key = min(kb + 16 * kt + c, max_ctx - 1);
+#pragma unroll
+      for (int st = 0; st < KST; ++st) {
+        const int d0 = 32 * st + 8 * gq;
+        kf[buf][kt][st] = load_g16(Kg + (size_t)key * HD + (d0 < HD ? d0 : 0));
+      }
+    }
+    const uint16_t* vb = Vg + (size_t)(min(kb, max_ctx - 1) / 32) * HD * 32;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const uint16_t* vp = vb + (size_t)(16 * dt + c) * 32 + 4 * gq;
+      const uint2 a = load_g8(vp);
+      const uint2 b = load_g8(vp + 16);
+      vf[buf][dt] = make_uint4(a.x, a.y, b.x, b.y);
+    }
+  };
+  // the first block is requested before q, so the two round trips overlap
+  if (j_lo < j_hi) load(0, j_lo);
+
+  // q of this lane's column, dims 32 st + 8 gq .. + 7, as three bf16 terms
+  uint4 qf[KST][3];
+#pragma unroll
+  for (int st = 0; st < KST; ++st) {
+    const int d0 = 32 * st + 8 * gq;
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = 0.f;
+    if (cvalid && d0 < HD) {
+      const float* qp = q + (size_t)crow * qs + (size_t)chead * HD + d0;
+      const float4 a = load_g4(qp), b = load_g4(qp + 4);
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+    uint32_t hi[8], mi[8], lo[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) split3(v[e], hi[e], mi[e], lo[e]);
+    qf[st][0] = make_uint4(hi[0] | hi[1] << 16, hi[2] | hi[3] << 16, hi[4] | hi[5] << 16, hi[6] | hi[7] << 16);
+    qf[st][1] = make_uint4(mi[0] | mi[1] << 16, mi[2] | mi[3] << 16, mi[4] | mi[5] << 16, mi[6] | mi[7] << 16);
+    qf[st][2] = make_uint4(lo[0] | lo[1] << 16, lo[2] | lo[3] << 16, lo[4] | lo[5] << 16, lo[6] | lo[7] << 16);
+  }
+
+  float m = -INFINITY, l = 0.f;
+  f32x4_t o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto block = [&](int buf, int j) {
+    const int kb = k_lo + 32 * j;
+    f32x4_t sc[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < KST; ++st) {
+        acc = mfma_bf16(kf[buf][kt][st], qf[st][2], acc);
+        acc = mfma_bf16(kf[buf][kt][st], qf[st][1], acc);
+        acc = mfma_bf16(kf[buf][kt][st], qf[st][0], acc);
+      }
+      sc[kt] = acc;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = kb + 16 * kt + 4 * gq + r;
+        const float v = key < clen && key < k_hi ? sc[kt][r] * scale : -INFINITY;
+        sc[kt][r] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mn = fmaxf(m, mx);
+    const bool live = mn != -INFINITY;
+    const float corr = live ? expf(m - mn) : 1.f;
+    float ps = 0.f;
+    uint32_t ph[8], pl[8];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float pv = live ? expf(sc[kt][r] - mn) : 0.f;
+        ps += pv;
+        ph[4 * kt + r] = f2bf(pv);
+        pl[4 * kt + r] = f2bf(pv - __uint_as_float(ph[4 * kt + r] << 16));
+      }
+    ps += __shfl_xor(ps, 16);
+    ps += __shfl_xor(ps, 32);
+    l = l * corr + ps;
+    m = mn;
+    const uint4 bh = make_uint4(ph[0] | ph[1] << 16, ph[2] | ph[3] << 16, ph[4] | ph[5] << 16, ph[6] | ph[7] << 16);
+    const uint4 bl = make_uint4(pl[0] | pl[1] << 16, pl[2] | pl[3] << 16, pl[4] | pl[5] << 16, pl[6] | pl[7] << 16);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[dt][r] *= corr;
+      o[dt] = mfma_bf16(vf[buf][dt], bl, o[dt]);
+      o[dt] = mfma_bf16(vf[buf][dt], bh, o[dt]);
+    }
+  };
+  // two blocks in flight per wave
+  if (j_lo < j_hi) {
+    for (int j = j_lo; j < j_hi; j += 2) {
+      load(1, j + 1);
+      block(0, j);
+      if (j + 1 < j_hi) {
+        load(0, j + 2);
+        block(1, j + 1);
+      }
+    }
+  }
+
+  // merge the four waves: mg[w][col] = {m, l, o[HD]}
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mg[w][c][2 + 16 * dt + 4 * gq + r] = o[dt][r];
+  if (gq == 0) { mg[w][c][0] = m; mg[w][c][1] = l; }
+  __syncthreads();
+  for (int t = threadIdx.x; t < ncol * HD; t += blockDim.x) {
+    const int cc = t / HD, d = t % HD;
+    float M = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kAttnWaves; ++u) M = fmaxf(M, mg[u][cc][0]);
+    float L = 0.f, a = 0.f;
+#pragma unroll
+    for (int u = 0; u < kAttnWaves; ++u) {
+      const float f = mg[u][cc][0] == -INFINITY ? 0.f : expf(mg[u][cc][0] - M);
+      L += mg[u][cc][1] * f;
+      a += mg[u][cc][2 + d] * f;
+    }
+    const int row = cc / G, head = g * G + cc % G;
+    if (nsplit == 1) {
+      out[(size_t)row * os + (size_t)head * HD + d] = a / L;
+    } else {
+      float* rec = partials + ((((size_t)slot * hkv + g) * kMaxSplit + s) * 16 + cc) * PW;
+      if (d == 0) { rec[0] = M; rec[1] = L; }
+      rec[2 + d] = a;
     }
   }
 }
 
 template <typename T, int HD, int GMAX>
-void launch_one(dim3 grid, hipStream_t st, const AttnProb* probs, int nprob, const float* pq,
-                int q_stride, float* pout, int out_stride, const void* pK, const void* pV,
-                int pos0, int G, int hkv, int max_ctx, int split, float* part, bool merge,
-                LaunchEv ev) {
+void launch_valu(dim3 grid, hipStream_t st, const AttnProb* probs, int nprob, const float* pq,
+                 int q_stride, float* pout, int out_stride, const void* pK, const void* pV,
+                 int pos0, int G, int hkv, int max_ctx, int split, float* part, bool merge,
+                 LaunchEv ev) {
   LaunchEv e1{ev.start, merge ? nullptr : ev.stop}, e2{nullptr, ev.stop};
   SPD_LAUNCH(e1, (attn_kernel<T, HD, GMAX>), grid, dim3(kAttnWaves * 64), 0, st, probs, nprob,
              pq, q_stride, pout, out_stride, pK, pV, pos0, G, hkv, max_ctx, split, part);
   if (merge)
     SPD_LAUNCH(e2, (attn_merge_kernel<HD>), dim3(nprob * hkv), dim3(kAttnWaves * 64), 0, st,
-               probs, G, hkv, part);
+               probs, G, hkv, G, part);
 }
 
-template <typename T>
-hipError_t dispatch(dim3 grid, hipStream_t st, const AttnProb* probs, int nprob, const float* pq,
-                    int q_stride, float* pout, int out_stride, const void* pK, const void* pV,
-                    int pos0, int hq, int hkv, int hd, int max_ctx, int split, float* part,
-                    bool merge, LaunchEv ev = {}) {
+template <int HD>
+void launch_mfma(dim3 grid, hipStream_t st, const AttnProb* probs, int nprob, const float* pq,
+                 int q_stride, float* pout, int out_stride, const void* pK, const void* pV,
+                 int pos0, int prows, int G, int hkv, int max_ctx, int split, float* part,
+                 bool merge, LaunchEv ev) {
+  LaunchEv e1{ev.start, merge ? nullptr : ev.stop}, e2{nullptr, ev.stop};
+  SPD_LAUNCH(e1, (attn_mfma_kernel<HD>), grid, dim3(kAttnWaves * 64), 0, st, probs, nprob, pq,
+             q_stride, pout, out_stride, pK, pV, pos0, prows, G, hkv, max_ctx, split, part);
+  if (merge)
+    SPD_LAUNCH(e2, (attn_merge_kernel<HD>), dim3(nprob * hkv), dim3(kAttnWaves * 64), 0, st,
+               probs, G, hkv, 16, part);
+}
+
+// grid: workgroups; prows: prompt rows in prefill mode (probs == nullptr)
+hipError_t dispatch(bool bf16, dim3 grid, hipStream_t st, const AttnProb* probs, int nprob,
+                    const float* pq, int q_stride, float* pout, int out_stride, const void* pK,
+                    const void* pV, int pos0, int prows, int hq, int hkv, int hd, int max_ctx,
+                    int split, float* part, bool merge, LaunchEv ev = {}) {
   const int G = hq / hkv;
+  if (bf16) {
+#define SPD_ATTN_CASE(HDV)                                                                    \
+    if (hd == HDV) {                                                                          \
+      launch_mfma<HDV>(grid, st, probs, nprob, pq, q_stride, pout, out_stride, pK, pV, pos0,  \
+                       prows, G, hkv, max_ctx, split, part, merge, ev);                       \
+      return hipGetLastError();                                                               \
+    }
+    SPD_ATTN_CASE(16)
+    SPD_ATTN_CASE(32)
+    SPD_ATTN_CASE(64)
+    SPD_ATTN_CASE(80)
+    SPD_ATTN_CASE(128)
+#undef SPD_ATTN_CASE
+    return hipErrorInvalidValue;
+  }
 #define SPD_ATTN_CASE(HDV)                                                                   \
   if (hd == HDV) {                                                                           \
     if (G <= 4)                                                                              \
-      launch_one<T, HDV, 4>(grid, st, probs, nprob, pq, q_stride, pout, out_stride, pK, pV,  \
-                            pos0, G, hkv, max_ctx, split, part, merge, ev);                        \
+      launch_valu<float, HDV, 4>(grid, st, probs, nprob, pq, q_stride, pout, out_stride, pK, \
+                                 pV, pos0, G, hkv, max_ctx, split, part, merge, ev);         \
     else                                                                                     \
-      launch_one<T, HDV, 16>(grid, st, probs, nprob, pq, q_stride, pout, out_stride, pK, pV, \
-                             pos0, G, hkv, max_ctx, split, part, merge, ev);                       \
+      launch_valu<float, HDV, 16>(grid, st, probs, nprob, pq, q_stride, pout, out_stride, pK,\
+                                  pV, pos0, G, hkv, max_ctx, split, part, merge, ev);        \
     return hipGetLastError();                                                                \
   }
   SPD_ATTN_CASE(16)
   SPD_ATTN_CASE(32)
   SPD_ATTN_CASE(64)
-  if constexpr (sizeof(T) == 2) {
-    SPD_ATTN_CASE(80)
-    SPD_ATTN_CASE(128)
-  }
 #undef SPD_ATTN_CASE
   return hipErrorInvalidValue;
 }
@@ -302,11 +560,8 @@ hipError_t launch_attention(const AttnProb* d_probs, int nprob, int ntiles, bool
                             int hkv, int hd, int max_ctx, int split_len, bool any_split,
                             float* partials, hipStream_t st, LaunchEv ev) {
   if (ntiles <= 0) return hipSuccess;
-  if (bf16)
-    return dispatch<uint16_t>(dim3(ntiles), st, d_probs, nprob, nullptr, 0, nullptr, 0, nullptr,
-                              nullptr, 0, hq, hkv, hd, max_ctx, split_len, partials, any_split, ev);
-  return dispatch<float>(dim3(ntiles), st, d_probs, nprob, nullptr, 0, nullptr, 0, nullptr,
-                         nullptr, 0, hq, hkv, hd, max_ctx, split_len, partials, any_split, ev);
+  return dispatch(bf16, dim3(ntiles), st, d_probs, nprob, nullptr, 0, nullptr, 0, nullptr, nullptr,
+                  0, 0, hq, hkv, hd, max_ctx, split_len, partials, any_split, ev);
 }
 
 hipError_t launch_attention_prefill(const float* q, int q_stride, float* out, int out_stride,
@@ -314,12 +569,14 @@ hipError_t launch_attention_prefill(const float* q, int q_stride, float* out, in
                                     int hq, int hkv, int hd, int max_ctx, hipStream_t st) {
   if (P <= 0) return hipSuccess;
   const int split = 1 << 30;
-  if (bf16)
-    return dispatch<uint16_t>(dim3(P * hkv), st, nullptr, 0, q, q_stride, out, out_stride, K, V,
-                              pos0, hq, hkv, hd, max_ctx, split, nullptr, false);
-  return dispatch<float>(dim3(P * hkv), st, nullptr, 0, q, q_stride, out, out_stride, K, V, pos0,
-                         hq, hkv, hd, max_ctx, split, nullptr, false);
+  // bf16: one workgroup per (16 / G prompt rows, kv head); fp32: per (row, kv head)
+  const int R = bf16 ? 16 / (hq / hkv) : 1;
+  const int groups = (P + R - 1) / R;
+  return dispatch(bf16, dim3(groups * hkv), st, nullptr, 0, q, q_stride, out, out_stride, K, V,
+                  pos0, P, hq, hkv, hd, max_ctx, split, nullptr, false);
 }
+
+int attn_rows_per_problem(bool bf16, int hq, int hkv) { return bf16 ? 16 / (hq / hkv) : 1; }
 
 int attn_max_split() { return kMaxSplit; }
 

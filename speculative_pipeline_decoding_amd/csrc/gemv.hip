@@ -121,9 +121,10 @@ __device__ void epilogue(const GemvProb& p, int v, int unit, float a, float b,
         store_kv<T>(p.kv_k, base + i, a * cs.x - b * cs.y);
         store_kv<T>(p.kv_k, base + i + half, a * cs.y + b * cs.x);
       } else {
-        const size_t base = ((size_t)(head - p.hq - p.hkv) * p.max_ctx + pos) * hd;
-        store_kv<T>(p.kv_v, base + i, a);
-        store_kv<T>(p.kv_v, base + i + half, b);
+        const int g = head - p.hq - p.hkv;
+        constexpr bool blocked = sizeof(T) == 2;
+        store_kv<T>(p.kv_v, v_index(blocked, g, pos, i, hd, p.max_ctx), a);
+        store_kv<T>(p.kv_v, v_index(blocked, g, pos, i + half, hd, p.max_ctx), b);
       }
       break;
     }

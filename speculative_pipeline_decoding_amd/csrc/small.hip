@@ -119,9 +119,10 @@ __global__ void rope_kv_kernel(float* __restrict__ QKV, int stride, T* __restric
         st(Kc, base + i + half, rb);
       }
     } else {
-      const size_t base = ((size_t)(head - hq - hkv) * max_ctx + pos) * hd;
-      st(Vc, base + i, a);
-      st(Vc, base + i + half, b);
+      const int g = head - hq - hkv;
+      constexpr bool blocked = sizeof(T) == 2;
+      st(Vc, v_index(blocked, g, pos, i, hd, max_ctx), a);
+      st(Vc, v_index(blocked, g, pos, i + half, hd, max_ctx), b);
     }
   }
 }

@@ -145,7 +145,7 @@ bool plan_config(const spd_model_config* c, Plan& p, std::string& err) {
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes); return at; };
   const size_t ctx = p.max_ctx;
-  p.kv_layer_bytes = 2 * (size_t)p.hkv * ctx * p.hd * p.esz;
+  p.kv_layer_bytes = 2 * (size_t)p.hkv * kv_ctx(p.max_ctx) * p.hd * p.esz;
   p.lin_state_bytes = (size_t)p.hq * p.hd * p.hd * 4;
   p.o_kv = take(p.nsoft * p.kv_layer_bytes);
   p.o_pkv = take((size_t)p.Ls * p.kv_layer_bytes);
@@ -167,7 +167,7 @@ bool plan_config(const spd_model_config* c, Plan& p, std::string& err) {
   p.o_verdict = take(sizeof(Verdict));
   p.o_desc = take(kDescBytes);
   const int G = p.hq / p.hkv;
-  p.o_apart = take((size_t)T * p.hkv * attn_max_split() * G * (p.hd + 2) * 4);
+  p.o_apart = take((size_t)T * p.hkv * attn_max_split() * std::max(G, 16) * (p.hd + 2) * 4);
   p.o_rope = take((size_t)ctx * (p.hd / 2) * sizeof(float2));
   p.o_forced = take(ctx * 4);
   const size_t CH = kPrefillChunk;
@@ -290,7 +290,11 @@ double gemv_bytes(const std::vector<GemvProb>& v, int esz) {
 int attn_split(const Plan& p, const std::vector<AttnProb>& v) {
   long long keys = 0;
   int maxlen = 1;
-  for (auto& a : v) { keys += a.len; maxlen = std::max(maxlen, a.len); }
+  for (auto& a : v) {
+    const int last = a.len + a.nrows - 1;   // keys of the problem's last row
+    keys += last;
+    maxlen = std::max(maxlen, last);
+  }
   const long long target = 2 * 256;   // workgroups to fill 256 CUs twice
   long long s = (keys * p.hkv + target - 1) / target;
   s = std::max<long long>(kAttnTile, (s + kAttnTile - 1) / kAttnTile * kAttnTile);
@@ -301,7 +305,7 @@ int attn_split(const Plan& p, const std::vector<AttnProb>& v) {
 int finish_attn(const Plan& p, std::vector<AttnProb>& v, int split, int slot0) {
   int t = 0;
   for (size_t i = 0; i < v.size(); ++i) {
-    v[i].nsplit = (v[i].len + split - 1) / split;
+    v[i].nsplit = (v[i].len + v[i].nrows - 1 + split - 1) / split;
     v[i].tile0 = t;
     v[i].slot = slot0 + (int)i;
     t += p.hkv * v[i].nsplit;
@@ -493,15 +497,19 @@ int build_step(spd_handle* h, DescWriter& dw) {
     q.kv_k = h->pK(r); q.kv_v = h->pV(r);
     q.pos0 = h->pdm_len; q.hq = p.hq; q.hkv = p.hkv; q.hd = p.hd; q.max_ctx = p.max_ctx;
     qkv.push_back(q);
-    for (int m = 0; m < M; ++m) {
+    // the last PDM layer only feeds the LM head: its attention, O and FFN run on the
+    // newest row alone (its QKV still writes every row's keys and values)
+    const int r0 = last ? M - 1 : 0, nr = last ? 1 : M;
+    const int rpp = attn_rows_per_problem(p.bf16, p.hq, p.hkv);
+    for (int m = r0; m < M; m += rpp) {
       AttnProb a{};
       a.q = qbuf + (size_t)(base + m) * p.qo; a.out = attn + (size_t)(base + m) * p.qo;
+      a.q_stride = p.qo; a.out_stride = p.qo;
       a.K = h->pK(r); a.V = h->pV(r); a.len = h->pdm_len + m + 1;
+      a.nrows = std::min(rpp, M - m);
       at.push_back(a);
     }
     const double kvb = 2.0 * (h->pdm_len + M) * p.hkv * p.hd * p.esz;
-    // the last PDM layer only feeds the LM head: its O / FFN run on the newest row alone
-    const int r0 = last ? M - 1 : 0, nr = last ? 1 : M;
     float* hrow = hp + (size_t)r0 * p.d;
     o.push_back(gemv(h->PW(r, T_O), p.d, p.qo, attn + (size_t)(base + r0) * p.qo, p.qo, nr,
                      EPI_ADD, hrow, p.d, nullptr, 0, 0.f));
@@ -541,6 +549,7 @@ int build_step(spd_handle* h, DescWriter& dw) {
       qkv.push_back(q);
       AttnProb a{};
       a.q = qbuf + (size_t)j * p.qo; a.out = attn + (size_t)j * p.qo;
+      a.q_stride = p.qo; a.out_stride = p.qo; a.nrows = 1;
       a.K = h->kvK(l); a.V = h->kvV(l); a.len = f.pos + 1;
       at.push_back(a);
       kvb += 2.0 * (f.pos + 1) * p.hkv * p.hd * p.esz;
@@ -701,6 +710,11 @@ int spd_init(const spd_model_config* cfg, const spd_weights* w, const spd_sampli
   if ((e = hipMemcpyAsync(h->ws + p.o_rope, rope.data(), rope.size() * sizeof(float2),
                           hipMemcpyHostToDevice, h->st)) != hipSuccess)
     return dev_fail(e, "hipMemcpyAsync(rope)");
+  // KV caches start zeroed: attention reads whole 32-key blocks, and the unwritten tail of
+  // the last one must hold finite values (its scores are masked, its values weigh 0)
+  if ((e = hipMemsetAsync(h->ws + p.o_kv, 0, (size_t)p.nsoft * p.kv_layer_bytes, h->st)) != hipSuccess ||
+      (e = hipMemsetAsync(h->ws + p.o_pkv, 0, (size_t)p.Ls * p.kv_layer_bytes, h->st)) != hipSuccess)
+    return dev_fail(e, "hipMemsetAsync(kv)");
   if ((e = hipStreamSynchronize(h->st)) != hipSuccess) return dev_fail(e, "hipStreamSynchronize");
   *out = h;
   return SPD_OK;
@@ -911,8 +925,8 @@ size_t spd_debug_size(const spd_handle* h, int32_t what) {
     case SPD_DBG_TARGET_LOGITS: case SPD_DBG_DRAFT_LOGITS: return (size_t)p.V * 4;
     case SPD_DBG_H_RING: case SPD_DBG_PDM_ROWS: return (size_t)p.ring * p.d * 4;
     case SPD_DBG_ANCHORS: return (size_t)p.ring * p.k * p.d * 4;
-    case SPD_DBG_TARGET_KV: return (size_t)p.nsoft * p.kv_layer_bytes;
-    case SPD_DBG_PDM_KV: return (size_t)p.Ls * p.kv_layer_bytes;
+    case SPD_DBG_TARGET_KV: return (size_t)p.nsoft * 2 * p.hkv * p.max_ctx * p.hd * p.esz;
+    case SPD_DBG_PDM_KV: return (size_t)p.Ls * 2 * p.hkv * p.max_ctx * p.hd * p.esz;
     case SPD_DBG_TOKENS: return (size_t)p.ring * 4;
   }
   return 0;
@@ -941,6 +955,28 @@ int spd_debug_copy(const spd_handle* hc, int32_t what, void* dst, size_t bytes) 
     case SPD_DBG_TOKENS: src = h->ws + p.o_tok; break;
   }
   HIPCHK(h, hipStreamSynchronize(h->st));
+  if (what == SPD_DBG_TARGET_KV || what == SPD_DBG_PDM_KV) {
+    // device layers hold K [hkv][max_ctx][hd] then V (v_index) in kv_layer_bytes; the copy
+    // is [layers][2][hkv][max_ctx][hd] row-major
+    const int layers = what == SPD_DBG_TARGET_KV ? p.nsoft : p.Ls;
+    std::vector<char> raw((size_t)layers * p.kv_layer_bytes);
+    HIPCHK(h, hipMemcpy(raw.data(), src, raw.size(), hipMemcpyDeviceToHost));
+    const size_t plane = (size_t)p.hkv * p.max_ctx * p.hd;   // elements of K (or V) of a layer
+    char* o = static_cast<char*>(dst);
+    for (int l = 0; l < layers; ++l) {
+      const char* kl = raw.data() + (size_t)l * p.kv_layer_bytes;
+      const char* vl = kl + p.kv_layer_bytes / 2;
+      char* ok = o + (size_t)l * 2 * plane * p.esz;
+      char* ov = ok + plane * p.esz;
+      std::memcpy(ok, kl, plane * p.esz);
+      for (int g = 0; g < p.hkv; ++g)
+        for (int pos = 0; pos < p.max_ctx; ++pos)
+          for (int d = 0; d < p.hd; ++d)
+            std::memcpy(ov + (((size_t)g * p.max_ctx + pos) * p.hd + d) * p.esz,
+                        vl + v_index(p.bf16, g, pos, d, p.hd, p.max_ctx) * p.esz, p.esz);
+    }
+    return SPD_OK;
+  }
   HIPCHK(h, hipMemcpy(dst, src, bytes, hipMemcpyDeviceToHost));
   return SPD_OK;
 }

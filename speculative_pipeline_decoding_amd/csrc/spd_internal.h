@@ -50,18 +50,37 @@ struct GemvProb {
   int pad;             // matrix-core kernel: row tiles per workgroup
 };
 
-// Attention over one layer's KV cache for a group of query rows.
-// Decode mode: one query per problem, keys 0..len-1.
+// Attention over one layer's KV cache for a group of query rows that share it: row r
+// (position pos0 + r) attends keys 0 .. len + r - 1. A row of the staircase is a
+// problem of its own; rows of the PDM window (one PDM layer) are grouped, up to
+// 16 / group query heads per problem on the bf16 path (one row on the fp32 path).
 struct AttnProb {
-  const float* q;      // [hq][hd], rotated
-  float* out;          // [hq][hd]
+  const float* q;      // row r: [hq][hd] at q + r * q_stride, rotated
+  float* out;          // row r: [hq][hd] at out + r * out_stride
   const void* K;       // [hkv][max_ctx][hd]
-  const void* V;
-  int len;             // keys 0..len-1
+  const void* V;       // bf16: key-blocked (v_index); fp32: [hkv][max_ctx][hd]
+  int len;             // keys of row 0
   int tile0;           // first workgroup: tile0 + g * nsplit + s
   int nsplit;
   int slot;            // index of this problem's partial area
+  int nrows;           // query rows
+  int q_stride, out_stride;
+  int pad;
 };
+
+// Rows of a layer's K or V cache, padded to whole 32-key blocks.
+__host__ __device__ constexpr int kv_ctx(int max_ctx) { return (max_ctx + 31) / 32 * 32; }
+
+// Element of V[kv head g][key pos][dim d] in a layer's V cache. bf16 caches keep every
+// block of 32 keys transposed ([dim][32 keys]), so the 8 consecutive keys of one dim
+// that a matrix-core operand lane takes are one contiguous piece; fp32 caches are
+// row-major.
+__host__ __device__ inline size_t v_index(bool blocked, int g, int pos, int d, int hd,
+                                          int max_ctx) {
+  if (blocked)
+    return (((size_t)g * (kv_ctx(max_ctx) / 32) + pos / 32) * hd + d) * 32 + (pos & 31);
+  return ((size_t)g * max_ctx + pos) * hd + d;
+}
 
 // Linear-attention (recurrent) step for one token at one layer.
 struct LinProb {
@@ -247,7 +266,17 @@ __device__ __forceinline__ uint4 load_stream(const void* p) {
   const u32x4 v = __builtin_nontemporal_load((const SPD_GLOBAL u32x4*)p);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
-// Ordinary 16-byte load through a global-memory pointer.
+// Ordinary 16- and 8-byte loads through a global-memory pointer.
+__device__ __forceinline__ uint4 load_g16(const void* p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = *(const SPD_GLOBAL u32x4*)p;
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 load_g8(const void* p) {
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 v = *(const SPD_GLOBAL u32x2*)p;
+  return make_uint2(v.x, v.y);
+}
 __device__ __forceinline__ float4 load_g4(const float* p) {
   const f32x4_t v = *(const SPD_GLOBAL f32x4_t*)p;
   return make_float4(v[0], v[1], v[2], v[3]);
@@ -309,6 +338,9 @@ hipError_t launch_attention(const AttnProb* d_probs, int nprob, int ntiles, bool
 hipError_t launch_attention_prefill(const float* q, int q_stride, float* out, int out_stride,
                                     const void* K, const void* V, int pos0, int P, bool bf16,
                                     int hq, int hkv, int hd, int max_ctx, hipStream_t st);
+int attn_max_split();
+// Query rows per attention problem when rows share a cache (bf16: 16 / group).
+int attn_rows_per_problem(bool bf16, int hq, int hkv);
 hipError_t launch_linear_step(const LinProb* d_probs, int nprob, int H, int hd, float eps,
                               hipStream_t st);
 hipError_t launch_linear_scan(const float* qkv, int qkv_stride, float* out, int out_stride,
