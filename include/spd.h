@@ -62,7 +62,12 @@ enum { SPD_LAYER_SOFTMAX = 0, SPD_LAYER_LINEAR = 1 };
  *     anchor b is the residual stream after b target layers (b = 0: embedding);
  *   pdm_layers = Ls >= 1 (Ls > L/n is allowed: the PDM is then simply not
  *     latency-masked, which the pages state as the condition Ls <= L/n);
- *   layer_kind [host, L entries] SPD_LAYER_* or NULL for all softmax;
+ *   layer_kind [host, L entries] SPD_LAYER_* or NULL for all softmax. A linear
+ *     layer has n_q_heads heads of head_dim with an hd x hd fp32 state per head,
+ *     S <- gamma_h S + k^ v^T, o = S^T q^ (q^, k^ unit-normalised, gamma_h =
+ *     1 - 2^-(5 + h mod 8), no RoPE); the state after each position is kept in a
+ *     ring of n + 1 slots, so a rejection restores it without a copy. PDM layers
+ *     are always softmax;
  *   anchor_fill: how a PDM row fills anchors deeper than its current depth:
  *     SPD_FILL_CLAMP repeats the deepest computed anchor (default), SPD_FILL_ZERO uses 0;
  *   max_ctx: KV capacity in positions; every in-flight position must stay below it.

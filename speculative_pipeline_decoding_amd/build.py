@@ -19,7 +19,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libspd.so")
 ARCH = os.environ.get("SPD_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["spd_api.hip", "gemv.hip", "attention.hip", "vocab.hip", "small.hip", "gemm.hip"]
+SOURCES = ["spd_api.hip", "gemv.hip", "attention.hip", "linear.hip", "vocab.hip", "small.hip", "gemm.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -116,8 +116,7 @@ bool plan_config(const spd_model_config* c, Plan& p, std::string& err) {
   if (c->layer_kind)
     for (int l = 0; l < p.L; ++l) p.kind[l] = c->layer_kind[l];
   for (int l = 0; l < p.L; ++l) {
-    if (p.kind[l] == SPD_LAYER_LINEAR) return bad("linear-attention layers are not supported yet");
-    if (p.kind[l] != SPD_LAYER_SOFTMAX) return bad("bad layer_kind");
+    if (p.kind[l] != SPD_LAYER_SOFTMAX && p.kind[l] != SPD_LAYER_LINEAR) return bad("bad layer_kind");
   }
   p.sizes.resize(p.n);
   if (c->stage_layers) {
@@ -239,6 +238,11 @@ struct spd_handle {
   void* kvK(int l) const { return ws + p.o_kv + (size_t)p.ord[l] * p.kv_layer_bytes; }
   void* kvV(int l) const { return (char*)kvK(l) + p.kv_layer_bytes / 2; }
   void* pK(int r) const { return ws + p.o_pkv + (size_t)r * p.kv_layer_bytes; }
+  // state of linear layer l after the position whose ring slot is `slot`
+  float* lin(int l, int slot) const {
+    return reinterpret_cast<float*>(ws + p.o_lin +
+                                    ((size_t)p.ord[l] * p.ring + slot) * p.lin_state_bytes);
+  }
   void* pV(int r) const { return (char*)pK(r) + p.kv_layer_bytes / 2; }
 };
 
@@ -363,6 +367,9 @@ hipError_t run_op(spd_handle* h, const Op& op, LaunchEv ev = {}) {
     case OP_GEMV_HEAD: case OP_PDM_QKV: case OP_PDM_O: case OP_PDM_GU: case OP_PDM_DOWN:
       return launch_gemv(gemv_role(op.kind), reinterpret_cast<const GemvProb*>(d + op.off),
                          op.count, op.plan, p.bf16, rope, st, ev);
+    case OP_LIN:
+      return launch_linear_step(reinterpret_cast<const LinProb*>(d + op.off), op.count, p.hq, p.hd,
+                                kLinEps, st, ev);
     case OP_ATTN: case OP_PDM_ATTN:
       return launch_attention(reinterpret_cast<const AttnProb*>(d + op.off), op.count, op.ntiles,
                               p.bf16, p.hq, p.hkv, p.hd, p.max_ctx, op.split,
@@ -428,6 +435,7 @@ int build_step(spd_handle* h, DescWriter& dw) {
   float* X = h->at<float>(p.o_X);
   float* qbuf = h->at<float>(p.o_qbuf);
   float* attn = h->at<float>(p.o_attn);
+  float* lqkv = h->at<float>(p.o_lqkv);
   float* act = h->at<float>(p.o_act);
   float* logits = h->at<float>(p.o_logits);
   float* qring = h->at<float>(p.o_qring);
@@ -534,25 +542,39 @@ int build_step(spd_handle* h, DescWriter& dw) {
   for (int r = 0; r < R; ++r) {
     std::vector<GemvProb> qkv, o, gu, down;
     std::vector<AttnProb> at;
-    double kvb = 0;
+    std::vector<LinProb> lin;
+    double kvb = 0, linb = 0;
     for (int j = 0; j < n_inf; ++j) {
       const Inflight f = h->F[j];
       if (p.sizes[f.stage] <= r) continue;
       const int l = p.starts[f.stage] + r;
       const int s = h->slot(f.pos);
       float* hv = hring + (size_t)s * p.d;
-      GemvProb q = gemv(h->W(l, T_QKV), p.qrows, p.d, hv, 0, 1, EPI_QKV, nullptr, 0,
-                        (const float*)h->W(l, T_ATTN_NORM), 0, p.eps);
-      q.aux = qbuf + (size_t)j * p.qo;
-      q.kv_k = h->kvK(l); q.kv_v = h->kvV(l);
-      q.pos0 = f.pos; q.hq = p.hq; q.hkv = p.hkv; q.hd = p.hd; q.max_ctx = p.max_ctx;
-      qkv.push_back(q);
-      AttnProb a{};
-      a.q = qbuf + (size_t)j * p.qo; a.out = attn + (size_t)j * p.qo;
-      a.q_stride = p.qo; a.out_stride = p.qo; a.nrows = 1;
-      a.K = h->kvK(l); a.V = h->kvV(l); a.len = f.pos + 1;
-      at.push_back(a);
-      kvb += 2.0 * (f.pos + 1) * p.hkv * p.hd * p.esz;
+      if (p.kind[l] == SPD_LAYER_LINEAR) {
+        // q, k, v to the token's scratch row, then the recurrent step from the state
+        // after pos - 1 to the state after pos
+        float* lrow = lqkv + (size_t)j * p.linrows;
+        qkv.push_back(gemv(h->W(l, T_QKV), p.linrows, p.d, hv, 0, 1, EPI_STORE, lrow, 0,
+                           (const float*)h->W(l, T_ATTN_NORM), 0, p.eps));
+        LinProb lp{};
+        lp.qkv = lrow; lp.out = attn + (size_t)j * p.qo;
+        lp.s_prev = h->lin(l, h->slot(f.pos - 1)); lp.s_next = h->lin(l, h->slot(f.pos));
+        lin.push_back(lp);
+        linb += 2.0 * p.lin_state_bytes;
+      } else {
+        GemvProb q = gemv(h->W(l, T_QKV), p.qrows, p.d, hv, 0, 1, EPI_QKV, nullptr, 0,
+                          (const float*)h->W(l, T_ATTN_NORM), 0, p.eps);
+        q.aux = qbuf + (size_t)j * p.qo;
+        q.kv_k = h->kvK(l); q.kv_v = h->kvV(l);
+        q.pos0 = f.pos; q.hq = p.hq; q.hkv = p.hkv; q.hd = p.hd; q.max_ctx = p.max_ctx;
+        qkv.push_back(q);
+        AttnProb a{};
+        a.q = qbuf + (size_t)j * p.qo; a.out = attn + (size_t)j * p.qo;
+        a.q_stride = p.qo; a.out_stride = p.qo; a.nrows = 1;
+        a.K = h->kvK(l); a.V = h->kvV(l); a.len = f.pos + 1;
+        at.push_back(a);
+        kvb += 2.0 * (f.pos + 1) * p.hkv * p.hd * p.esz;
+      }
       o.push_back(gemv(h->W(l, T_O), p.d, p.qo, attn + (size_t)j * p.qo, 0, 1, EPI_ADD, hv, 0,
                        nullptr, 0, 0.f));
       GemvProb g = gemv(h->W(l, T_GATE), p.F, p.d, hv, 0, 1, EPI_SWIGLU, act + (size_t)j * p.F, 0,
@@ -568,6 +590,11 @@ int build_step(spd_handle* h, DescWriter& dw) {
     }
     push_gemv(OP_GEMV_QKV, qkv, 0);
     push_attn(OP_ATTN, at, 0, 0, kvb);
+    if (!lin.empty()) {
+      Op op{OP_LIN, dw.put(lin.data(), (int)lin.size()), (int)lin.size(), (int)lin.size() * p.hq,
+            0, linb};
+      h->ops.push_back(op);
+    }
     push_gemv(OP_GEMV_O, o, 0);
     push_gemv(OP_GEMV_GU, gu, 0);
     push_gemv(OP_GEMV_DOWN, down, 0);
@@ -754,12 +781,22 @@ int spd_prefill(spd_handle* h, const int32_t* prompt, int32_t len, int32_t* firs
   const int CH = kPrefillChunk;
   const int kd = p.k * p.d;
   // one decoder layer over P rows of the residual Rb (fp32 activations throughout)
-  auto layer = [&](float* Rb, int P, int pos0, const void* const* wt, void* Kc, void* Vc) -> int {
+  // lin_l >= 0: a linear-attention target layer (its state ring), else a softmax layer
+  auto layer = [&](float* Rb, int P, int pos0, const void* const* wt, void* Kc, void* Vc,
+                   int lin_l = -1) -> int {
     HIPCHK(h, launch_rmsnorm_rows(Rb, p.d, (const float*)wt[T_ATTN_NORM], A, p.d, P, p.d, p.eps, false, st));
-    HIPCHK(h, launch_gemm(A, p.d, wt[T_QKV], QKV, p.qrows, P, p.qrows, p.d, false, bf, st));
-    HIPCHK(h, launch_rope_kv(QKV, p.qrows, Kc, Vc, rope, pos0, P, p.hq, p.hkv, p.hd, p.max_ctx, bf, st));
-    HIPCHK(h, launch_attention_prefill(QKV, p.qrows, O, p.qo, Kc, Vc, pos0, P, bf, p.hq, p.hkv,
-                                       p.hd, p.max_ctx, st));
+    if (lin_l >= 0) {
+      // the state after the previous chunk to the state after this chunk's last row
+      HIPCHK(h, launch_gemm(A, p.d, wt[T_QKV], QKV, p.linrows, P, p.linrows, p.d, false, bf, st));
+      const float* s_in = pos0 > 0 ? h->lin(lin_l, h->slot(pos0 - 1)) : nullptr;
+      HIPCHK(h, launch_linear_scan(QKV, p.linrows, O, p.qo, s_in, h->lin(lin_l, h->slot(pos0 + P - 1)),
+                                   P, p.hq, p.hd, kLinEps, st));
+    } else {
+      HIPCHK(h, launch_gemm(A, p.d, wt[T_QKV], QKV, p.qrows, P, p.qrows, p.d, false, bf, st));
+      HIPCHK(h, launch_rope_kv(QKV, p.qrows, Kc, Vc, rope, pos0, P, p.hq, p.hkv, p.hd, p.max_ctx, bf, st));
+      HIPCHK(h, launch_attention_prefill(QKV, p.qrows, O, p.qo, Kc, Vc, pos0, P, bf, p.hq, p.hkv,
+                                         p.hd, p.max_ctx, st));
+    }
     HIPCHK(h, launch_gemm(O, p.qo, wt[T_O], Rb, p.d, P, p.d, p.qo, true, bf, st));
     HIPCHK(h, launch_rmsnorm_rows(Rb, p.d, (const float*)wt[T_FFN_NORM], A, p.d, P, p.d, p.eps, false, st));
     HIPCHK(h, launch_gemm(A, p.d, wt[T_GATE], Gb, p.F, P, p.F, p.d, false, bf, st));
@@ -773,7 +810,9 @@ int spd_prefill(spd_handle* h, const int32_t* prompt, int32_t len, int32_t* firs
     HIPCHK(h, launch_embed_rows(h->embed, toks + c0, H, P, p.d, bf, st));
     HIPCHK(h, launch_copy_rows(H, p.d, AN, p.d, P, p.d, st));   // anchor 0: the embedding
     for (int l = 0; l < p.L; ++l) {
-      const int rc = layer(H, P, c0, &h->lw[(size_t)l * kTensorsPerLayer], h->kvK(l), h->kvV(l));
+      const bool lin = p.kind[l] == SPD_LAYER_LINEAR;
+      const int rc = layer(H, P, c0, &h->lw[(size_t)l * kTensorsPerLayer], lin ? nullptr : h->kvK(l),
+                           lin ? nullptr : h->kvV(l), lin ? l : -1);
       if (rc != SPD_OK) return rc;
       for (int i = 1; i < p.k; ++i)
         if (p.anchors[i] == l + 1)

@@ -17,6 +17,7 @@ constexpr int kMaxVec = kMaxRows;       // input vectors of one GEMV problem
 constexpr int kAttnTile = 64;           // keys per attention tile
 constexpr int kVocabBlock = 1024;       // threads of the vocabulary reduction blocks
 constexpr float kNearTie = 1e-3f;
+constexpr float kLinEps = 1e-6f;          // linear attention: q, k / sqrt(|.|^2 + eps)
 
 // GEMV epilogues.
 enum Epi : int {
@@ -342,7 +343,7 @@ int attn_max_split();
 // Query rows per attention problem when rows share a cache (bf16: 16 / group).
 int attn_rows_per_problem(bool bf16, int hq, int hkv);
 hipError_t launch_linear_step(const LinProb* d_probs, int nprob, int H, int hd, float eps,
-                              hipStream_t st);
+                              hipStream_t st, LaunchEv ev = {});
 hipError_t launch_linear_scan(const float* qkv, int qkv_stride, float* out, int out_stride,
                               const float* s_in, float* s_out, int P, int H, int hd, float eps,
                               hipStream_t st);

@@ -101,6 +101,7 @@ def run_parity(cfg, W, dW, prompt, G=None, T=0.0, seed=0, n=None, fill="clamp",
     if rep["stopped_at_near_tie"] is None:
         assert (st.N, st.K, st.accepted, st.rejected) == (orc.N, orc.K, orc.accepted, orc.rejected)
         assert abs(st.s0 - orc.s0) < 1e-12
-    rep.update(N=st.N, K=st.K, alpha=st.alpha, s0=st.s0, tokens_match=orc.committed)
+    rep.update(N=st.N, K=st.K, alpha=st.alpha, s0=st.s0, rejected=st.rejected,
+               tokens_match=orc.committed)
     gpu.close()
     return rep

@@ -54,13 +54,15 @@ def test_tiny_forced_and_zero_fill():
 
 
 @pytest.mark.parametrize("name", ["mid_bf16_L6_d384_n3", "mid_bf16_L7_d256_n3_uneven",
-                                  "mid_f32_L4_d128_n1", "mid_bf16_L4_d512_hd128_n4"])
+                                  "mid_f32_L4_d128_n1", "mid_bf16_L4_d512_hd128_n4",
+                                  "mid_hybrid_bf16_L8_d256_n4"])
 def test_mid_greedy(name):
     rep = _run(name)
     assert rep["steps"] > 0
 
 
-@pytest.mark.parametrize("name", ["mid_bf16_L6_d384_n3", "mid_bf16_L4_d512_hd128_n4"])
+@pytest.mark.parametrize("name", ["mid_bf16_L6_d384_n3", "mid_bf16_L4_d512_hd128_n4",
+                                  "mid_hybrid_bf16_L8_d256_n4"])
 def test_mid_sampled(name):
     rep = _run(name, T=1.0, seed=7)
     assert rep["steps"] > 0
@@ -72,6 +74,15 @@ def test_mid_forced_acceptance():
     ref = ar_decode(cfg, W, prompt, G=cfg.gen_len + 8)
     rep = _run("mid_bf16_L6_d384_n3", forced_p=0.8, forced_ref=ref, seed=2)
     assert rep["stopped_at_near_tie"] is None
+
+
+def test_hybrid_rollback_restores_linear_state():
+    """Frequent rejections: every reseed must continue from the linear states saved at v - 1."""
+    from oracle.spd import ar_decode
+    cfg, W, prompt = workload("mid_hybrid_bf16_L8_d256_n4")
+    ref = ar_decode(cfg, W, prompt, G=cfg.gen_len + 8)
+    rep = _run("mid_hybrid_bf16_L8_d256_n4", forced_p=0.4, forced_ref=ref, seed=4)
+    assert rep["stopped_at_near_tie"] is None and rep["rejected"] > 3
 
 
 def test_determinism_same_seed_same_bits():
