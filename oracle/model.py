@@ -221,9 +221,10 @@ class Model:
     """Target decoder + PDM decoder sharing one weight table (the LM head is tied)."""
 
     def __init__(self, cfg: ModelConfig, arrays: Dict[str, np.ndarray], ft=np.float64,
-                 cache: bool = True):
+                 cache: bool = True, weights: Optional[Weights] = None):
         self.cfg = cfg
-        self.W = Weights(arrays, ft, cache)
+        # a prebuilt Weights shares its upcast tensors between several runs of one model
+        self.W = weights if weights is not None else Weights(arrays, ft, cache)
         self.ft = ft
         self.target = Stack(cfg, self.W, "layers", cfg.kinds)
         self.pdm = Stack(cfg, self.W, "pdm.layers", (SOFTMAX,) * cfg.pdm_layers)

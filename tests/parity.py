@@ -27,7 +27,8 @@ def rel(a, b):
 
 
 def run_parity(cfg, W, dW, prompt, G=None, T=0.0, seed=0, n=None, fill="clamp",
-               forced_p=None, forced_ref=None, check_states=True, max_steps=None):
+               forced_p=None, forced_ref=None, check_states=True, max_steps=None,
+               oracle_weights=None):
     from speculative_pipeline_decoding_amd import SPD
     G = cfg.gen_len if G is None else G
     tol_l, tol_h = tolerances(cfg)
@@ -37,7 +38,11 @@ def run_parity(cfg, W, dW, prompt, G=None, T=0.0, seed=0, n=None, fill="clamp",
         s.forced_p, s.forced_ref, s.forced_base = forced_p, np.asarray(forced_ref), len(prompt)
         kw = dict(forced_p=forced_p, forced_ref=list(forced_ref))
     gpu = SPD(cfg, dW, temperature=T, seed=seed, n=n, fill=fill, **kw)
-    orc = OracleSPD(cfg, W, s, n=n, fill=fill)
+    model = None
+    if oracle_weights is not None:
+        from oracle.model import Model
+        model = Model(cfg, W, weights=oracle_weights)
+    orc = OracleSPD(cfg, W, s, n=n, fill=fill, model=model)
     rep = {"steps": 0, "max_logit_err": 0.0, "max_state_rel": 0.0, "stopped_at_near_tie": None,
            "flagged": 0}
     t0o = orc.prefill(prompt)
