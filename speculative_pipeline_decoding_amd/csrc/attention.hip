@@ -21,7 +21,7 @@
 namespace spd {
 namespace {
 
-constexpr int kMaxSplit = 64;
+constexpr int kMaxSplit = 16;     // key splits per (problem, kv head)
 constexpr int kAttnWaves = 4;
 
 
@@ -232,49 +232,51 @@ template <int HD>
 __global__ __launch_bounds__(kAttnWaves * 64) void attn_merge_kernel(
     const AttnProb* __restrict__ probs, int G, int hkv, int CW, const float* __restrict__ partials) {
   constexpr int PW = HD + 2;
+  constexpr int PER = (16 * HD + kAttnWaves * 64 - 1) / (kAttnWaves * 64);   // workgroups per pair
   __shared__ float wgt[kMaxSplit][16];      // e^(m_s - M) / L per split and column
   __shared__ float ml[kMaxSplit][16][2];
-  const AttnProb& P = probs[blockIdx.x / hkv];
-  const int g = blockIdx.x % hkv;
+  const int pair = blockIdx.x / PER, part = blockIdx.x % PER;
+  const AttnProb& P = probs[pair / hkv];
+  const int g = pair % hkv;
   const int nsplit = P.nsplit;
   if (nsplit == 1) return;
   const int ncol = P.nrows * G;
+  const int t = part * blockDim.x + threadIdx.x;          // this thread's (column, dim)
+  if (part * (int)blockDim.x >= ncol * HD) return;        // nothing for this workgroup
   const float* base = partials + ((size_t)P.slot * hkv + g) * kMaxSplit * CW * PW;
-  for (int t = threadIdx.x; t < nsplit * ncol; t += blockDim.x) {
-    const int u = t / ncol, c = t % ncol;
-    const float2 v = *reinterpret_cast<const float2*>(base + ((size_t)u * CW + c) * PW);
-    ml[u][c][0] = v.x;
-    ml[u][c][1] = v.y;
+  // the element loads go out first, so both round trips overlap
+  const int c = min(t / HD, ncol - 1), d = t % HD;
+  float v[kMaxSplit];
+#pragma unroll
+  for (int u = 0; u < kMaxSplit; ++u)
+    v[u] = u < nsplit ? base[((size_t)u * CW + c) * PW + 2 + d] : 0.f;
+  for (int i = threadIdx.x; i < nsplit * ncol; i += blockDim.x) {
+    const int u = i / ncol, cc = i % ncol;
+    const float2 mv = *reinterpret_cast<const float2*>(base + ((size_t)u * CW + cc) * PW);
+    ml[u][cc][0] = mv.x;
+    ml[u][cc][1] = mv.y;
   }
   __syncthreads();
   if (threadIdx.x < ncol) {
-    const int c = threadIdx.x;
+    const int cc = threadIdx.x;
     float M = -INFINITY;
-    for (int u = 0; u < nsplit; ++u) M = fmaxf(M, ml[u][c][0]);
+    for (int u = 0; u < nsplit; ++u) M = fmaxf(M, ml[u][cc][0]);
     float L = 0.f;
     for (int u = 0; u < nsplit; ++u) {
-      const float f = ml[u][c][0] == -INFINITY ? 0.f : expf(ml[u][c][0] - M);
-      wgt[u][c] = f;
-      L += ml[u][c][1] * f;
+      const float f = ml[u][cc][0] == -INFINITY ? 0.f : expf(ml[u][cc][0] - M);
+      wgt[u][cc] = f;
+      L += ml[u][cc][1] * f;
     }
     const float inv = 1.f / L;
-    for (int u = 0; u < nsplit; ++u) wgt[u][c] *= inv;
+    for (int u = 0; u < nsplit; ++u) wgt[u][cc] *= inv;
   }
   __syncthreads();
-  for (int t = threadIdx.x; t < ncol * HD; t += blockDim.x) {
-    const int c = t / HD, d = t % HD;
-    const float* rec = base + (size_t)c * PW + 2 + d;
-    float a = 0.f;
-    for (int u0 = 0; u0 < nsplit; u0 += 8) {
-      float v[8];
+  if (t >= ncol * HD) return;
+  float a = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = u0 + i < nsplit ? rec[(size_t)(u0 + i) * CW * PW] : 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (u0 + i < nsplit) a += v[i] * wgt[u0 + i][c];
-    }
-    P.out[(size_t)(c / G) * P.out_stride + (size_t)(g * G + c % G) * HD + d] = a;
-  }
+  for (int u = 0; u < kMaxSplit; ++u)
+    if (u < nsplit) a += v[u] * wgt[u][c];
+  P.out[(size_t)(c / G) * P.out_stride + (size_t)(g * G + c % G) * HD + d] = a;
 }
 
 // ---- matrix-core kernel (bf16 caches) ------------------------------------------------
@@ -486,6 +488,9 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_mfma_kernel(
   }
 }
 
+// workgroups of the merge per (problem, kv head): one thread per (column, dim)
+constexpr int merge_parts(int hd) { return (16 * hd + kAttnWaves * 64 - 1) / (kAttnWaves * 64); }
+
 template <typename T, int HD, int GMAX>
 void launch_valu(dim3 grid, hipStream_t st, const AttnProb* probs, int nprob, const float* pq,
                  int q_stride, float* pout, int out_stride, const void* pK, const void* pV,
@@ -495,8 +500,8 @@ void launch_valu(dim3 grid, hipStream_t st, const AttnProb* probs, int nprob, co
   SPD_LAUNCH(e1, (attn_kernel<T, HD, GMAX>), grid, dim3(kAttnWaves * 64), 0, st, probs, nprob,
              pq, q_stride, pout, out_stride, pK, pV, pos0, G, hkv, max_ctx, split, part);
   if (merge)
-    SPD_LAUNCH(e2, (attn_merge_kernel<HD>), dim3(nprob * hkv), dim3(kAttnWaves * 64), 0, st,
-               probs, G, hkv, G, part);
+    SPD_LAUNCH(e2, (attn_merge_kernel<HD>), dim3(nprob * hkv * merge_parts(HD)),
+               dim3(kAttnWaves * 64), 0, st, probs, G, hkv, G, part);
 }
 
 template <int HD>
@@ -508,8 +513,8 @@ void launch_mfma(dim3 grid, hipStream_t st, const AttnProb* probs, int nprob, co
   SPD_LAUNCH(e1, (attn_mfma_kernel<HD>), grid, dim3(kAttnWaves * 64), 0, st, probs, nprob, pq,
              q_stride, pout, out_stride, pK, pV, pos0, prows, G, hkv, max_ctx, split, part);
   if (merge)
-    SPD_LAUNCH(e2, (attn_merge_kernel<HD>), dim3(nprob * hkv), dim3(kAttnWaves * 64), 0, st,
-               probs, G, hkv, 16, part);
+    SPD_LAUNCH(e2, (attn_merge_kernel<HD>), dim3(nprob * hkv * merge_parts(HD)),
+               dim3(kAttnWaves * 64), 0, st, probs, G, hkv, 16, part);
 }
 
 // grid: workgroups; prows: prompt rows in prefill mode (probs == nullptr)
@@ -578,6 +583,7 @@ hipError_t launch_attention_prefill(const float* q, int q_stride, float* out, in
 
 int attn_rows_per_problem(bool bf16, int hq, int hkv) { return bf16 ? 16 / (hq / hkv) : 1; }
 
+// splits per (problem, kv head): the merge keeps every split's value in registers
 int attn_max_split() { return kMaxSplit; }
 
 }  // namespace spd

@@ -873,6 +873,24 @@ int spd_prefill(spd_handle* h, const int32_t* prompt, int32_t len, int32_t* firs
   return SPD_OK;
 }
 
+// The host issues launches one at a time, so the order of the two streams' work in the
+// op list is the order in which each stream receives it. build_step lists the whole PDM
+// chain before the target's sub-layers; interleave them so neither stream waits behind
+// the other's launches (each stream keeps its own order).
+void interleave_streams(std::vector<Op>& ops) {
+  auto f = std::find_if(ops.begin(), ops.end(), [](const Op& o) { return o.kind == OP_FORK; });
+  auto j = std::find_if(ops.begin(), ops.end(), [](const Op& o) { return o.kind == OP_JOIN; });
+  if (f == ops.end() || j == ops.end() || j < f) return;
+  std::vector<Op> side, main;
+  for (auto it = f + 1; it != j; ++it) (it->stream ? side : main).push_back(*it);
+  auto out = f + 1;
+  size_t a = 0, b = 0;
+  while (a < main.size() || b < side.size()) {
+    if (a < main.size()) *out++ = main[a++];
+    if (b < side.size()) *out++ = side[b++];
+  }
+}
+
 int spd_step(spd_handle* h) {
   if (!h) return SPD_E_ARG;
   h->err.clear();
@@ -883,6 +901,7 @@ int spd_step(spd_handle* h) {
   DescWriter dw{h->h_desc};
   int rc = build_step(h, dw);
   if (rc != SPD_OK) return rc;
+  interleave_streams(h->ops);
   if (dw.used > kDescBytes) return fail(h, SPD_E_CAPACITY, "internal: descriptor block overflow");
   HIPCHK(h, hipMemcpyAsync(h->ws + h->p.o_desc, h->h_desc, dw.used, hipMemcpyHostToDevice, h->st));
   rc = run_ops(h);
