@@ -31,6 +31,8 @@ import statistics
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -66,23 +68,26 @@ def run_spd(cfg, dW, prompt, T, seed, warmup, steps, kernel_timing):
 
     def region():
         s0 = spd.stats()
-        evs, kinds = [], []
+        # events are created before the clock starts; recording one costs a few µs of host time
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        kinds, host = [], []
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for _ in range(steps):
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
+        for a, b in evs:
             a.record(stream)
+            h0 = time.perf_counter()
             spd.step()
+            host.append(time.perf_counter() - h0)
             b.record(stream)
             c = spd.verify_commit()
-            evs.append((a, b))
             kinds.append(bool(c.verified))
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         s1 = spd.stats()
         step_ms = [a.elapsed_time(b) for a, b in evs]
         return s1, {"wall_s": wall, "N": s1.N - s0.N, "K": s1.K - s0.K, "step_ms": step_ms,
+                    "host_step_us": 1e6 * float(np.median(host)),
                     "full": [m for m, k in zip(step_ms, kinds) if k],
                     "refill": [m for m, k in zip(step_ms, kinds) if not k]}
 
@@ -164,7 +169,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--workload", default="cfg3")
-    ap.add_argument("--temperature", type=float, default=1.0)
+    ap.add_argument("--temperature", type=float, default=None,
+                    help="sampling temperature (default: the workload's first one)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--t0-run", action="store_true",
                     help="also time the same steps at T=0 (greedy, lossless) and report them")
@@ -185,6 +191,8 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     cfg = get(args.workload)
+    if args.temperature is None:
+        args.temperature = float(cfg.temperatures[0])
     if args.warmup + args.steps > cfg.gen_len:
         print(f"warmup + steps must be <= {cfg.gen_len} (the workload generates {cfg.gen_len} "
               "tokens; each step commits at most one)", file=sys.stderr)
@@ -263,7 +271,8 @@ def main():
                     "p10": 1e3 * pct(tm["step_ms"], 0.1), "p90": 1e3 * pct(tm["step_ms"], 0.9),
                     "full_median": 1e3 * statistics.median(tm["full"]) if tm["full"] else None,
                     "refill_median": 1e3 * statistics.median(tm["refill"]) if tm["refill"] else None,
-                    "full_steps": len(tm["full"]), "refill_steps": len(tm["refill"])},
+                    "full_steps": len(tm["full"]), "refill_steps": len(tm["refill"]),
+                    "host_enqueue_median": tm["host_step_us"]},
         "alpha": alpha,
         "s0": alpha * cfg.n_stages,
         "step_hbm_roofline": {"algorithmic_bytes_per_step": step_bytes,
