@@ -208,7 +208,8 @@ struct spd_handle {
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   // pinned host staging
   char* h_desc = nullptr;
-  Verdict* h_verdict = nullptr;
+  Verdict* h_verdict = nullptr;   // pinned; written by the verdict kernels through d_hverdict
+  Verdict* d_hverdict = nullptr;
   // state machine
   enum { S_INIT, S_READY, S_PENDING } state = S_INIT;
   int P0 = 0;
@@ -639,6 +640,7 @@ int build_step(spd_handle* h, DescWriter& dw) {
   fd.lse_q_new = qlse + h->slot(dpos);
   fd.tok_ring = h->at<int>(p.o_tok);
   fd.verdict = h->at<Verdict>(p.o_verdict);
+  fd.host_verdict = h->d_hverdict;
   fd.part = h->at<VocabPartial>(p.o_part);
   const size_t foff = dw.put(&fd, 1);
   h->ops.push_back({OP_FINAL, foff, 1, 1, 0, 0.0});
@@ -725,6 +727,8 @@ int spd_init(const spd_model_config* cfg, const spd_weights* w, const spd_sampli
     return dev_fail(e, "hipHostMalloc");
   if ((e = hipHostMalloc((void**)&h->h_verdict, sizeof(Verdict), hipHostMallocDefault)) != hipSuccess)
     return dev_fail(e, "hipHostMalloc");
+  if ((e = hipHostGetDevicePointer((void**)&h->d_hverdict, h->h_verdict, 0)) != hipSuccess)
+    return dev_fail(e, "hipHostGetDevicePointer");
   // the PDM stream (default priority) and the events that fork and join it each step
   if ((e = hipStreamCreateWithFlags(&h->st2, hipStreamNonBlocking)) != hipSuccess)
     return dev_fail(e, "hipStreamCreateWithFlags");
@@ -845,6 +849,7 @@ int spd_prefill(spd_handle* h, const int32_t* prompt, int32_t len, int32_t* firs
       fd.mode = 1; fd.dpos = len; fd.ring = p.ring; fd.V = p.V; fd.nblocks = kVocabBlocks;
       fd.temp = h->temp; fd.inv_temp = vd.inv_temp; fd.seed = h->seed;
       fd.tok_ring = h->at<int>(p.o_tok); fd.verdict = h->at<Verdict>(p.o_verdict);
+      fd.host_verdict = h->d_hverdict;
       fd.part = h->at<VocabPartial>(p.o_part);
       const size_t fo = dw.put(&fd, 1);
       char* d = h->ws + p.o_desc;
@@ -853,8 +858,6 @@ int spd_prefill(spd_handle* h, const int32_t* prompt, int32_t len, int32_t* firs
       HIPCHK(h, launch_vocab_stats(reinterpret_cast<const VocabDesc*>(d + vo), kVocabBlocks,
                                    h->at<VocabPartial>(p.o_part), st));
       HIPCHK(h, launch_finalize(reinterpret_cast<const FinalizeDesc*>(d + fo), st));
-      HIPCHK(h, hipMemcpyAsync(h->h_verdict, h->at<Verdict>(p.o_verdict), sizeof(Verdict),
-                               hipMemcpyDeviceToHost, st));
       // the exiting-row residual of the last prompt position (debug view)
       HIPCHK(h, launch_copy_rows(H + (size_t)(P - 1) * p.d, p.d, h->at<float>(p.o_h) +
                                  (size_t)h->slot(len - 1) * p.d, p.d, 1, p.d, st));
@@ -906,8 +909,6 @@ int spd_step(spd_handle* h) {
   HIPCHK(h, hipMemcpyAsync(h->ws + h->p.o_desc, h->h_desc, dw.used, hipMemcpyHostToDevice, h->st));
   rc = run_ops(h);
   if (rc != SPD_OK) return rc;
-  HIPCHK(h, hipMemcpyAsync(h->h_verdict, h->at<Verdict>(h->p.o_verdict), sizeof(Verdict),
-                           hipMemcpyDeviceToHost, h->st));
   h->state = spd_handle::S_PENDING;
   return SPD_OK;
 }
@@ -916,7 +917,13 @@ int spd_verify_commit(spd_handle* h, spd_commit* out) {
   if (!h) return SPD_E_ARG;
   h->err.clear();
   if (h->state != spd_handle::S_PENDING) return fail(h, SPD_E_STATE, "no pending step");
-  HIPCHK(h, hipStreamSynchronize(h->st));
+  // The verdict kernels wrote their result straight to pinned host memory; poll the
+  // stream rather than block on it, so the host sees the end of the step at once (the
+  // PDM stream was joined into it before the head).
+  hipError_t qe;
+  while ((qe = hipStreamQuery(h->st)) == hipErrorNotReady) {
+  }
+  HIPCHK(h, qe);
   if (h->timing) {
     const int rc = collect_timing(h);
     if (rc != SPD_OK) return rc;

@@ -162,6 +162,8 @@ struct FinalizeDesc {
   float* lse_q_new;     // where to store this draft's log-sum-exp
   int* tok_ring;
   Verdict* verdict;
+  Verdict* host_verdict;     // device view of pinned host memory: the finished verdict, so the
+                             // host reads it once the stream is idle, with no copy
   const VocabPartial* part;  // [2][nblocks]
 };
 

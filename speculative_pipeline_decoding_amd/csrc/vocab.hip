@@ -131,6 +131,7 @@ __global__ __launch_bounds__(kVocabBlock) void finalize_kernel(const FinalizeDes
     v.flags = flag ? 1 : 0;
     f.tok_ring[f.dpos % f.ring] = y;
     *f.verdict = v;
+    *f.host_verdict = v;
     return;
   }
   // draft for position dpos
@@ -175,6 +176,7 @@ __global__ __launch_bounds__(kVocabBlock) void finalize_kernel(const FinalizeDes
     }
   }
   *f.verdict = v;
+  *f.host_verdict = v;
 }
 
 // Residual sample after a rejection at T > 0: every block writes the Gumbel
@@ -219,6 +221,7 @@ __global__ __launch_bounds__(kVocabBlock) void residual_final_kernel(
     v->committed = m.garg;
     if ((m.gmax - m.gsecond) < kNearTie) v->flags |= 1;
     f.tok_ring[f.v % f.ring] = m.garg;
+    *f.host_verdict = *v;
   }
 }
 
