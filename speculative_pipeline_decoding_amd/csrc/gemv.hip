@@ -23,7 +23,9 @@
 namespace spd {
 namespace {
 
-constexpr int RW = 4;         // weight rows per wave (rows kernel) / per workgroup (split-K)
+constexpr int RW = 4;         // weight rows per workgroup (split-K kernel) / per wave (rows kernel)
+constexpr int RWIDE = 8;      // rows per wave of the rows kernel for tall matrices (>= kTall units)
+constexpr int kTall = 8192;
 constexpr int kSplit = 4;     // waves sharing the rows of a split-K workgroup
 
 template <typename T> struct Elt;
@@ -58,7 +60,7 @@ __device__ __forceinline__ bool paired(const GemvProb& p) {
 // Weight row feeding slot j of a group of RW rows whose first unit is u0.
 // Plain: slot j -> row u0 + j. SWIGLU: slots [0, RW/2) gate rows, [RW/2, RW) up rows.
 // QKV: slots (2t, 2t+1) -> the RoPE pair (i, i + hd/2) of unit u0 + t.
-template <typename T>
+template <typename T, int RW>
 __device__ __forceinline__ const T* row_ptr(const GemvProb& p, int u0, int j, int nunits) {
   int row;
   const T* M = static_cast<const T*>(p.W);
@@ -76,6 +78,7 @@ __device__ __forceinline__ const T* row_ptr(const GemvProb& p, int u0, int j, in
 }
 
 // Slots holding the two values of unit ut: (a, b) = gate/up, RoPE pair, or (a, a).
+template <int RW>
 __device__ __forceinline__ void unit_slots(const GemvProb& p, int ut, int& ja, int& jb) {
   ja = ut; jb = ut;
   if (p.epi == EPI_SWIGLU) jb = ut + RW / 2;
@@ -132,10 +135,11 @@ __device__ void epilogue(const GemvProb& p, int v, int unit, float a, float b,
 }
 
 // ---- rows kernel: one wave = RW weight rows over all of K, NV <= 2 vectors ------------
-template <typename T, int NV>
+template <typename T, int NV, int RR>
 __device__ void rows_body(const GemvProb& p, int tile, const float2* __restrict__ rope) {
   constexpr int E = Elt<T>::N;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int RW = RR;
   const int upw = paired(p) ? RW / 2 : RW;
   const int nunits = units_of(p);
   const int u0 = (tile * kWaves + wave) * upw;
@@ -143,7 +147,7 @@ __device__ void rows_body(const GemvProb& p, int tile, const float2* __restrict_
   const int nv = p.nvec;
   const T* rp[RW];
 #pragma unroll
-  for (int j = 0; j < RW; ++j) rp[j] = row_ptr<T>(p, u0, j, nunits);
+  for (int j = 0; j < RW; ++j) rp[j] = row_ptr<T, RW>(p, u0, j, nunits);
   float acc[RW][NV], ss[NV];
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
@@ -193,7 +197,7 @@ __device__ void rows_body(const GemvProb& p, int tile, const float2* __restrict_
   if (lane < upw * nv) {
     const int ut = lane % upw, v = lane / upw;
     int ja, jb;
-    unit_slots(p, ut, ja, jb);
+    unit_slots<RW>(p, ut, ja, jb);
     float a = 0.f, b = 0.f, sc = 1.f;
 #pragma unroll
     for (int vv = 0; vv < NV; ++vv) {
@@ -224,7 +228,7 @@ __device__ void splitk_body(const GemvProb& p, int tile, float* red,
   const int nv = p.nvec;
   const T* rp[RW];
 #pragma unroll
-  for (int j = 0; j < RW; ++j) rp[j] = row_ptr<T>(p, u0, j, nunits);
+  for (int j = 0; j < RW; ++j) rp[j] = row_ptr<T, RW>(p, u0, j, nunits);
   float acc[RW][kMaxVec], ss[kMaxVec];
 #pragma unroll
   for (int v = 0; v < kMaxVec; ++v) {
@@ -281,7 +285,7 @@ __device__ void splitk_body(const GemvProb& p, int tile, float* red,
     const int ut = t % upw, v = t / upw;
     if (u0 + ut >= nunits) continue;
     int ja, jb;
-    unit_slots(p, ut, ja, jb);
+    unit_slots<RW>(p, ut, ja, jb);
     float a = 0.f, b = 0.f, s2 = 0.f;
 #pragma unroll
     for (int u = 0; u < kSplit; ++u) {
@@ -485,9 +489,10 @@ __device__ void mfma_body(const GemvProb& p, int tile, const float2* __restrict_
   }
 }
 
-// Kernel kinds: 1 or 2 vectors (rows kernel), 3..16 vectors on the matrix cores (bf16
-// weights, input staged whole in LDS), else up to kMaxVec (split-K).
-enum Kind { K_ROWS1 = 0, K_ROWS2 = 1, K_SPLITK = 2, K_MFMA = 3 };
+// Kernel kinds: 1 or 2 vectors (rows kernel; the W kinds give each wave 8 rows, for tall
+// matrices), 3..16 vectors on the matrix cores (bf16 weights, input staged whole in LDS),
+// else up to kMaxVec (split-K).
+enum Kind { K_ROWS1 = 0, K_ROWS2 = 1, K_SPLITK = 2, K_MFMA = 3, K_ROWS1W = 4, K_ROWS2W = 5 };
 
 template <typename T, int KIND>
 __device__ __forceinline__ void gemv_body(const GemvProb* __restrict__ probs, int nprob,
@@ -504,8 +509,10 @@ __device__ __forceinline__ void gemv_body(const GemvProb* __restrict__ probs, in
     __shared__ __attribute__((aligned(16))) uint16_t planes[kMcLdsElems];
     __shared__ float red[kMcMaxWaves * kMcMaxVec];
     mfma_body(p, tile, rope, planes, red);
+  } else if constexpr (KIND == K_ROWS1W || KIND == K_ROWS2W) {
+    rows_body<T, KIND == K_ROWS1W ? 1 : 2, RWIDE>(p, tile, rope);
   } else {
-    rows_body<T, KIND == K_ROWS1 ? 1 : 2>(p, tile, rope);
+    rows_body<T, KIND == K_ROWS1 ? 1 : 2, RW>(p, tile, rope);
   }
 }
 
@@ -563,6 +570,12 @@ int gemv_plan(GemvProb* v, int n, bool bf16) {
   }
   int kind = mv <= 1 ? K_ROWS1 : mv == 2 ? K_ROWS2 : K_SPLITK;
   if (mc && mv > 2) kind = K_MFMA;
+  if (kind <= K_ROWS2) {
+    bool tall = true;
+    for (int i = 0; i < n; ++i)
+      tall = tall && (v[i].epi == EPI_QKV ? v[i].rows / 2 : v[i].rows) >= kTall;
+    if (tall) kind = kind == K_ROWS1 ? K_ROWS1W : K_ROWS2W;
+  }
   int t = 0;
   for (int i = 0; i < n; ++i) {
     GemvProb& g = v[i];
@@ -579,8 +592,8 @@ int gemv_plan(GemvProb* v, int n, bool bf16) {
       g.pad = rt;
       g.ntiles = (wt + rt - 1) / rt;
     } else {
-      const int upw = pr ? RW / 2 : RW;
-      const int upt = kind == K_SPLITK ? upw : kWaves * upw;
+      const int rw = kind == K_ROWS1W || kind == K_ROWS2W ? RWIDE : RW;
+      const int upt = kind == K_SPLITK ? (pr ? RW / 2 : RW) : kWaves * (pr ? rw / 2 : rw);
       g.ntiles = (units + upt - 1) / upt;
     }
     g.tile0 = t;
@@ -601,6 +614,8 @@ hipError_t launch_gemv(int role, const GemvProb* d_probs, int nprob, int plan, b
       case K_ROWS2: launch_kind<uint16_t, K_ROWS2>(role, grid, d_probs, nprob, rope, st, ev); break;
       case K_SPLITK: launch_kind<uint16_t, K_SPLITK>(role, grid, d_probs, nprob, rope, st, ev); break;
       case K_MFMA: launch_kind<uint16_t, K_MFMA>(role, grid, d_probs, nprob, rope, st, ev, waves); break;
+      case K_ROWS1W: launch_kind<uint16_t, K_ROWS1W>(role, grid, d_probs, nprob, rope, st, ev); break;
+      case K_ROWS2W: launch_kind<uint16_t, K_ROWS2W>(role, grid, d_probs, nprob, rope, st, ev); break;
       default: return hipErrorInvalidValue;
     }
   } else {
@@ -608,6 +623,8 @@ hipError_t launch_gemv(int role, const GemvProb* d_probs, int nprob, int plan, b
       case K_ROWS1: launch_kind<float, K_ROWS1>(role, grid, d_probs, nprob, rope, st, ev); break;
       case K_ROWS2: launch_kind<float, K_ROWS2>(role, grid, d_probs, nprob, rope, st, ev); break;
       case K_SPLITK: launch_kind<float, K_SPLITK>(role, grid, d_probs, nprob, rope, st, ev); break;
+      case K_ROWS1W: launch_kind<float, K_ROWS1W>(role, grid, d_probs, nprob, rope, st, ev); break;
+      case K_ROWS2W: launch_kind<float, K_ROWS2W>(role, grid, d_probs, nprob, rope, st, ev); break;
       default: return hipErrorInvalidValue;
     }
   }
