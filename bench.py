@@ -16,6 +16,8 @@ synthetic data of the workload's shape.
 
 Timed region: W warm-up steps, then exactly K steps between two device
 synchronisations, with inputs resident in HBM. value = committed tokens / s.
+step_us is each step's full cycle as a caller sees it (enqueue, GPU execution and
+verdict read-back), taken on the host between successive verify_commit returns.
 Per-launch durations for the roofline come from HIP start/stop events that the
 library binds to each launch's dispatch packet (hipExtLaunchKernel), on the
 stream the launch runs on, over a second pass of the same warm-up and timed
@@ -67,25 +69,25 @@ def run_spd(cfg, dW, prompt, T, seed, warmup, steps, kernel_timing):
         spd.verify_commit()
 
     def region():
+        # Step latency is taken on the host, between successive verify_commit returns: one
+        # full cycle of enqueue, GPU execution and verdict read-back, as a caller sees it.
         s0 = spd.stats()
-        # events are created before the clock starts; recording one costs a few µs of host time
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(steps)]
-        kinds, host = [], []
+        kinds, host, step_ms = [], [], []
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for a, b in evs:
-            a.record(stream)
+        t_prev = t0
+        for _ in range(steps):
             h0 = time.perf_counter()
             spd.step()
             host.append(time.perf_counter() - h0)
-            b.record(stream)
             c = spd.verify_commit()
+            t_now = time.perf_counter()
+            step_ms.append(1e3 * (t_now - t_prev))
+            t_prev = t_now
             kinds.append(bool(c.verified))
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         s1 = spd.stats()
-        step_ms = [a.elapsed_time(b) for a, b in evs]
         return s1, {"wall_s": wall, "N": s1.N - s0.N, "K": s1.K - s0.K, "step_ms": step_ms,
                     "host_step_us": 1e6 * float(np.median(host)),
                     "full": [m for m, k in zip(step_ms, kinds) if k],
