@@ -28,10 +28,12 @@ def rel(a, b):
 
 def run_parity(cfg, W, dW, prompt, G=None, T=0.0, seed=0, n=None, fill="clamp",
                forced_p=None, forced_ref=None, check_states=True, max_steps=None,
-               oracle_weights=None):
+               oracle_weights=None, tol_logits=None):
     from speculative_pipeline_decoding_amd import SPD
     G = cfg.gen_len if G is None else G
     tol_l, tol_h = tolerances(cfg)
+    if tol_logits is not None:
+        tol_l = tol_logits
     s = Sampling(temperature=T, seed=seed)
     kw = {}
     if forced_p is not None:

@@ -1,59 +1,76 @@
-"""Full-size checks at the headline model's shapes (MI355X; ~45 GB of host memory).
+"""Full-size checks at the real model shapes (MI355X; up to ~90 GB of host memory).
 
-* Lockstep with the oracle on the n=8 model itself (d=2560, 32 layers, 32/8 heads x 80,
-  FFN 9728, vocabulary 151936, n=8, Ls=4): every kernel runs at its benchmark launch
-  shape, on a short prompt so that the fp64 oracle finishes in about a minute; T=0 and T=1.
-* At the benchmark's own configuration (1792-token prompt, context 2048), properties that
-  hold at any size:
-    - lossless at T=0: the n=8 stream equals the same model decoded autoregressively
-      (the library at n=1), up to the first decision either run flags as a near-tie;
-    - the scheduler's counting identity K = N + (n-1)(1 + R') and S0 = alpha n at T=1,
-      with KV lengths non-increasing over layers after every step.
+For each of the three large workloads (the n=8 d2560 model the benchmark runs, the n=8
+d4096 / head_dim 128 model, and the n=16 hybrid with 24 linear-attention layers):
+  * lockstep with the oracle on the model itself: every kernel runs at its benchmark
+    launch shape, on a short prompt so that the fp64 oracle finishes in about a minute;
+  * at the workload's own context (its full prompt), properties that hold at any size:
+      - lossless at T=0: the n-stage stream equals the same model decoded
+        autoregressively (the library at n=1), up to the first decision either run
+        flags as a near-tie;
+      - the scheduler's counting identity K = N + (n-1)(1 + R') and S0 = alpha n at T=1,
+        with KV lengths non-increasing over layers after every step.
+One workload's weights are resident at a time (host and device).
 """
+import json
+import os
+
 import numpy as np
 import pytest
 
+import conftest
 from conftest import workload
 from parity import run_parity
 
 pytestmark = pytest.mark.gpu
 
-NAME = "dense_bf16_L32_d2560_n8_ctx2048"
+NAMES = ["dense_bf16_L32_d2560_n8_ctx2048", "dense_bf16_L36_d4096_n8_ctx4096",
+         "hybrid_bf16_L32_d2560_n16_ctx8192"]
 _state = {}
 
 
-def _dev():
-    if "dW" not in _state:
-        import torch
-        from speculative_pipeline_decoding_amd import upload_weights
-        cfg, W, _ = workload(NAME)
+@pytest.fixture(scope="module", params=NAMES)
+def wl(request):
+    """(name, device weights, oracle weights) of one workload; the previous one is dropped."""
+    import torch
+    from oracle.model import Weights
+    from speculative_pipeline_decoding_amd import upload_weights
+    name = request.param
+    if _state.get("name") != name:
+        _state.clear()
+        for k in [k for k in conftest._cache if k in NAMES and k != name]:
+            del conftest._cache[k]
         torch.cuda.empty_cache()
-        _state["dW"] = upload_weights(cfg, W)
-    return _state["dW"]
+        cfg, W, _ = workload(name)
+        _state.update(name=name, dW=upload_weights(cfg, W), oW=Weights(W, np.float64, cache=True))
+    return name, _state["dW"], _state["oW"]
 
 
-def _oracle_weights():
-    if "oW" not in _state:
-        from oracle.model import Weights
-        _, W, _ = workload(NAME)
-        _state["oW"] = Weights(W, np.float64, cache=True)
-    return _state["oW"]
+def logit_tolerance(name, T):
+    """5e-2 (bf16 bound), or twice the oracle's own fp32-vs-fp64 logit gap on this lockstep
+    where that floor is higher (tests/golden/fp32_sensitivity.py: bf16 KV rounding makes a
+    deep, wide model's logits sensitive at the fp32 level; no fp32 path can beat the floor)."""
+    with open(os.path.join(os.path.dirname(__file__), "golden", "fp32_sensitivity.json")) as f:
+        gaps = json.load(f)["gaps"]
+    return max(5e-2, 2.0 * gaps[name][f"T{T:g}"])
 
 
 @pytest.mark.parametrize("T,seed", [(0.0, 0), (1.0, 11)])
-def test_fullsize_lockstep_with_oracle(T, seed):
-    cfg, W, prompt = workload(NAME)
-    print(f"[fullsize] lockstep {NAME} T={T}", flush=True)
-    rep = run_parity(cfg, W, _dev(), prompt[:40], T=T, seed=seed, max_steps=14,
-                     oracle_weights=_oracle_weights())
+def test_fullsize_lockstep_with_oracle(wl, T, seed):
+    name, dW, oW = wl
+    cfg, W, prompt = workload(name)
+    tol = logit_tolerance(name, T)
+    print(f"[fullsize] lockstep {name} T={T} logit tolerance {tol:.3g}", flush=True)
+    rep = run_parity(cfg, W, dW, prompt[:40], T=T, seed=seed, max_steps=cfg.n_stages + 6,
+                     oracle_weights=oW, tol_logits=tol)
     print(f"[fullsize] -> {rep}", flush=True)
-    assert rep["steps"] >= 8 or rep["stopped_at_near_tie"] is not None
+    assert rep["steps"] >= cfg.n_stages or rep["stopped_at_near_tie"] is not None
 
 
-def _stream(n, prompt, T, G, seed=0):
+def _stream(name, dW, n, T, G, seed=0):
     from speculative_pipeline_decoding_amd import SPD
-    cfg, _, _ = workload(NAME)
-    gpu = SPD(cfg, _dev(), temperature=T, seed=seed, n=n)
+    cfg, _, prompt = workload(name)
+    gpu = SPD(cfg, dW, temperature=T, seed=seed, n=n)
     toks = [(gpu.prefill(prompt), 0)]
     steps = []
     while len(toks) < G:
@@ -68,27 +85,28 @@ def _stream(n, prompt, T, G, seed=0):
     return toks, steps, st
 
 
-def test_fullsize_lossless_matches_autoregressive():
-    cfg, _, prompt = workload(NAME)
-    print(f"[fullsize] lossless n=8 vs n=1 on the {len(prompt)}-token prompt", flush=True)
-    a, _, sa = _stream(8, prompt, 0.0, 48)
-    b, _, sb = _stream(1, prompt, 0.0, 48)
+def test_fullsize_lossless_matches_autoregressive(wl):
+    name, dW, _ = wl
+    cfg, _, prompt = workload(name)
+    print(f"[fullsize] lossless n={cfg.n_stages} vs n=1 on the {len(prompt)}-token prompt "
+          f"of {name}", flush=True)
+    a, _, _ = _stream(name, dW, cfg.n_stages, 0.0, 32)
+    b, _, sb = _stream(name, dW, 1, 0.0, 32)
     assert sb.N == sb.K and abs(sb.alpha - 1.0) < 1e-12   # n=1: every step commits
     for i, ((ta, fa), (tb, fb)) in enumerate(zip(a, b)):
         if fa or fb:
             print(f"[fullsize] near-tie flagged at commit {i}; compared {i} tokens", flush=True)
             break
-        assert ta == tb, f"commit {i}: n=8 gives {ta}, n=1 gives {tb}"
+        assert ta == tb, f"commit {i}: n={cfg.n_stages} gives {ta}, n=1 gives {tb}"
 
 
-def test_fullsize_counting_identity_and_kv_invariants():
-    cfg, _, prompt = workload(NAME)
+def test_fullsize_counting_identity_and_kv_invariants(wl):
+    name, dW, _ = wl
+    cfg, _, _ = workload(name)
     n = cfg.n_stages
-    toks, steps, st = _stream(n, prompt, 1.0, 40, seed=5)
-    # end on a verification step so every rejection's refill lies inside the run
-    while steps and not steps[-1][0]:
-        steps.pop()
+    toks, steps, st = _stream(name, dW, n, 1.0, 24, seed=5)
     rejects = [i for i, (v, acc, _, _) in enumerate(steps) if v and not acc]
+    # the run ends on a verification step; a rejection there has no refill inside the run
     r_prime = len(rejects) - (1 if rejects and rejects[-1] == len(steps) - 1 else 0)
     N = sum(1 for v, _, _, _ in steps if v)
     K = len(steps)
@@ -96,6 +114,6 @@ def test_fullsize_counting_identity_and_kv_invariants():
     assert abs(st.s0 - st.alpha * n) < 1e-12 and abs(st.alpha - st.N / st.K) < 1e-12
     for v, acc, kv, pl in steps:
         assert all(x >= y for x, y in zip(kv, kv[1:])), kv   # deeper layers never ahead
-        assert pl <= kv[-1] + 1
+        assert pl <= kv[-1]                                   # the PDM keeps exited rows only
         if v and not acc:
             assert len(set(kv)) == 1, kv                      # a reject truncates every layer to v
