@@ -170,7 +170,8 @@ int spd_prefill(spd_handle* h, const int32_t* prompt, int32_t len, int32_t* firs
 int spd_step(spd_handle* h);
 
 /*
- * Wait for the pending step and apply its verdict: on accept the ring shifts
+ * Wait for the pending step (polling the stream; the verdict kernels write their
+ * result to pinned host memory) and apply its verdict: on accept the ring shifts
  * and the draft enters stage 0; on reject every layer's KV length becomes the
  * verified position v, the pipeline is flushed and reseeded with the
  * corrected token at v. This is the only per-step device-to-host wait.
@@ -215,8 +216,10 @@ size_t spd_debug_size(const spd_handle* h, int32_t what);
 int spd_debug_copy(const spd_handle* h, int32_t what, void* host_dst, size_t bytes);
 
 /*
- * Measurement. When enabled, every launch of a step is bracketed by HIP events
- * on the handle's stream, and spd_verify_commit accumulates per launch kind:
+ * Measurement. When enabled, the first and last launch of every operation of a
+ * step carry HIP start / stop events bound to their dispatch packets
+ * (hipExtLaunchKernelGGL), on the stream the operation runs on, so a duration is
+ * the kernels' own; spd_verify_commit accumulates per launch kind:
  * the number of launches, their total duration and their algorithmic HBM
  * bytes (weights read once, KV rows read once). Kinds, in order: 0 embed,
  * 1 PDM projection GEMV, 2 QKV GEMV, 3 attention, 4 linear attention, 5 O GEMV,
