@@ -21,7 +21,14 @@ __device__ __forceinline__ void st(T* p, size_t i, float v) {
 // ascending depth; a segment deeper than the row's current depth repeats its
 // deepest computed anchor (clamp) or is zero, as the host encoded in src.
 template <typename T>
-__global__ __launch_bounds__(256) void embed_gather_kernel(const EmbedGather* __restrict__ dd) {
+// Also uploads the step's descriptor block: the host wrote it to pinned memory, and every
+// later launch of the step reads the device copy (they run after this kernel). The
+// kernel's own descriptor is read from the pinned copy.
+__global__ __launch_bounds__(256) void embed_gather_kernel(const EmbedGather* __restrict__ dd,
+                                                           const uint4* __restrict__ blk_src,
+                                                           uint4* __restrict__ blk_dst, int n16) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += gridDim.x * blockDim.x)
+    blk_dst[i] = blk_src[i];
   const EmbedGather& e = *dd;
   const int d = e.d;
   const T* __restrict__ E = static_cast<const T*>(e.embed);
@@ -145,12 +152,16 @@ __global__ void copy_rows_kernel(const float* __restrict__ s, int ss, float* __r
 
 }  // namespace
 
-hipError_t launch_embed_gather(const EmbedGather* d_desc, int M, int k, int d, bool bf16,
-                               hipStream_t s, LaunchEv ev) {
+hipError_t launch_embed_gather(const EmbedGather* desc, const void* blk_src, void* blk_dst,
+                               size_t blk_bytes, int M, int k, int d, bool bf16, hipStream_t s,
+                               LaunchEv ev) {
   (void)d;
   const dim3 grid(1 + M * k);
-  if (bf16) SPD_LAUNCH(ev, embed_gather_kernel<uint16_t>, grid, dim3(256), 0, s, d_desc);
-  else SPD_LAUNCH(ev, embed_gather_kernel<float>, grid, dim3(256), 0, s, d_desc);
+  const int n16 = (int)((blk_bytes + 15) / 16);
+  const uint4* src = static_cast<const uint4*>(blk_src);
+  uint4* dst = static_cast<uint4*>(blk_dst);
+  if (bf16) SPD_LAUNCH(ev, embed_gather_kernel<uint16_t>, grid, dim3(256), 0, s, desc, src, dst, n16);
+  else SPD_LAUNCH(ev, embed_gather_kernel<float>, grid, dim3(256), 0, s, desc, src, dst, n16);
   return hipGetLastError();
 }
 

@@ -207,7 +207,9 @@ struct spd_handle {
   hipStream_t st2 = nullptr;      // library-owned stream for the PDM chain
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   // pinned host staging
-  char* h_desc = nullptr;
+  char* h_desc = nullptr;          // pinned staging of the step's descriptor block
+  char* d_hdesc = nullptr;         // its device view
+  size_t desc_used = 0;            // bytes of the current step's block
   Verdict* h_verdict = nullptr;   // pinned; written by the verdict kernels through d_hverdict
   Verdict* d_hverdict = nullptr;
   // state machine
@@ -362,8 +364,10 @@ hipError_t run_op(spd_handle* h, const Op& op, LaunchEv ev = {}) {
       return e != hipSuccess ? e : hipStreamWaitEvent(h->st, h->ev_join, 0);
     }
     case OP_EMBED:
-      return launch_embed_gather(reinterpret_cast<const EmbedGather*>(d + op.off), op.count, p.k,
-                                 p.d, p.bf16, st, ev);
+      // the step's first launch: it reads its own descriptor from the pinned staging and
+      // copies the whole block to the device for the launches that follow
+      return launch_embed_gather(reinterpret_cast<const EmbedGather*>(h->d_hdesc + op.off),
+                                 h->d_hdesc, d, h->desc_used, op.count, p.k, p.d, p.bf16, st, ev);
     case OP_GEMV_PROJ: case OP_GEMV_QKV: case OP_GEMV_O: case OP_GEMV_GU: case OP_GEMV_DOWN:
     case OP_GEMV_HEAD: case OP_PDM_QKV: case OP_PDM_O: case OP_PDM_GU: case OP_PDM_DOWN:
       return launch_gemv(gemv_role(op.kind), reinterpret_cast<const GemvProb*>(d + op.off),
@@ -725,6 +729,8 @@ int spd_init(const spd_model_config* cfg, const spd_weights* w, const spd_sampli
   hipError_t e;
   if ((e = hipHostMalloc((void**)&h->h_desc, kDescBytes, hipHostMallocDefault)) != hipSuccess)
     return dev_fail(e, "hipHostMalloc");
+  if ((e = hipHostGetDevicePointer((void**)&h->d_hdesc, h->h_desc, 0)) != hipSuccess)
+    return dev_fail(e, "hipHostGetDevicePointer");
   if ((e = hipHostMalloc((void**)&h->h_verdict, sizeof(Verdict), hipHostMallocDefault)) != hipSuccess)
     return dev_fail(e, "hipHostMalloc");
   if ((e = hipHostGetDevicePointer((void**)&h->d_hverdict, h->h_verdict, 0)) != hipSuccess)
@@ -906,7 +912,9 @@ int spd_step(spd_handle* h) {
   if (rc != SPD_OK) return rc;
   interleave_streams(h->ops);
   if (dw.used > kDescBytes) return fail(h, SPD_E_CAPACITY, "internal: descriptor block overflow");
-  HIPCHK(h, hipMemcpyAsync(h->ws + h->p.o_desc, h->h_desc, dw.used, hipMemcpyHostToDevice, h->st));
+  if (h->ops.empty() || h->ops.front().kind != OP_EMBED)
+    return fail(h, SPD_E_STATE, "internal: a step must start with the embedding");
+  h->desc_used = dw.used;   // uploaded by the embedding kernel
   rc = run_ops(h);
   if (rc != SPD_OK) return rc;
   h->state = spd_handle::S_PENDING;

@@ -349,8 +349,11 @@ hipError_t launch_linear_step(const LinProb* d_probs, int nprob, int H, int hd, 
 hipError_t launch_linear_scan(const float* qkv, int qkv_stride, float* out, int out_stride,
                               const float* s_in, float* s_out, int P, int H, int hd, float eps,
                               hipStream_t st);
-hipError_t launch_embed_gather(const EmbedGather* d_desc, int M, int k, int d, bool bf16,
-                               hipStream_t st, LaunchEv ev = {});
+// desc: the gather descriptor, readable by the device (it may sit in pinned host memory);
+// blk_src / blk_dst / blk_bytes: the step's descriptor block, copied to the device first.
+hipError_t launch_embed_gather(const EmbedGather* desc, const void* blk_src, void* blk_dst,
+                               size_t blk_bytes, int M, int k, int d, bool bf16, hipStream_t st,
+                               LaunchEv ev = {});
 hipError_t launch_vocab_stats(const VocabDesc* d_desc, int nblocks, VocabPartial* part,
                               hipStream_t st, LaunchEv ev = {});
 hipError_t launch_finalize(const FinalizeDesc* d_desc, hipStream_t st, LaunchEv ev = {});
