@@ -20,6 +20,16 @@ Readings (the pages are silent):
     where mix is the SplitMix64 output function (Steele, Lea & Flood 2014);
   * forced mode (acceptance sweep): the draft at position x becomes the
     reference greedy token r[x] when u_FORCE(x) < p_force, else (r[x] + 1) mod V.
+
+Near-ties at top_p < 1. Another implementation computes the same decisions from
+logits that differ from these by at most Sampling.logit_slack (delta) each, and
+sums masses with a relative rounding of at most TOP_P_EPS. Every probability it
+sees is then within a factor exp(+-2 delta / T) of ours, so a token's mass ahead
+(the sum over the tokens before it in the nucleus order) lies in a known interval,
+and so does the renormalised probability of every token (prob_range). A decision
+is flagged whenever some logits inside that envelope would change it: a sampled
+token whose win is not certain over every token that may be in the set, a verified
+draft whose accept test can go either way, a residual winner that may be overtaken.
 """
 from __future__ import annotations
 
@@ -38,6 +48,7 @@ STREAM_FORCE = 4
 STREAM_FIRST = 5
 
 NEAR_TIE = 1e-3
+TOP_P_EPS = 1e-6
 
 
 def mix64(z) -> np.ndarray:
@@ -97,6 +108,64 @@ def nucleus(p: np.ndarray, top_p: float) -> np.ndarray:
     return keep
 
 
+def softmax_t(z: np.ndarray, T: float) -> np.ndarray:
+    """softmax(z / T) over the whole vocabulary."""
+    p = np.exp(z / T - np.max(z / T))
+    return p / p.sum()
+
+
+def nucleus_bounds(z: np.ndarray, T: float, top_p: float, slack: float):
+    """(certain, band): tokens inside the top-p set for every logit vector within `slack`
+    of z, and tokens that are inside for some and outside for others."""
+    V = z.size
+    if top_p >= 1.0:
+        return np.ones(V, dtype=bool), np.zeros(V, dtype=bool)
+    p0 = softmax_t(z, T)
+    f = np.exp(2.0 * slack / T)
+    order = np.argsort(-z, kind="stable")
+    cum = np.concatenate([[0.0], np.cumsum(p0[order])])
+    neg = -z[order]                                    # ascending
+    n_above = np.searchsorted(neg, -(z + 2.0 * slack), side="left")   # z_j > z_i + 2 slack
+    n_atleast = np.searchsorted(neg, -(z - 2.0 * slack), side="right")  # z_j >= z_i - 2 slack
+    ahead_lo = cum[n_above] / f
+    ahead_hi = (cum[n_atleast] - p0) * f
+    certain = ahead_hi < top_p * (1.0 - TOP_P_EPS)
+    out = ahead_lo >= top_p * (1.0 + TOP_P_EPS)
+    return certain, ~certain & ~out
+
+
+def prob_range(z: np.ndarray, T: float, top_p: float, slack: float):
+    """Per-token [lo, hi] of the renormalised top-p probability over the same envelope."""
+    p0 = softmax_t(z, T)
+    certain, band = nucleus_bounds(z, T, top_p, slack)
+    f = np.exp(2.0 * slack / T)
+    m_lo = p0[certain].sum() / f
+    m_hi = p0[certain | band].sum() * f
+    lo = np.where(certain, p0 / (f * m_hi), 0.0)
+    with np.errstate(divide="ignore"):
+        hi = np.where(certain | band, p0 * f / m_lo, 0.0)   # inf when no token is certain
+    return lo, hi
+
+
+def _uncertain_winner(lo_score: np.ndarray, hi_score: np.ndarray, y: int) -> bool:
+    """y wins for sure iff its lowest score beats every other token's highest by NEAR_TIE."""
+    if lo_score[y] == -np.inf:
+        return True
+    others = np.delete(hi_score, y)
+    best = others.max() if others.size else -np.inf
+    return not (lo_score[y] - best >= NEAR_TIE)
+
+
+def top_p_gumbel_flag(z: np.ndarray, s: "Sampling", stream: int, pos: int, y: int) -> bool:
+    """Near-tie flag of a Gumbel-max draw over the top-p set (top_p < 1)."""
+    certain, band = nucleus_bounds(z, s.temperature, s.top_p, s.slack())
+    sc = z / s.temperature + gumbel(uniform(s.seed, stream, pos, np.arange(z.size)))
+    e = s.slack() / s.temperature
+    lo = np.where(certain, sc - e, -np.inf)
+    hi = np.where(certain | band, sc + e, -np.inf)
+    return _uncertain_winner(lo, hi, y)
+
+
 def distribution(z: np.ndarray, T: float, top_p: float) -> np.ndarray:
     """softmax(z / T) restricted to its top-p nucleus and renormalised."""
     p = np.exp(z / T - np.max(z / T))
@@ -122,12 +191,20 @@ class Sampling:
     forced_p: Optional[float] = None       # forced mode when not None (T = 0 only)
     forced_ref: Optional[np.ndarray] = None  # reference tokens for positions P0, P0+1, ...
     forced_base: int = 0                   # position of forced_ref[0]
+    logit_slack: Optional[float] = None    # top_p < 1 near-ties: logit error allowed to
+                                           # the compared implementation (None: 1e-4)
+
+    def slack(self) -> float:
+        return 1e-4 if self.logit_slack is None else float(self.logit_slack)
 
 
 def first_token(z: np.ndarray, s: Sampling, pos: int) -> Tuple[int, bool]:
     if s.temperature == 0.0:
         return argmax_lowest(z), top2_gap(z) < NEAR_TIE
-    return gumbel_max(distribution(z, s.temperature, s.top_p), s.seed, STREAM_FIRST, pos)
+    y, flag = gumbel_max(distribution(z, s.temperature, s.top_p), s.seed, STREAM_FIRST, pos)
+    if s.top_p < 1.0:
+        flag = flag or top_p_gumbel_flag(z, s, STREAM_FIRST, pos, y)
+    return y, flag
 
 
 def select_draft(z_q: np.ndarray, s: Sampling, pos: int):
@@ -138,6 +215,8 @@ def select_draft(z_q: np.ndarray, s: Sampling, pos: int):
     else:
         q = distribution(z_q, s.temperature, s.top_p)
         d, flag = gumbel_max(q, s.seed, STREAM_DRAFT, pos)
+        if s.top_p < 1.0:
+            flag = flag or top_p_gumbel_flag(z_q, s, STREAM_DRAFT, pos, d)
     if s.forced_p is not None and s.forced_ref is not None:
         j = pos - s.forced_base
         if 0 <= j < len(s.forced_ref):
@@ -148,9 +227,11 @@ def select_draft(z_q: np.ndarray, s: Sampling, pos: int):
     return int(d), q, bool(flag)
 
 
-def verify(z_t: np.ndarray, d: int, q: Optional[np.ndarray], s: Sampling, v: int):
+def verify(z_t: np.ndarray, d: int, q: Optional[np.ndarray], s: Sampling, v: int,
+           z_q: Optional[np.ndarray] = None):
     """Verify draft d at position v against target logits z_t.
 
+    z_q: the draft logits q was computed from (for the top_p < 1 near-tie flags).
     Returns (y, accepted, near-tie flag): y is the committed token.
     """
     if s.temperature == 0.0:
@@ -160,9 +241,22 @@ def verify(z_t: np.ndarray, d: int, q: Optional[np.ndarray], s: Sampling, v: int
     u = uniform(s.seed, STREAM_ACC, v, 0)[()]
     lhs, rhs = u * q[d], p[d]
     flag = abs(lhs - rhs) < NEAR_TIE * q[d]
+    top_p_ranges = s.top_p < 1.0 and z_q is not None
+    if top_p_ranges:
+        pl, ph = prob_range(z_t, s.temperature, s.top_p, s.slack())
+        ql, qh = prob_range(z_q, s.temperature, s.top_p, s.slack())
+        sure_accept = u * qh[d] < pl[d]
+        sure_reject = u * ql[d] >= ph[d]
+        flag = flag or not (sure_accept or sure_reject)
     if lhs < rhs:
         return int(d), True, bool(flag)
     y, rflag = gumbel_max(np.maximum(p - q, 0.0), s.seed, STREAM_RES, v)
+    if top_p_ranges and not rflag:
+        G = gumbel(uniform(s.seed, STREAM_RES, v, np.arange(p.size)))
+        with np.errstate(divide="ignore"):
+            lo = np.log(np.maximum(pl - qh, 0.0)) + G
+            hi = np.log(np.maximum(ph - ql, 0.0)) + G
+        rflag = _uncertain_winner(lo, hi, y)
     return int(y), False, bool(flag or rflag)
 
 

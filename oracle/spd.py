@@ -99,6 +99,7 @@ class SPD:
         self.anch: Dict[int, Dict[int, np.ndarray]] = {}   # position -> anchor index -> state
         self.depth: Dict[int, int] = {}        # delta(p): target layers applied to p
         self.q: Dict[int, np.ndarray] = {}     # PDM distribution each draft was drawn from
+        self.zq: Dict[int, np.ndarray] = {}    # and the logits it was computed from
         self.F: List[List[int]] = []           # in flight, oldest first: [pos, stage]
         self.kv_len = [0] * self.L
         self.pdm_len = 0
@@ -174,6 +175,7 @@ class SPD:
         d, q, dflag = select_draft(z_q, self.s, dpos)
         if q is not None:
             self.q[dpos] = q
+            self.zq[dpos] = z_q
         # positions whose depth is already L become permanent PDM rows
         self.pdm_len = max(self.pdm_len, self.F[0][0])
         # 3. target: each in-flight token runs its stage's layers
@@ -196,7 +198,7 @@ class SPD:
             v = p + 1
             z_t = m.logits(self.h[p])
             dv = self.tok[v] if len(self.F) > 1 else d
-            y, acc, vflag = verify(z_t, dv, self.q.get(v), self.s, v)
+            y, acc, vflag = verify(z_t, dv, self.q.get(v), self.s, v, self.zq.get(v))
             self.N += 1
             self.committed.append(y)
             rec.exited, rec.exit_pos, rec.verified_pos = True, p, v
@@ -229,6 +231,7 @@ class SPD:
             self.depth.pop(old, None)
         for old in [x for x in self.q if x < self.pdm_len]:
             self.q.pop(old, None)
+            self.zq.pop(old, None)
         rec.kv_len = list(self.kv_len)
         rec.pdm_len = self.pdm_len
         rec.inflight = [tuple(f) for f in self.F]

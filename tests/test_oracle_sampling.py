@@ -138,3 +138,72 @@ def test_forced_mode_replaces_the_draft():
         assert d in (r, (r + 1) % 16)
         hits += d == r
     assert 0.45 < hits / 200 < 0.75
+
+
+def test_top_p_envelope_closed_case():
+    # p = [0.4, 0.3, 0.2, 0.1]: masses ahead 0, 0.4, 0.7, 0.9; at top_p = 0.7 the third
+    # token sits exactly on the edge, so with no logit slack it alone is undecided
+    z = np.log(np.array([0.4, 0.3, 0.2, 0.1]))
+    certain, band = S.nucleus_bounds(z, 1.0, 0.7, 0.0)
+    assert certain.tolist() == [True, True, False, False]
+    assert band.tolist() == [False, False, True, False]
+    certain, band = S.nucleus_bounds(z, 1.0, 0.6, 0.0)
+    assert certain.tolist() == [True, True, False, False] and not band.any()
+    certain, band = S.nucleus_bounds(z, 1.0, 1.0, 0.3)
+    assert certain.all() and not band.any()
+
+
+def _perturbed(rng, z, slack):
+    # mostly the envelope's corners, where a wrong bound shows first
+    if rng.random() < 0.7:
+        return z + slack * rng.choice([-1.0, 1.0], z.size)
+    return z + rng.uniform(-slack, slack, z.size)
+
+
+@pytest.mark.parametrize("top_p", [0.3, 0.8, 0.95])
+def test_top_p_envelope_holds_under_logit_perturbation(top_p):
+    """Brute force: for logits moved by at most the slack, the exact top-p set and the
+    renormalised probabilities stay inside nucleus_bounds / prob_range."""
+    rng = np.random.default_rng(21)
+    T, slack = 0.7, 2e-3
+    for trial in range(200):
+        V = int(rng.integers(2, 60))
+        z = rng.standard_normal(V) * rng.choice([0.05, 0.5, 2.0])
+        if trial % 7 == 0:
+            z[: V // 2] = z[0]                      # ties
+        certain, band = S.nucleus_bounds(z, T, top_p, slack)
+        lo, hi = S.prob_range(z, T, top_p, slack)
+        for _ in range(5):
+            z2 = _perturbed(rng, z, slack)
+            keep = S.nucleus(S.softmax_t(z2, T), top_p)
+            assert np.all(keep[certain]) and not np.any(keep & ~(certain | band))
+            q = S.distribution(z2, T, top_p)
+            assert np.all(q >= lo * (1 - 1e-12)) and np.all(q <= hi * (1 + 1e-12))
+
+
+def test_top_p_unflagged_decisions_survive_logit_perturbation():
+    """Brute force: a sampled draw, an accept test or a residual draw that the oracle does
+    not flag comes out the same from every logit vector within the slack."""
+    rng = np.random.default_rng(5)
+    T, slack = 1.0, 2e-2
+    seen = {"flag": 0, "clean": 0, "reject": 0}
+    for pos in range(1500):
+        V = int(rng.integers(3, 12))
+        s = S.Sampling(temperature=T, top_p=float(rng.choice([0.5, 0.9])), seed=9,
+                       logit_slack=slack)
+        z_t = rng.standard_normal(V) * 0.8
+        z_q = z_t + rng.standard_normal(V) * 0.5
+        d, q, dflag = S.select_draft(z_q, s, pos)
+        y, acc, vflag = S.verify(z_t, d, q, s, pos, z_q)
+        seen["flag"] += int(dflag or vflag)
+        if dflag or vflag:
+            continue
+        seen["clean"] += 1
+        seen["reject"] += int(not acc)
+        for _ in range(8):
+            zt2, zq2 = _perturbed(rng, z_t, slack), _perturbed(rng, z_q, slack)
+            d2, q2, _ = S.select_draft(zq2, s, pos)
+            assert d2 == d
+            y2, acc2, _ = S.verify(zt2, d2, q2, s, pos, zq2)
+            assert (y2, acc2) == (y, acc)
+    assert seen["clean"] > 500 and seen["reject"] > 100 and seen["flag"] > 0
