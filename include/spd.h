@@ -117,8 +117,11 @@ typedef struct {
  * (lossless: the committed stream is the target's greedy stream).
  * temperature > 0: drafts d ~ q = softmax(z_pdm/T), target p = softmax(z/T);
  * accept iff u*q(d) < p(d), else commit y ~ max(0, p - q) (normalised).
- * top_p >= 1 disables nucleus filtering (top_p < 1 is SPD_E_CONFIG in this
- * version). Random numbers are a pure function of (seed, stream, position,
+ * 0 < top_p < 1 (temperature > 0) restricts both q and p to their top-p sets and
+ * renormalises: the smallest prefix of the tokens in order of decreasing
+ * probability, lower id first on ties, whose mass reaches top_p (Holtzman et al.
+ * 2019); drafts and the first token are drawn from that set. top_p >= 1 disables the
+ * filter; top_p <= 0 or NaN is SPD_E_ARG. Random numbers are a pure function of (seed, stream, position,
  * index): SplitMix64 output function, u = ((x >> 41) + 0.5) * 2^-23.
  * forced_mode = 1 (temperature 0 only) replaces each draft at position x by
  * forced_ref[x - P0] with probability forced_p, else by (forced_ref[x - P0] + 1) mod V,
@@ -210,7 +213,12 @@ enum {
   SPD_DBG_PDM_ROWS = 5,        /* f32 [n+1][d]: PDM residual rows of the last step */
   SPD_DBG_TARGET_KV = 6,       /* dtype [softmax layers][2][hkv][max_ctx][hd] */
   SPD_DBG_PDM_KV = 7,          /* dtype [Ls][2][hkv][max_ctx][hd] */
-  SPD_DBG_TOKENS = 8           /* i32 [n+1]: token of position p in slot p mod (n+1) */
+  SPD_DBG_TOKENS = 8,          /* i32 [n+1]: token of position p in slot p mod (n+1) */
+  SPD_DBG_TOP_P = 9            /* [1 + (n+1)] x {f32 zb, i32 id_cut, f32 lse, i32 0}: top-p
+                                  sets (top_p < 1, T > 0) of the last target row, then of the
+                                  draft of position p in entry 1 + p mod (n+1); a set is the
+                                  tokens with z > zb or z == zb and id <= id_cut, and lse is
+                                  log sum over it of exp(z / T). Zero until computed. */
 };
 size_t spd_debug_size(const spd_handle* h, int32_t what);
 int spd_debug_copy(const spd_handle* h, int32_t what, void* host_dst, size_t bytes);
@@ -225,7 +233,8 @@ int spd_debug_copy(const spd_handle* h, int32_t what, void* host_dst, size_t byt
  * 1 PDM projection GEMV, 2 QKV GEMV, 3 attention, 4 linear attention, 5 O GEMV,
  * 6 gate/up GEMV, 7 down GEMV, 8 LM-head GEMV, 9 vocabulary stats, 10 verify,
  * 11 residual sample, then the PDM's own launches: 12 QKV GEMV, 13 attention,
- * 14 O GEMV, 15 gate/up GEMV, 16 down GEMV. Kinds 0-11 except 1 run on the
+ * 14 O GEMV, 15 gate/up GEMV, 16 down GEMV; 17 top-p sets (top_p < 1 only).
+ * Kinds 0-11 and 17 except 1 run on the
  * caller's stream; the PDM's run on a second, library-owned stream that forks
  * after the embedding and joins before the LM head, so their durations overlap.
  * Enabling or disabling clears the totals; a pending step gives SPD_E_STATE.

@@ -19,11 +19,11 @@ SPD_OK, SPD_E_ARG, SPD_E_CONFIG, SPD_E_STATE, SPD_E_CAPACITY, SPD_E_DEVICE = 0, 
 SPD_F32, SPD_BF16 = 0, 1
 SPD_FILL_CLAMP, SPD_FILL_ZERO = 0, 1
 DBG = {"target_logits": 1, "draft_logits": 2, "h_ring": 3, "anchors": 4, "pdm_rows": 5,
-       "target_kv": 6, "pdm_kv": 7, "tokens": 8}
+       "target_kv": 6, "pdm_kv": 7, "tokens": 8, "top_p": 9}
 # launch kinds reported by spd_timing_read
 OP_NAMES = ["embed", "gemv_proj", "gemv_qkv", "attention", "linear", "gemv_o", "gemv_gate_up",
             "gemv_down", "gemv_head", "vocab", "finalize", "residual", "pdm_qkv", "pdm_attention",
-            "pdm_o", "pdm_gate_up", "pdm_down"]
+            "pdm_o", "pdm_gate_up", "pdm_down", "nucleus"]
 TENSORS = ("attn_norm", "w_qkv", "w_o", "ffn_norm", "w_gate", "w_up", "w_down")
 
 
@@ -252,6 +252,9 @@ class SPD:
             dt = np.uint16 if self.cfg.dtype == "bf16" else np.float32
         elif what == "tokens":
             dt = np.int32
+        elif what == "top_p":
+            dt = np.dtype([("zb", np.float32), ("id_cut", np.int32), ("lse", np.float32),
+                           ("pad", np.int32)])
         else:
             dt = np.float32
         out = np.empty(nb // np.dtype(dt).itemsize, dtype=dt)

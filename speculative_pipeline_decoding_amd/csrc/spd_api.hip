@@ -54,7 +54,8 @@ struct Inflight {
 // join before the LM head).
 enum OpKind { OP_EMBED = 0, OP_GEMV_PROJ, OP_GEMV_QKV, OP_ATTN, OP_LIN, OP_GEMV_O, OP_GEMV_GU,
               OP_GEMV_DOWN, OP_GEMV_HEAD, OP_VOCAB, OP_FINAL, OP_RESID, OP_PDM_QKV, OP_PDM_ATTN,
-              OP_PDM_O, OP_PDM_GU, OP_PDM_DOWN, OP_NKINDS, OP_FORK = 100, OP_JOIN = 101 };
+              OP_PDM_O, OP_PDM_GU, OP_PDM_DOWN, OP_NUCLEUS, OP_NKINDS, OP_FORK = 100,
+              OP_JOIN = 101 };
 
 struct Op {
   int kind;
@@ -77,7 +78,7 @@ struct Plan {
   int nsoft = 0, nlin = 0;
   int R = 0;   // sub-layer launches per step
   // workspace offsets
-  size_t o_kv, o_pkv, o_lin, o_h, o_anch, o_tok, o_qring, o_qlse, o_X, o_hp, o_qbuf, o_attn,
+  size_t o_kv, o_pkv, o_lin, o_h, o_anch, o_tok, o_qring, o_qlse, o_cut, o_X, o_hp, o_qbuf, o_attn,
       o_act, o_lqkv, o_logits, o_part, o_verdict, o_desc, o_apart, o_rope,
       o_forced, o_ptok, o_pH, o_pA, o_pQKV, o_pO, o_pG, o_pU, o_pZ, o_panch, total;
   size_t kv_layer_bytes;     // K and V of one layer
@@ -154,6 +155,7 @@ bool plan_config(const spd_model_config* c, Plan& p, std::string& err) {
   p.o_tok = take((size_t)p.ring * 4);
   p.o_qring = take((size_t)p.ring * p.V * 4);
   p.o_qlse = take((size_t)p.ring * 4);
+  p.o_cut = take((size_t)(1 + p.ring) * sizeof(NucleusCut));   // target row, then draft ring
   const int T = p.n + p.ring;   // decode rows: target tokens + PDM rows
   p.o_X = take((size_t)p.ring * p.k * p.d * 4);
   p.o_hp = take((size_t)p.ring * p.d * 4);
@@ -382,6 +384,9 @@ hipError_t run_op(spd_handle* h, const Op& op, LaunchEv ev = {}) {
     case OP_VOCAB:
       return launch_vocab_stats(reinterpret_cast<const VocabDesc*>(d + op.off), kVocabBlocks,
                                 h->at<VocabPartial>(p.o_part), st, ev);
+    case OP_NUCLEUS:
+      return launch_nucleus(reinterpret_cast<const VocabDesc*>(d + op.off), kVocabBlocks,
+                            h->at<VocabPartial>(p.o_part), st, ev);
     case OP_FINAL:
       return launch_finalize(reinterpret_cast<const FinalizeDesc*>(d + op.off), st, ev);
     case OP_RESID:
@@ -631,7 +636,13 @@ int build_step(spd_handle* h, DescWriter& dw) {
   vd.gumbel_pos[1] = dpos;
   vd.V = p.V; vd.nblocks = kVocabBlocks; vd.inv_temp = inv_t; vd.sampled = sampled;
   vd.seed = h->seed;
-  h->ops.push_back({OP_VOCAB, dw.put(&vd, 1), 1, kVocabBlocks, 0, 0.0});
+  const bool nucleus = sampled && h->top_p < 1.f;
+  NucleusCut* cuts = h->at<NucleusCut>(p.o_cut);
+  vd.nucleus = nucleus; vd.top_p = h->top_p;
+  vd.cut[0] = cuts; vd.cut[1] = cuts + 1 + h->slot(dpos);
+  const size_t voff = dw.put(&vd, 1);
+  h->ops.push_back({OP_VOCAB, voff, 1, kVocabBlocks, 0, 0.0});
+  if (nucleus) h->ops.push_back({OP_NUCLEUS, voff, 1, kVocabBlocks, 0, 0.0});
   FinalizeDesc fd{};
   fd.mode = 0; fd.exited = exited; fd.single = n_inf == 1; fd.v = v; fd.dpos = dpos;
   fd.ring = p.ring; fd.V = p.V; fd.nblocks = kVocabBlocks; fd.temp = h->temp; fd.inv_temp = inv_t;
@@ -646,6 +657,8 @@ int build_step(spd_handle* h, DescWriter& dw) {
   fd.verdict = h->at<Verdict>(p.o_verdict);
   fd.host_verdict = h->d_hverdict;
   fd.part = h->at<VocabPartial>(p.o_part);
+  fd.nucleus = nucleus;
+  fd.cut_t = cuts; fd.cut_q = cuts + 1 + h->slot(dpos); fd.cut_q_v = cuts + 1 + h->slot(v);
   const size_t foff = dw.put(&fd, 1);
   h->ops.push_back({OP_FINAL, foff, 1, 1, 0, 0.0});
   if (sampled && exited) h->ops.push_back({OP_RESID, foff, 1, kVocabBlocks, 0, 0.0});
@@ -684,7 +697,7 @@ int spd_init(const spd_model_config* cfg, const spd_weights* w, const spd_sampli
     return SPD_E_CAPACITY;
   }
   if (!(s->temperature >= 0.f)) { g_init_error = "temperature must be >= 0"; return SPD_E_ARG; }
-  if (s->top_p < 1.f) { g_init_error = "top_p < 1 is not supported by the GPU path"; return SPD_E_CONFIG; }
+  if (!(s->top_p > 0.f)) { g_init_error = "top_p must be > 0"; return SPD_E_ARG; }
   if (s->forced_mode && s->temperature != 0.f) {
     g_init_error = "forced mode needs temperature 0";
     return SPD_E_CONFIG;
@@ -750,7 +763,8 @@ int spd_init(const spd_model_config* cfg, const spd_weights* w, const spd_sampli
   // KV caches start zeroed: attention reads whole 32-key blocks, and the unwritten tail of
   // the last one must hold finite values (its scores are masked, its values weigh 0)
   if ((e = hipMemsetAsync(h->ws + p.o_kv, 0, (size_t)p.nsoft * p.kv_layer_bytes, h->st)) != hipSuccess ||
-      (e = hipMemsetAsync(h->ws + p.o_pkv, 0, (size_t)p.Ls * p.kv_layer_bytes, h->st)) != hipSuccess)
+      (e = hipMemsetAsync(h->ws + p.o_pkv, 0, (size_t)p.Ls * p.kv_layer_bytes, h->st)) != hipSuccess ||
+      (e = hipMemsetAsync(h->ws + p.o_cut, 0, (size_t)(1 + p.ring) * sizeof(NucleusCut), h->st)) != hipSuccess)
     return dev_fail(e, "hipMemsetAsync(kv)");
   if ((e = hipStreamSynchronize(h->st)) != hipSuccess) return dev_fail(e, "hipStreamSynchronize");
   *out = h;
@@ -850,6 +864,9 @@ int spd_prefill(spd_handle* h, const int32_t* prompt, int32_t len, int32_t* firs
       vd.gumbel_stream[0] = sampled ? RNG_FIRST : 0; vd.gumbel_pos[0] = len;
       vd.V = p.V; vd.nblocks = kVocabBlocks; vd.inv_temp = sampled ? 1.f / h->temp : 1.f;
       vd.sampled = sampled; vd.seed = h->seed;
+      const bool nucleus = sampled && h->top_p < 1.f;
+      vd.nucleus = nucleus; vd.top_p = h->top_p;
+      vd.cut[0] = h->at<NucleusCut>(p.o_cut);
       const size_t vo = dw.put(&vd, 1);
       FinalizeDesc fd{};
       fd.mode = 1; fd.dpos = len; fd.ring = p.ring; fd.V = p.V; fd.nblocks = kVocabBlocks;
@@ -857,12 +874,16 @@ int spd_prefill(spd_handle* h, const int32_t* prompt, int32_t len, int32_t* firs
       fd.tok_ring = h->at<int>(p.o_tok); fd.verdict = h->at<Verdict>(p.o_verdict);
       fd.host_verdict = h->d_hverdict;
       fd.part = h->at<VocabPartial>(p.o_part);
+      fd.nucleus = nucleus; fd.cut_t = vd.cut[0];
       const size_t fo = dw.put(&fd, 1);
       char* d = h->ws + p.o_desc;
       HIPCHK(h, hipMemcpyAsync(d, h->h_desc, dw.used, hipMemcpyHostToDevice, st));
       HIPCHK(h, launch_gemv(GEMV_HEAD, reinterpret_cast<const GemvProb*>(d + go), 1, plan, bf, rope, st));
       HIPCHK(h, launch_vocab_stats(reinterpret_cast<const VocabDesc*>(d + vo), kVocabBlocks,
                                    h->at<VocabPartial>(p.o_part), st));
+      if (nucleus)
+        HIPCHK(h, launch_nucleus(reinterpret_cast<const VocabDesc*>(d + vo), kVocabBlocks,
+                                 h->at<VocabPartial>(p.o_part), st));
       HIPCHK(h, launch_finalize(reinterpret_cast<const FinalizeDesc*>(d + fo), st));
       // the exiting-row residual of the last prompt position (debug view)
       HIPCHK(h, launch_copy_rows(H + (size_t)(P - 1) * p.d, p.d, h->at<float>(p.o_h) +
@@ -1001,6 +1022,7 @@ size_t spd_debug_size(const spd_handle* h, int32_t what) {
     case SPD_DBG_TARGET_KV: return (size_t)p.nsoft * 2 * p.hkv * p.max_ctx * p.hd * p.esz;
     case SPD_DBG_PDM_KV: return (size_t)p.Ls * 2 * p.hkv * p.max_ctx * p.hd * p.esz;
     case SPD_DBG_TOKENS: return (size_t)p.ring * 4;
+    case SPD_DBG_TOP_P: return (size_t)(1 + p.ring) * sizeof(NucleusCut);
   }
   return 0;
 }
@@ -1026,6 +1048,7 @@ int spd_debug_copy(const spd_handle* hc, int32_t what, void* dst, size_t bytes) 
     case SPD_DBG_TARGET_KV: src = h->ws + p.o_kv; break;
     case SPD_DBG_PDM_KV: src = h->ws + p.o_pkv; break;
     case SPD_DBG_TOKENS: src = h->ws + p.o_tok; break;
+    case SPD_DBG_TOP_P: src = h->ws + p.o_cut; break;
   }
   HIPCHK(h, hipStreamSynchronize(h->st));
   if (what == SPD_DBG_TARGET_KV || what == SPD_DBG_PDM_KV) {

@@ -105,6 +105,19 @@ struct EmbedGather {
 };
 
 // The vocabulary pass: statistics of up to two logit rows (target, draft).
+// Top-p set of one logit row (T > 0, top_p < 1): the tokens with z > zb, and the
+// tokens with z == zb and id <= id_cut. lse: log of the sum over the set of exp(z / T).
+struct NucleusCut {
+  float zb;
+  int id_cut;
+  float lse;
+  int pad;
+};
+
+__device__ __forceinline__ bool in_cut(float z, int i, const NucleusCut& c) {
+  return z > c.zb || (z == c.zb && i <= c.id_cut);
+}
+
 struct VocabDesc {
   const float* logits[2];     // row 0: target head output, row 1: draft (PDM) head output
   int active[2];
@@ -115,6 +128,9 @@ struct VocabDesc {
   float inv_temp;             // 1/T (T > 0) else 1
   int sampled;                // T > 0
   unsigned long long seed;
+  int nucleus;                // T > 0 and top_p < 1: the Gumbel draw runs over the top-p set
+  float top_p;
+  NucleusCut* cut[2];         // where each active row's top-p set is written
 };
 
 struct VocabPartial {
@@ -165,6 +181,10 @@ struct FinalizeDesc {
   Verdict* host_verdict;     // device view of pinned host memory: the finished verdict, so the
                              // host reads it once the stream is idle, with no copy
   const VocabPartial* part;  // [2][nblocks]
+  int nucleus;               // top_p < 1: probabilities are renormalised over the top-p sets
+  const NucleusCut* cut_t;   // the target row's set (this step)
+  const NucleusCut* cut_q;   // this step's draft row's set
+  const NucleusCut* cut_q_v; // the set of the draft at v
 };
 
 enum RngStream : int { RNG_DRAFT = 1, RNG_ACC = 2, RNG_RES = 3, RNG_FORCE = 4, RNG_FIRST = 5 };
@@ -356,6 +376,8 @@ hipError_t launch_embed_gather(const EmbedGather* desc, const void* blk_src, voi
                                LaunchEv ev = {});
 hipError_t launch_vocab_stats(const VocabDesc* d_desc, int nblocks, VocabPartial* part,
                               hipStream_t st, LaunchEv ev = {});
+hipError_t launch_nucleus(const VocabDesc* d_desc, int nblocks, VocabPartial* part,
+                          hipStream_t st, LaunchEv ev = {});
 hipError_t launch_finalize(const FinalizeDesc* d_desc, hipStream_t st, LaunchEv ev = {});
 hipError_t launch_residual_impl(const FinalizeDesc* d_desc, VocabPartial* part, int nblocks,
                                 hipStream_t st, LaunchEv ev = {});

@@ -10,6 +10,10 @@
 //   al. 2023, the paper's section 3.5 assumption on the pith.science review).
 // residual (rejections at T > 0 only): y = argmax over {p > q} of
 //   log(p - q) + G, per-block partials merged by a one-block kernel.
+// nucleus (T > 0 and top_p < 1): the top-p set of each row, the smallest prefix of
+//   the tokens in order of decreasing probability (lower id first on ties) whose
+//   mass reaches top_p (Holtzman et al. 2019), found by selection rather than a
+//   sort; then the Gumbel draw restricted to the set, one partial per block.
 #include <climits>
 
 #include "spd_internal.h"
@@ -83,7 +87,7 @@ __global__ __launch_bounds__(kVocabBlock) void vocab_stats_kernel(const VocabDes
     if (!d.active[r]) continue;
     const float* z = d.logits[r];
     Stat s = stat_empty();
-    const bool gum = d.gumbel_stream[r] != 0;
+    const bool gum = d.gumbel_stream[r] != 0 && !d.nucleus;
     for (int i = lo + threadIdx.x; i < hi; i += blockDim.x) {
       const float v = z[i];
       if (d.sampled) {
@@ -101,6 +105,212 @@ __global__ __launch_bounds__(kVocabBlock) void vocab_stats_kernel(const VocabDes
     }
     const Stat b = block_reduce(s, d.inv_temp, sh);
     if (threadIdx.x == 0) part[r * d.nblocks + blockIdx.x] = to_partial(b);
+  }
+}
+
+// ---- top-p set ---------------------------------------------------------------
+// Masses are fixed point: w(z) = floor(exp((z - max) / T) 2^40) as a 64-bit integer,
+// so every sum is exact and independent of the order of the additions. A token is in
+// the set iff the mass ahead of it is < top_p W (W: the row's total), i.e. < ceil(top_p W).
+//   1. histogram of the mass over depth bins of (max - z) / T, 64 per unit (monotone in
+//      z); a block scan finds the bin where the running mass crosses the threshold;
+//   2. the tokens of that bin (in LDS when they fit) go through four 8-bit radix
+//      passes over the order-preserving integer key of z, each keeping the digit where
+//      the running mass crosses: the result is zb, the logit of the last token kept;
+//   3. of the tokens tied at zb the first j* in id order are kept, j* = ceil(rest / w(zb));
+//      when that splits the ties, a scan over id ranges names the last id kept.
+constexpr int kNucBins = 2 * kVocabBlock;   // depth bins
+constexpr int kNucList = 8192;              // crossing-bin tokens kept in LDS
+typedef unsigned long long u64;
+
+__device__ __forceinline__ int nuc_bin(float z, float M, float invT) {
+  // explicitly rounded operations: every evaluation of a token's bin gives the same bin
+  const float b = __fmul_rn(__fmul_rn(__fsub_rn(M, z), invT), 64.f);
+  return b < (float)(kNucBins - 1) ? (int)b : kNucBins - 1;
+}
+__device__ __forceinline__ u64 nuc_weight(float z, float M, float invT) {
+  return (u64)(expf((z - M) * invT) * 1099511627776.f);   // 2^40
+}
+// order-preserving key of a float (-0 and +0 share the key of +0)
+__device__ __forceinline__ uint32_t f_key(float z) {
+  uint32_t b = __float_as_uint(z);
+  if (b == 0x80000000u) b = 0u;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float key_f(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+__device__ __forceinline__ u64 shfl_up64(u64 v, int d) {
+  const int lo = __shfl_up((int)(uint32_t)v, d), hi = __shfl_up((int)(uint32_t)(v >> 32), d);
+  return ((u64)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+// Exclusive prefix sum over the block in thread order; `total` gets the block's sum.
+__device__ u64 block_excl_scan(u64 v, u64* wsum, u64& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  u64 inc = v;
+  for (int o = 1; o < 64; o <<= 1) {
+    const u64 t = shfl_up64(inc, o);
+    if (lane >= o) inc += t;
+  }
+  if (lane == 63) wsum[w] = inc;
+  __syncthreads();
+  u64 before = 0, tot = 0;
+  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) {
+    const u64 s = wsum[i];
+    if (i < w) before += s;
+    tot += s;
+  }
+  __syncthreads();
+  total = tot;
+  return before + inc - v;
+}
+
+__global__ __launch_bounds__(kVocabBlock) void nucleus_kernel(const VocabDesc* __restrict__ dd,
+                                                               const VocabPartial* __restrict__ part) {
+  __shared__ u64 hist[kNucBins];
+  __shared__ float lz[kNucList];
+  __shared__ u64 wsum[kVocabBlock / 64];
+  __shared__ float red[kVocabBlock / 64];
+  __shared__ int s_bin, s_count, s_digit, s_id;
+  __shared__ u64 s_above, s_mass;
+  const VocabDesc& d = *dd;
+  const int r = blockIdx.x;
+  if (!d.active[r]) return;
+  const float* z = d.logits[r];
+  const int V = d.V, t = threadIdx.x, nthr = blockDim.x;
+  const float invT = d.inv_temp;
+  // the row's largest logit, from the statistics partials
+  float m = -INFINITY;
+  for (int i = t; i < d.nblocks; i += nthr) m = fmaxf(m, part[r * d.nblocks + i].max);
+  m = wave_max(m);
+  if ((t & 63) == 0) red[t >> 6] = m;
+  for (int b = t; b < kNucBins; b += nthr) hist[b] = 0;
+  if (t == 0) { s_count = 0; s_bin = kNucBins - 1; s_above = 0; s_digit = 0; s_mass = 0; s_id = INT_MAX; }
+  __syncthreads();
+  float M = red[0];
+  for (int i = 1; i < nthr / 64; ++i) M = fmaxf(M, red[i]);
+
+  // 1. mass per depth bin; bin 0 holds the largest logits
+  for (int i = t; i < V; i += nthr) {
+    const float v = z[i];
+    atomicAdd(&hist[nuc_bin(v, M, invT)], nuc_weight(v, M, invT));
+  }
+  __syncthreads();
+  const u64 h0 = hist[2 * t], h1 = hist[2 * t + 1];
+  u64 W;
+  const u64 ex = block_excl_scan(h0 + h1, wsum, W);
+  double thr = ceil((double)d.top_p * (double)W);
+  const u64 T = thr < 1.0 ? 1ull : (thr >= (double)W ? W : (u64)thr);
+  if (ex < T && T <= ex + h0) { s_bin = 2 * t; s_above = ex; }
+  else if (ex + h0 < T && T <= ex + h0 + h1) { s_bin = 2 * t + 1; s_above = ex + h0; }
+  __syncthreads();
+  const int bc = s_bin;
+  u64 above = s_above;
+
+  // 2. the crossing bin's tokens, then a radix select of the last key kept
+  for (int i = t; i < V; i += nthr) {
+    const float v = z[i];
+    if (nuc_bin(v, M, invT) == bc) {
+      const int k = atomicAdd(&s_count, 1);
+      if (k < kNucList) lz[k] = v;
+    }
+  }
+  __syncthreads();
+  const int cnt = s_count;
+  const bool in_lds = cnt <= kNucList;
+  uint32_t prefix = 0;
+  u64 tie_mass = 0;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    if (t < 256) hist[t] = 0;
+    __syncthreads();
+    const uint32_t hmask = shift == 24 ? 0u : (0xffffffffu << (shift + 8));
+    if (in_lds) {
+      for (int j = t; j < cnt; j += nthr) {
+        const float v = lz[j];
+        const uint32_t k = f_key(v);
+        if ((k & hmask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], nuc_weight(v, M, invT));
+      }
+    } else {
+      for (int i = t; i < V; i += nthr) {
+        const float v = z[i];
+        if (nuc_bin(v, M, invT) != bc) continue;
+        const uint32_t k = f_key(v);
+        if ((k & hmask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], nuc_weight(v, M, invT));
+      }
+    }
+    __syncthreads();
+    // thread t holds digit 255 - t: the prefix sum in thread order is the mass of larger digits
+    const u64 hv = t < 256 ? hist[255 - t] : 0ull;
+    u64 tot;
+    const u64 e = block_excl_scan(hv, wsum, tot);
+    if (t < 256 && above + e < T && T <= above + e + hv) {
+      s_digit = 255 - t; s_above = above + e; s_mass = hv;
+    }
+    __syncthreads();
+    prefix |= (uint32_t)s_digit << shift;
+    above = s_above;
+    tie_mass = s_mass;
+    __syncthreads();
+  }
+  const float zb = key_f(prefix);
+
+  // 3. ties at zb: the first j* of them (by id) are kept
+  const u64 wb = nuc_weight(zb, M, invT);
+  const u64 c = wb ? tie_mass / wb : 0ull;
+  const u64 js = wb ? (T - above + wb - 1) / wb : 0ull;
+  int id_cut = INT_MAX;
+  if (js < c) {
+    const int C = (V + nthr - 1) / nthr;
+    const int lo = min(V, t * C), hi = min(V, lo + C);
+    int mine = 0;
+    for (int i = lo; i < hi; ++i) mine += z[i] == zb;
+    u64 all;
+    const u64 before = block_excl_scan((u64)mine, wsum, all);
+    const u64 want = js - 1;              // 0-based rank of the last tie kept
+    if (want >= before && want < before + (u64)mine) {
+      u64 k = before;
+      for (int i = lo; i < hi; ++i)
+        if (z[i] == zb) { if (k == want) { s_id = i; break; } ++k; }
+    }
+    __syncthreads();
+    id_cut = s_id;
+  }
+  if (t == 0) {
+    NucleusCut out;
+    out.zb = zb;
+    out.id_cut = id_cut;
+    out.lse = (float)((double)M * invT + log((double)(above + js * wb)) - 40.0 * 0.69314718055994531);
+    out.pad = 0;
+    *d.cut[r] = out;
+  }
+}
+
+// Gumbel-max over each row's top-p set: per block top-2 of z/T + G over the set, into the
+// Gumbel fields of the row's statistics partials.
+__global__ __launch_bounds__(kVocabBlock) void nucleus_gumbel_kernel(const VocabDesc* __restrict__ dd,
+                                                                      VocabPartial* __restrict__ part) {
+  __shared__ Stat sh[kVocabBlock];
+  const VocabDesc& d = *dd;
+  const int chunk = (d.V + d.nblocks - 1) / d.nblocks;
+  const int lo = blockIdx.x * chunk, hi = min(d.V, lo + chunk);
+  for (int r = 0; r < 2; ++r) {
+    if (!d.active[r] || d.gumbel_stream[r] == 0) continue;
+    const float* z = d.logits[r];
+    const NucleusCut c = *d.cut[r];
+    Stat s = stat_empty();
+    for (int i = lo + threadIdx.x; i < hi; i += blockDim.x) {
+      const float v = z[i];
+      if (!in_cut(v, i, c)) continue;
+      const float u = rng_uniform(d.seed, d.gumbel_stream[r], d.gumbel_pos[r], (unsigned long long)i);
+      const float g = v * d.inv_temp + gumbel_of(u);
+      if (g > s.gmax) { s.gsecond = s.gmax; s.gmax = g; s.garg = i; }
+      else if (g > s.gsecond) { s.gsecond = g; }
+    }
+    const Stat b = block_reduce(s, 1.f, sh);
+    if (threadIdx.x == 0) {
+      VocabPartial& p = part[r * d.nblocks + blockIdx.x];
+      p.gmax = b.gmax; p.gsecond = b.gsecond; p.garg = b.garg;
+    }
   }
 }
 
@@ -122,6 +332,7 @@ __global__ __launch_bounds__(kVocabBlock) void finalize_kernel(const FinalizeDes
   v.committed = -1;
   v.verified_draft = -1;
   v.lse_t = t.max * f.inv_temp + logf(t.sum);
+  if (f.nucleus && (f.mode == 1 || f.exited)) v.lse_t = f.cut_t->lse;
   if (f.mode == 1) {
     int y;
     bool flag;
@@ -139,7 +350,7 @@ __global__ __launch_bounds__(kVocabBlock) void finalize_kernel(const FinalizeDes
   bool dflag;
   if (sampled) { d = q.garg; dflag = (q.gmax - q.gsecond) < kNearTie; }
   else { d = q.arg; dflag = (q.max - q.second) < kNearTie; }
-  v.lse_q = q.max * f.inv_temp + logf(q.sum);
+  v.lse_q = f.nucleus ? f.cut_q->lse : q.max * f.inv_temp + logf(q.sum);
   *f.lse_q_new = v.lse_q;
   if (f.forced_mode) {
     const int j = f.dpos - f.forced_base;
@@ -164,8 +375,12 @@ __global__ __launch_bounds__(kVocabBlock) void finalize_kernel(const FinalizeDes
       if ((t.max - t.second) < kNearTie) v.flags |= 1;
       if (!v.accepted) f.tok_ring[f.v % f.ring] = y;
     } else {
-      const float pd = expf(f.zt[dv] * f.inv_temp - v.lse_t);
-      const float qd = expf(f.zq_v[dv] * f.inv_temp - *f.lse_q_v);
+      float pd = expf(f.zt[dv] * f.inv_temp - v.lse_t);
+      float qd = expf(f.zq_v[dv] * f.inv_temp - *f.lse_q_v);
+      if (f.nucleus) {
+        if (!in_cut(f.zt[dv], dv, *f.cut_t)) pd = 0.f;
+        if (!in_cut(f.zq_v[dv], dv, *f.cut_q_v)) qd = 0.f;
+      }
       const float u = rng_uniform(f.seed, RNG_ACC, f.v, 0);
       v.p_d = pd;
       v.q_d = qd;
@@ -190,10 +405,14 @@ __global__ __launch_bounds__(kVocabBlock) void residual_kernel(const FinalizeDes
   const float lse_q = *f.lse_q_v;
   const int chunk = (f.V + f.nblocks - 1) / f.nblocks;
   const int lo = blockIdx.x * chunk, hi = min(f.V, lo + chunk);
+  const bool nuc = f.nucleus != 0;
+  NucleusCut ct{}, cq{};
+  if (nuc) { ct = *f.cut_t; cq = *f.cut_q_v; }
   Stat s = stat_empty();
   for (int i = lo + threadIdx.x; i < hi; i += blockDim.x) {
-    const float p = expf(f.zt[i] * f.inv_temp - lse_t);
-    const float qq = expf(f.zq_v[i] * f.inv_temp - lse_q);
+    const float zt = f.zt[i], zq = f.zq_v[i];
+    const float p = nuc && !in_cut(zt, i, ct) ? 0.f : expf(zt * f.inv_temp - lse_t);
+    const float qq = nuc && !in_cut(zq, i, cq) ? 0.f : expf(zq * f.inv_temp - lse_q);
     const float r = p - qq;
     if (r > 0.f) {
       const float u = rng_uniform(f.seed, RNG_RES, f.v, (unsigned long long)i);
@@ -230,6 +449,14 @@ __global__ __launch_bounds__(kVocabBlock) void residual_final_kernel(
 hipError_t launch_vocab_stats(const VocabDesc* d_desc, int nblocks, VocabPartial* part,
                               hipStream_t st, LaunchEv ev) {
   SPD_LAUNCH(ev, vocab_stats_kernel, dim3(nblocks), dim3(kVocabBlock), 0, st, d_desc, part);
+  return hipGetLastError();
+}
+
+hipError_t launch_nucleus(const VocabDesc* d_desc, int nblocks, VocabPartial* part,
+                          hipStream_t st, LaunchEv ev) {
+  const LaunchEv e1{ev.start, nullptr}, e2{nullptr, ev.stop};
+  SPD_LAUNCH(e1, nucleus_kernel, dim3(2), dim3(kVocabBlock), 0, st, d_desc, part);
+  SPD_LAUNCH(e2, nucleus_gumbel_kernel, dim3(nblocks), dim3(kVocabBlock), 0, st, d_desc, part);
   return hipGetLastError();
 }
 

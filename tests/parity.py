@@ -6,14 +6,51 @@ Comparison rule:
   * floats: logits max-abs <= 1e-4 (f32 weights) / 5e-2 (bf16 weights);
     residual and anchor states relative L2 <= 1e-5 (f32) / 2e-2 (bf16);
   * a token decision may differ only where the oracle flags a near-tie
-    (top-2 gap < 1e-3, or |u q(d) - p(d)| < 1e-3 q(d)); the comparison stops there.
+    (top-2 gap < 1e-3, or |u q(d) - p(d)| < 1e-3 q(d)); the comparison stops there;
+  * top_p < 1: every logit row must lie within `slack` of the oracle's (the envelope its
+    near-tie flags assume); each top-p set the library reports must hold every token
+    the oracle's envelope keeps for sure and nothing outside its band, and must be the
+    top-p set of the library's own logits (check_top_p_set).
 """
 from __future__ import annotations
 
 import numpy as np
 
-from oracle.sampling import Sampling
+from oracle.sampling import Sampling, nucleus_bounds
 from oracle.spd import SPD as OracleSPD
+
+TOP_P_MASS_EPS = 1e-6     # fp32 exponentials and 2^-40 fixed-point masses
+
+
+def check_top_p_set(z, cut, T, top_p, where):
+    """The reported set {z > zb} + {z == zb, id <= id_cut} is the top-p set of z itself:
+    a prefix of the tokens by decreasing logit (lower id first) that reaches top_p and
+    does not without its last token; lse is log sum over it of exp(z / T)."""
+    z = np.asarray(z, dtype=np.float32)
+    zb, idc = np.float32(cut["zb"]), int(cut["id_cut"])
+    ids = np.arange(z.size)
+    keep = (z > zb) | ((z == zb) & (ids <= idc))
+    assert np.any(z == zb) and keep.any(), f"{where}: zb {zb} is not a logit of the row"
+    zd = z.astype(np.float64) / T
+    w = np.exp(zd - zd.max())
+    p = w / w.sum()
+    order = np.lexsort((ids, -z.astype(np.float64)))
+    k = int(keep.sum())
+    assert keep[order[:k]].all(), f"{where}: the set is not a prefix of the order"
+    mass = p[keep].sum()
+    last = p[order[k - 1]]
+    assert mass >= top_p - TOP_P_MASS_EPS, f"{where}: set mass {mass} < top_p {top_p}"
+    assert mass - last < top_p + TOP_P_MASS_EPS, f"{where}: set not minimal ({mass - last})"
+    lse = zd.max() + np.log(w[keep].sum())
+    assert abs(float(cut["lse"]) - lse) <= 1e-5 * max(1.0, abs(lse)), f"{where}: lse"
+    split = bool(np.any((z == zb) & ~keep))      # the edge fell inside a group of ties
+    return keep, split
+
+
+def check_against_envelope(keep, z_oracle, s, where):
+    certain, band = nucleus_bounds(z_oracle, s.temperature, s.top_p, s.slack())
+    assert keep[certain].all(), f"{where}: a token the oracle keeps for sure is left out"
+    assert not (keep & ~(certain | band)).any(), f"{where}: a token outside the band is kept"
 
 
 def tolerances(cfg):
@@ -28,17 +65,20 @@ def rel(a, b):
 
 def run_parity(cfg, W, dW, prompt, G=None, T=0.0, seed=0, n=None, fill="clamp",
                forced_p=None, forced_ref=None, check_states=True, max_steps=None,
-               oracle_weights=None, tol_logits=None):
+               oracle_weights=None, tol_logits=None, top_p=1.0, slack=None):
     from speculative_pipeline_decoding_amd import SPD
     G = cfg.gen_len if G is None else G
     tol_l, tol_h = tolerances(cfg)
     if tol_logits is not None:
         tol_l = tol_logits
-    s = Sampling(temperature=T, seed=seed)
-    kw = {}
+    s = Sampling(temperature=T, seed=seed, top_p=top_p, logit_slack=slack)
+    nucleus = T > 0 and top_p < 1.0
+    if nucleus:
+        tol_l = min(tol_l, s.slack())
+    kw = {"top_p": top_p}
     if forced_p is not None:
         s.forced_p, s.forced_ref, s.forced_base = forced_p, np.asarray(forced_ref), len(prompt)
-        kw = dict(forced_p=forced_p, forced_ref=list(forced_ref))
+        kw.update(forced_p=forced_p, forced_ref=list(forced_ref))
     gpu = SPD(cfg, dW, temperature=T, seed=seed, n=n, fill=fill, **kw)
     model = None
     if oracle_weights is not None:
@@ -53,6 +93,12 @@ def run_parity(cfg, W, dW, prompt, G=None, T=0.0, seed=0, n=None, fill="clamp",
     err = float(np.abs(zt - orc.prefill_logits).max())
     rep["max_logit_err"] = err
     assert err <= tol_l, f"prefill logits err {err}"
+    rep["top_p_sets"] = rep["top_p_split_ties"] = 0
+    if nucleus:
+        keep, split = check_top_p_set(zt, gpu.debug("top_p")[0], T, top_p, "prefill")
+        check_against_envelope(keep, orc.prefill_logits, s, "prefill")
+        rep["top_p_sets"] += 1
+        rep["top_p_split_ties"] += int(split)
     if t0g != t0o:
         assert orc.prefill_flag, f"first token {t0g} != {t0o} without a near tie"
         rep["stopped_at_near_tie"] = 0
@@ -71,6 +117,19 @@ def run_parity(cfg, W, dW, prompt, G=None, T=0.0, seed=0, n=None, fill="clamp",
         rep["max_logit_err"] = max(rep["max_logit_err"], e)
         assert e <= tol_l, f"step {k}: draft logits err {e}"
         rep["flagged"] += int(rec.draft_flag) + int(rec.verify_flag)
+        if nucleus:
+            cuts = gpu.debug("top_p")
+            dpos = rec.newest + 1
+            keep, split = check_top_p_set(zq, cuts[1 + dpos % ring], T, top_p, f"step {k} draft")
+            check_against_envelope(keep, rec.draft_logits, s, f"step {k} draft")
+            rep["top_p_sets"] += 1
+            rep["top_p_split_ties"] += int(split)
+            if rec.exited:
+                zt = gpu.debug("target_logits")
+                keep, split = check_top_p_set(zt, cuts[0], T, top_p, f"step {k} target")
+                check_against_envelope(keep, rec.target_logits, s, f"step {k} target")
+                rep["top_p_sets"] += 1
+                rep["top_p_split_ties"] += int(split)
         if c.new_draft != rec.draft:
             assert rec.draft_flag, f"step {k}: draft {c.new_draft} != {rec.draft} without a near tie"
             rep["stopped_at_near_tie"] = k

@@ -69,10 +69,12 @@ def test_init_rejects_bad_arguments_without_a_gpu():
     assert L.spd_init(ctypes.byref(c), ctypes.byref(w), ctypes.byref(s), fake, nb - 1, None,
                       ctypes.byref(h)) == binding.SPD_E_CAPACITY
     assert b"workspace" in L.spd_init_error()
-    # top_p < 1 is not supported on the GPU path
-    s.top_p = 0.9
-    assert L.spd_init(ctypes.byref(c), ctypes.byref(w), ctypes.byref(s), fake, nb, None,
-                      ctypes.byref(h)) == binding.SPD_E_CONFIG
+    # top_p must be > 0 (and not NaN)
+    for bad in (0.0, -0.5, float("nan")):
+        s.top_p = bad
+        assert L.spd_init(ctypes.byref(c), ctypes.byref(w), ctypes.byref(s), fake, nb, None,
+                          ctypes.byref(h)) == binding.SPD_E_ARG
+        assert b"top_p" in L.spd_init_error()
     s.top_p = 1.0
     # forced mode needs T = 0
     s.temperature, s.forced_mode = 1.0, 1

@@ -9,7 +9,10 @@ d4096 / head_dim 128 model, and the n=16 hybrid with 24 linear-attention layers)
         autoregressively (the library at n=1), up to the first decision either run
         flags as a near-tie;
       - the scheduler's counting identity K = N + (n-1)(1 + R') and S0 = alpha n at T=1,
-        with KV lengths non-increasing over layers after every step.
+        with KV lengths non-increasing over layers after every step;
+      - at T=1, top_p=0.875: every top-p set the library reports is the top-p set of its
+        own logit row over the full vocabulary (parity.check_top_p_set), and every
+        draft lies in its set.
 One workload's weights are resident at a time (host and device).
 """
 import json
@@ -20,7 +23,7 @@ import pytest
 
 import conftest
 from conftest import workload
-from parity import run_parity
+from parity import check_top_p_set, run_parity
 
 pytestmark = pytest.mark.gpu
 
@@ -117,3 +120,33 @@ def test_fullsize_counting_identity_and_kv_invariants(wl):
         assert pl <= kv[-1]                                   # the PDM keeps exited rows only
         if v and not acc:
             assert len(set(kv)) == 1, kv                      # a reject truncates every layer to v
+
+
+def test_fullsize_top_p_sets(wl):
+    from speculative_pipeline_decoding_amd import SPD
+    name, dW, _ = wl
+    cfg, _, prompt = workload(name)
+    top_p = 0.875
+    print(f"[fullsize] top-p sets of {name} at top_p={top_p}", flush=True)
+    gpu = SPD(cfg, dW, temperature=1.0, top_p=top_p, seed=13)
+    ring = gpu.n + 1
+    t0 = gpu.prefill(prompt)
+    keep, _ = check_top_p_set(gpu.debug("target_logits"), gpu.debug("top_p")[0], 1.0, top_p,
+                              "prefill")
+    assert keep[t0]
+    sizes = []
+    for k in range(2 * cfg.n_stages):
+        gpu.step()
+        c = gpu.verify_commit()
+        cuts = gpu.debug("top_p")
+        dpos = c.newest + 1
+        keep, _ = check_top_p_set(gpu.debug("draft_logits"), cuts[1 + dpos % ring], 1.0, top_p,
+                                  f"step {k} draft")
+        assert keep[c.new_draft], f"step {k}: draft {c.new_draft} outside its top-p set"
+        sizes.append(int(keep.sum()))
+        if c.verified:
+            keep, _ = check_top_p_set(gpu.debug("target_logits"), cuts[0], 1.0, top_p,
+                                      f"step {k} target")
+            assert keep[c.token], f"step {k}: committed {c.token} outside the target's set"
+    gpu.close()
+    print(f"[fullsize] draft set sizes {sizes[:4]} ... of V={cfg.vocab}", flush=True)

@@ -68,6 +68,39 @@ def test_mid_sampled(name):
     assert rep["steps"] > 0
 
 
+@pytest.mark.parametrize("top_p,T,seed", [(0.875, 1.0, 3), (0.25, 0.7, 4)])
+def test_tiny_top_p(top_p, T, seed):
+    rep = _run("tiny", T=T, seed=seed, top_p=top_p, slack=1e-5)
+    assert rep["steps"] > 0 and rep["top_p_sets"] > rep["steps"]
+
+
+def test_tiny_top_p_tied_logits():
+    """LM-head rows duplicated in pairs: every logit row is made of exact ties, and the
+    top-p edge often splits a pair, so the lower-id rule decides membership."""
+    import torch
+    from speculative_pipeline_decoding_amd import upload_weights
+    cfg, W, prompt = workload("tiny")
+    W2 = dict(W)
+    lm = np.array(W["lm_head"], copy=True)
+    lm[1::2] = lm[0::2]
+    W2["lm_head"] = lm
+    _dev.clear()
+    torch.cuda.empty_cache()
+    dW2 = upload_weights(cfg, W2)
+    print("[parity] tiny, paired LM-head rows, T=1 top_p=0.625", flush=True)
+    rep = run_parity(cfg, W2, dW2, prompt, T=1.0, seed=8, top_p=0.625, slack=1e-5)
+    print(f"[parity] -> {rep}", flush=True)
+    assert rep["steps"] > 0 and rep["top_p_sets"] > rep["steps"]
+    assert rep["top_p_split_ties"] > 0      # the lower-id rule was exercised
+
+
+@pytest.mark.parametrize("name,top_p", [("mid_bf16_L6_d384_n3", 0.875),
+                                         ("mid_hybrid_bf16_L8_d256_n4", 0.5)])
+def test_mid_top_p(name, top_p):
+    rep = _run(name, T=1.0, seed=7, top_p=top_p, slack=5e-4)
+    assert rep["steps"] > 0
+
+
 def test_mid_forced_acceptance():
     from oracle.spd import ar_decode
     cfg, W, prompt = workload("mid_bf16_L6_d384_n3")
