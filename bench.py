@@ -54,11 +54,11 @@ def pct(xs, q):
     return xs[i]
 
 
-def run_spd(cfg, dW, prompt, T, seed, warmup, steps, kernel_timing):
+def run_spd(cfg, dW, prompt, T, seed, warmup, steps, kernel_timing, top_p=1.0):
     import torch
     from speculative_pipeline_decoding_amd import SPD
     stream = torch.cuda.current_stream()
-    spd = SPD(cfg, dW, temperature=T, seed=seed, stream=stream)
+    spd = SPD(cfg, dW, temperature=T, top_p=top_p, seed=seed, stream=stream)
     t = time.perf_counter()
     spd.prefill(prompt)
     torch.cuda.synchronize()
@@ -131,7 +131,7 @@ def traffic_from_profile(workload: str, kernel: str):
     return value
 
 
-def cpu_baseline(cfg, W, T, seed, alpha, budget_s):
+def cpu_baseline(cfg, W, T, seed, alpha, budget_s, top_p=1.0):
     """The oracle as it stands, on the host cores, over a bounded sample of the same model."""
     import numpy as np
     from oracle.spd import SPD as OracleSPD
@@ -143,7 +143,7 @@ def cpu_baseline(cfg, W, T, seed, alpha, budget_s):
     except Exception:
         threads = os.cpu_count() or 1
     plen = 16
-    o = OracleSPD(cfg, W, Sampling(temperature=T, seed=seed))
+    o = OracleSPD(cfg, W, Sampling(temperature=T, top_p=top_p, seed=seed))
     t = time.perf_counter()
     o.prefill(make_prompt(cfg, length=plen))
     setup = time.perf_counter() - t
@@ -173,6 +173,8 @@ def main():
     ap.add_argument("--workload", default="cfg3")
     ap.add_argument("--temperature", type=float, default=None,
                     help="sampling temperature (default: the workload's first one)")
+    ap.add_argument("--top-p", type=float, default=None,
+                    help="top-p of the sampled run (default: the workload's, 1.0)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--t0-run", action="store_true",
                     help="also time the same steps at T=0 (greedy, lossless) and report them")
@@ -195,6 +197,8 @@ def main():
     cfg = get(args.workload)
     if args.temperature is None:
         args.temperature = float(cfg.temperatures[0])
+    if args.top_p is None:
+        args.top_p = float(cfg.top_p)
     if args.warmup + args.steps > cfg.gen_len:
         print(f"warmup + steps must be <= {cfg.gen_len} (the workload generates {cfg.gen_len} "
               "tokens; each step commits at most one)", file=sys.stderr)
@@ -216,7 +220,8 @@ def main():
         log(f"calibration copy: {args.calib_copy_mib} MiB read + {args.calib_copy_mib} MiB written")
         del src, dst
 
-    main_run = run_spd(cfg, dW, prompt, args.temperature, args.seed, args.warmup, args.steps, True)
+    main_run = run_spd(cfg, dW, prompt, args.temperature, args.seed, args.warmup, args.steps, True,
+                       args.top_p)
     tm = main_run["timed"]
     log(f"T={args.temperature}: prefill {main_run['prefill_s']:.2f}s, timed {tm['K']} steps in "
         f"{tm['wall_s'] * 1e3:.1f} ms, N={tm['N']}")
@@ -260,7 +265,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "n": cfg.n_stages, "Ls": cfg.pdm_layers,
                    "anchors": list(cfg.anchors), "context": cfg.prompt_len + cfg.gen_len,
-                   "prompt": cfg.prompt_len, "temperature": args.temperature, "top_p": 1.0,
+                   "prompt": cfg.prompt_len, "temperature": args.temperature, "top_p": args.top_p,
                    "weights": "bf16 N(0,0.02) seeded", "kv_cache": "bf16",
                    "prompt_ids": "uniform random"},
         "roofline": {"bound": "hbm", "kernel": dominant,
@@ -288,7 +293,7 @@ def main():
         del dW
         torch.cuda.empty_cache()
         res["cpu_baseline"] = cpu_baseline(cfg, W, args.temperature, args.seed, alpha,
-                                           args.cpu_budget)
+                                           args.cpu_budget, args.top_p)
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)

@@ -78,7 +78,7 @@ struct Plan {
   int nsoft = 0, nlin = 0;
   int R = 0;   // sub-layer launches per step
   // workspace offsets
-  size_t o_kv, o_pkv, o_lin, o_h, o_anch, o_tok, o_qring, o_qlse, o_cut, o_X, o_hp, o_qbuf, o_attn,
+  size_t o_kv, o_pkv, o_lin, o_h, o_anch, o_tok, o_qring, o_qlse, o_cut, o_nuc, o_X, o_hp, o_qbuf, o_attn,
       o_act, o_lqkv, o_logits, o_part, o_verdict, o_desc, o_apart, o_rope,
       o_forced, o_ptok, o_pH, o_pA, o_pQKV, o_pO, o_pG, o_pU, o_pZ, o_panch, total;
   size_t kv_layer_bytes;     // K and V of one layer
@@ -156,6 +156,7 @@ bool plan_config(const spd_model_config* c, Plan& p, std::string& err) {
   p.o_qring = take((size_t)p.ring * p.V * 4);
   p.o_qlse = take((size_t)p.ring * 4);
   p.o_cut = take((size_t)(1 + p.ring) * sizeof(NucleusCut));   // target row, then draft ring
+  p.o_nuc = take(kNucPartBytes + kNucHistBytes + kNucCntBytes + (size_t)2 * p.V * sizeof(int2));
   const int T = p.n + p.ring;   // decode rows: target tokens + PDM rows
   p.o_X = take((size_t)p.ring * p.k * p.d * 4);
   p.o_hp = take((size_t)p.ring * p.d * 4);
@@ -249,6 +250,15 @@ struct spd_handle {
                                     ((size_t)p.ord[l] * p.ring + slot) * p.lin_state_bytes);
   }
   void* pV(int r) const { return (char*)pK(r) + p.kv_layer_bytes / 2; }
+  // the top-p selection's scratch regions
+  void nucleus_scratch(VocabDesc& vd) const {
+    char* b = ws + p.o_nuc;
+    vd.nuc_part = reinterpret_cast<unsigned long long*>(b);
+    vd.nuc_hist = reinterpret_cast<unsigned long long*>(b + kNucPartBytes);
+    vd.nuc_cnt = reinterpret_cast<int*>(b + kNucPartBytes + kNucHistBytes);
+    vd.nuc_max = reinterpret_cast<float*>(b + kNucPartBytes + kNucHistBytes + 2 * 64 * 4);
+    vd.nuc_cand = reinterpret_cast<int2*>(b + kNucPartBytes + kNucHistBytes + kNucCntBytes);
+  }
 };
 
 namespace {
@@ -640,6 +650,7 @@ int build_step(spd_handle* h, DescWriter& dw) {
   NucleusCut* cuts = h->at<NucleusCut>(p.o_cut);
   vd.nucleus = nucleus; vd.top_p = h->top_p;
   vd.cut[0] = cuts; vd.cut[1] = cuts + 1 + h->slot(dpos);
+  h->nucleus_scratch(vd);
   const size_t voff = dw.put(&vd, 1);
   h->ops.push_back({OP_VOCAB, voff, 1, kVocabBlocks, 0, 0.0});
   if (nucleus) h->ops.push_back({OP_NUCLEUS, voff, 1, kVocabBlocks, 0, 0.0});
@@ -867,6 +878,7 @@ int spd_prefill(spd_handle* h, const int32_t* prompt, int32_t len, int32_t* firs
       const bool nucleus = sampled && h->top_p < 1.f;
       vd.nucleus = nucleus; vd.top_p = h->top_p;
       vd.cut[0] = h->at<NucleusCut>(p.o_cut);
+      h->nucleus_scratch(vd);
       const size_t vo = dw.put(&vd, 1);
       FinalizeDesc fd{};
       fd.mode = 1; fd.dpos = len; fd.ring = p.ring; fd.V = p.V; fd.nblocks = kVocabBlocks;

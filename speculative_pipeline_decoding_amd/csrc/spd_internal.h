@@ -131,7 +131,17 @@ struct VocabDesc {
   int nucleus;                // T > 0 and top_p < 1: the Gumbel draw runs over the top-p set
   float top_p;
   NucleusCut* cut[2];         // where each active row's top-p set is written
+  unsigned long long* nuc_part;   // scratch: per-slice histograms [2][64][4096]
+  unsigned long long* nuc_hist;   // scratch: merged histograms [2][4096]
+  int2* nuc_cand;                 // scratch: listed (logit bits, id) [2][V]
+  int* nuc_cnt;                   // scratch: listed per slice [2][64]
+  float* nuc_max;                 // scratch: each row's largest logit [2]
 };
+
+// top-p scratch sizes (bytes), for the workspace plan
+constexpr size_t kNucPartBytes = (size_t)2 * 64 * 4096 * 8;
+constexpr size_t kNucHistBytes = (size_t)2 * 4096 * 8;
+constexpr size_t kNucCntBytes = (size_t)2 * 64 * 4 + 16;   // counts, then the two maxima
 
 struct VocabPartial {
   float max, second;          // raw logit max and runner-up

@@ -112,20 +112,33 @@ __global__ __launch_bounds__(kVocabBlock) void vocab_stats_kernel(const VocabDes
 // Masses are fixed point: w(z) = floor(exp((z - max) / T) 2^40) as a 64-bit integer,
 // so every sum is exact and independent of the order of the additions. A token is in
 // the set iff the mass ahead of it is < top_p W (W: the row's total), i.e. < ceil(top_p W).
-//   1. histogram of the mass over depth bins of (max - z) / T, 64 per unit (monotone in
-//      z); a block scan finds the bin where the running mass crosses the threshold;
-//   2. the tokens of that bin (in LDS when they fit) go through four 8-bit radix
-//      passes over the order-preserving integer key of z, each keeping the digit where
-//      the running mass crosses: the result is zb, the logit of the last token kept;
-//   3. of the tokens tied at zb the first j* in id order are kept, j* = ceil(rest / w(zb));
-//      when that splits the ties, a scan over id ranges names the last id kept.
-constexpr int kNucBins = 2 * kVocabBlock;   // depth bins
-constexpr int kNucList = 8192;              // crossing-bin tokens kept in LDS
+// Four launches, both rows at once:
+//   hist   (kNucBlocks blocks per row) the mass of each slice over depth bins of
+//          (max - z) / T, 256 per unit up to depth 16 (a bin index is monotone in z;
+//          fine bins keep the crossing bin's tokens few enough for LDS);
+//   merge  the slices' histograms, bin by bin;
+//   cand   every block finds the bin where the running mass crosses the threshold
+//          (a block scan of the merged histogram) and lists its slice's tokens in it;
+//   select (one block per row) four 8-bit radix passes over the order-preserving
+//          integer key of the listed logits, each keeping the digit where the running
+//          mass crosses, give zb, the logit of the last token kept; of the tokens tied
+//          at zb the first j* = ceil(rest / w(zb)) in id order are kept, and when that
+//          splits the ties a bisection over ids names the last one.
+constexpr int kNucBins = 4096;       // depth bins
+constexpr int kNucBlocks = 64;       // slices per row
+constexpr int kNucThreads = 256;
+constexpr int kNucMergeThreads = 64;
+constexpr int kNucList = 8192;       // listed tokens the select kernel keeps in LDS
+constexpr int kNucBatch = 10;        // logits a thread loads at once (a slice is <= 10 per thread
+                                     // at V = 151936)
+static_assert(kNucBlocks * kNucBins * 8 * 2 == kNucPartBytes, "top-p histogram scratch");
+static_assert(kNucBins * 8 * 2 == kNucHistBytes, "top-p merged histogram scratch");
+static_assert(kNucBins % kNucMergeThreads == 0, "merge grid");
 typedef unsigned long long u64;
 
 __device__ __forceinline__ int nuc_bin(float z, float M, float invT) {
   // explicitly rounded operations: every evaluation of a token's bin gives the same bin
-  const float b = __fmul_rn(__fmul_rn(__fsub_rn(M, z), invT), 64.f);
+  const float b = __fmul_rn(__fmul_rn(__fsub_rn(M, z), invT), 256.f);
   return b < (float)(kNucBins - 1) ? (int)b : kNucBins - 1;
 }
 __device__ __forceinline__ u64 nuc_weight(float z, float M, float invT) {
@@ -145,6 +158,7 @@ __device__ __forceinline__ u64 shfl_up64(u64 v, int d) {
   return ((u64)(uint32_t)hi << 32) | (uint32_t)lo;
 }
 // Exclusive prefix sum over the block in thread order; `total` gets the block's sum.
+// wsum holds one entry per wave.
 __device__ u64 block_excl_scan(u64 v, u64* wsum, u64& total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   u64 inc = v;
@@ -165,79 +179,205 @@ __device__ u64 block_excl_scan(u64 v, u64* wsum, u64& total) {
   return before + inc - v;
 }
 
-__global__ __launch_bounds__(kVocabBlock) void nucleus_kernel(const VocabDesc* __restrict__ dd,
-                                                               const VocabPartial* __restrict__ part) {
+// The row's largest logit, from the statistics partials (red: one float per wave).
+__device__ float row_max(const VocabPartial* part, int r, int nblocks, float* red) {
+  float m = -INFINITY;
+  for (int i = threadIdx.x; i < nblocks; i += blockDim.x) m = fmaxf(m, part[r * nblocks + i].max);
+  m = wave_max(m);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  float M = red[0];
+  for (int i = 1; i < (int)(blockDim.x >> 6); ++i) M = fmaxf(M, red[i]);
+  return M;
+}
+
+struct Crossing {
+  int bin;      // the bin holding the last token kept
+  u64 above;    // mass of the bins before it
+  u64 T;        // ceil(top_p W), at least 1 and at most W
+};
+// PER consecutive bins per thread, read once into registers.
+template <int PER>
+__device__ Crossing find_crossing(const u64* hist, float top_p, u64* wsum, Crossing* sh) {
+  const int b0 = threadIdx.x * PER;
+  if (threadIdx.x == 0) sh->bin = kNucBins - 1;
+  u64 h[PER];
+  u64 mine = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    h[j] = b0 + j < kNucBins ? hist[b0 + j] : 0ull;
+    mine += h[j];
+  }
+  u64 W;
+  u64 run = block_excl_scan(mine, wsum, W);
+  const double thr = ceil((double)top_p * (double)W);
+  const u64 T = thr < 1.0 ? 1ull : (thr >= (double)W ? W : (u64)thr);
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    if (run < T && T <= run + h[j]) { sh->bin = b0 + j; sh->above = run; }
+    run += h[j];
+  }
+  __syncthreads();
+  Crossing c = *sh;
+  c.T = T;
+  __syncthreads();
+  return c;
+}
+
+__global__ __launch_bounds__(kNucThreads) void nuc_hist_kernel(const VocabDesc* __restrict__ dd,
+                                                                const VocabPartial* __restrict__ part) {
   __shared__ u64 hist[kNucBins];
+  __shared__ float red[kNucThreads / 64];
+  const VocabDesc& d = *dd;
+  const int r = blockIdx.y, b = blockIdx.x;
+  if (!d.active[r]) return;
+  for (int i = threadIdx.x; i < kNucBins; i += blockDim.x) hist[i] = 0;
+  const float M = row_max(part, r, d.nblocks, red), invT = d.inv_temp;
+  if (b == 0 && threadIdx.x == 0) d.nuc_max[r] = M;    // for the kernels that follow
+  const int C = (d.V + kNucBlocks - 1) / kNucBlocks;
+  const int lo = min(d.V, b * C), hi = min(d.V, lo + C);
+  const float* z = d.logits[r];
+  // loads in batches of kNucBatch per thread, issued before any of them is used
+  for (int base = lo + threadIdx.x; base < hi; base += kNucBatch * kNucThreads) {
+    float v[kNucBatch];
+#pragma unroll
+    for (int k = 0; k < kNucBatch; ++k) {
+      const int i = base + k * kNucThreads;
+      v[k] = i < hi ? z[i] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < kNucBatch; ++k)
+      if (base + k * kNucThreads < hi) atomicAdd(&hist[nuc_bin(v[k], M, invT)], nuc_weight(v[k], M, invT));
+  }
+  __syncthreads();
+  u64* out = d.nuc_part + ((size_t)r * kNucBlocks + b) * kNucBins;
+  for (int i = threadIdx.x; i < kNucBins; i += blockDim.x) out[i] = hist[i];
+}
+
+__global__ __launch_bounds__(kNucMergeThreads) void nuc_merge_kernel(const VocabDesc* __restrict__ dd) {
+  const VocabDesc& d = *dd;
+  const int r = blockIdx.y;
+  if (!d.active[r]) return;
+  const int bin = blockIdx.x * blockDim.x + threadIdx.x;
+  const u64* p = d.nuc_part + (size_t)r * kNucBlocks * kNucBins + bin;
+  u64 s = 0;
+  for (int b = 0; b < kNucBlocks; ++b) s += p[(size_t)b * kNucBins];
+  d.nuc_hist[r * kNucBins + bin] = s;
+}
+
+__global__ __launch_bounds__(kNucThreads) void nuc_cand_kernel(const VocabDesc* __restrict__ dd,
+                                                                const VocabPartial* __restrict__ part) {
+  __shared__ u64 wsum[kNucThreads / 64];
+  __shared__ Crossing sh;
+  __shared__ int s_n;
+  const VocabDesc& d = *dd;
+  const int r = blockIdx.y, b = blockIdx.x;
+  if (!d.active[r]) return;
+  if (threadIdx.x == 0) s_n = 0;
+  const float M = d.nuc_max[r], invT = d.inv_temp;
+  const Crossing c = find_crossing<kNucBins / kNucThreads>(d.nuc_hist + r * kNucBins, d.top_p,
+                                                           wsum, &sh);
+  const int C = (d.V + kNucBlocks - 1) / kNucBlocks;
+  const int lo = min(d.V, b * C), hi = min(d.V, lo + C);
+  const float* z = d.logits[r];
+  int2* seg = d.nuc_cand + (size_t)r * d.V + lo;     // room for hi - lo entries
+  for (int base = lo + threadIdx.x; base < hi; base += kNucBatch * kNucThreads) {
+    float v[kNucBatch];
+#pragma unroll
+    for (int k = 0; k < kNucBatch; ++k) {
+      const int i = base + k * kNucThreads;
+      v[k] = i < hi ? z[i] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < kNucBatch; ++k) {
+      const int i = base + k * kNucThreads;
+      if (i < hi && nuc_bin(v[k], M, invT) == c.bin) {
+        const int n = atomicAdd(&s_n, 1);
+        seg[n] = make_int2(__float_as_int(v[k]), i);
+      }
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) d.nuc_cnt[r * kNucBlocks + b] = s_n;
+}
+
+__global__ __launch_bounds__(kVocabBlock) void nuc_select_kernel(const VocabDesc* __restrict__ dd,
+                                                                  const VocabPartial* __restrict__ part) {
   __shared__ float lz[kNucList];
+  __shared__ int lid[kNucList];
+  __shared__ u64 hist[256];
   __shared__ u64 wsum[kVocabBlock / 64];
-  __shared__ float red[kVocabBlock / 64];
-  __shared__ int s_bin, s_count, s_digit, s_id;
+  __shared__ Crossing sh;
+  __shared__ int s_off[kNucBlocks + 1];
+  __shared__ int s_digit;
   __shared__ u64 s_above, s_mass;
   const VocabDesc& d = *dd;
   const int r = blockIdx.x;
   if (!d.active[r]) return;
-  const float* z = d.logits[r];
   const int V = d.V, t = threadIdx.x, nthr = blockDim.x;
-  const float invT = d.inv_temp;
-  // the row's largest logit, from the statistics partials
-  float m = -INFINITY;
-  for (int i = t; i < d.nblocks; i += nthr) m = fmaxf(m, part[r * d.nblocks + i].max);
-  m = wave_max(m);
-  if ((t & 63) == 0) red[t >> 6] = m;
-  for (int b = t; b < kNucBins; b += nthr) hist[b] = 0;
-  if (t == 0) { s_count = 0; s_bin = kNucBins - 1; s_above = 0; s_digit = 0; s_mass = 0; s_id = INT_MAX; }
+  const float M = d.nuc_max[r], invT = d.inv_temp;
+  const Crossing c = find_crossing<kNucBins / kVocabBlock>(d.nuc_hist + r * kNucBins, d.top_p,
+                                                           wsum, &sh);
+  const int C = (V + kNucBlocks - 1) / kNucBlocks;
+  const int2* cand = d.nuc_cand + (size_t)r * V;
+  // where each slice's listed tokens start (the counts load in parallel, then one wave scans)
+  if (t < kNucBlocks) s_off[t + 1] = d.nuc_cnt[r * kNucBlocks + t];
+  if (t == 0) { s_off[0] = 0; s_digit = 0; s_above = c.above; s_mass = 0; }
   __syncthreads();
-  float M = red[0];
-  for (int i = 1; i < nthr / 64; ++i) M = fmaxf(M, red[i]);
-
-  // 1. mass per depth bin; bin 0 holds the largest logits
-  for (int i = t; i < V; i += nthr) {
-    const float v = z[i];
-    atomicAdd(&hist[nuc_bin(v, M, invT)], nuc_weight(v, M, invT));
+  if (t < 64) {
+    static_assert(kNucBlocks == 64, "one wave scans the slice counts");
+    int v = s_off[t + 1];
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(v, o);
+      if ((t & 63) >= o) v += u;
+    }
+    s_off[t + 1] = v;
   }
   __syncthreads();
-  const u64 h0 = hist[2 * t], h1 = hist[2 * t + 1];
-  u64 W;
-  const u64 ex = block_excl_scan(h0 + h1, wsum, W);
-  double thr = ceil((double)d.top_p * (double)W);
-  const u64 T = thr < 1.0 ? 1ull : (thr >= (double)W ? W : (u64)thr);
-  if (ex < T && T <= ex + h0) { s_bin = 2 * t; s_above = ex; }
-  else if (ex + h0 < T && T <= ex + h0 + h1) { s_bin = 2 * t + 1; s_above = ex + h0; }
-  __syncthreads();
-  const int bc = s_bin;
-  u64 above = s_above;
-
-  // 2. the crossing bin's tokens, then a radix select of the last key kept
-  for (int i = t; i < V; i += nthr) {
-    const float v = z[i];
-    if (nuc_bin(v, M, invT) == bc) {
-      const int k = atomicAdd(&s_count, 1);
-      if (k < kNucList) lz[k] = v;
+  const int total = s_off[kNucBlocks];
+  const bool in_lds = total <= kNucList;
+  if (in_lds) {
+    // listed token j lives in slice b with s_off[b] <= j < s_off[b + 1]
+    for (int j = t; j < total; j += nthr) {
+      int lo = 0, hi = kNucBlocks - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_off[mid] <= j) lo = mid; else hi = mid - 1;
+      }
+      const int2 e = cand[(size_t)lo * C + (j - s_off[lo])];
+      lz[j] = __int_as_float(e.x);
+      lid[j] = e.y;
     }
   }
   __syncthreads();
-  const int cnt = s_count;
-  const bool in_lds = cnt <= kNucList;
+  // every listed token once, over the block: f(logit, id)
+  auto visit = [&](auto&& f) {
+    if (in_lds) {
+      for (int j = t; j < total; j += nthr) f(lz[j], lid[j]);
+    } else {
+      for (int b = 0; b < kNucBlocks; ++b) {
+        const int n = s_off[b + 1] - s_off[b];
+        const int2* sg = cand + (size_t)b * C;
+        for (int j = t; j < n; j += nthr) {
+          const int2 e = sg[j];
+          f(__int_as_float(e.x), e.y);
+        }
+      }
+    }
+  };
+  const u64 T = c.T;
+  u64 above = c.above;
   uint32_t prefix = 0;
   u64 tie_mass = 0;
   for (int shift = 24; shift >= 0; shift -= 8) {
     if (t < 256) hist[t] = 0;
     __syncthreads();
     const uint32_t hmask = shift == 24 ? 0u : (0xffffffffu << (shift + 8));
-    if (in_lds) {
-      for (int j = t; j < cnt; j += nthr) {
-        const float v = lz[j];
-        const uint32_t k = f_key(v);
-        if ((k & hmask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], nuc_weight(v, M, invT));
-      }
-    } else {
-      for (int i = t; i < V; i += nthr) {
-        const float v = z[i];
-        if (nuc_bin(v, M, invT) != bc) continue;
-        const uint32_t k = f_key(v);
-        if ((k & hmask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], nuc_weight(v, M, invT));
-      }
-    }
+    visit([&](float v, int) {
+      const uint32_t k = f_key(v);
+      if ((k & hmask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], nuc_weight(v, M, invT));
+    });
     __syncthreads();
     // thread t holds digit 255 - t: the prefix sum in thread order is the mass of larger digits
     const u64 hv = t < 256 ? hist[255 - t] : 0ull;
@@ -253,27 +393,23 @@ __global__ __launch_bounds__(kVocabBlock) void nucleus_kernel(const VocabDesc* _
     __syncthreads();
   }
   const float zb = key_f(prefix);
-
-  // 3. ties at zb: the first j* of them (by id) are kept
+  // ties at zb (all of them are listed: equal logits share a bin): keep the first j*
   const u64 wb = nuc_weight(zb, M, invT);
-  const u64 c = wb ? tie_mass / wb : 0ull;
+  const u64 ties = wb ? tie_mass / wb : 0ull;
   const u64 js = wb ? (T - above + wb - 1) / wb : 0ull;
   int id_cut = INT_MAX;
-  if (js < c) {
-    const int C = (V + nthr - 1) / nthr;
-    const int lo = min(V, t * C), hi = min(V, lo + C);
-    int mine = 0;
-    for (int i = lo; i < hi; ++i) mine += z[i] == zb;
-    u64 all;
-    const u64 before = block_excl_scan((u64)mine, wsum, all);
-    const u64 want = js - 1;              // 0-based rank of the last tie kept
-    if (want >= before && want < before + (u64)mine) {
-      u64 k = before;
-      for (int i = lo; i < hi; ++i)
-        if (z[i] == zb) { if (k == want) { s_id = i; break; } ++k; }
+  if (js < ties) {
+    // smallest id X with at least j* tied tokens of id <= X
+    int lo = 0, hi = V - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      u64 n = 0;
+      visit([&](float v, int id) { n += (v == zb && id <= mid) ? 1ull : 0ull; });
+      u64 all;
+      (void)block_excl_scan(n, wsum, all);
+      if (all >= js) hi = mid; else lo = mid + 1;
     }
-    __syncthreads();
-    id_cut = s_id;
+    id_cut = lo;
   }
   if (t == 0) {
     NucleusCut out;
@@ -454,8 +590,12 @@ hipError_t launch_vocab_stats(const VocabDesc* d_desc, int nblocks, VocabPartial
 
 hipError_t launch_nucleus(const VocabDesc* d_desc, int nblocks, VocabPartial* part,
                           hipStream_t st, LaunchEv ev) {
-  const LaunchEv e1{ev.start, nullptr}, e2{nullptr, ev.stop};
-  SPD_LAUNCH(e1, nucleus_kernel, dim3(2), dim3(kVocabBlock), 0, st, d_desc, part);
+  const LaunchEv e1{ev.start, nullptr}, e0{nullptr, nullptr}, e2{nullptr, ev.stop};
+  SPD_LAUNCH(e1, nuc_hist_kernel, dim3(kNucBlocks, 2), dim3(kNucThreads), 0, st, d_desc, part);
+  SPD_LAUNCH(e0, nuc_merge_kernel, dim3(kNucBins / kNucMergeThreads, 2), dim3(kNucMergeThreads), 0,
+             st, d_desc);
+  SPD_LAUNCH(e0, nuc_cand_kernel, dim3(kNucBlocks, 2), dim3(kNucThreads), 0, st, d_desc, part);
+  SPD_LAUNCH(e0, nuc_select_kernel, dim3(2), dim3(kVocabBlock), 0, st, d_desc, part);
   SPD_LAUNCH(e2, nucleus_gumbel_kernel, dim3(nblocks), dim3(kVocabBlock), 0, st, d_desc, part);
   return hipGetLastError();
 }
