@@ -165,6 +165,39 @@ def cpu_baseline(cfg, W, T, seed, alpha, budget_s, top_p=1.0):
             "steps_per_s": steps_per_s}
 
 
+def stage_plan_report(cfg, dW, prompt, steps):
+    """Per-layer cost of one token through each target layer (the library at n = 1, where
+    every sub-layer launch serves one layer), and the stage split balanced on it against
+    the default split: per-stage time and its spread. With one GPU per stage, a pipeline
+    step lasts as long as its slowest stage."""
+    import numpy as np
+    from speculative_pipeline_decoding_amd import SPD, balance_stages
+    spd = SPD(cfg, dW, temperature=0.0, n=1)
+    spd.prefill(prompt)
+    spd.timing(True, serial=True)     # no launch shares the GPU with the PDM chain
+    for _ in range(steps):
+        spd.step()
+        spd.verify_commit()
+    ms, passes = spd.timing_read_layers()
+    spd.close()
+    us = 1e3 * ms / np.maximum(passes, 1)
+    n = cfg.n_stages
+
+    def stages(sizes):
+        b = np.concatenate([[0], np.cumsum(sizes)])
+        t = [float(us[b[i]:b[i + 1]].sum()) for i in range(n)]
+        return {"sizes": [int(x) for x in sizes], "stage_us": [round(x, 1) for x in t],
+                "max_us": round(max(t), 1), "spread": round(max(t) / min(t) - 1.0, 4)}
+
+    default = [len(a) for a in np.array_split(np.arange(cfg.n_layers), n)]
+    balanced = balance_stages(us, n)
+    kinds = np.asarray(cfg.kinds)
+    per_kind = {("linear" if k else "softmax"): round(float(us[kinds == k].mean()), 1)
+                for k in sorted(set(kinds.tolist()))}
+    return {"layer_us_per_token": per_kind, "passes": int(passes.min()),
+            "default": stages(default), "balanced": stages(balanced)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -178,6 +211,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--t0-run", action="store_true",
                     help="also time the same steps at T=0 (greedy, lossless) and report them")
+    ap.add_argument("--stage-plan", action="store_true",
+                    help="also time one token through each layer (n = 1) and report the "
+                         "stage split balanced on those costs against the default split")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -289,6 +325,9 @@ def main():
         "prefill_s": main_run["prefill_s"],
         "device": torch.cuda.get_device_name(0),
     }
+    if args.stage_plan:
+        res["stage_plan"] = stage_plan_report(cfg, dW, prompt, 24)
+        log(f"stage plan: {res['stage_plan']}")
     if not args.no_cpu_baseline:
         del dW
         torch.cuda.empty_cache()

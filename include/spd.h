@@ -56,8 +56,9 @@ enum { SPD_LAYER_SOFTMAX = 0, SPD_LAYER_LINEAR = 1 };
  * (pith.science review, "Assumptions & free parameters"): anchors B, pipeline
  * width n, speculation layers Ls, temperature T.
  *   n_layers = L; n_stages = n (1 <= n <= L);
- *   stage_layers [host, n entries, sum = L] or NULL for the default split
- *     (the first L mod n stages get ceil(L/n) layers);
+ *   stage_layers [host, n entries, each >= 1, sum = L, never larger than the entry
+ *     before it: a split with a larger later stage is SPD_E_CONFIG in this version] or
+ *     NULL for the default split (the first L mod n stages get ceil(L/n) layers);
  *   anchors [host, k entries]: depths b in [0, L], strictly ascending, anchors[0] == 0;
  *     anchor b is the residual stream after b target layers (b = 0: embedding);
  *   pdm_layers = Ls >= 1 (Ls > L/n is allowed: the PDM is then simply not
@@ -238,10 +239,42 @@ int spd_debug_copy(const spd_handle* h, int32_t what, void* host_dst, size_t byt
  * caller's stream; the PDM's run on a second, library-owned stream that forks
  * after the embedding and joins before the LM head, so their durations overlap.
  * Enabling or disabling clears the totals; a pending step gives SPD_E_STATE.
+ * on = 2 also runs the PDM's launches on the caller's stream, one after another with
+ * the target's, so that no launch shares the GPU with another (per-layer costs for
+ * spd_timing_read_layers); 1 keeps the two streams.
  */
 int spd_timing_enable(spd_handle* h, int on);
 int spd_timing_read(const spd_handle* h, int32_t kind, int64_t* count, double* total_ms,
                     double* bytes);
+/*
+ * Per-layer time, for planning stages (pith.science review of the paper: the referee's
+ * remarks on its Appendix C.1, non-uniform stage partitioning). While timing is enabled, the launches of a
+ * sub-layer round that carries a single token (every round at n = 1; the first rounds
+ * after a reseed at n > 1) serve one target layer alone; their durations add up per
+ * layer. total_ms [host, L] receives each layer's total kernel time and passes [host, L]
+ * the number of such single-token passes through it; the mean per pass is the cost of
+ * one token through that layer, which is one pipeline stage's unit of work when each
+ * stage has a GPU of its own. SPD_E_ARG for NULL arguments.
+ */
+int spd_timing_read_layers(const spd_handle* h, double* total_ms, int64_t* passes);
+
+/*
+ * Non-uniform stage partitioning (pith.science review of the paper: the referee's
+ * remarks on its Appendix C.1, and on the compute imbalance of mixed attention layers
+ * that its Section 6 admits). Splits n_layers layers, in order,
+ * into n_stages contiguous stages of at least one layer each, minimising the largest
+ * stage cost, where a stage's cost is the sum of layer_cost [host, n_layers] over its
+ * layers, added in double from its first layer upward. Among the splits that reach that
+ * minimum, it maximises the smallest stage cost; among those, the first stage takes as
+ * many layers as it can, then the second, and so on (with equal costs this is the
+ * default split: the first L mod n stages one layer larger). Writes stage_layers
+ * [host, n_stages]; spd_model_config accepts it when no stage is larger than the one
+ * before it. Host only; no device or handle is needed. SPD_E_ARG for NULL pointers,
+ * n_stages outside [1, n_layers], n_layers outside [1, 4096], or a cost that is
+ * negative, infinite or NaN.
+ */
+int spd_balance_stages(int32_t n_layers, const float* layer_cost, int32_t n_stages,
+                       int32_t* stage_layers);
 
 /* Return to the post-init state (no prefill); device buffers are reused. */
 int spd_reset(spd_handle* h);

@@ -8,7 +8,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from typing import Dict, Optional, Sequence
+from typing import Dict, List, Optional, Sequence
 
 import numpy as np
 
@@ -75,7 +75,7 @@ class Stats(ctypes.Structure):
 SYMBOLS = ["spd_workspace_bytes", "spd_init", "spd_init_error", "spd_prefill", "spd_step",
            "spd_verify_commit", "spd_get_stats", "spd_get_kv_lens", "spd_debug_size",
            "spd_debug_copy", "spd_reset", "spd_last_error", "spd_destroy", "spd_timing_enable",
-           "spd_timing_read"]
+           "spd_timing_read", "spd_timing_read_layers", "spd_balance_stages"]
 
 _lib = None
 
@@ -109,12 +109,26 @@ def load() -> ctypes.CDLL:
     L.spd_timing_enable.argtypes = [VP, I]
     L.spd_timing_read.argtypes = [VP, ctypes.c_int32, P(ctypes.c_int64), P(ctypes.c_double),
                                   P(ctypes.c_double)]
+    L.spd_timing_read_layers.argtypes = [VP, P(ctypes.c_double), P(ctypes.c_int64)]
+    L.spd_balance_stages.argtypes = [ctypes.c_int32, P(ctypes.c_float), ctypes.c_int32,
+                                     P(ctypes.c_int32)]
     for name in ("spd_init", "spd_prefill", "spd_step", "spd_verify_commit", "spd_get_stats",
                  "spd_get_kv_lens", "spd_debug_copy", "spd_reset", "spd_timing_enable",
-                 "spd_timing_read"):
+                 "spd_timing_read", "spd_timing_read_layers", "spd_balance_stages"):
         getattr(L, name).restype = I
     _lib = L
     return L
+
+
+def balance_stages(layer_cost: Sequence[float], n: int) -> List[int]:
+    """Stage sizes from per-layer costs (spd_balance_stages); host only."""
+    L = load()
+    cost = np.ascontiguousarray(layer_cost, dtype=np.float32)
+    out = (ctypes.c_int32 * n)()
+    rc = L.spd_balance_stages(cost.size, cost.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), n, out)
+    if rc != SPD_OK:
+        raise SpdError(rc, "spd_balance_stages: bad arguments")
+    return list(out)
 
 
 def _i32(vals) -> ctypes.Array:
@@ -264,8 +278,9 @@ class SPD:
     def reset(self):
         self._chk(self.L.spd_reset(self.h))
 
-    def timing(self, on: bool):
-        self._chk(self.L.spd_timing_enable(self.h, 1 if on else 0))
+    def timing(self, on, serial: bool = False):
+        """Per-launch timing on or off; serial also puts the PDM chain on the caller's stream."""
+        self._chk(self.L.spd_timing_enable(self.h, (2 if serial else 1) if on else 0))
 
     def timing_read(self):
         out = {}
@@ -274,6 +289,13 @@ class SPD:
             self._chk(self.L.spd_timing_read(self.h, k, ctypes.byref(c), ctypes.byref(ms), ctypes.byref(b)))
             out[name] = {"count": c.value, "ms": ms.value, "bytes": b.value}
         return out
+
+    def timing_read_layers(self):
+        """Per target layer: (total kernel ms, single-token passes)."""
+        ms = (ctypes.c_double * self.cfg.n_layers)()
+        passes = (ctypes.c_int64 * self.cfg.n_layers)()
+        self._chk(self.L.spd_timing_read_layers(self.h, ms, passes))
+        return np.array(ms[:]), np.array(passes[:])
 
     def close(self):
         if getattr(self, "h", None):

@@ -66,6 +66,7 @@ struct Op {
   double bytes;    // algorithmic HBM bytes (weights + KV) for the timing report
   int stream = 0;  // 0: the caller's stream, 1: the PDM stream
   int plan = 0;    // GEMV: kernel kind and workgroups (gemv_plan)
+  int layer = -1;  // the one target layer this launch serves, when only one token is in it
 };
 
 struct Plan {
@@ -128,6 +129,10 @@ bool plan_config(const spd_model_config* c, Plan& p, std::string& err) {
       s += p.sizes[i];
     }
     if (s != p.L) return bad("stage sizes must sum to n_layers");
+    // A split whose later stage is larger than an earlier one ended its first GPU run in a
+    // crash whose cause is not yet found; until it is, such splits are refused.
+    for (int i = 1; i < p.n; ++i)
+      if (p.sizes[i] > p.sizes[i - 1]) return bad("stage sizes must not increase along the pipeline");
   } else {
     for (int i = 0; i < p.n; ++i) p.sizes[i] = p.L / p.n + (i < p.L % p.n ? 1 : 0);
   }
@@ -229,8 +234,12 @@ struct spd_handle {
   std::vector<Op> ops;
   // timing
   bool timing = false;
+  bool serial = false;            // the PDM chain on the caller's stream (timing mode 2)
   std::vector<hipEvent_t> ev;
   std::vector<int> ev_kind;
+  std::vector<int> ev_layer;
+  std::vector<double> kl_ms;        // per target layer: kernel time of its single-token passes
+  std::vector<long long> kl_passes;
   std::vector<double> ev_bytes;
   double kt_ms[OP_NKINDS] = {};
   double kt_bytes[OP_NKINDS] = {};
@@ -343,7 +352,9 @@ void fill_rope(const Plan& p, std::vector<float2>& tab) {
     }
 }
 
-hipStream_t op_stream(const spd_handle* h, const Op& op) { return op.stream ? h->st2 : h->st; }
+hipStream_t op_stream(const spd_handle* h, const Op& op) {
+  return op.stream && !h->serial ? h->st2 : h->st;
+}
 
 int gemv_role(int kind) {
   switch (kind) {
@@ -414,6 +425,7 @@ int run_ops(spd_handle* h) {
       const LaunchEv ev{h->ev[2 * k], h->ev[2 * k + 1]};
       HIPCHK(h, run_op(h, op, ev));
       h->ev_kind.push_back(op.kind);
+      h->ev_layer.push_back(op.layer);
       h->ev_bytes.push_back(op.bytes);
       ++k;
     } else {
@@ -430,8 +442,14 @@ int collect_timing(spd_handle* h) {
     h->kt_ms[h->ev_kind[i]] += ms;
     h->kt_bytes[h->ev_kind[i]] += h->ev_bytes[i];
     h->kt_count[h->ev_kind[i]] += 1;
+    const int l = h->ev_layer[i];
+    if (l >= 0 && l < (int)h->kl_ms.size()) {
+      h->kl_ms[l] += ms;
+      if (h->ev_kind[i] == OP_GEMV_QKV) h->kl_passes[l] += 1;   // one per pass through the layer
+    }
   }
   h->ev_kind.clear();
+  h->ev_layer.clear();
   h->ev_bytes.clear();
   return SPD_OK;
 }
@@ -564,12 +582,16 @@ int build_step(spd_handle* h, DescWriter& dw) {
     std::vector<AttnProb> at;
     std::vector<LinProb> lin;
     double kvb = 0, linb = 0;
+    const size_t first_op = h->ops.size();
+    int round_layer = -1, round_tokens = 0;
     for (int j = 0; j < n_inf; ++j) {
       const Inflight f = h->F[j];
       if (p.sizes[f.stage] <= r) continue;
       const int l = p.starts[f.stage] + r;
       const int s = h->slot(f.pos);
       float* hv = hring + (size_t)s * p.d;
+      round_layer = l;
+      ++round_tokens;
       if (p.kind[l] == SPD_LAYER_LINEAR) {
         // q, k, v to the token's scratch row, then the recurrent step from the state
         // after pos - 1 to the state after pos
@@ -618,6 +640,9 @@ int build_step(spd_handle* h, DescWriter& dw) {
     push_gemv(OP_GEMV_O, o, 0);
     push_gemv(OP_GEMV_GU, gu, 0);
     push_gemv(OP_GEMV_DOWN, down, 0);
+    if (round_tokens == 1)   // these launches serve one layer alone: its per-layer time
+      for (size_t i = first_op; i < h->ops.size(); ++i)
+        if (h->ops[i].stream == 0) h->ops[i].layer = round_layer;
   }
   h->ops.push_back({OP_JOIN, 0, 0, 0, 0, 0.0});
 
@@ -1122,7 +1147,10 @@ int spd_timing_enable(spd_handle* h, int on) {
   if (!h) return SPD_E_ARG;
   if (h->state == spd_handle::S_PENDING) return fail(h, SPD_E_STATE, "a step is pending");
   h->timing = on != 0;
+  h->serial = on == 2;
   for (int i = 0; i < OP_NKINDS; ++i) { h->kt_ms[i] = 0; h->kt_bytes[i] = 0; h->kt_count[i] = 0; }
+  h->kl_ms.assign(h->p.L, 0.0);
+  h->kl_passes.assign(h->p.L, 0);
   // two events per timed launch of a step, created once and reused every step
   const size_t want = 2 * (size_t)(8 + 5 * (h->p.L + h->p.Ls));
   while (h->timing && h->ev.size() < want) {
@@ -1139,6 +1167,84 @@ int spd_timing_read(const spd_handle* h, int32_t kind, int64_t* count, double* t
   if (count) *count = h->kt_count[kind];
   if (total_ms) *total_ms = h->kt_ms[kind];
   if (bytes) *bytes = h->kt_bytes[kind];
+  return SPD_OK;
+}
+
+int spd_timing_read_layers(const spd_handle* h, double* total_ms, int64_t* passes) {
+  if (!h || !total_ms || !passes) return SPD_E_ARG;
+  for (int l = 0; l < h->p.L; ++l) {
+    total_ms[l] = l < (int)h->kl_ms.size() ? h->kl_ms[l] : 0.0;
+    passes[l] = l < (int)h->kl_passes.size() ? h->kl_passes[l] : 0;
+  }
+  return SPD_OK;
+}
+
+// ---- stage planning (host only) -----------------------------------------------------
+int spd_balance_stages(int32_t n_layers, const float* layer_cost, int32_t n_stages,
+                       int32_t* stage_layers) {
+  const int L = n_layers, n = n_stages;
+  if (!layer_cost || !stage_layers || L < 1 || L > 4096 || n < 1 || n > L) return SPD_E_ARG;
+  for (int l = 0; l < L; ++l)
+    if (!(layer_cost[l] >= 0.f) || !std::isfinite(layer_cost[l])) return SPD_E_ARG;
+  // cost of layers [i, j), summed in double from i upward
+  auto seg = [&](int i, int j) {
+    double s = 0.0;
+    for (int l = i; l < j; ++l) s += (double)layer_cost[l];
+    return s;
+  };
+  // ok[i * (n + 1) + k]: layers [i, L) split into exactly k stages, each of cost in [A, B]
+  std::vector<char> ok((size_t)(L + 1) * (n + 1));
+  auto solve = [&](double A, double B) {
+    std::fill(ok.begin(), ok.end(), 0);
+    ok[(size_t)L * (n + 1)] = 1;
+    for (int i = L - 1; i >= 0; --i) {
+      double s = 0.0;
+      for (int j = i + 1; j <= L; ++j) {
+        s += (double)layer_cost[j - 1];
+        if (s > B) break;
+        if (s < A) continue;
+        for (int k = 1; k <= n; ++k)
+          if (ok[(size_t)j * (n + 1) + k - 1]) ok[(size_t)i * (n + 1) + k] = 1;
+      }
+    }
+    return ok[n] != 0;
+  };
+  // both bounds of an optimal split are segment costs
+  std::vector<double> cand;
+  cand.reserve((size_t)L * (L + 1) / 2);
+  for (int i = 0; i < L; ++i) {
+    double s = 0.0;
+    for (int j = i; j < L; ++j) { s += (double)layer_cost[j]; cand.push_back(s); }
+  }
+  std::sort(cand.begin(), cand.end());
+  // 1. the smallest largest-stage cost B
+  size_t lo = 0, hi = cand.size() - 1;          // one stage per layer run is always possible
+  while (lo < hi) {
+    const size_t mid = (lo + hi) / 2;
+    if (solve(0.0, cand[mid])) hi = mid; else lo = mid + 1;
+  }
+  const double B = cand[lo];
+  // 2. with that, the largest smallest-stage cost A
+  lo = 0; hi = cand.size() - 1;
+  while (lo < hi) {
+    const size_t mid = (lo + hi + 1) / 2;
+    if (solve(cand[mid], B)) lo = mid; else hi = mid - 1;
+  }
+  const double A = cand[lo];
+  // 3. among splits within [A, B], each stage in turn takes as many layers as it can
+  solve(A, B);
+  int i = 0;
+  for (int st = 0; st < n; ++st) {
+    const int rest = n - st - 1;
+    int take = 0;
+    for (int j = L - rest; j > i; --j) {
+      const double c = seg(i, j);
+      if (c >= A && c <= B && ok[(size_t)j * (n + 1) + rest]) { take = j - i; break; }
+    }
+    if (take < 1) return SPD_E_ARG;   // unreachable for valid input
+    stage_layers[st] = take;
+    i += take;
+  }
   return SPD_OK;
 }
 

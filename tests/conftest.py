@@ -9,6 +9,10 @@ if ROOT not in sys.path:
 
 
 def pytest_configure(config):
+    # short tracebacks: a failure report must not print device tensors (their repr runs
+    # GPU work in a process whose device state may be what failed)
+    if config.option.tbstyle == "auto":
+        config.option.tbstyle = "short"
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: long CPU test, skipped unless SPD_SLOW=1")
 

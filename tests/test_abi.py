@@ -93,3 +93,40 @@ def test_null_handle_calls():
     assert L.spd_verify_commit(None, None) == binding.SPD_E_ARG
     assert L.spd_prefill(None, None, 0, None) == binding.SPD_E_ARG
     L.spd_destroy(None)
+
+
+def test_stage_planner_matches_the_oracle_bit_for_bit():
+    """spd_balance_stages is host code: it runs here. Same sizes as the oracle's planner."""
+    import numpy as np
+    from oracle.plan import balance_stages as oracle_plan
+    binding, L = _lib()
+    rng = np.random.default_rng(17)
+    cases = [([1.0] * 36, 8), ([1.0] * 32, 16), ([3, 1, 1, 1, 2, 2, 1, 1], 4)]
+    # the hybrid's pattern (three linear layers, then one softmax layer) at two costs
+    cases += [([1.1, 1.1, 1.1, 1.0] * 8, n) for n in (4, 8, 16)]
+    for _ in range(60):
+        Ln = int(rng.integers(1, 40))
+        n = int(rng.integers(1, min(Ln, 16) + 1))
+        costs = rng.choice([rng.uniform(0.5, 1.5, Ln), rng.integers(0, 5, Ln).astype(float)])
+        cases.append((list(costs), n))
+    for costs, n in cases:
+        assert binding.balance_stages(costs, n) == oracle_plan(costs, n), (costs, n)
+
+
+def test_stage_planner_rejects_bad_arguments():
+    binding, L = _lib()
+    for costs, n in [([1.0, 2.0], 3), ([1.0, 2.0], 0), ([1.0, float("nan")], 1),
+                     ([1.0, -1.0], 1), ([1.0, float("inf")], 2)]:
+        with pytest.raises(binding.SpdError):
+            binding.balance_stages(costs, n)
+
+
+def test_stage_split_with_a_larger_later_stage_is_refused():
+    binding, L = _lib()
+    import dataclasses
+    cfg = dataclasses.replace(get("mid_hybrid_bf16_L8_d256_n4"), stage_layers=(2, 3, 1, 2))
+    c, keep = binding.make_config(cfg)
+    assert L.spd_workspace_bytes(ctypes.byref(c)) == 0
+    cfg = dataclasses.replace(get("mid_hybrid_bf16_L8_d256_n4"), stage_layers=(3, 2, 2, 1))
+    c, keep = binding.make_config(cfg)
+    assert L.spd_workspace_bytes(ctypes.byref(c)) > 0

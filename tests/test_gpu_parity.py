@@ -101,6 +101,51 @@ def test_mid_top_p(name, top_p):
     assert rep["steps"] > 0
 
 
+@pytest.mark.skip(reason="its first GPU run (T=0) ended in a crash inside the test process "
+                         "whose cause is not found; splits with a larger later stage are "
+                         "refused by spd_init until it is")
+@pytest.mark.parametrize("T", [0.0, 1.0])
+def test_mid_hybrid_planned_uneven_split(T):
+    """A split from the stage planner that the default never makes ([2, 3, 1, 2] on the
+    8-layer hybrid): both sides run it, in lockstep."""
+    import dataclasses
+    from speculative_pipeline_decoding_amd import balance_stages
+    name = "mid_hybrid_bf16_L8_d256_n4"
+    cfg, W, prompt = workload(name)
+    sizes = balance_stages([3, 1, 1, 1, 2, 2, 1, 1], cfg.n_stages)
+    assert sizes == [2, 3, 1, 2]
+    cfg2 = dataclasses.replace(cfg, stage_layers=tuple(sizes))
+    print(f"[parity] {name} stages {sizes} T={T}", flush=True)
+    rep = run_parity(cfg2, W, dev_weights(name), prompt, T=T, seed=9)
+    print(f"[parity] -> {rep}", flush=True)
+    assert rep["steps"] > 0
+
+
+def test_layer_timing_single_token_passes():
+    """At n = 1 every sub-layer launch serves one layer: each layer gets one timed pass
+    per step, with a positive kernel time."""
+    from speculative_pipeline_decoding_amd import SPD
+    cfg, W, prompt = workload("mid_hybrid_bf16_L8_d256_n4")
+    streams = []
+    for serial in (True, None):
+        gpu = SPD(cfg, dev_weights("mid_hybrid_bf16_L8_d256_n4"), n=1)
+        toks = [gpu.prefill(prompt)]
+        if serial:
+            gpu.timing(True, serial=True)    # the PDM chain on the caller's stream
+        for _ in range(6):
+            gpu.step()
+            toks.append(gpu.verify_commit().token)
+        if serial:
+            ms, passes = gpu.timing_read_layers()
+        gpu.close()
+        streams.append(toks)
+    assert streams[0] == streams[1]          # one stream or two: the same tokens
+    print(f"[timing] per-layer us per pass {np.round(1e3 * ms / np.maximum(passes, 1), 1)}",
+          flush=True)
+    assert passes.tolist() == [6] * cfg.n_layers
+    assert np.all(ms > 0)
+
+
 def test_mid_forced_acceptance():
     from oracle.spd import ar_decode
     cfg, W, prompt = workload("mid_bf16_L6_d384_n3")
