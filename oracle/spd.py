@@ -27,6 +27,13 @@ Readings, where the pages leave a step open (each also listed in the design doc):
   R10 N excludes the prefill's first token; K counts every step;
   the embedding of the stage-0 token is part of the step's input state, so
   the newest PDM row sees it (depth 0).
+
+Output-state speculation, the ablation the pith.science review mentions against the
+input-state ("early start") schedule of its "Core claim": with speculate_from="output"
+the PDM runs after the step's target layers and reads each position's states at its
+depth after the step (one stage deeper; the exiting token at depth L), so it cannot
+overlap the step. A position whose depth reaches L in this step becomes a permanent PDM
+row in the same step. Everything else (drafting, verification, rollback) is unchanged.
 """
 from __future__ import annotations
 
@@ -77,7 +84,10 @@ class SPD:
     def __init__(self, cfg: ModelConfig, arrays: Dict[str, np.ndarray], sampling: Sampling,
                  n: Optional[int] = None, anchors: Optional[Sequence[int]] = None,
                  Ls: Optional[int] = None, fill: str = "clamp", ft=np.float64,
-                 model: Optional[Model] = None, record_logits: bool = True):
+                 model: Optional[Model] = None, record_logits: bool = True,
+                 speculate_from: str = "input"):
+        assert speculate_from in ("input", "output")
+        self.output_states = speculate_from == "output"
         self.cfg = cfg
         self.n = cfg.n_stages if n is None else n
         self.B = list(cfg.anchors if anchors is None else anchors)
@@ -163,31 +173,48 @@ class SPD:
         self.h[newest] = h0
         self.anch[newest] = {0: h0.copy()}
         self.depth[newest] = 0
-        # 2. PDM on the step's input states (early start)
-        rows = list(range(self.pdm_len, newest + 1))
-        depths = [self.depth.get(x, L) for x in rows]
-        Z = {x: self.feature(x) for x in rows}
-        for r in range(self.Ls):
-            for x in rows:
-                Z[x] = m.pdm.decode_layer(r, Z[x], x)
-        z_q = m.logits(Z[newest], "pdm.final_norm")
+        exiting = self.F[0][1] == n - 1
+
+        def pdm_pass():
+            """PDM over the rows pdm_len .. newest at the depths they have now."""
+            rows = list(range(self.pdm_len, newest + 1))
+            depths = [self.depth.get(x, L) for x in rows]
+            Z = {x: self.feature(x) for x in rows}
+            for r in range(self.Ls):
+                for x in rows:
+                    Z[x] = m.pdm.decode_layer(r, Z[x], x)
+            return rows, depths, m.logits(Z[newest], "pdm.final_norm")
+
+        def target_pass():
+            """Each in-flight token runs its stage's layers."""
+            for pos, st in self.F:
+                h = self.h[pos]
+                for l in range(self.starts[st], self.starts[st] + self.sizes[st]):
+                    h = m.target.decode_layer(l, h, pos)
+                    if (l + 1) in B:
+                        self.anch[pos][B.index(l + 1)] = h.copy()
+                    self.kv_len[l] = pos + 1
+                self.h[pos] = h
+                self.depth[pos] += self.sizes[st]
+
+        if self.output_states:
+            # 3, then 2: the PDM reads the states the step produced
+            target_pass()
+            rows, depths, z_q = pdm_pass()
+            # positions whose depth is L now (the exiting one included) become permanent
+            self.pdm_len = max(self.pdm_len, self.F[0][0] + (1 if exiting else 0))
+        else:
+            # 2. PDM on the step's input states (early start)
+            rows, depths, z_q = pdm_pass()
+            # positions whose depth is already L become permanent PDM rows
+            self.pdm_len = max(self.pdm_len, self.F[0][0])
+            # 3. target
+            target_pass()
         dpos = newest + 1
         d, q, dflag = select_draft(z_q, self.s, dpos)
         if q is not None:
             self.q[dpos] = q
             self.zq[dpos] = z_q
-        # positions whose depth is already L become permanent PDM rows
-        self.pdm_len = max(self.pdm_len, self.F[0][0])
-        # 3. target: each in-flight token runs its stage's layers
-        for pos, st in self.F:
-            h = self.h[pos]
-            for l in range(self.starts[st], self.starts[st] + self.sizes[st]):
-                h = m.target.decode_layer(l, h, pos)
-                if (l + 1) in B:
-                    self.anch[pos][B.index(l + 1)] = h.copy()
-                self.kv_len[l] = pos + 1
-            self.h[pos] = h
-            self.depth[pos] += self.sizes[st]
         self.K += 1
         rec = StepRecord(K=self.K, newest=newest, draft=d, draft_flag=dflag, exited=False,
                          draft_logits=z_q if self.record_logits else None,

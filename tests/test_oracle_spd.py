@@ -194,3 +194,51 @@ def test_anchor_clamp_rule():
     np.testing.assert_allclose(spd.feature(x0), Wr @ np.tile(g0, k), rtol=1e-12)
     spd.fill = "zero"
     np.testing.assert_allclose(spd.feature(x0), Wr[:, :d] @ g0, rtol=1e-12)
+
+
+# ---- output-state speculation (the ablation of the early start) ----------------------
+
+@pytest.mark.parametrize("name,ns", [("tiny", (1, 2, 3, 4)),
+                                     ("mid_hybrid_bf16_L8_d256_n4", (4,))])
+def test_output_states_lossless_at_temperature_zero(name, ns):
+    cfg, W, prompt = workload(name)
+    G = min(cfg.gen_len, 24)
+    ref = ar_decode(cfg, W, prompt, G=G)
+    for n in ns:
+        r = spd_run(cfg, W, prompt, G=G, n=n, speculate_from="output")
+        assert r.tokens == ref, n
+
+
+def test_output_states_forced_drafts_and_counting_identity():
+    cfg, W, prompt = workload("tiny")
+    ref = ar_decode(cfg, W, prompt, G=48)
+    for p in (0.0, 0.6, 1.0):
+        s = Sampling(forced_p=p, forced_ref=np.array(ref), forced_base=cfg.prompt_len, seed=4)
+        r = spd_run(cfg, W, prompt, G=40, sampling=s, n=3, speculate_from="output")
+        assert r.tokens == ref[:40]
+        _refills_identity(r, 3, 40)
+    r = spd_run(cfg, W, prompt, G=30, sampling=Sampling(temperature=1.0, seed=1), n=4,
+                speculate_from="output")
+    _refills_identity(r, 4, 30)
+
+
+@pytest.mark.parametrize("name,n", [("tiny", 2), ("mid_bf16_L7_d256_n3_uneven", 3),
+                                    ("mid_hybrid_bf16_L8_d256_n4", 4)])
+def test_output_states_read_one_stage_deeper(name, n):
+    """Every PDM row sits at the depth its token has after the step: the in-flight rows one
+    stage deeper than at the step's start, the exiting row at L (permanent at once)."""
+    cfg, W, prompt = workload(name)
+    P0 = len(prompt)
+    spd = SPD(cfg, W, Sampling(temperature=1.0, seed=3), n=n, speculate_from="output")
+    spd.prefill(prompt)
+    L, starts, sizes = cfg.n_layers, spd.starts, spd.sizes
+    for _ in range(24):
+        F_start = [tuple(f) for f in spd.F]
+        rec = spd.step()
+        want = [starts[st] + sizes[st] for _, st in F_start]          # L for the exiting one
+        assert rec.pdm_row_depths[-len(want):] == want
+        assert all(dep == L for dep in rec.pdm_row_depths[:-len(want)])
+        assert rec.pdm_row_depths[-1] == sizes[0]                     # the newest token
+        assert rec.pdm_len == P0 + spd.N                               # exited rows are final
+        kv = rec.kv_len
+        assert all(a >= b for a, b in zip(kv, kv[1:]))
