@@ -54,11 +54,13 @@ def pct(xs, q):
     return xs[i]
 
 
-def run_spd(cfg, dW, prompt, T, seed, warmup, steps, kernel_timing, top_p=1.0):
+def run_spd(cfg, dW, prompt, T, seed, warmup, steps, kernel_timing, top_p=1.0,
+            speculate_from="input"):
     import torch
     from speculative_pipeline_decoding_amd import SPD
     stream = torch.cuda.current_stream()
-    spd = SPD(cfg, dW, temperature=T, top_p=top_p, seed=seed, stream=stream)
+    spd = SPD(cfg, dW, temperature=T, top_p=top_p, seed=seed, stream=stream,
+              speculate_from=speculate_from)
     t = time.perf_counter()
     spd.prefill(prompt)
     torch.cuda.synchronize()
@@ -131,7 +133,7 @@ def traffic_from_profile(workload: str, kernel: str):
     return value
 
 
-def cpu_baseline(cfg, W, T, seed, alpha, budget_s, top_p=1.0):
+def cpu_baseline(cfg, W, T, seed, alpha, budget_s, top_p=1.0, speculate_from="input"):
     """The oracle as it stands, on the host cores, over a bounded sample of the same model."""
     import numpy as np
     from oracle.spd import SPD as OracleSPD
@@ -143,7 +145,8 @@ def cpu_baseline(cfg, W, T, seed, alpha, budget_s, top_p=1.0):
     except Exception:
         threads = os.cpu_count() or 1
     plen = 16
-    o = OracleSPD(cfg, W, Sampling(temperature=T, top_p=top_p, seed=seed))
+    o = OracleSPD(cfg, W, Sampling(temperature=T, top_p=top_p, seed=seed),
+                  speculate_from=speculate_from)
     t = time.perf_counter()
     o.prefill(make_prompt(cfg, length=plen))
     setup = time.perf_counter() - t
@@ -209,6 +212,9 @@ def main():
     ap.add_argument("--top-p", type=float, default=None,
                     help="top-p of the sampled run (default: the workload's, 1.0)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--speculate-from", choices=["input", "output"], default="input",
+                    help="input: the PDM beside the step on its input states (the method); "
+                         "output: after the step on its output states (the ablation)")
     ap.add_argument("--t0-run", action="store_true",
                     help="also time the same steps at T=0 (greedy, lossless) and report them")
     ap.add_argument("--stage-plan", action="store_true",
@@ -257,13 +263,14 @@ def main():
         del src, dst
 
     main_run = run_spd(cfg, dW, prompt, args.temperature, args.seed, args.warmup, args.steps, True,
-                       args.top_p)
+                       args.top_p, args.speculate_from)
     tm = main_run["timed"]
     log(f"T={args.temperature}: prefill {main_run['prefill_s']:.2f}s, timed {tm['K']} steps in "
         f"{tm['wall_s'] * 1e3:.1f} ms, N={tm['N']}")
     t0_run = None
     if args.t0_run and args.temperature != 0.0:
-        r = run_spd(cfg, dW, prompt, 0.0, args.seed, args.warmup, args.steps, False)
+        r = run_spd(cfg, dW, prompt, 0.0, args.seed, args.warmup, args.steps, False,
+                    speculate_from=args.speculate_from)
         rt = r["timed"]
         t0_run = {"temperature": 0.0, "tokens_per_s": rt["N"] / rt["wall_s"], "N": rt["N"],
                   "K": rt["K"], "alpha": rt["N"] / rt["K"], "s0": rt["N"] / rt["K"] * cfg.n_stages,
@@ -302,6 +309,7 @@ def main():
         "config": {"workload": cfg.name, "n": cfg.n_stages, "Ls": cfg.pdm_layers,
                    "anchors": list(cfg.anchors), "context": cfg.prompt_len + cfg.gen_len,
                    "prompt": cfg.prompt_len, "temperature": args.temperature, "top_p": args.top_p,
+                   "speculate_from": args.speculate_from,
                    "weights": "bf16 N(0,0.02) seeded", "kv_cache": "bf16",
                    "prompt_ids": "uniform random"},
         "roofline": {"bound": "hbm", "kernel": dominant,
@@ -332,7 +340,7 @@ def main():
         del dW
         torch.cuda.empty_cache()
         res["cpu_baseline"] = cpu_baseline(cfg, W, args.temperature, args.seed, alpha,
-                                           args.cpu_budget, args.top_p)
+                                           args.cpu_budget, args.top_p, args.speculate_from)
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)

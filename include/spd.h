@@ -50,6 +50,7 @@ enum {
 enum { SPD_F32 = 0, SPD_BF16 = 1 };                 /* weight (and KV cache) storage */
 enum { SPD_FILL_CLAMP = 0, SPD_FILL_ZERO = 1 };      /* anchors not computed yet */
 enum { SPD_LAYER_SOFTMAX = 0, SPD_LAYER_LINEAR = 1 };
+enum { SPD_SPEC_INPUT = 0, SPD_SPEC_OUTPUT = 1 };     /* which states the PDM reads */
 
 /*
  * Model and SPD configuration. Free parameters in the pages' notation
@@ -71,7 +72,13 @@ enum { SPD_LAYER_SOFTMAX = 0, SPD_LAYER_LINEAR = 1 };
  *     are always softmax;
  *   anchor_fill: how a PDM row fills anchors deeper than its current depth:
  *     SPD_FILL_CLAMP repeats the deepest computed anchor (default), SPD_FILL_ZERO uses 0;
- *   max_ctx: KV capacity in positions; every in-flight position must stay below it.
+ *   max_ctx: KV capacity in positions; every in-flight position must stay below it;
+ *   speculate_from: SPD_SPEC_INPUT (0, the method's early start, pith.science review
+ *     "Core claim"): the PDM reads the step's input states and runs alongside the step
+ *     on a second stream. SPD_SPEC_OUTPUT (1, the input- vs output-state ablation its
+ *     referee summary mentions): the PDM runs after the step's target layers on the
+ *     states they produced, one stage deeper (the exiting token at depth L, whose PDM
+ *     row becomes permanent in the same step), on the caller's stream.
  * Limits: d_model, d_ffn, n_q_heads*head_dim multiples of 8; head_dim in
  * {16, 32, 64, 80, 128} (bf16) or {16, 32, 64} (f32); n_q_heads a multiple of
  * n_kv_heads with at most 16 query heads per KV head; n <= 16; k <= 8; Ls <= 16.
@@ -88,6 +95,7 @@ typedef struct {
   int32_t pdm_layers;
   int32_t anchor_fill;
   int32_t max_ctx;
+  int32_t speculate_from;         /* SPD_SPEC_INPUT | SPD_SPEC_OUTPUT */
 } spd_model_config;
 
 /*
@@ -234,7 +242,8 @@ int spd_debug_copy(const spd_handle* h, int32_t what, void* host_dst, size_t byt
  * 1 PDM projection GEMV, 2 QKV GEMV, 3 attention, 4 linear attention, 5 O GEMV,
  * 6 gate/up GEMV, 7 down GEMV, 8 LM-head GEMV, 9 vocabulary stats, 10 verify,
  * 11 residual sample, then the PDM's own launches: 12 QKV GEMV, 13 attention,
- * 14 O GEMV, 15 gate/up GEMV, 16 down GEMV; 17 top-p sets (top_p < 1 only).
+ * 14 O GEMV, 15 gate/up GEMV, 16 down GEMV; 17 top-p sets (top_p < 1 only); 18 the PDM
+ * feature gather after the target layers (SPD_SPEC_OUTPUT only).
  * Kinds 0-11 and 17 except 1 run on the
  * caller's stream; the PDM's run on a second, library-owned stream that forks
  * after the embedding and joins before the LM head, so their durations overlap.

@@ -23,7 +23,7 @@ DBG = {"target_logits": 1, "draft_logits": 2, "h_ring": 3, "anchors": 4, "pdm_ro
 # launch kinds reported by spd_timing_read
 OP_NAMES = ["embed", "gemv_proj", "gemv_qkv", "attention", "linear", "gemv_o", "gemv_gate_up",
             "gemv_down", "gemv_head", "vocab", "finalize", "residual", "pdm_qkv", "pdm_attention",
-            "pdm_o", "pdm_gate_up", "pdm_down", "nucleus"]
+            "pdm_o", "pdm_gate_up", "pdm_down", "nucleus", "gather"]
 TENSORS = ("attn_norm", "w_qkv", "w_o", "ffn_norm", "w_gate", "w_up", "w_down")
 
 
@@ -41,7 +41,8 @@ class ModelConfig(ctypes.Structure):
                 ("layer_kind", ctypes.POINTER(ctypes.c_uint8)), ("n_stages", ctypes.c_int32),
                 ("stage_layers", ctypes.POINTER(ctypes.c_int32)), ("n_anchors", ctypes.c_int32),
                 ("anchors", ctypes.POINTER(ctypes.c_int32)), ("pdm_layers", ctypes.c_int32),
-                ("anchor_fill", ctypes.c_int32), ("max_ctx", ctypes.c_int32)]
+                ("anchor_fill", ctypes.c_int32), ("max_ctx", ctypes.c_int32),
+                ("speculate_from", ctypes.c_int32)]
 
 
 class Weights(ctypes.Structure):
@@ -137,7 +138,7 @@ def _i32(vals) -> ctypes.Array:
 
 
 def make_config(cfg, n: Optional[int] = None, anchors: Optional[Sequence[int]] = None,
-                Ls: Optional[int] = None, fill: str = "clamp"):
+                Ls: Optional[int] = None, fill: str = "clamp", speculate_from: str = "input"):
     """spd_model_config from a workload description; returns (struct, keep-alive list)."""
     n = cfg.n_stages if n is None else n
     anchors = list(cfg.anchors if anchors is None else anchors)
@@ -164,6 +165,7 @@ def make_config(cfg, n: Optional[int] = None, anchors: Optional[Sequence[int]] =
     c.pdm_layers = Ls
     c.anchor_fill = SPD_FILL_ZERO if fill == "zero" else SPD_FILL_CLAMP
     c.max_ctx = cfg.max_ctx
+    c.speculate_from = {"input": 0, "output": 1}[speculate_from]
     return c, keep
 
 
@@ -186,12 +188,13 @@ class SPD:
     def __init__(self, cfg, weights, temperature: float = 0.0, top_p: float = 1.0, seed: int = 0,
                  forced_p: Optional[float] = None, forced_ref: Optional[Sequence[int]] = None,
                  n: Optional[int] = None, anchors: Optional[Sequence[int]] = None,
-                 Ls: Optional[int] = None, fill: str = "clamp", stream=None):
+                 Ls: Optional[int] = None, fill: str = "clamp", stream=None,
+                 speculate_from: str = "input"):
         import torch
         self.L = load()
         self.cfg = cfg
         self._keep = []
-        self.c, keep = make_config(cfg, n, anchors, Ls, fill)
+        self.c, keep = make_config(cfg, n, anchors, Ls, fill, speculate_from)
         self._keep += keep
         self.n = self.c.n_stages
         self.Ls = self.c.pdm_layers

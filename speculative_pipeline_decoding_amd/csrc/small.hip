@@ -16,7 +16,9 @@ __device__ __forceinline__ void st(T* p, size_t i, float v) {
   else p[i] = v;
 }
 
-// Block 0 embeds the stage-0 token into its residual slot and anchor 0 (depth 0).
+// Block 0 embeds the stage-0 token into its residual slot and anchor 0 (depth 0),
+// unless this is a gather-only launch (the PDM reading output states gathers after the
+// target's layers, when the embedding is long done).
 // Block 1 + r * k + s copies segment s of PDM row r's feature: anchor segments in
 // ascending depth; a segment deeper than the row's current depth repeats its
 // deepest computed anchor (clamp) or is zero, as the host encoded in src.
@@ -35,6 +37,7 @@ __global__ __launch_bounds__(256) void embed_gather_kernel(const EmbedGather* __
   const int tok = e.tok_ring[e.newest_slot];
   const T* __restrict__ erow = E + (size_t)tok * d;
   if (blockIdx.x == 0) {
+    if (!e.embed_new) return;
     float* __restrict__ h = e.h_ring + (size_t)e.newest_slot * d;
     float* __restrict__ a0 = e.anchors + (size_t)e.newest_slot * e.k * d;
     for (int i = threadIdx.x; i < d; i += blockDim.x) {

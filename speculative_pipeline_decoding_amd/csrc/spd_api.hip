@@ -54,7 +54,7 @@ struct Inflight {
 // join before the LM head).
 enum OpKind { OP_EMBED = 0, OP_GEMV_PROJ, OP_GEMV_QKV, OP_ATTN, OP_LIN, OP_GEMV_O, OP_GEMV_GU,
               OP_GEMV_DOWN, OP_GEMV_HEAD, OP_VOCAB, OP_FINAL, OP_RESID, OP_PDM_QKV, OP_PDM_ATTN,
-              OP_PDM_O, OP_PDM_GU, OP_PDM_DOWN, OP_NUCLEUS, OP_NKINDS, OP_FORK = 100,
+              OP_PDM_O, OP_PDM_GU, OP_PDM_DOWN, OP_NUCLEUS, OP_GATHER, OP_NKINDS, OP_FORK = 100,
               OP_JOIN = 101 };
 
 struct Op {
@@ -75,6 +75,7 @@ struct Plan {
   int esz;
   float theta, eps;
   int fill;
+  int spec_output;   // the PDM reads the step's output states, after the target layers
   std::vector<int> kind, sizes, starts, anchors, ord;   // ord: index among softmax / linear layers
   int nsoft = 0, nlin = 0;
   int R = 0;   // sub-layer launches per step
@@ -94,6 +95,9 @@ bool plan_config(const spd_model_config* c, Plan& p, std::string& err) {
   p.hd = c->head_dim; p.F = c->d_ffn; p.V = c->vocab; p.n = c->n_stages; p.k = c->n_anchors;
   p.Ls = c->pdm_layers; p.max_ctx = c->max_ctx; p.theta = c->rope_theta; p.eps = c->rms_eps;
   p.fill = c->anchor_fill;
+  if (c->speculate_from != SPD_SPEC_INPUT && c->speculate_from != SPD_SPEC_OUTPUT)
+    return bad("speculate_from must be SPD_SPEC_INPUT or SPD_SPEC_OUTPUT");
+  p.spec_output = c->speculate_from == SPD_SPEC_OUTPUT;
   if (c->dtype != SPD_F32 && c->dtype != SPD_BF16) return bad("dtype must be SPD_F32 or SPD_BF16");
   p.bf16 = c->dtype == SPD_BF16;
   p.esz = p.bf16 ? 2 : 4;
@@ -391,6 +395,10 @@ hipError_t run_op(spd_handle* h, const Op& op, LaunchEv ev = {}) {
       // copies the whole block to the device for the launches that follow
       return launch_embed_gather(reinterpret_cast<const EmbedGather*>(h->d_hdesc + op.off),
                                  h->d_hdesc, d, h->desc_used, op.count, p.k, p.d, p.bf16, st, ev);
+    case OP_GATHER:
+      // gather-only (output states): the descriptor block is on the device by now
+      return launch_embed_gather(reinterpret_cast<const EmbedGather*>(d + op.off), nullptr,
+                                 nullptr, 0, op.count, p.k, p.d, p.bf16, st, ev);
     case OP_GEMV_PROJ: case OP_GEMV_QKV: case OP_GEMV_O: case OP_GEMV_GU: case OP_GEMV_DOWN:
     case OP_GEMV_HEAD: case OP_PDM_QKV: case OP_PDM_O: case OP_PDM_GU: case OP_PDM_DOWN:
       return launch_gemv(gemv_role(op.kind), reinterpret_cast<const GemvProb*>(d + op.off),
@@ -506,12 +514,19 @@ int build_step(spd_handle* h, DescWriter& dw) {
   eg.anchors = anch;
   eg.X = X;
   eg.newest_slot = h->slot(newest);
+  eg.embed_new = 1;
   eg.d = p.d; eg.k = p.k; eg.M = M;
+  const bool out_states = p.spec_output != 0;
   for (int r = 0; r < M; ++r) {
     const int x = h->pdm_len + r;
     eg.row_slot[r] = h->slot(x);
+    // the row's depth when the PDM reads it: at the step's start, or (output states)
+    // after its stage's layers
     int depth = p.L;
-    if (x >= first) depth = p.starts[h->F[x - first].stage];
+    if (x >= first) {
+      const int st = h->F[x - first].stage;
+      depth = p.starts[st] + (out_states ? p.sizes[st] : 0);
+    }
     int deepest = 0;
     for (int i = 0; i < p.k; ++i)
       if (p.anchors[i] <= depth) deepest = i;
@@ -519,18 +534,110 @@ int build_step(spd_handle* h, DescWriter& dw) {
       int src;
       if (p.anchors[i] <= depth) src = i;
       else src = p.fill == SPD_FILL_CLAMP ? deepest : -1;
-      if (x == newest && src == 0) src = -2;   // the newest g0 is embedded in this launch
+      // the newest g0 is embedded in this launch (input states); after the target layers
+      // it is read from its anchor slot like any other
+      if (!out_states && x == newest && src == 0) src = -2;
       eg.src[r][i] = (signed char)src;
     }
   }
-  h->ops.push_back({OP_EMBED, dw.put(&eg, 1), M, 0, 0, 0.0});
-  h->ops.push_back({OP_FORK, 0, 0, 0, 0, 0.0});
+  // the PDM chain: on its own stream beside the target (input states), or after the
+  // target's layers on the caller's stream (output states)
+  const int pdm_stream = out_states ? 0 : 1;
+  size_t gather_off = 0;
+  if (out_states) {
+    EmbedGather e0 = eg;
+    e0.M = 0;
+    h->ops.push_back({OP_EMBED, dw.put(&e0, 1), 0, 0, 0, 0.0});
+    eg.embed_new = 0;
+    gather_off = dw.put(&eg, 1);
+  } else {
+    h->ops.push_back({OP_EMBED, dw.put(&eg, 1), M, 0, 0, 0.0});
+    h->ops.push_back({OP_FORK, 0, 0, 0, 0, 0.0});
+  }
+  // 3. target sub-layers on the caller's stream: every in-flight token at layer
+  //    start(stage) + r, all stages in one launch per sub-layer op (output states: before
+  //    the PDM chain, which then reads what they produced)
+  const int n_inf = (int)h->F.size();
+  auto target_rounds = [&]() {
+    const int R = *std::max_element(p.sizes.begin(), p.sizes.end());
+    for (int r = 0; r < R; ++r) {
+      std::vector<GemvProb> qkv, o, gu, down;
+      std::vector<AttnProb> at;
+      std::vector<LinProb> lin;
+      double kvb = 0, linb = 0;
+      const size_t first_op = h->ops.size();
+      int round_layer = -1, round_tokens = 0;
+      for (int j = 0; j < n_inf; ++j) {
+        const Inflight f = h->F[j];
+        if (p.sizes[f.stage] <= r) continue;
+        const int l = p.starts[f.stage] + r;
+        const int s = h->slot(f.pos);
+        float* hv = hring + (size_t)s * p.d;
+        round_layer = l;
+        ++round_tokens;
+        if (p.kind[l] == SPD_LAYER_LINEAR) {
+          // q, k, v to the token's scratch row, then the recurrent step from the state
+          // after pos - 1 to the state after pos
+          float* lrow = lqkv + (size_t)j * p.linrows;
+          qkv.push_back(gemv(h->W(l, T_QKV), p.linrows, p.d, hv, 0, 1, EPI_STORE, lrow, 0,
+                             (const float*)h->W(l, T_ATTN_NORM), 0, p.eps));
+          LinProb lp{};
+          lp.qkv = lrow; lp.out = attn + (size_t)j * p.qo;
+          lp.s_prev = h->lin(l, h->slot(f.pos - 1)); lp.s_next = h->lin(l, h->slot(f.pos));
+          lin.push_back(lp);
+          linb += 2.0 * p.lin_state_bytes;
+        } else {
+          GemvProb q = gemv(h->W(l, T_QKV), p.qrows, p.d, hv, 0, 1, EPI_QKV, nullptr, 0,
+                            (const float*)h->W(l, T_ATTN_NORM), 0, p.eps);
+          q.aux = qbuf + (size_t)j * p.qo;
+          q.kv_k = h->kvK(l); q.kv_v = h->kvV(l);
+          q.pos0 = f.pos; q.hq = p.hq; q.hkv = p.hkv; q.hd = p.hd; q.max_ctx = p.max_ctx;
+          qkv.push_back(q);
+          AttnProb a{};
+          a.q = qbuf + (size_t)j * p.qo; a.out = attn + (size_t)j * p.qo;
+          a.q_stride = p.qo; a.out_stride = p.qo; a.nrows = 1;
+          a.K = h->kvK(l); a.V = h->kvV(l); a.len = f.pos + 1;
+          at.push_back(a);
+          kvb += 2.0 * (f.pos + 1) * p.hkv * p.hd * p.esz;
+        }
+        o.push_back(gemv(h->W(l, T_O), p.d, p.qo, attn + (size_t)j * p.qo, 0, 1, EPI_ADD, hv, 0,
+                         nullptr, 0, 0.f));
+        GemvProb g = gemv(h->W(l, T_GATE), p.F, p.d, hv, 0, 1, EPI_SWIGLU, act + (size_t)j * p.F, 0,
+                          (const float*)h->W(l, T_FFN_NORM), 0, p.eps);
+        g.W2 = h->W(l, T_UP);
+        gu.push_back(g);
+        GemvProb dn = gemv(h->W(l, T_DOWN), p.d, p.F, act + (size_t)j * p.F, 0, 1, EPI_ADD, hv, 0,
+                           nullptr, 0, 0.f);
+        for (int i = 0; i < p.k; ++i)
+          if (p.anchors[i] == l + 1) dn.aux = anch + ((size_t)s * p.k + i) * p.d;
+        down.push_back(dn);
+        h->pend_layers.push_back({l, f.pos});
+      }
+      push_gemv(OP_GEMV_QKV, qkv, 0);
+      push_attn(OP_ATTN, at, 0, 0, kvb);
+      if (!lin.empty()) {
+        Op op{OP_LIN, dw.put(lin.data(), (int)lin.size()), (int)lin.size(), (int)lin.size() * p.hq,
+              0, linb};
+        h->ops.push_back(op);
+      }
+      push_gemv(OP_GEMV_O, o, 0);
+      push_gemv(OP_GEMV_GU, gu, 0);
+      push_gemv(OP_GEMV_DOWN, down, 0);
+      if (round_tokens == 1)   // these launches serve one layer alone: its per-layer time
+        for (size_t i = first_op; i < h->ops.size(); ++i)
+          if (h->ops[i].stream == 0) h->ops[i].layer = round_layer;
+    }
+  };
+  if (out_states) {
+    target_rounds();
+    h->ops.push_back({OP_GATHER, gather_off, M, 0, 0, 0.0});
+  }
 
-  // 2. the PDM chain on its own stream: projection of the gathered features, then Ls
-  //    decoder layers over the M window rows (decode rows n .. n + M - 1)
+  // 2. the PDM chain: projection of the gathered features, then Ls decoder layers over
+  //    the M window rows (decode rows n .. n + M - 1)
   {
     std::vector<GemvProb> g{gemv(h->proj, p.d, kd, X, kd, M, EPI_STORE, hp, p.d, nullptr, 0, 0.f)};
-    push_gemv(OP_GEMV_PROJ, g, 1);
+    push_gemv(OP_GEMV_PROJ, g, pdm_stream);
   }
   const int base = p.n;
   for (int r = 0; r < p.Ls; ++r) {
@@ -566,85 +673,17 @@ int build_step(spd_handle* h, DescWriter& dw) {
     gu.push_back(g);
     down.push_back(gemv(h->PW(r, T_DOWN), p.d, p.F, act + (size_t)(base + r0) * p.F, p.F, nr,
                         EPI_ADD, hrow, p.d, nullptr, 0, 0.f));
-    push_gemv(OP_PDM_QKV, qkv, 1);
-    push_attn(OP_PDM_ATTN, at, 1, p.n, kvb);
-    push_gemv(OP_PDM_O, o, 1);
-    push_gemv(OP_PDM_GU, gu, 1);
-    push_gemv(OP_PDM_DOWN, down, 1);
+    push_gemv(OP_PDM_QKV, qkv, pdm_stream);
+    push_attn(OP_PDM_ATTN, at, pdm_stream, p.n, kvb);
+    push_gemv(OP_PDM_O, o, pdm_stream);
+    push_gemv(OP_PDM_GU, gu, pdm_stream);
+    push_gemv(OP_PDM_DOWN, down, pdm_stream);
   }
 
-  // 3. target sub-layers on the caller's stream: every in-flight token at layer
-  //    start(stage) + r, all stages in one launch per sub-layer op
-  const int n_inf = (int)h->F.size();
-  const int R = *std::max_element(p.sizes.begin(), p.sizes.end());
-  for (int r = 0; r < R; ++r) {
-    std::vector<GemvProb> qkv, o, gu, down;
-    std::vector<AttnProb> at;
-    std::vector<LinProb> lin;
-    double kvb = 0, linb = 0;
-    const size_t first_op = h->ops.size();
-    int round_layer = -1, round_tokens = 0;
-    for (int j = 0; j < n_inf; ++j) {
-      const Inflight f = h->F[j];
-      if (p.sizes[f.stage] <= r) continue;
-      const int l = p.starts[f.stage] + r;
-      const int s = h->slot(f.pos);
-      float* hv = hring + (size_t)s * p.d;
-      round_layer = l;
-      ++round_tokens;
-      if (p.kind[l] == SPD_LAYER_LINEAR) {
-        // q, k, v to the token's scratch row, then the recurrent step from the state
-        // after pos - 1 to the state after pos
-        float* lrow = lqkv + (size_t)j * p.linrows;
-        qkv.push_back(gemv(h->W(l, T_QKV), p.linrows, p.d, hv, 0, 1, EPI_STORE, lrow, 0,
-                           (const float*)h->W(l, T_ATTN_NORM), 0, p.eps));
-        LinProb lp{};
-        lp.qkv = lrow; lp.out = attn + (size_t)j * p.qo;
-        lp.s_prev = h->lin(l, h->slot(f.pos - 1)); lp.s_next = h->lin(l, h->slot(f.pos));
-        lin.push_back(lp);
-        linb += 2.0 * p.lin_state_bytes;
-      } else {
-        GemvProb q = gemv(h->W(l, T_QKV), p.qrows, p.d, hv, 0, 1, EPI_QKV, nullptr, 0,
-                          (const float*)h->W(l, T_ATTN_NORM), 0, p.eps);
-        q.aux = qbuf + (size_t)j * p.qo;
-        q.kv_k = h->kvK(l); q.kv_v = h->kvV(l);
-        q.pos0 = f.pos; q.hq = p.hq; q.hkv = p.hkv; q.hd = p.hd; q.max_ctx = p.max_ctx;
-        qkv.push_back(q);
-        AttnProb a{};
-        a.q = qbuf + (size_t)j * p.qo; a.out = attn + (size_t)j * p.qo;
-        a.q_stride = p.qo; a.out_stride = p.qo; a.nrows = 1;
-        a.K = h->kvK(l); a.V = h->kvV(l); a.len = f.pos + 1;
-        at.push_back(a);
-        kvb += 2.0 * (f.pos + 1) * p.hkv * p.hd * p.esz;
-      }
-      o.push_back(gemv(h->W(l, T_O), p.d, p.qo, attn + (size_t)j * p.qo, 0, 1, EPI_ADD, hv, 0,
-                       nullptr, 0, 0.f));
-      GemvProb g = gemv(h->W(l, T_GATE), p.F, p.d, hv, 0, 1, EPI_SWIGLU, act + (size_t)j * p.F, 0,
-                        (const float*)h->W(l, T_FFN_NORM), 0, p.eps);
-      g.W2 = h->W(l, T_UP);
-      gu.push_back(g);
-      GemvProb dn = gemv(h->W(l, T_DOWN), p.d, p.F, act + (size_t)j * p.F, 0, 1, EPI_ADD, hv, 0,
-                         nullptr, 0, 0.f);
-      for (int i = 0; i < p.k; ++i)
-        if (p.anchors[i] == l + 1) dn.aux = anch + ((size_t)s * p.k + i) * p.d;
-      down.push_back(dn);
-      h->pend_layers.push_back({l, f.pos});
-    }
-    push_gemv(OP_GEMV_QKV, qkv, 0);
-    push_attn(OP_ATTN, at, 0, 0, kvb);
-    if (!lin.empty()) {
-      Op op{OP_LIN, dw.put(lin.data(), (int)lin.size()), (int)lin.size(), (int)lin.size() * p.hq,
-            0, linb};
-      h->ops.push_back(op);
-    }
-    push_gemv(OP_GEMV_O, o, 0);
-    push_gemv(OP_GEMV_GU, gu, 0);
-    push_gemv(OP_GEMV_DOWN, down, 0);
-    if (round_tokens == 1)   // these launches serve one layer alone: its per-layer time
-      for (size_t i = first_op; i < h->ops.size(); ++i)
-        if (h->ops[i].stream == 0) h->ops[i].layer = round_layer;
+  if (!out_states) {
+    target_rounds();
+    h->ops.push_back({OP_JOIN, 0, 0, 0, 0, 0.0});
   }
-  h->ops.push_back({OP_JOIN, 0, 0, 0, 0, 0.0});
 
   // 4. one sweep of the tied LM head: the exiting token's row and the PDM's newest row
   float* qnew = qring + (size_t)h->slot(dpos) * p.V;
@@ -998,7 +1037,9 @@ int spd_verify_commit(spd_handle* h, spd_commit* out) {
   const Plan& p = h->p;
   h->K += 1;
   for (auto& lp : h->pend_layers) h->kv_len[lp.first] = lp.second + 1;
-  h->pdm_len = std::max(h->pdm_len, h->F.front().pos);
+  // rows whose depth is L are final: those before the oldest in flight, and (output
+  // states) the exiting one, whose row the PDM read at depth L in this step
+  h->pdm_len = std::max(h->pdm_len, h->F.front().pos + (p.spec_output && h->pend_exit ? 1 : 0));
   for (auto& f : h->F) f.stage += 1;
   spd_commit c{};
   c.newest = h->pend_newest;

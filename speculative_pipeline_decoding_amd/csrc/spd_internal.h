@@ -99,6 +99,7 @@ struct EmbedGather {
   float* anchors;             // [ring][k][d]
   float* X;                   // [M][k * d] gathered PDM features
   int newest_slot;
+  int embed_new;              // 1: block 0 embeds the newest token (0: a gather-only launch)
   int d, k, M;
   int row_slot[kMaxRows];     // ring slot of PDM row r
   signed char src[kMaxRows][kMaxAnchors];  // anchor index feeding segment i; -1: zeros; -2: newest g0

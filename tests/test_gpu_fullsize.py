@@ -70,10 +70,10 @@ def test_fullsize_lockstep_with_oracle(wl, T, seed):
     assert rep["steps"] >= cfg.n_stages or rep["stopped_at_near_tie"] is not None
 
 
-def _stream(name, dW, n, T, G, seed=0):
+def _stream(name, dW, n, T, G, seed=0, speculate_from="input"):
     from speculative_pipeline_decoding_amd import SPD
     cfg, _, prompt = workload(name)
-    gpu = SPD(cfg, dW, temperature=T, seed=seed, n=n)
+    gpu = SPD(cfg, dW, temperature=T, seed=seed, n=n, speculate_from=speculate_from)
     toks = [(gpu.prefill(prompt), 0)]
     steps = []
     while len(toks) < G:
@@ -150,3 +150,27 @@ def test_fullsize_top_p_sets(wl):
             assert keep[c.token], f"step {k}: committed {c.token} outside the target's set"
     gpu.close()
     print(f"[fullsize] draft set sizes {sizes[:4]} ... of V={cfg.vocab}", flush=True)
+
+
+def test_fullsize_output_states_lossless(wl):
+    """Output-state speculation at full size: the T=0 stream still equals autoregressive
+    decoding (the library at n = 1), and the counting identity holds at T=1."""
+    name, dW, _ = wl
+    cfg, _, _ = workload(name)
+    n = cfg.n_stages
+    print(f"[fullsize] output states, {name}", flush=True)
+    a, _, _ = _stream(name, dW, n, 0.0, 32, speculate_from="output")
+    b, _, _ = _stream(name, dW, 1, 0.0, 32)
+    for i, ((ta, fa), (tb, fb)) in enumerate(zip(a, b)):
+        if fa or fb:
+            print(f"[fullsize] near-tie flagged at commit {i}; compared {i} tokens", flush=True)
+            break
+        assert ta == tb, f"commit {i}: output states give {ta}, n=1 gives {tb}"
+    toks, steps, st = _stream(name, dW, n, 1.0, 16, seed=5, speculate_from="output")
+    rejects = [i for i, (v, acc, _, _) in enumerate(steps) if v and not acc]
+    r_prime = len(rejects) - (1 if rejects and rejects[-1] == len(steps) - 1 else 0)
+    N = sum(1 for v, _, _, _ in steps if v)
+    assert len(steps) == N + (n - 1) * (1 + r_prime)
+    for v, acc, kv, pl in steps:
+        assert all(x >= y for x, y in zip(kv, kv[1:]))
+        assert pl <= kv[-1]

@@ -146,6 +146,28 @@ def test_layer_timing_single_token_passes():
     assert np.all(ms > 0)
 
 
+@pytest.mark.parametrize("name,kw", [("tiny", {}), ("tiny", {"T": 1.0, "seed": 3}),
+                                     ("tiny", {"n": 1, "G": 30}),
+                                     ("mid_bf16_L6_d384_n3", {}),
+                                     ("mid_bf16_L6_d384_n3", {"T": 1.0, "seed": 7}),
+                                     ("mid_hybrid_bf16_L8_d256_n4", {}),
+                                     ("mid_bf16_L7_d256_n3_uneven", {"T": 1.0, "seed": 2})])
+def test_output_state_speculation(name, kw):
+    """The PDM after the step's target layers, on their output states (the ablation of
+    the early start): lockstep with the oracle in the same mode."""
+    rep = _run(name, speculate_from="output", **kw)
+    assert rep["steps"] > 0
+
+
+def test_output_state_speculation_forced_rollbacks():
+    from oracle.spd import ar_decode
+    cfg, W, prompt = workload("mid_hybrid_bf16_L8_d256_n4")
+    ref = ar_decode(cfg, W, prompt, G=cfg.gen_len + 8)
+    rep = _run("mid_hybrid_bf16_L8_d256_n4", forced_p=0.5, forced_ref=ref, seed=4,
+               speculate_from="output")
+    assert rep["stopped_at_near_tie"] is None and rep["rejected"] > 2
+
+
 def test_mid_forced_acceptance():
     from oracle.spd import ar_decode
     cfg, W, prompt = workload("mid_bf16_L6_d384_n3")
