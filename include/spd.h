@@ -57,9 +57,8 @@ enum { SPD_SPEC_INPUT = 0, SPD_SPEC_OUTPUT = 1 };     /* which states the PDM re
  * (pith.science review, "Assumptions & free parameters"): anchors B, pipeline
  * width n, speculation layers Ls, temperature T.
  *   n_layers = L; n_stages = n (1 <= n <= L);
- *   stage_layers [host, n entries, each >= 1, sum = L, never larger than the entry
- *     before it: a split with a larger later stage is SPD_E_CONFIG in this version] or
- *     NULL for the default split (the first L mod n stages get ceil(L/n) layers);
+ *   stage_layers [host, n entries, each >= 1, sum = L] or NULL for the default split
+ *     (the first L mod n stages get ceil(L/n) layers);
  *   anchors [host, k entries]: depths b in [0, L], strictly ascending, anchors[0] == 0;
  *     anchor b is the residual stream after b target layers (b = 0: embedding);
  *   pdm_layers = Ls >= 1 (Ls > L/n is allowed: the PDM is then simply not
@@ -277,8 +276,8 @@ int spd_timing_read_layers(const spd_handle* h, double* total_ms, int64_t* passe
  * minimum, it maximises the smallest stage cost; among those, the first stage takes as
  * many layers as it can, then the second, and so on (with equal costs this is the
  * default split: the first L mod n stages one layer larger). Writes stage_layers
- * [host, n_stages]; spd_model_config accepts it when no stage is larger than the one
- * before it. Host only; no device or handle is needed. SPD_E_ARG for NULL pointers,
+ * [host, n_stages], suitable for spd_model_config's stage_layers. Host only; no device
+ * or handle is needed. SPD_E_ARG for NULL pointers,
  * n_stages outside [1, n_layers], n_layers outside [1, 4096], or a cost that is
  * negative, infinite or NaN.
  */

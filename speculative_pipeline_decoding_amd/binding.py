@@ -88,6 +88,14 @@ def load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
                           "`python -m speculative_pipeline_decoding_amd.build` (no fallback exists)")
+    # One HIP runtime per process: torch ships its own libamdhip64.so.7, and libspd.so needs a
+    # library of that name. Loaded first, libspd.so would pull in the system copy, and torch
+    # imported later would bind to it instead of its own (its GPU ops then crash). Importing
+    # torch first makes libspd.so use torch's copy.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     L = ctypes.CDLL(LIB_PATH)
     P, I, VP = ctypes.POINTER, ctypes.c_int, ctypes.c_void_p
     L.spd_workspace_bytes.argtypes = [P(ModelConfig)]

@@ -133,10 +133,6 @@ bool plan_config(const spd_model_config* c, Plan& p, std::string& err) {
       s += p.sizes[i];
     }
     if (s != p.L) return bad("stage sizes must sum to n_layers");
-    // A split whose later stage is larger than an earlier one ended its first GPU run in a
-    // crash whose cause is not yet found; until it is, such splits are refused.
-    for (int i = 1; i < p.n; ++i)
-      if (p.sizes[i] > p.sizes[i - 1]) return bad("stage sizes must not increase along the pipeline");
   } else {
     for (int i = 0; i < p.n; ++i) p.sizes[i] = p.L / p.n + (i < p.L % p.n ? 1 : 0);
   }

@@ -121,12 +121,24 @@ def test_stage_planner_rejects_bad_arguments():
             binding.balance_stages(costs, n)
 
 
-def test_stage_split_with_a_larger_later_stage_is_refused():
+def test_explicit_stage_splits():
     binding, L = _lib()
     import dataclasses
-    cfg = dataclasses.replace(get("mid_hybrid_bf16_L8_d256_n4"), stage_layers=(2, 3, 1, 2))
-    c, keep = binding.make_config(cfg)
-    assert L.spd_workspace_bytes(ctypes.byref(c)) == 0
-    cfg = dataclasses.replace(get("mid_hybrid_bf16_L8_d256_n4"), stage_layers=(3, 2, 2, 1))
-    c, keep = binding.make_config(cfg)
-    assert L.spd_workspace_bytes(ctypes.byref(c)) > 0
+    base = get("mid_hybrid_bf16_L8_d256_n4")
+    for ok in [(2, 3, 1, 2), (3, 2, 2, 1), (1, 1, 1, 5)]:
+        c, keep = binding.make_config(dataclasses.replace(base, stage_layers=ok))
+        assert L.spd_workspace_bytes(ctypes.byref(c)) > 0, ok
+    for bad in [(2, 3, 1, 1), (0, 4, 2, 2), (2, 2, 2, 3)]:
+        c, keep = binding.make_config(dataclasses.replace(base, stage_layers=bad))
+        assert L.spd_workspace_bytes(ctypes.byref(c)) == 0, bad
+
+
+def test_binding_loads_torch_before_the_library():
+    """libspd.so must bind to the HIP runtime torch already loaded (one per process)."""
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "from speculative_pipeline_decoding_amd import binding\n"
+            "binding.load()\n"
+            "assert 'torch' in sys.modules\n") % ROOT
+    subprocess.run([sys.executable, "-c", code], check=True, timeout=300)

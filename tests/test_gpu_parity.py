@@ -101,9 +101,6 @@ def test_mid_top_p(name, top_p):
     assert rep["steps"] > 0
 
 
-@pytest.mark.skip(reason="its first GPU run (T=0) ended in a crash inside the test process "
-                         "whose cause is not found; splits with a larger later stage are "
-                         "refused by spd_init until it is")
 @pytest.mark.parametrize("T", [0.0, 1.0])
 def test_mid_hybrid_planned_uneven_split(T):
     """A split from the stage planner that the default never makes ([2, 3, 1, 2] on the
