@@ -218,6 +218,19 @@ struct spd_handle {
   char* h_desc = nullptr;          // pinned staging of the step's descriptor block
   char* d_hdesc = nullptr;         // its device view
   size_t desc_used = 0;            // bytes of the current step's block
+  // two staging blocks: while a step runs, the next one (when nothing exits, its state
+  // is known at launch) is built into the other block, off the critical path
+  char* h_desc_base = nullptr;
+  char* d_hdesc_base = nullptr;
+  int next_buf = 0;
+  bool pre_valid = false;
+  std::deque<Inflight> pre_F;      // the state the prebuilt step was built for
+  int pre_pdm_len = 0;
+  std::vector<Op> pre_ops;
+  std::vector<std::pair<int, int>> pre_layers;
+  bool pre_exit = false;
+  int pre_v = 0, pre_dpos = 0, pre_newest = 0;
+  size_t pre_used = 0;
   Verdict* h_verdict = nullptr;   // pinned; written by the verdict kernels through d_hverdict
   Verdict* d_hverdict = nullptr;
   // state machine
@@ -802,7 +815,7 @@ int spd_init(const spd_model_config* cfg, const spd_weights* w, const spd_sampli
   h->kv_len.assign(p.L, 0);
   auto dev_fail = [&](hipError_t e, const char* what) {
     g_init_error = std::string(what) + ": " + hipGetErrorString(e);
-    if (h->h_desc) (void)hipHostFree(h->h_desc);
+    if (h->h_desc_base) (void)hipHostFree(h->h_desc_base);
     if (h->h_verdict) (void)hipHostFree(h->h_verdict);
     if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
     if (h->ev_join) (void)hipEventDestroy(h->ev_join);
@@ -811,10 +824,12 @@ int spd_init(const spd_model_config* cfg, const spd_weights* w, const spd_sampli
     return SPD_E_DEVICE;
   };
   hipError_t e;
-  if ((e = hipHostMalloc((void**)&h->h_desc, kDescBytes, hipHostMallocDefault)) != hipSuccess)
+  if ((e = hipHostMalloc((void**)&h->h_desc_base, 2 * kDescBytes, hipHostMallocDefault)) != hipSuccess)
     return dev_fail(e, "hipHostMalloc");
-  if ((e = hipHostGetDevicePointer((void**)&h->d_hdesc, h->h_desc, 0)) != hipSuccess)
+  if ((e = hipHostGetDevicePointer((void**)&h->d_hdesc_base, h->h_desc_base, 0)) != hipSuccess)
     return dev_fail(e, "hipHostGetDevicePointer");
+  h->h_desc = h->h_desc_base;
+  h->d_hdesc = h->d_hdesc_base;
   if ((e = hipHostMalloc((void**)&h->h_verdict, sizeof(Verdict), hipHostMallocDefault)) != hipSuccess)
     return dev_fail(e, "hipHostMalloc");
   if ((e = hipHostGetDevicePointer((void**)&h->d_hverdict, h->h_verdict, 0)) != hipSuccess)
@@ -993,6 +1008,71 @@ void interleave_streams(std::vector<Op>& ops) {
   }
 }
 
+void use_desc_buf(spd_handle* h, int b) {
+  h->h_desc = h->h_desc_base + (size_t)b * kDescBytes;
+  h->d_hdesc = h->d_hdesc_base + (size_t)b * kDescBytes;
+}
+
+bool same_inflight(const std::deque<Inflight>& a, const std::deque<Inflight>& b) {
+  if (a.size() != b.size()) return false;
+  for (size_t i = 0; i < a.size(); ++i)
+    if (a[i].pos != b[i].pos || a[i].stage != b[i].stage) return false;
+  return true;
+}
+
+// Builds the step that will follow the pending one when the pending one verifies nothing
+// (a refill step): verify_commit then only advances every stage and appends the draft, so
+// the next state is known now. The pending step's bookkeeping is left as it was.
+void prebuild_next(spd_handle* h) {
+  const Plan& p = h->p;
+  h->pre_valid = false;
+  if (h->pend_exit) return;
+  std::deque<Inflight> F2 = h->F;
+  for (auto& f : F2) f.stage += 1;
+  F2.push_back({h->pend_dpos, 0});
+  if (F2.back().pos >= p.max_ctx || F2.front().stage >= p.n) return;
+  const int pdm2 = std::max(h->pdm_len, h->F.front().pos);
+  // save the pending step's state
+  std::deque<Inflight> F0 = h->F;
+  const int pdm0 = h->pdm_len;
+  std::vector<Op> ops0;
+  ops0.swap(h->ops);
+  std::vector<std::pair<int, int>> layers0;
+  layers0.swap(h->pend_layers);
+  const bool ex0 = h->pend_exit;
+  const int v0 = h->pend_v, d0 = h->pend_dpos, n0 = h->pend_newest;
+  char* hd0 = h->h_desc;
+  char* dd0 = h->d_hdesc;
+  const std::string err0 = h->err;
+  // build for the predicted state into the block the next step uses
+  h->F = F2;
+  h->pdm_len = pdm2;
+  use_desc_buf(h, h->next_buf);
+  DescWriter dw{h->h_desc};
+  const int rc = build_step(h, dw);
+  if (rc == SPD_OK && dw.used <= kDescBytes && !h->ops.empty() && h->ops.front().kind == OP_EMBED) {
+    interleave_streams(h->ops);
+    h->pre_ops.swap(h->ops);
+    h->pre_layers.swap(h->pend_layers);
+    h->pre_exit = h->pend_exit;
+    h->pre_v = h->pend_v; h->pre_dpos = h->pend_dpos; h->pre_newest = h->pend_newest;
+    h->pre_used = dw.used;
+    h->pre_F = F2;
+    h->pre_pdm_len = pdm2;
+    h->pre_valid = true;
+  }
+  // restore
+  h->F = F0;
+  h->pdm_len = pdm0;
+  h->ops.swap(ops0);
+  h->pend_layers.swap(layers0);
+  h->pend_exit = ex0;
+  h->pend_v = v0; h->pend_dpos = d0; h->pend_newest = n0;
+  h->h_desc = hd0;
+  h->d_hdesc = dd0;
+  h->err = err0;
+}
+
 int spd_step(spd_handle* h) {
   if (!h) return SPD_E_ARG;
   h->err.clear();
@@ -1000,17 +1080,30 @@ int spd_step(spd_handle* h) {
     return fail(h, SPD_E_STATE, h->state == spd_handle::S_INIT ? "no prefill" : "a step is pending");
   const int newest = h->F.back().pos;
   if (newest >= h->p.max_ctx) return fail(h, SPD_E_CAPACITY, "newest position reached max_ctx");
-  DescWriter dw{h->h_desc};
-  int rc = build_step(h, dw);
-  if (rc != SPD_OK) return rc;
-  interleave_streams(h->ops);
-  if (dw.used > kDescBytes) return fail(h, SPD_E_CAPACITY, "internal: descriptor block overflow");
-  if (h->ops.empty() || h->ops.front().kind != OP_EMBED)
-    return fail(h, SPD_E_STATE, "internal: a step must start with the embedding");
-  h->desc_used = dw.used;   // uploaded by the embedding kernel
-  rc = run_ops(h);
+  use_desc_buf(h, h->next_buf);
+  if (h->pre_valid && h->pre_pdm_len == h->pdm_len && same_inflight(h->pre_F, h->F)) {
+    // built while the previous step ran, for exactly this state
+    h->ops.swap(h->pre_ops);
+    h->pend_layers.swap(h->pre_layers);
+    h->pend_exit = h->pre_exit;
+    h->pend_v = h->pre_v; h->pend_dpos = h->pre_dpos; h->pend_newest = h->pre_newest;
+    h->desc_used = h->pre_used;
+  } else {
+    DescWriter dw{h->h_desc};
+    int rc = build_step(h, dw);
+    if (rc != SPD_OK) return rc;
+    interleave_streams(h->ops);
+    if (dw.used > kDescBytes) return fail(h, SPD_E_CAPACITY, "internal: descriptor block overflow");
+    if (h->ops.empty() || h->ops.front().kind != OP_EMBED)
+      return fail(h, SPD_E_STATE, "internal: a step must start with the embedding");
+    h->desc_used = dw.used;   // uploaded by the embedding kernel
+  }
+  h->pre_valid = false;
+  const int rc = run_ops(h);
   if (rc != SPD_OK) return rc;
   h->state = spd_handle::S_PENDING;
+  h->next_buf ^= 1;
+  prebuild_next(h);
   return SPD_OK;
 }
 
@@ -1161,6 +1254,7 @@ int spd_reset(spd_handle* h) {
   h->N = h->K = h->acc = h->rej = 0;
   h->P0 = 0;
   h->pend_dpos = 0;
+  h->pre_valid = false;
   return SPD_OK;
 }
 
@@ -1171,7 +1265,7 @@ void spd_destroy(spd_handle* h) {
   (void)hipStreamSynchronize(h->st);
   for (auto e : h->ev) (void)hipEventDestroy(e);
   if (h->st2) (void)hipStreamSynchronize(h->st2);
-  if (h->h_desc) (void)hipHostFree(h->h_desc);
+  if (h->h_desc_base) (void)hipHostFree(h->h_desc_base);
   if (h->h_verdict) (void)hipHostFree(h->h_verdict);
   if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
   if (h->ev_join) (void)hipEventDestroy(h->ev_join);
