@@ -125,7 +125,7 @@ def traffic_from_profile(workload: str, kernel: str):
     digest, value = None, None
     for line in open(path):
         if line.startswith("gemv source sha256[:16]:"):
-            digest = line.split(":", 1)[1].strip()
+            digest = line.split()[-1]
         if line.startswith("traffic_bytes_per_launch"):
             value = float(line.split()[-1])
     if digest != source_hash() or value is None:
