@@ -40,6 +40,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "committed tokens/s (1 seq, 1 GPU) + step µs + % HBM roofline, n=8"
 HBM_PEAK_GBS = 8000.0
+FP32_MATRIX_PEAK_TFLOPS = 157.3     # MI355X dense fp32 matrix-core peak (the prefill GEMM)
 
 
 def log(msg):
@@ -52,6 +53,71 @@ def pct(xs, q):
         return None
     i = min(len(xs) - 1, max(0, int(round(q * (len(xs) - 1)))))
     return xs[i]
+
+
+def hbm_ceiling():
+    """Measured streaming rates of plain library kernels on 1 GiB (best of five, host-timed):
+    a device-to-device copy (read + write) and a sum (read only)."""
+    import torch
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+
+    def best(fn):
+        b = None
+        for _ in range(5):
+            torch.cuda.synchronize()
+            t = time.perf_counter()
+            fn()
+            torch.cuda.synchronize()
+            dt = time.perf_counter() - t
+            b = dt if b is None else min(b, dt)
+        return b
+
+    copy = 2.0 * (1 << 30) / best(lambda: dst.copy_(src)) / 1e9
+    read = 1.0 * (1 << 30) / best(lambda: src.sum()) / 1e9
+    del src, dst
+    return {"kind": "torch copy_ and sum over 1 GiB, best of 5, host-timed",
+            "copy_GBps": copy, "read_GBps": read,
+            "frac_of_peak": max(copy, read) / HBM_PEAK_GBS}
+
+
+def prefill_flops(cfg, P):
+    """Matrix flops of a P-token prefill: target layers, prefix aggregation, PDM layers,
+    causal attention (QK and PV), and the head for the last row."""
+    d, F, hd = cfg.d_model, cfg.d_ffn, cfg.head_dim
+    qo, kvd = cfg.n_q_heads * hd, cfg.n_kv_heads * hd
+    soft = d * (qo + 2 * kvd) + qo * d + 3 * d * F
+    lin = 4 * d * qo + 3 * d * F
+    k = len(cfg.anchors)
+    w = sum(lin if kind else soft for kind in cfg.kinds)
+    w += k * d * d + cfg.pdm_layers * soft
+    attn_layers = sum(1 for kind in cfg.kinds if not kind) + cfg.pdm_layers
+    attn = attn_layers * 2 * qo * P * (P + 1)            # QK^T and PV, causal
+    lin_flops = sum(1 for kind in cfg.kinds if kind) * P * cfg.n_q_heads * 4 * hd * hd
+    return 2.0 * P * w + attn + lin_flops + 2.0 * cfg.vocab * d
+
+
+def prefill_rate(cfg, dW, prompt):
+    """Prefill of the workload's prompt, timed warm (the second of two), with its matrix
+    flops against the fp32 matrix-core peak (the whole prefill, GEMM and the rest)."""
+    import torch
+    from speculative_pipeline_decoding_amd import SPD
+    spd = SPD(cfg, dW, stream=torch.cuda.current_stream())
+    spd.prefill(prompt)
+    torch.cuda.synchronize()
+    spd.reset()
+    t = time.perf_counter()
+    spd.prefill(prompt)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t
+    spd.close()
+    fl = prefill_flops(cfg, len(prompt))
+    return {"tokens": len(prompt), "seconds": dt, "tokens_per_s": len(prompt) / dt,
+            "matrix_tflops": fl / dt / 1e12, "peak_tflops": FP32_MATRIX_PEAK_TFLOPS,
+            "frac": fl / dt / 1e12 / FP32_MATRIX_PEAK_TFLOPS,
+            "note": "fp32-accumulating MFMA GEMM with bf16 weights widened in LDS; the time "
+                    "includes norms, RoPE, attention and the host's chunk loop"}
 
 
 def run_spd(cfg, dW, prompt, T, seed, warmup, steps, kernel_timing, top_p=1.0,
@@ -333,6 +399,11 @@ def main():
         "prefill_s": main_run["prefill_s"],
         "device": torch.cuda.get_device_name(0),
     }
+    res["hbm_ceiling"] = hbm_ceiling()
+    res["prefill"] = prefill_rate(cfg, dW, prompt)
+    log(f"HBM copy {res['hbm_ceiling']['copy_GBps']:.0f} GB/s, read {res['hbm_ceiling']['read_GBps']:.0f}"
+        f" GB/s; prefill "
+        f"{res['prefill']['tokens_per_s']:.0f} tok/s, {res['prefill']['matrix_tflops']:.1f} TFLOP/s")
     if args.stage_plan:
         res["stage_plan"] = stage_plan_report(cfg, dW, prompt, 24)
         log(f"stage plan: {res['stage_plan']}")
