@@ -293,8 +293,8 @@ def main():
                          "known traffic, to scale hardware byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this build runs the "
-              "SPD hot path on a single MI355X, with no multi-GPU path.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the library runs the "
+              "SPD hot path on a single MI355X and has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch

@@ -78,14 +78,12 @@ struct Plan {
   int spec_output;   // the PDM reads the step's output states, after the target layers
   std::vector<int> kind, sizes, starts, anchors, ord;   // ord: index among softmax / linear layers
   int nsoft = 0, nlin = 0;
-  int R = 0;   // sub-layer launches per step
   // workspace offsets
   size_t o_kv, o_pkv, o_lin, o_h, o_anch, o_tok, o_qring, o_qlse, o_cut, o_nuc, o_X, o_hp, o_qbuf, o_attn,
       o_act, o_lqkv, o_logits, o_part, o_verdict, o_desc, o_apart, o_rope,
       o_forced, o_ptok, o_pH, o_pA, o_pQKV, o_pO, o_pG, o_pU, o_pZ, o_panch, total;
   size_t kv_layer_bytes;     // K and V of one layer
   size_t lin_state_bytes;    // one state [hq][hd][hd] f32
-  int maxprob;               // problems per launch
 };
 
 bool plan_config(const spd_model_config* c, Plan& p, std::string& err) {
@@ -144,8 +142,6 @@ bool plan_config(const spd_model_config* c, Plan& p, std::string& err) {
   p.qrows = (p.hq + 2 * p.hkv) * p.hd;
   p.linrows = 3 * p.hq * p.hd;
   p.qo = p.hq * p.hd;
-  p.R = std::max(*std::max_element(p.sizes.begin(), p.sizes.end()), p.Ls);
-  p.maxprob = p.n + 1;
   // workspace plan
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes); return at; };
