@@ -66,7 +66,7 @@ def rel(a, b):
 def run_parity(cfg, W, dW, prompt, G=None, T=0.0, seed=0, n=None, fill="clamp",
                forced_p=None, forced_ref=None, check_states=True, max_steps=None,
                oracle_weights=None, tol_logits=None, top_p=1.0, slack=None,
-               speculate_from="input"):
+               speculate_from="input", anchors=None, Ls=None):
     from speculative_pipeline_decoding_amd import SPD
     G = cfg.gen_len if G is None else G
     tol_l, tol_h = tolerances(cfg)
@@ -76,7 +76,7 @@ def run_parity(cfg, W, dW, prompt, G=None, T=0.0, seed=0, n=None, fill="clamp",
     nucleus = T > 0 and top_p < 1.0
     if nucleus:
         tol_l = min(tol_l, s.slack())
-    kw = {"top_p": top_p, "speculate_from": speculate_from}
+    kw = {"top_p": top_p, "speculate_from": speculate_from, "anchors": anchors, "Ls": Ls}
     if forced_p is not None:
         s.forced_p, s.forced_ref, s.forced_base = forced_p, np.asarray(forced_ref), len(prompt)
         kw.update(forced_p=forced_p, forced_ref=list(forced_ref))
@@ -85,7 +85,8 @@ def run_parity(cfg, W, dW, prompt, G=None, T=0.0, seed=0, n=None, fill="clamp",
     if oracle_weights is not None:
         from oracle.model import Model
         model = Model(cfg, W, weights=oracle_weights)
-    orc = OracleSPD(cfg, W, s, n=n, fill=fill, model=model, speculate_from=speculate_from)
+    orc = OracleSPD(cfg, W, s, n=n, fill=fill, model=model, speculate_from=speculate_from,
+                    anchors=anchors, Ls=Ls)
     rep = {"steps": 0, "max_logit_err": 0.0, "max_state_rel": 0.0, "stopped_at_near_tie": None,
            "flagged": 0}
     t0o = orc.prefill(prompt)

@@ -165,6 +165,38 @@ def test_output_state_speculation_forced_rollbacks():
     assert rep["stopped_at_near_tie"] is None and rep["rejected"] > 2
 
 
+@pytest.mark.parametrize("name,kw", [
+    ("tiny", {"prompt_len": 1}),                                   # a one-token prompt
+    ("tiny", {"prompt_len": 1, "T": 1.0, "seed": 2}),
+    ("tiny", {"anchors": (0,)}),                                   # k = 1: the embedding only
+    ("tiny", {"n": 4, "G": 30}),                                   # n = L: one layer per stage
+    ("mid_bf16_L6_d384_n3", {"anchors": (0, 6), "Ls": 1, "T": 1.0, "seed": 4}),
+    ("mid_bf16_L7_d256_n3_uneven", {"Ls": 3, "n": 2}),             # Ls > L / n
+])
+def test_degenerate_shapes(name, kw):
+    import dataclasses
+    import torch
+    from spd_inputs import make_weights
+    from speculative_pipeline_decoding_amd import upload_weights
+    cfg, W, prompt = workload(name)
+    kw = dict(kw)
+    P = kw.pop("prompt_len", len(prompt))
+    if "anchors" in kw:
+        # another anchor count changes the projection's width: a model of its own
+        cfg = dataclasses.replace(cfg, anchors=kw.pop("anchors"))
+        W = make_weights(cfg)
+        _dev.clear()
+        torch.cuda.empty_cache()
+        dW = upload_weights(cfg, W)
+    else:
+        dW = dev_weights(name)
+    print(f"[parity] {name} anchors {cfg.anchors} prompt {P} {kw}", flush=True)
+    rep = run_parity(cfg, W, dW, prompt[:P], **kw)
+    print(f"[parity] -> steps {rep['steps']} N {rep.get('N')} err {rep['max_logit_err']:.2e}",
+          flush=True)
+    assert rep["steps"] > 0
+
+
 def test_mid_forced_acceptance():
     from oracle.spd import ar_decode
     cfg, W, prompt = workload("mid_bf16_L6_d384_n3")
