@@ -20,11 +20,15 @@ What it computes, and from which passage:
     as the paper's section 3.5 assumption);
   * plain autoregressive decoding (spd.ar_decode), the plain definition of
     the result at temperature 0;
-  * sampling rules and the counter-based RNG (sampling.py).
+  * the output-state variant of the PDM schedule, the ablation the review
+    sets against the early start (spd.py, speculate_from="output");
+  * sampling rules, top-p sets and their near-tie envelope, and the
+    counter-based RNG (sampling.py);
+  * stage planning by per-layer cost (plan.py).
 
 Arithmetic is float64 (numpy), with float32 available for the oracle's own
-error check. Storage roundings that the precision contract fixes (bf16 KV
-cache, bf16 inputs of the prefill GEMMs) are applied explicitly.
+error check. The one storage rounding the precision contract fixes, the bf16
+KV cache, is applied explicitly.
 
 Parity pins live in tests/test_oracle_*.py. Every function here is pinned by
 at least one of them; none is "parity unpinned" except the pages' printed
