@@ -224,7 +224,7 @@ def cpu_baseline(cfg, W, T, seed, alpha, budget_s, top_p=1.0, speculate_from="in
     log(f"cpu baseline: oracle set up in {setup:.1f}s (weights upcast to float64, untimed)")
     t0 = time.perf_counter()
     k = 0
-    while k < 2 or (time.perf_counter() - t0 < budget_s and k < 64):
+    while k < 2 or (time.perf_counter() - t0 < budget_s and k < 160):
         o.step()
         k += 1
         log(f"cpu baseline: oracle step {k} at {time.perf_counter() - t0:.1f}s")
