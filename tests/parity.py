@@ -66,7 +66,7 @@ def rel(a, b):
 def run_parity(cfg, W, dW, prompt, G=None, T=0.0, seed=0, n=None, fill="clamp",
                forced_p=None, forced_ref=None, check_states=True, max_steps=None,
                oracle_weights=None, tol_logits=None, top_p=1.0, slack=None,
-               speculate_from="input", anchors=None, Ls=None):
+               speculate_from="input", anchors=None, Ls=None, progress_every=0):
     from speculative_pipeline_decoding_amd import SPD
     G = cfg.gen_len if G is None else G
     tol_l, tol_h = tolerances(cfg)
@@ -113,6 +113,9 @@ def run_parity(cfg, W, dW, prompt, G=None, T=0.0, seed=0, n=None, fill="clamp",
         c = gpu.verify_commit()
         rep["steps"] += 1
         k = rep["steps"]
+        if progress_every and k % progress_every == 0:
+            print(f"[parity] step {k}: committed {orc.N}, max logit err {rep['max_logit_err']:.3g}",
+                  flush=True)
         assert c.newest == rec.newest, (k, c.newest, rec.newest)
         zq = gpu.debug("draft_logits")
         e = float(np.abs(zq - rec.draft_logits).max())

@@ -174,3 +174,17 @@ def test_fullsize_output_states_lossless(wl):
     for v, acc, kv, pl in steps:
         assert all(x >= y for x, y in zip(kv, kv[1:]))
         assert pl <= kv[-1]
+
+
+@pytest.mark.skipif(os.environ.get("SPD_FULL_CONTEXT_LOCKSTEP") != "1",
+                    reason="minutes of fp64 oracle work; set SPD_FULL_CONTEXT_LOCKSTEP=1")
+def test_fullsize_lockstep_at_full_context(wl):
+    """Lockstep with the oracle at the workload's own prompt (the benchmark's context), T=0,
+    until 32 tokens are committed or a near-tie is flagged."""
+    name, dW, oW = wl
+    cfg, W, prompt = workload(name)
+    print(f"[fullsize] full-context lockstep {name}: {len(prompt)}-token prompt", flush=True)
+    rep = run_parity(cfg, W, dW, prompt, G=33, T=0.0, oracle_weights=oW,
+                     tol_logits=logit_tolerance(name, 0.0), progress_every=8)
+    print(f"[fullsize] -> { {k: v for k, v in rep.items() if k != 'tokens_match'} }", flush=True)
+    assert rep["steps"] > 0
