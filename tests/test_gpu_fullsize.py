@@ -178,13 +178,15 @@ def test_fullsize_output_states_lossless(wl):
 
 @pytest.mark.skipif(os.environ.get("SPD_FULL_CONTEXT_LOCKSTEP") != "1",
                     reason="minutes of fp64 oracle work; set SPD_FULL_CONTEXT_LOCKSTEP=1")
-def test_fullsize_lockstep_at_full_context(wl):
-    """Lockstep with the oracle at the workload's own prompt (the benchmark's context), T=0,
+@pytest.mark.parametrize("T,seed", [(0.0, 0), (1.0, 11)])
+def test_fullsize_lockstep_at_full_context(wl, T, seed):
+    """Lockstep with the oracle at the workload's own prompt (the benchmark's context),
     until 32 tokens are committed or a near-tie is flagged."""
     name, dW, oW = wl
     cfg, W, prompt = workload(name)
-    print(f"[fullsize] full-context lockstep {name}: {len(prompt)}-token prompt", flush=True)
-    rep = run_parity(cfg, W, dW, prompt, G=33, T=0.0, oracle_weights=oW,
-                     tol_logits=logit_tolerance(name, 0.0), progress_every=8)
+    print(f"[fullsize] full-context lockstep {name}: {len(prompt)}-token prompt, T={T}",
+          flush=True)
+    rep = run_parity(cfg, W, dW, prompt, G=33, T=T, seed=seed, oracle_weights=oW,
+                     tol_logits=logit_tolerance(name, T), progress_every=8)
     print(f"[fullsize] -> { {k: v for k, v in rep.items() if k != 'tokens_match'} }", flush=True)
     assert rep["steps"] > 0
