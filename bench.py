@@ -239,6 +239,41 @@ def cpu_baseline(cfg, W, T, seed, alpha, budget_s, top_p=1.0, speculate_from="in
             "steps_per_s": steps_per_s}
 
 
+def forced_sweep(cfg, dW, prompt, ps, warmup, steps):
+    """Throughput at controlled acceptance (T=0 forced mode): each draft at position x is
+    the target's own greedy token with probability p, else a wrong one, so every
+    verification accepts with probability p. The reference stream is the library's own
+    greedy decode at n = 1 (autoregressive). Under this reading p = 0.77 gives the pages'
+    alpha n = 3.04 at n = 8."""
+    import torch
+    from speculative_pipeline_decoding_amd import SPD
+    stream = torch.cuda.current_stream()
+    ar = SPD(cfg, dW, n=1, stream=stream)
+    ref, _ = ar.generate(prompt, warmup + steps + cfg.n_stages + 8)
+    ar.close()
+    out = []
+    for p in ps:
+        spd = SPD(cfg, dW, forced_p=p, forced_ref=ref, stream=stream)
+        spd.prefill(prompt)
+        for _ in range(warmup):
+            spd.step()
+            spd.verify_commit()
+        s0 = spd.stats()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            spd.step()
+            spd.verify_commit()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        s1 = spd.stats()
+        spd.close()
+        N, K = s1.N - s0.N, s1.K - s0.K
+        out.append({"p": p, "alpha": N / K, "s0": N / K * cfg.n_stages,
+                    "tokens_per_s": N / wall, "ms_per_step": 1e3 * wall / K})
+    return out
+
+
 def stage_plan_report(cfg, dW, prompt, steps):
     """Per-layer cost of one token through each target layer (the library at n = 1, where
     every sub-layer launch serves one layer), and the stage split balanced on it against
@@ -291,6 +326,8 @@ def main():
     ap.add_argument("--stage-plan", action="store_true",
                     help="also time one token through each layer (n = 1) and report the "
                          "stage split balanced on those costs against the default split")
+    ap.add_argument("--forced-sweep", action="store_true",
+                    help="also time T=0 forced-acceptance runs at p = 0.5, 0.77, 0.9")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -409,6 +446,10 @@ def main():
     log(f"HBM copy {res['hbm_ceiling']['copy_GBps']:.0f} GB/s, read {res['hbm_ceiling']['read_GBps']:.0f}"
         f" GB/s; prefill "
         f"{res['prefill']['tokens_per_s']:.0f} tok/s, {res['prefill']['matrix_tflops']:.1f} TFLOP/s")
+    if args.forced_sweep:
+        res["forced_sweep"] = forced_sweep(cfg, dW, prompt, (0.5, 0.77, 0.9), args.warmup,
+                                           args.steps)
+        log(f"forced sweep: {res['forced_sweep']}")
     if args.stage_plan:
         res["stage_plan"] = stage_plan_report(cfg, dW, prompt, 24)
         log(f"stage plan: {res['stage_plan']}")
