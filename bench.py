@@ -126,12 +126,15 @@ def prefill_rate(cfg, dW, prompt):
 
 
 def run_spd(cfg, dW, prompt, T, seed, warmup, steps, kernel_timing, top_p=1.0,
-            speculate_from="input"):
+            speculate_from="input", lookahead=True):
     import torch
     from speculative_pipeline_decoding_amd import SPD
     stream = torch.cuda.current_stream()
     spd = SPD(cfg, dW, temperature=T, top_p=top_p, seed=seed, stream=stream,
               speculate_from=speculate_from)
+    # a refill step's successor is enqueued together with it (the library skips this while
+    # per-launch timing is on)
+    spd.lookahead(lookahead)
     t = time.perf_counter()
     spd.prefill(prompt)
     torch.cuda.synchronize()
@@ -239,7 +242,7 @@ def cpu_baseline(cfg, W, T, seed, alpha, budget_s, top_p=1.0, speculate_from="in
             "steps_per_s": steps_per_s}
 
 
-def forced_sweep(cfg, dW, prompt, ps, warmup, steps):
+def forced_sweep(cfg, dW, prompt, ps, warmup, steps, lookahead=True):
     """Throughput at controlled acceptance (T=0 forced mode): each draft at position x is
     the target's own greedy token with probability p, else a wrong one, so every
     verification accepts with probability p. The reference stream is the library's own
@@ -254,6 +257,7 @@ def forced_sweep(cfg, dW, prompt, ps, warmup, steps):
     out = []
     for p in ps:
         spd = SPD(cfg, dW, forced_p=p, forced_ref=ref, stream=stream)
+        spd.lookahead(lookahead)
         spd.prefill(prompt)
         for _ in range(warmup):
             spd.step()
@@ -328,6 +332,9 @@ def main():
                          "stage split balanced on those costs against the default split")
     ap.add_argument("--forced-sweep", action="store_true",
                     help="also time T=0 forced-acceptance runs at p = 0.5, 0.77, 0.9")
+    ap.add_argument("--no-lookahead", action="store_true",
+                    help="enqueue every step only after the previous one's verdict (no "
+                         "lookahead launch of a refill step's successor)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -370,15 +377,16 @@ def main():
         log(f"calibration copy: {args.calib_copy_mib} MiB read + {args.calib_copy_mib} MiB written")
         del src, dst
 
+    lookahead = not args.no_lookahead
     main_run = run_spd(cfg, dW, prompt, args.temperature, args.seed, args.warmup, args.steps, True,
-                       args.top_p, args.speculate_from)
+                       args.top_p, args.speculate_from, lookahead)
     tm = main_run["timed"]
     log(f"T={args.temperature}: prefill {main_run['prefill_s']:.2f}s, timed {tm['K']} steps in "
         f"{tm['wall_s'] * 1e3:.1f} ms, N={tm['N']}")
     t0_run = None
     if args.t0_run and args.temperature != 0.0:
         r = run_spd(cfg, dW, prompt, 0.0, args.seed, args.warmup, args.steps, False,
-                    speculate_from=args.speculate_from)
+                    speculate_from=args.speculate_from, lookahead=lookahead)
         rt = r["timed"]
         t0_run = {"temperature": 0.0, "tokens_per_s": rt["N"] / rt["wall_s"], "N": rt["N"],
                   "K": rt["K"], "alpha": rt["N"] / rt["K"], "s0": rt["N"] / rt["K"] * cfg.n_stages,
@@ -417,7 +425,7 @@ def main():
         "config": {"workload": cfg.name, "n": cfg.n_stages, "Ls": cfg.pdm_layers,
                    "anchors": list(cfg.anchors), "context": cfg.prompt_len + cfg.gen_len,
                    "prompt": cfg.prompt_len, "temperature": args.temperature, "top_p": args.top_p,
-                   "speculate_from": args.speculate_from,
+                   "speculate_from": args.speculate_from, "lookahead": lookahead,
                    "weights": "bf16 N(0,0.02) seeded", "kv_cache": "bf16",
                    "prompt_ids": "uniform random"},
         "roofline": {"bound": "hbm", "kernel": dominant,
@@ -448,7 +456,7 @@ def main():
         f"{res['prefill']['tokens_per_s']:.0f} tok/s, {res['prefill']['matrix_tflops']:.1f} TFLOP/s")
     if args.forced_sweep:
         res["forced_sweep"] = forced_sweep(cfg, dW, prompt, (0.5, 0.77, 0.9), args.warmup,
-                                           args.steps)
+                                           args.steps, lookahead)
         log(f"forced sweep: {res['forced_sweep']}")
     if args.stage_plan:
         res["stage_plan"] = stage_plan_report(cfg, dW, prompt, 24)

@@ -181,8 +181,24 @@ int spd_prefill(spd_handle* h, const int32_t* prompt, int32_t len, int32_t* firs
 int spd_step(spd_handle* h);
 
 /*
- * Wait for the pending step (polling the stream; the verdict kernels write their
- * result to pinned host memory) and apply its verdict: on accept the ring shifts
+ * Lookahead (on != 0; off by default). A step in which no token leaves the last
+ * stage (a refill step) verifies nothing, so the state of the step after it is
+ * fixed when it is enqueued. With lookahead on, spd_step enqueues that following
+ * step as well, right behind the pending one, so the GPU starts it as soon as the
+ * pending one ends instead of waiting for the host's next spd_step; the next
+ * spd_step then only takes it over. Results are bit for bit those of a run
+ * without lookahead; the call order stays init -> prefill -> (step -> verify)*.
+ * While a step runs ahead, the buffers that spd_debug_copy reads may already hold
+ * its values, and spd_timing_enable returns SPD_E_STATE; lookahead is skipped
+ * while timing is enabled. The review of the paper (pith.science, "What carries
+ * the argument") describes the pipeline this keeps fed: one token enters stage 0
+ * per step. Errors: SPD_E_ARG (NULL handle).
+ */
+int spd_lookahead(spd_handle* h, int on);
+
+/*
+ * Wait for the pending step (polling its end-of-step event; the verdict kernels
+ * write their result to pinned host memory) and apply its verdict: on accept the ring shifts
  * and the draft enters stage 0; on reject every layer's KV length becomes the
  * verified position v, the pipeline is flushed and reseeded with the
  * corrected token at v. This is the only per-step device-to-host wait.

@@ -75,7 +75,8 @@ class Stats(ctypes.Structure):
 
 SYMBOLS = ["spd_workspace_bytes", "spd_init", "spd_init_error", "spd_prefill", "spd_step",
            "spd_verify_commit", "spd_get_stats", "spd_get_kv_lens", "spd_debug_size",
-           "spd_debug_copy", "spd_reset", "spd_last_error", "spd_destroy", "spd_timing_enable",
+           "spd_debug_copy", "spd_reset", "spd_last_error", "spd_destroy", "spd_lookahead",
+           "spd_timing_enable",
            "spd_timing_read", "spd_timing_read_layers", "spd_balance_stages"]
 
 _lib = None
@@ -115,6 +116,8 @@ def load() -> ctypes.CDLL:
     L.spd_last_error.restype = ctypes.c_char_p
     L.spd_destroy.argtypes = [VP]
     L.spd_destroy.restype = None
+    L.spd_lookahead.argtypes = [VP, I]
+    L.spd_lookahead.restype = I
     L.spd_timing_enable.argtypes = [VP, I]
     L.spd_timing_read.argtypes = [VP, ctypes.c_int32, P(ctypes.c_int64), P(ctypes.c_double),
                                   P(ctypes.c_double)]
@@ -288,6 +291,10 @@ class SPD:
 
     def reset(self):
         self._chk(self.L.spd_reset(self.h))
+
+    def lookahead(self, on: bool = True):
+        """Enqueue the step after a refill step together with it (spd_lookahead)."""
+        self._chk(self.L.spd_lookahead(self.h, 1 if on else 0))
 
     def timing(self, on, serial: bool = False):
         """Per-launch timing on or off; serial also puts the PDM chain on the caller's stream."""

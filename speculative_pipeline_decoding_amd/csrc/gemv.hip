@@ -3,8 +3,10 @@
 // One launch runs a list of problems, y = epilogue(W (g ⊙ x) / rms(x)):
 //   * the in-flight tokens, each at its own layer with one input vector, and the
 //     LM head with one or two vectors (the exiting token and the PDM's newest
-//     row share one sweep of the tied head): the "rows" kernel, in which a wave
-//     owns four weight rows and walks all of K;
+//     row share one sweep of the tied head): the "rows" kernel, in which a
+//     workgroup stages its input in LDS once and each wave owns four weight rows
+//     (eight for the two-vector head) and walks all of K with two iterations of
+//     weight loads in flight;
 //   * the PDM's matrix with its n+1 rows: with bf16 weights the matrix-core
 //     kernel (below); with fp32 weights the "split-K" kernel, in which the four
 //     waves of a workgroup share four weight rows and take alternate chunks of K.
@@ -13,9 +15,9 @@
 // moves inside a wavefront.
 //
 // RMSNorm is fused without a prologue: W (g ⊙ x) / rms(x) is linear in the
-// scale, so the kernel accumulates sum(x^2) next to the dot products (every
-// wave uses the same lane partition, so all agree bit for bit) and scales the
-// reduced result once.
+// scale, so the kernel accumulates sum(x^2) while it reads the input (added in a
+// fixed order, so every wave of a workgroup scales by the same bits) and scales
+// the reduced result once.
 #include "spd_internal.h"
 
 #include <algorithm>
@@ -24,9 +26,12 @@ namespace spd {
 namespace {
 
 constexpr int RW = 4;         // weight rows per workgroup (split-K kernel) / per wave (rows kernel)
-constexpr int RWIDE = 8;      // rows per wave of the rows kernel for tall matrices (>= kTall units)
+constexpr int RWIDE = 8;      // rows per wave of the rows kernel: two vectors, >= kTall units
 constexpr int kTall = 8192;
 constexpr int kSplit = 4;     // waves sharing the rows of a split-K workgroup
+constexpr int kRing = 2;      // rows kernel: iterations of weight loads in flight per wave
+constexpr int kRingWide = 1;  // the same with RWIDE rows per wave
+constexpr int kRowsLds = 65536 - 256;   // bytes of staged input the rows kernel may take (64 KiB with its reduction)
 
 template <typename T> struct Elt;
 template <> struct Elt<uint16_t> { static constexpr int N = 8; };   // bf16 per 16 bytes
@@ -134,83 +139,165 @@ __device__ void epilogue(const GemvProb& p, int v, int unit, float a, float b,
   }
 }
 
-// ---- rows kernel: one wave = RW weight rows over all of K, NV <= 2 vectors ------------
-template <typename T, int NV, int RR>
-__device__ void rows_body(const GemvProb& p, int tile, const float2* __restrict__ rope) {
+// ---- rows kernel: one wave = RR weight rows over all of K, NV <= 2 vectors ------------
+// The workgroup first stages g ⊙ x of every vector in LDS, one pass over the input (each
+// thread sums x^2 over its columns; the waves' sums are then added in a fixed order, so
+// every wave scales by the same bits). The loop then reads inputs on the LDS counter
+// only, and each wave keeps U iterations of weight loads in flight: a wait for the
+// oldest iteration never drains the younger ones behind it.
+//
+// LDS layout of one vector, per 64·E-element chunk of K: the E elements a lane takes
+// (columns k0 + E·lane ..) sit as E/4 float4 at k0 + 256·h + 4·lane, h = 0 .. E/4-1, so
+// the lanes of a wave read consecutive 16-byte pieces.
+template <typename T>
+__host__ __device__ constexpr int rows_kpad(int K) {
+  return (K + 64 * Elt<T>::N - 1) / (64 * Elt<T>::N) * (64 * Elt<T>::N);
+}
+template <typename T>
+__device__ __forceinline__ int rows_lds_col(int c) {   // c: a multiple of 4
+  constexpr int E = Elt<T>::N, C = 64 * E;
+  const int r = c % C;
+  return c - r + ((r % E) / 4) * 256 + (r / E) * 4;
+}
+constexpr int kRowsStage = 4;   // float4 of each input per thread per staging round
+
+template <typename T, int NV, int RR, int U>
+__device__ void rows_body(const GemvProb& p, int tile, const float2* __restrict__ rope,
+                          float* __restrict__ xs, float* __restrict__ red) {
   constexpr int E = Elt<T>::N;
+  constexpr int C = 64 * E;          // K elements per wave iteration
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  constexpr int RW = RR;
-  const int upw = paired(p) ? RW / 2 : RW;
+  const int upw = paired(p) ? RR / 2 : RR;
   const int nunits = units_of(p);
-  const int u0 = (tile * kWaves + wave) * upw;
-  if (u0 >= nunits) return;
+  const int u0 = (tile * kWaves + wave) * upw;   // waves past the end stream clamped rows
   const int nv = p.nvec;
-  const T* rp[RW];
-#pragma unroll
-  for (int j = 0; j < RW; ++j) rp[j] = row_ptr<T, RW>(p, u0, j, nunits);
-  float acc[RW][NV], ss[NV];
-#pragma unroll
-  for (int v = 0; v < NV; ++v) {
-    ss[v] = 0.f;
-#pragma unroll
-    for (int j = 0; j < RW; ++j) acc[j][v] = 0.f;
-  }
-  const int K = p.K;
+  const int K = p.K, KP = rows_kpad<T>(K);
+  const int niter = KP / C;
   const float* __restrict__ g = p.gain;
-  for (int k0 = lane * E; k0 < K; k0 += 64 * E) {
-    uint4 w[RW];
+
+  // staging loads of the first round go out before the weight ring
+  const int NT = blockDim.x;
+  float4 xr[NV][kRowsStage], gr[kRowsStage];
+  auto stage_load = [&](int c0) {
 #pragma unroll
-    for (int j = 0; j < RW; ++j) w[j] = load_stream(rp[j] + k0);
-    float xv[NV][E];
-#pragma unroll
-    for (int v = 0; v < NV; ++v) {
-      if (v < nv) {
-        load_f32<E>(p.x + v * p.x_stride + k0, xv[v]);
-        if (g) {
-          float gv[E];
-          load_f32<E>(g + v * p.gain_stride + k0, gv);
-#pragma unroll
-          for (int e = 0; e < E; ++e) { ss[v] += xv[v][e] * xv[v][e]; xv[v][e] *= gv[e]; }
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < E; ++e) xv[v][e] = 0.f;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < RW; ++j) {
-      float wf[E];
-      to_f32(w[j], wf, (const T*)nullptr);
+    for (int u = 0; u < kRowsStage; ++u) {
+      const int c = min(c0 + 4 * NT * u, K - 4);
+      gr[u] = g ? load_g4(g + c) : make_float4(1.f, 1.f, 1.f, 1.f);
 #pragma unroll
       for (int v = 0; v < NV; ++v)
+        xr[v][u] = v < nv ? load_g4(p.x + v * p.x_stride + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  stage_load(4 * threadIdx.x);
+
+  const T* rp[RR];
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[j][v] += wf[e] * xv[v][e];
+  for (int j = 0; j < RR; ++j) rp[j] = row_ptr<T, RR>(p, u0, j, nunits);
+  uint4 w[U][RR];
+  // iterations past the end re-read the row's first piece: every load is issued, so the
+  // compiler's count of loads in flight stays exact
+  auto issue = [&](int s, int it) {
+    const int k = it * C + lane * E;
+    const int kk = it < niter && k < K ? k : 0;
+#pragma unroll
+    for (int j = 0; j < RR; ++j) w[s][j] = load_stream(rp[j] + kk);
+  };
+#pragma unroll
+  for (int s = 0; s < U; ++s) issue(s, s);
+
+  float ss[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) ss[v] = 0.f;
+  for (int c0 = 4 * threadIdx.x; c0 < K; c0 += 4 * NT * kRowsStage) {
+    if (c0 != 4 * (int)threadIdx.x) stage_load(c0);
+#pragma unroll
+    for (int u = 0; u < kRowsStage; ++u) {
+      const int c = c0 + 4 * NT * u;
+      if (c < K) {
+        float* dst = xs + rows_lds_col<T>(c);
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+          const float4 x = xr[v][u], gg = gr[u];
+          ss[v] += x.x * x.x; ss[v] += x.y * x.y; ss[v] += x.z * x.z; ss[v] += x.w * x.w;
+          *reinterpret_cast<float4*>(dst + v * KP) =
+              make_float4(x.x * gg.x, x.y * gg.y, x.z * gg.z, x.w * gg.w);
+        }
+      }
+    }
+  }
+  if (g) {
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const float t = wave_sum(ss[v]);
+      if (lane == 0) red[wave * NV + v] = t;
+    }
+  }
+  __syncthreads();
+  float sc[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    sc[v] = 1.f;
+    if (g) {
+      float t = 0.f;
+      for (int q = 0; q < kWaves; ++q) t += red[q * NV + v];
+      sc[v] = rsqrtf(t / (float)K + p.eps);
+    }
+  }
+
+  float acc[RR][NV];
+#pragma unroll
+  for (int j = 0; j < RR; ++j)
+#pragma unroll
+    for (int v = 0; v < NV; ++v) acc[j][v] = 0.f;
+  for (int i0 = 0; i0 < niter; i0 += U) {
+#pragma unroll
+    for (int s = 0; s < U; ++s) {
+      const int it = i0 + s;
+      const int k = it * C + lane * E;
+      if (it < niter && k < K) {
+        float xv[NV][E];
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+#pragma unroll
+          for (int h = 0; h < E / 4; ++h) {
+            const float4 t = *reinterpret_cast<const float4*>(xs + v * KP + it * C + 256 * h + 4 * lane);
+            xv[v][4 * h] = t.x; xv[v][4 * h + 1] = t.y; xv[v][4 * h + 2] = t.z; xv[v][4 * h + 3] = t.w;
+          }
+#pragma unroll
+        for (int j = 0; j < RR; ++j) {
+          float wf[E];
+          to_f32(w[s][j], wf, (const T*)nullptr);
+#pragma unroll
+          for (int v = 0; v < NV; ++v)
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[j][v] += wf[e] * xv[v][e];
+        }
+      }
+      issue(s, it + U);
     }
   }
 #pragma unroll
-  for (int v = 0; v < NV; ++v) {
+  for (int v = 0; v < NV; ++v)
 #pragma unroll
-    for (int j = 0; j < RW; ++j) acc[j][v] = wave_sum(acc[j][v]);
-    ss[v] = g ? rsqrtf(wave_sum(ss[v]) / (float)K + p.eps) : 1.f;
-  }
+    for (int j = 0; j < RR; ++j) acc[j][v] = wave_sum(acc[j][v]);
   // every lane holds every reduced sum; lane t finishes (unit t % upw, vector t / upw)
   if (lane < upw * nv) {
     const int ut = lane % upw, v = lane / upw;
     int ja, jb;
-    unit_slots<RW>(p, ut, ja, jb);
-    float a = 0.f, b = 0.f, sc = 1.f;
+    unit_slots<RR>(p, ut, ja, jb);
+    float a = 0.f, b = 0.f, scv = 1.f;
 #pragma unroll
     for (int vv = 0; vv < NV; ++vv) {
       if (vv == v) {
-        sc = ss[vv];
+        scv = sc[vv];
 #pragma unroll
-        for (int j = 0; j < RW; ++j) {
+        for (int j = 0; j < RR; ++j) {
           if (j == ja) a = acc[j][vv];
           if (j == jb) b = acc[j][vv];
         }
       }
     }
-    if (u0 + ut < nunits) epilogue<T>(p, v, u0 + ut, a * sc, b * sc, rope);
+    if (u0 + ut < nunits) epilogue<T>(p, v, u0 + ut, a * scv, b * scv, rope);
   }
 }
 
@@ -324,9 +411,15 @@ constexpr int kMcLdsElems = 76800;           // bf16 elements of staged planes (
 constexpr int kMcMaxVec = 16;
 
 __device__ __forceinline__ int mc_units(const GemvProb& p) { return paired(p) ? 8 : 16; }
+// Dynamic LDS of one workgroup: the three input planes, which the K-range hand-off of
+// NW waves (NW x 4 x 64 floats) reuses afterwards.
+inline int mc_lds_bytes(int nvec, int K, int waves);
 // LDS row stride: whole 64-column blocks (zero past K) plus 16 bytes, so the 16 rows read
 // by one lane group start in distinct banks
 __host__ __device__ __forceinline__ int mc_ldk(int K) { return (K + 63) / 64 * 64 + 8; }
+inline int mc_lds_bytes(int nvec, int K, int waves) {
+  return std::max(3 * nvec * mc_ldk(K) * 2, waves * 4 * 64 * 4);
+}
 
 __device__ __forceinline__ const uint16_t* mc_row(const GemvProb& p, int u0, int slot, int nunits) {
   const uint16_t* M = static_cast<const uint16_t*>(p.W);
@@ -506,13 +599,17 @@ __device__ __forceinline__ void gemv_body(const GemvProb* __restrict__ probs, in
     splitk_body<T>(p, tile, red, rope);
   } else if constexpr (KIND == K_MFMA) {
     static_assert(sizeof(T) == 2, "matrix-core GEMV takes bf16 weights");
-    __shared__ __attribute__((aligned(16))) uint16_t planes[kMcLdsElems];
+    // the planes take only the LDS this launch needs (mc_lds_bytes), so workgroups of
+    // other kernels can share the CU
+    extern __shared__ __attribute__((aligned(16))) uint16_t planes[];
     __shared__ float red[kMcMaxWaves * kMcMaxVec];
     mfma_body(p, tile, rope, planes, red);
-  } else if constexpr (KIND == K_ROWS1W || KIND == K_ROWS2W) {
-    rows_body<T, KIND == K_ROWS1W ? 1 : 2, RWIDE>(p, tile, rope);
   } else {
-    rows_body<T, KIND == K_ROWS1 ? 1 : 2, RW>(p, tile, rope);
+    constexpr bool wide = KIND == K_ROWS1W || KIND == K_ROWS2W;
+    constexpr int NV = KIND == K_ROWS1 || KIND == K_ROWS1W ? 1 : 2;
+    extern __shared__ float rows_xs[];
+    __shared__ float red[kWaves * NV];
+    rows_body<T, NV, wide ? RWIDE : RW, wide ? kRingWide : kRing>(p, tile, rope, rows_xs, red);
   }
 }
 
@@ -538,25 +635,45 @@ SPD_GEMV_KERNEL(pdm_gemv_down)
 
 template <typename T, int KIND>
 void launch_kind(int role, dim3 grid, const GemvProb* d_probs, int nprob, const float2* rope,
-                 hipStream_t st, LaunchEv ev, int waves = kWaves) {
+                 hipStream_t st, LaunchEv ev, int waves = kWaves, size_t shm = 0) {
   const dim3 block(waves * 64);
+  if constexpr (KIND == K_MFMA) {
+    // more than 64 KiB of dynamic LDS: raise each role's limit once
+    static bool raised[GEMV_NROLES] = {};
+    if (!raised[role]) {
+      const int lim = kMcLdsElems * 2;
+      switch (role) {
+        case GEMV_PROJ: hipFuncSetAttribute((const void*)gemv_proj<T, KIND>, hipFuncAttributeMaxDynamicSharedMemorySize, lim); break;
+        case GEMV_QKV: hipFuncSetAttribute((const void*)gemv_qkv<T, KIND>, hipFuncAttributeMaxDynamicSharedMemorySize, lim); break;
+        case GEMV_O: hipFuncSetAttribute((const void*)gemv_o<T, KIND>, hipFuncAttributeMaxDynamicSharedMemorySize, lim); break;
+        case GEMV_GATE_UP: hipFuncSetAttribute((const void*)gemv_gate_up<T, KIND>, hipFuncAttributeMaxDynamicSharedMemorySize, lim); break;
+        case GEMV_DOWN: hipFuncSetAttribute((const void*)gemv_down<T, KIND>, hipFuncAttributeMaxDynamicSharedMemorySize, lim); break;
+        case GEMV_PDM_QKV: hipFuncSetAttribute((const void*)pdm_gemv_qkv<T, KIND>, hipFuncAttributeMaxDynamicSharedMemorySize, lim); break;
+        case GEMV_PDM_O: hipFuncSetAttribute((const void*)pdm_gemv_o<T, KIND>, hipFuncAttributeMaxDynamicSharedMemorySize, lim); break;
+        case GEMV_PDM_GATE_UP: hipFuncSetAttribute((const void*)pdm_gemv_gate_up<T, KIND>, hipFuncAttributeMaxDynamicSharedMemorySize, lim); break;
+        case GEMV_PDM_DOWN: hipFuncSetAttribute((const void*)pdm_gemv_down<T, KIND>, hipFuncAttributeMaxDynamicSharedMemorySize, lim); break;
+        default: hipFuncSetAttribute((const void*)gemv_head<T, KIND>, hipFuncAttributeMaxDynamicSharedMemorySize, lim); break;
+      }
+      raised[role] = true;
+    }
+  }
   switch (role) {
-    case GEMV_PROJ: SPD_LAUNCH(ev, (gemv_proj<T, KIND>), grid, block, 0, st, d_probs, nprob, rope); break;
-    case GEMV_QKV: SPD_LAUNCH(ev, (gemv_qkv<T, KIND>), grid, block, 0, st, d_probs, nprob, rope); break;
-    case GEMV_O: SPD_LAUNCH(ev, (gemv_o<T, KIND>), grid, block, 0, st, d_probs, nprob, rope); break;
-    case GEMV_GATE_UP: SPD_LAUNCH(ev, (gemv_gate_up<T, KIND>), grid, block, 0, st, d_probs, nprob, rope); break;
-    case GEMV_DOWN: SPD_LAUNCH(ev, (gemv_down<T, KIND>), grid, block, 0, st, d_probs, nprob, rope); break;
-    case GEMV_PDM_QKV: SPD_LAUNCH(ev, (pdm_gemv_qkv<T, KIND>), grid, block, 0, st, d_probs, nprob, rope); break;
-    case GEMV_PDM_O: SPD_LAUNCH(ev, (pdm_gemv_o<T, KIND>), grid, block, 0, st, d_probs, nprob, rope); break;
-    case GEMV_PDM_GATE_UP: SPD_LAUNCH(ev, (pdm_gemv_gate_up<T, KIND>), grid, block, 0, st, d_probs, nprob, rope); break;
-    case GEMV_PDM_DOWN: SPD_LAUNCH(ev, (pdm_gemv_down<T, KIND>), grid, block, 0, st, d_probs, nprob, rope); break;
-    default: SPD_LAUNCH(ev, (gemv_head<T, KIND>), grid, block, 0, st, d_probs, nprob, rope); break;
+    case GEMV_PROJ: SPD_LAUNCH(ev, (gemv_proj<T, KIND>), grid, block, shm, st, d_probs, nprob, rope); break;
+    case GEMV_QKV: SPD_LAUNCH(ev, (gemv_qkv<T, KIND>), grid, block, shm, st, d_probs, nprob, rope); break;
+    case GEMV_O: SPD_LAUNCH(ev, (gemv_o<T, KIND>), grid, block, shm, st, d_probs, nprob, rope); break;
+    case GEMV_GATE_UP: SPD_LAUNCH(ev, (gemv_gate_up<T, KIND>), grid, block, shm, st, d_probs, nprob, rope); break;
+    case GEMV_DOWN: SPD_LAUNCH(ev, (gemv_down<T, KIND>), grid, block, shm, st, d_probs, nprob, rope); break;
+    case GEMV_PDM_QKV: SPD_LAUNCH(ev, (pdm_gemv_qkv<T, KIND>), grid, block, shm, st, d_probs, nprob, rope); break;
+    case GEMV_PDM_O: SPD_LAUNCH(ev, (pdm_gemv_o<T, KIND>), grid, block, shm, st, d_probs, nprob, rope); break;
+    case GEMV_PDM_GATE_UP: SPD_LAUNCH(ev, (pdm_gemv_gate_up<T, KIND>), grid, block, shm, st, d_probs, nprob, rope); break;
+    case GEMV_PDM_DOWN: SPD_LAUNCH(ev, (pdm_gemv_down<T, KIND>), grid, block, shm, st, d_probs, nprob, rope); break;
+    default: SPD_LAUNCH(ev, (gemv_head<T, KIND>), grid, block, shm, st, d_probs, nprob, rope); break;
   }
 }
 
 }  // namespace
 
-int gemv_plan(GemvProb* v, int n, bool bf16) {
+GemvPlan gemv_plan(GemvProb* v, int n, bool bf16) {
   int mv = 1;
   bool mc = bf16 && n == 1;   // the matrix-core kernel takes one problem per launch
   auto a16 = [](const void* q) { return q == nullptr || ((uintptr_t)q & 15) == 0; };
@@ -568,9 +685,15 @@ int gemv_plan(GemvProb* v, int n, bool bf16) {
          a16(g.W2) && a16(g.x) && a16(g.gain) && g.nvec <= kMcMaxVec &&
          (size_t)3 * g.nvec * mc_ldk(g.K) <= (size_t)kMcLdsElems;
   }
+  int kmax = 0;
+  for (int i = 0; i < n; ++i) kmax = std::max(kmax, v[i].K);
+  const int kpad = bf16 ? rows_kpad<uint16_t>(kmax) : rows_kpad<float>(kmax);
   int kind = mv <= 1 ? K_ROWS1 : mv == 2 ? K_ROWS2 : K_SPLITK;
+  // the rows kernel stages every vector whole in LDS; longer inputs take the split-K kernel
+  if (kind != K_SPLITK && (size_t)mv * kpad * 4 > (size_t)kRowsLds) kind = K_SPLITK;
   if (mc && mv > 2) kind = K_MFMA;
-  if (kind <= K_ROWS2) {
+  // two vectors over a tall matrix (the shared head sweep): eight rows per wave
+  if (kind == K_ROWS2) {
     bool tall = true;
     for (int i = 0; i < n; ++i)
       tall = tall && (v[i].epi == EPI_QKV ? v[i].rows / 2 : v[i].rows) >= kTall;
@@ -599,32 +722,40 @@ int gemv_plan(GemvProb* v, int n, bool bf16) {
     g.tile0 = t;
     t += g.ntiles;
   }
-  const int waves = kind == K_MFMA ? v[0].pad * v[0].ksplit : kWaves;
-  return kind << 28 | waves << 20 | t;
+  GemvPlan out;
+  out.kind = kind;
+  out.ntiles = t;
+  out.waves = kind == K_MFMA ? v[0].pad * v[0].ksplit : kWaves;
+  const int nvs = kind == K_ROWS2 || kind == K_ROWS2W ? 2 : 1;
+  out.shm = kind == K_MFMA     ? mc_lds_bytes(v[0].nvec, v[0].K, out.waves)
+            : kind == K_SPLITK ? 0
+                               : nvs * kpad * (int)sizeof(float);
+  return out;
 }
 
-hipError_t launch_gemv(int role, const GemvProb* d_probs, int nprob, int plan, bool bf16,
+hipError_t launch_gemv(int role, const GemvProb* d_probs, int nprob, const GemvPlan& plan, bool bf16,
                        const float2* rope, hipStream_t st, LaunchEv ev) {
-  const int kind = plan >> 28, waves = (plan >> 20) & 255, ntiles = plan & ((1 << 20) - 1);
+  const int kind = plan.kind, waves = plan.waves, ntiles = plan.ntiles;
   if (ntiles <= 0 || nprob <= 0) return hipSuccess;
   const dim3 grid(ntiles);
+  const size_t shm = plan.shm;
   if (bf16) {
     switch (kind) {
-      case K_ROWS1: launch_kind<uint16_t, K_ROWS1>(role, grid, d_probs, nprob, rope, st, ev); break;
-      case K_ROWS2: launch_kind<uint16_t, K_ROWS2>(role, grid, d_probs, nprob, rope, st, ev); break;
+      case K_ROWS1: launch_kind<uint16_t, K_ROWS1>(role, grid, d_probs, nprob, rope, st, ev, kWaves, shm); break;
+      case K_ROWS2: launch_kind<uint16_t, K_ROWS2>(role, grid, d_probs, nprob, rope, st, ev, kWaves, shm); break;
       case K_SPLITK: launch_kind<uint16_t, K_SPLITK>(role, grid, d_probs, nprob, rope, st, ev); break;
-      case K_MFMA: launch_kind<uint16_t, K_MFMA>(role, grid, d_probs, nprob, rope, st, ev, waves); break;
-      case K_ROWS1W: launch_kind<uint16_t, K_ROWS1W>(role, grid, d_probs, nprob, rope, st, ev); break;
-      case K_ROWS2W: launch_kind<uint16_t, K_ROWS2W>(role, grid, d_probs, nprob, rope, st, ev); break;
+      case K_MFMA: launch_kind<uint16_t, K_MFMA>(role, grid, d_probs, nprob, rope, st, ev, waves, shm); break;
+      case K_ROWS1W: launch_kind<uint16_t, K_ROWS1W>(role, grid, d_probs, nprob, rope, st, ev, kWaves, shm); break;
+      case K_ROWS2W: launch_kind<uint16_t, K_ROWS2W>(role, grid, d_probs, nprob, rope, st, ev, kWaves, shm); break;
       default: return hipErrorInvalidValue;
     }
   } else {
     switch (kind) {
-      case K_ROWS1: launch_kind<float, K_ROWS1>(role, grid, d_probs, nprob, rope, st, ev); break;
-      case K_ROWS2: launch_kind<float, K_ROWS2>(role, grid, d_probs, nprob, rope, st, ev); break;
+      case K_ROWS1: launch_kind<float, K_ROWS1>(role, grid, d_probs, nprob, rope, st, ev, kWaves, shm); break;
+      case K_ROWS2: launch_kind<float, K_ROWS2>(role, grid, d_probs, nprob, rope, st, ev, kWaves, shm); break;
       case K_SPLITK: launch_kind<float, K_SPLITK>(role, grid, d_probs, nprob, rope, st, ev); break;
-      case K_ROWS1W: launch_kind<float, K_ROWS1W>(role, grid, d_probs, nprob, rope, st, ev); break;
-      case K_ROWS2W: launch_kind<float, K_ROWS2W>(role, grid, d_probs, nprob, rope, st, ev); break;
+      case K_ROWS1W: launch_kind<float, K_ROWS1W>(role, grid, d_probs, nprob, rope, st, ev, kWaves, shm); break;
+      case K_ROWS2W: launch_kind<float, K_ROWS2W>(role, grid, d_probs, nprob, rope, st, ev, kWaves, shm); break;
       default: return hipErrorInvalidValue;
     }
   }

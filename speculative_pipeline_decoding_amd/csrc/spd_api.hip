@@ -65,7 +65,7 @@ struct Op {
   int split;       // attention split length
   double bytes;    // algorithmic HBM bytes (weights + KV) for the timing report
   int stream = 0;  // 0: the caller's stream, 1: the PDM stream
-  int plan = 0;    // GEMV: kernel kind and workgroups (gemv_plan)
+  GemvPlan plan;   // GEMV: kernel kind, workgroups and LDS (gemv_plan)
   int layer = -1;  // the one target layer this launch serves, when only one token is in it
 };
 
@@ -227,8 +227,19 @@ struct spd_handle {
   bool pre_exit = false;
   int pre_v = 0, pre_dpos = 0, pre_newest = 0;
   size_t pre_used = 0;
-  Verdict* h_verdict = nullptr;   // pinned; written by the verdict kernels through d_hverdict
+  // pinned verdicts, one per staging block: the verdict kernels of a step write the slot of
+  // the block that step was built in (d_hverdict: the current block's device view)
+  Verdict* h_verdict_base = nullptr;
+  Verdict* d_hverdict_base = nullptr;
   Verdict* d_hverdict = nullptr;
+  int cur_buf = 0;                 // the staging block h_desc / d_hdesc / d_hverdict point at
+  int pend_buf = 0;                // the block of the pending step
+  hipEvent_t ev_step[2] = {nullptr, nullptr};   // end of the last step run from each block
+  // lookahead: a step that verifies nothing fixes the next step's state at launch, so that
+  // step is launched at once (from the other block) and the GPU never waits for the host
+  bool lookahead = false;
+  bool ahead = false;              // the prebuilt step has been launched already
+  int pre_buf = 0;
   // state machine
   enum { S_INIT, S_READY, S_PENDING } state = S_INIT;
   int P0 = 0;
@@ -281,6 +292,14 @@ struct spd_handle {
 
 namespace {
 
+// Points the step-building state at staging block b (descriptors and verdict slot).
+void use_desc_buf(spd_handle* h, int b) {
+  h->cur_buf = b;
+  h->h_desc = h->h_desc_base + (size_t)b * kDescBytes;
+  h->d_hdesc = h->d_hdesc_base + (size_t)b * kDescBytes;
+  h->d_hverdict = h->d_hverdict_base + b;
+}
+
 int fail(spd_handle* h, int code, const std::string& m) {
   if (h) h->err = m;
   return code;
@@ -306,7 +325,7 @@ struct DescWriter {
   }
 };
 
-int finish_tiles(const Plan& p, std::vector<GemvProb>& v) {
+GemvPlan finish_tiles(const Plan& p, std::vector<GemvProb>& v) {
   return gemv_plan(v.data(), (int)v.size(), p.bf16);
 }
 
@@ -430,9 +449,13 @@ hipError_t run_op(spd_handle* h, const Op& op, LaunchEv ev = {}) {
   return hipErrorInvalidValue;
 }
 
-int run_ops(spd_handle* h) {
+// Launches one step's ops from staging block buf (used bytes of it) and records the
+// block's end-of-step event on the caller's stream.
+int run_ops(spd_handle* h, const std::vector<Op>& ops, int buf, size_t used) {
+  use_desc_buf(h, buf);
+  h->desc_used = used;
   size_t k = 0;
-  for (const Op& op : h->ops) {
+  for (const Op& op : ops) {
     if (h->timing && op.kind < OP_NKINDS) {
       if (2 * k + 1 >= h->ev.size()) return fail(h, SPD_E_CAPACITY, "internal: timing event pool");
       const LaunchEv ev{h->ev[2 * k], h->ev[2 * k + 1]};
@@ -445,6 +468,7 @@ int run_ops(spd_handle* h) {
       HIPCHK(h, run_op(h, op));
     }
   }
+  HIPCHK(h, hipEventRecord(h->ev_step[buf], h->st));
   return SPD_OK;
 }
 
@@ -494,8 +518,8 @@ int build_step(spd_handle* h, DescWriter& dw) {
   const int kd = p.k * p.d;
   auto push_gemv = [&](int kind, std::vector<GemvProb>& g, int stream) {
     if (g.empty()) return;
-    const int plan = finish_tiles(p, g);
-    Op op{kind, dw.put(g.data(), (int)g.size()), (int)g.size(), plan & 0xfffff, 0,
+    const GemvPlan plan = finish_tiles(p, g);
+    Op op{kind, dw.put(g.data(), (int)g.size()), (int)g.size(), plan.ntiles, 0,
           gemv_bytes(g, p.esz)};
     op.stream = stream;
     op.plan = plan;
@@ -812,9 +836,11 @@ int spd_init(const spd_model_config* cfg, const spd_weights* w, const spd_sampli
   auto dev_fail = [&](hipError_t e, const char* what) {
     g_init_error = std::string(what) + ": " + hipGetErrorString(e);
     if (h->h_desc_base) (void)hipHostFree(h->h_desc_base);
-    if (h->h_verdict) (void)hipHostFree(h->h_verdict);
+    if (h->h_verdict_base) (void)hipHostFree(h->h_verdict_base);
     if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
     if (h->ev_join) (void)hipEventDestroy(h->ev_join);
+    for (hipEvent_t ev : h->ev_step)
+      if (ev) (void)hipEventDestroy(ev);
     if (h->st2) (void)hipStreamDestroy(h->st2);
     delete h;
     return SPD_E_DEVICE;
@@ -824,12 +850,14 @@ int spd_init(const spd_model_config* cfg, const spd_weights* w, const spd_sampli
     return dev_fail(e, "hipHostMalloc");
   if ((e = hipHostGetDevicePointer((void**)&h->d_hdesc_base, h->h_desc_base, 0)) != hipSuccess)
     return dev_fail(e, "hipHostGetDevicePointer");
-  h->h_desc = h->h_desc_base;
-  h->d_hdesc = h->d_hdesc_base;
-  if ((e = hipHostMalloc((void**)&h->h_verdict, sizeof(Verdict), hipHostMallocDefault)) != hipSuccess)
+  if ((e = hipHostMalloc((void**)&h->h_verdict_base, 2 * sizeof(Verdict), hipHostMallocDefault)) != hipSuccess)
     return dev_fail(e, "hipHostMalloc");
-  if ((e = hipHostGetDevicePointer((void**)&h->d_hverdict, h->h_verdict, 0)) != hipSuccess)
+  if ((e = hipHostGetDevicePointer((void**)&h->d_hverdict_base, h->h_verdict_base, 0)) != hipSuccess)
     return dev_fail(e, "hipHostGetDevicePointer");
+  use_desc_buf(h, 0);
+  for (hipEvent_t& ev : h->ev_step)
+    if ((e = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess)
+      return dev_fail(e, "hipEventCreateWithFlags");
   // the PDM stream (default priority) and the events that fork and join it each step
   if ((e = hipStreamCreateWithFlags(&h->st2, hipStreamNonBlocking)) != hipSuccess)
     return dev_fail(e, "hipStreamCreateWithFlags");
@@ -937,7 +965,7 @@ int spd_prefill(spd_handle* h, const int32_t* prompt, int32_t len, int32_t* firs
       DescWriter dw{h->h_desc};
       std::vector<GemvProb> g{gemv(h->head, p.V, p.d, H + (size_t)(P - 1) * p.d, 0, 1, EPI_STORE,
                                    h->at<float>(p.o_logits), 0, h->final_norm, 0, p.eps)};
-      const int plan = finish_tiles(p, g);
+      const GemvPlan plan = finish_tiles(p, g);
       const size_t go = dw.put(g.data(), 1);
       const bool sampled = h->temp > 0.f;
       VocabDesc vd{};
@@ -974,7 +1002,7 @@ int spd_prefill(spd_handle* h, const int32_t* prompt, int32_t len, int32_t* firs
     }
   }
   HIPCHK(h, hipStreamSynchronize(st));
-  const int t0 = h->h_verdict->first_token;
+  const int t0 = h->h_verdict_base[h->cur_buf].first_token;
   if (first_token) *first_token = t0;
   h->P0 = len;
   h->F.clear();
@@ -1002,11 +1030,6 @@ void interleave_streams(std::vector<Op>& ops) {
     if (a < main.size()) *out++ = main[a++];
     if (b < side.size()) *out++ = side[b++];
   }
-}
-
-void use_desc_buf(spd_handle* h, int b) {
-  h->h_desc = h->h_desc_base + (size_t)b * kDescBytes;
-  h->d_hdesc = h->d_hdesc_base + (size_t)b * kDescBytes;
 }
 
 bool same_inflight(const std::deque<Inflight>& a, const std::deque<Inflight>& b) {
@@ -1037,8 +1060,7 @@ void prebuild_next(spd_handle* h) {
   layers0.swap(h->pend_layers);
   const bool ex0 = h->pend_exit;
   const int v0 = h->pend_v, d0 = h->pend_dpos, n0 = h->pend_newest;
-  char* hd0 = h->h_desc;
-  char* dd0 = h->d_hdesc;
+  const int buf0 = h->cur_buf;
   const std::string err0 = h->err;
   // build for the predicted state into the block the next step uses
   h->F = F2;
@@ -1064,9 +1086,18 @@ void prebuild_next(spd_handle* h) {
   h->pend_layers.swap(layers0);
   h->pend_exit = ex0;
   h->pend_v = v0; h->pend_dpos = d0; h->pend_newest = n0;
-  h->h_desc = hd0;
-  h->d_hdesc = dd0;
+  use_desc_buf(h, buf0);
   h->err = err0;
+}
+
+// The prebuilt step becomes the pending one.
+void take_prebuilt(spd_handle* h) {
+  h->ops.swap(h->pre_ops);
+  h->pend_layers.swap(h->pre_layers);
+  h->pend_exit = h->pre_exit;
+  h->pend_v = h->pre_v; h->pend_dpos = h->pre_dpos; h->pend_newest = h->pre_newest;
+  h->desc_used = h->pre_used;
+  h->pre_valid = false;
 }
 
 int spd_step(spd_handle* h) {
@@ -1076,30 +1107,47 @@ int spd_step(spd_handle* h) {
     return fail(h, SPD_E_STATE, h->state == spd_handle::S_INIT ? "no prefill" : "a step is pending");
   const int newest = h->F.back().pos;
   if (newest >= h->p.max_ctx) return fail(h, SPD_E_CAPACITY, "newest position reached max_ctx");
-  use_desc_buf(h, h->next_buf);
-  if (h->pre_valid && h->pre_pdm_len == h->pdm_len && same_inflight(h->pre_F, h->F)) {
-    // built while the previous step ran, for exactly this state
-    h->ops.swap(h->pre_ops);
-    h->pend_layers.swap(h->pre_layers);
-    h->pend_exit = h->pre_exit;
-    h->pend_v = h->pre_v; h->pend_dpos = h->pre_dpos; h->pend_newest = h->pre_newest;
-    h->desc_used = h->pre_used;
+  const bool pre_ok = h->pre_valid && h->pre_pdm_len == h->pdm_len && same_inflight(h->pre_F, h->F);
+  if (h->ahead) {
+    // launched while the previous step ran (that step verified nothing, so this state was
+    // fixed at its launch)
+    if (!pre_ok) return fail(h, SPD_E_STATE, "internal: the step launched ahead does not match");
+    take_prebuilt(h);
+    h->pend_buf = h->pre_buf;
+    h->ahead = false;
   } else {
-    DescWriter dw{h->h_desc};
-    int rc = build_step(h, dw);
+    const int b = h->next_buf;
+    if (pre_ok) {
+      // built while the previous step ran, for exactly this state
+      take_prebuilt(h);
+    } else {
+      use_desc_buf(h, b);
+      DescWriter dw{h->h_desc};
+      int rc = build_step(h, dw);
+      if (rc != SPD_OK) return rc;
+      interleave_streams(h->ops);
+      if (dw.used > kDescBytes) return fail(h, SPD_E_CAPACITY, "internal: descriptor block overflow");
+      if (h->ops.empty() || h->ops.front().kind != OP_EMBED)
+        return fail(h, SPD_E_STATE, "internal: a step must start with the embedding");
+      h->desc_used = dw.used;   // uploaded by the embedding kernel
+    }
+    h->pre_valid = false;
+    const int rc = run_ops(h, h->ops, b, h->desc_used);
     if (rc != SPD_OK) return rc;
-    interleave_streams(h->ops);
-    if (dw.used > kDescBytes) return fail(h, SPD_E_CAPACITY, "internal: descriptor block overflow");
-    if (h->ops.empty() || h->ops.front().kind != OP_EMBED)
-      return fail(h, SPD_E_STATE, "internal: a step must start with the embedding");
-    h->desc_used = dw.used;   // uploaded by the embedding kernel
+    h->pend_buf = b;
+    h->next_buf = b ^ 1;
   }
-  h->pre_valid = false;
-  const int rc = run_ops(h);
-  if (rc != SPD_OK) return rc;
   h->state = spd_handle::S_PENDING;
-  h->next_buf ^= 1;
+  // the other block is free: the step that used it last has been verified
   prebuild_next(h);
+  if (h->lookahead && !h->timing && h->pre_valid) {
+    const int rc = run_ops(h, h->pre_ops, h->next_buf, h->pre_used);
+    if (rc != SPD_OK) return rc;
+    h->pre_buf = h->next_buf;
+    h->next_buf ^= 1;
+    h->ahead = true;
+    use_desc_buf(h, h->pend_buf);
+  }
   return SPD_OK;
 }
 
@@ -1107,18 +1155,19 @@ int spd_verify_commit(spd_handle* h, spd_commit* out) {
   if (!h) return SPD_E_ARG;
   h->err.clear();
   if (h->state != spd_handle::S_PENDING) return fail(h, SPD_E_STATE, "no pending step");
-  // The verdict kernels wrote their result straight to pinned host memory; poll the
-  // stream rather than block on it, so the host sees the end of the step at once (the
-  // PDM stream was joined into it before the head).
+  // The verdict kernels wrote their result straight to pinned host memory (this step's
+  // block's slot); poll the step's end event rather than block on it, so the host sees the
+  // end of the step at once (the PDM stream was joined into the caller's before the head;
+  // a step launched ahead may still be running behind it).
   hipError_t qe;
-  while ((qe = hipStreamQuery(h->st)) == hipErrorNotReady) {
+  while ((qe = hipEventQuery(h->ev_step[h->pend_buf])) == hipErrorNotReady) {
   }
   HIPCHK(h, qe);
   if (h->timing) {
     const int rc = collect_timing(h);
     if (rc != SPD_OK) return rc;
   }
-  const Verdict vd = *h->h_verdict;
+  const Verdict vd = h->h_verdict_base[h->pend_buf];
   const Plan& p = h->p;
   h->K += 1;
   for (auto& lp : h->pend_layers) h->kv_len[lp.first] = lp.second + 1;
@@ -1242,7 +1291,8 @@ int spd_debug_copy(const spd_handle* hc, int32_t what, void* dst, size_t bytes) 
 
 int spd_reset(spd_handle* h) {
   if (!h) return SPD_E_ARG;
-  if (h->state == spd_handle::S_PENDING) HIPCHK(h, hipStreamSynchronize(h->st));
+  if (h->state == spd_handle::S_PENDING || h->ahead) HIPCHK(h, hipStreamSynchronize(h->st));
+  h->ahead = false;
   h->state = spd_handle::S_INIT;
   h->F.clear();
   h->pdm_len = 0;
@@ -1262,17 +1312,26 @@ void spd_destroy(spd_handle* h) {
   for (auto e : h->ev) (void)hipEventDestroy(e);
   if (h->st2) (void)hipStreamSynchronize(h->st2);
   if (h->h_desc_base) (void)hipHostFree(h->h_desc_base);
-  if (h->h_verdict) (void)hipHostFree(h->h_verdict);
+  if (h->h_verdict_base) (void)hipHostFree(h->h_verdict_base);
   if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
   if (h->ev_join) (void)hipEventDestroy(h->ev_join);
+  for (hipEvent_t ev : h->ev_step)
+    if (ev) (void)hipEventDestroy(ev);
   if (h->st2) (void)hipStreamDestroy(h->st2);
   delete h;
 }
 
 // ---- measurement -------------------------------------------------------------------
+int spd_lookahead(spd_handle* h, int on) {
+  if (!h) return SPD_E_ARG;
+  h->err.clear();
+  h->lookahead = on != 0;
+  return SPD_OK;
+}
+
 int spd_timing_enable(spd_handle* h, int on) {
   if (!h) return SPD_E_ARG;
-  if (h->state == spd_handle::S_PENDING) return fail(h, SPD_E_STATE, "a step is pending");
+  if (h->state == spd_handle::S_PENDING || h->ahead) return fail(h, SPD_E_STATE, "a step is pending");
   h->timing = on != 0;
   h->serial = on == 2;
   for (int i = 0; i < OP_NKINDS; ++i) { h->kt_ms[i] = 0; h->kt_bytes[i] = 0; h->kt_count[i] = 0; }

@@ -359,12 +359,16 @@ struct LaunchEv {
   } while (0)
 
 enum GemvRole : int { GEMV_PROJ = 0, GEMV_QKV, GEMV_O, GEMV_GATE_UP, GEMV_DOWN, GEMV_HEAD,
-                      GEMV_PDM_QKV, GEMV_PDM_O, GEMV_PDM_GATE_UP, GEMV_PDM_DOWN };
-// Chooses the kernel kind for a grouped launch, fills tile0 / ntiles / ksplit of every
-// problem, and returns the launch plan (kind << 28 | waves per workgroup << 20 |
-// workgroups) for launch_gemv.
-int gemv_plan(GemvProb* probs, int nprob, bool bf16);
-hipError_t launch_gemv(int role, const GemvProb* d_probs, int nprob, int plan, bool bf16,
+                      GEMV_PDM_QKV, GEMV_PDM_O, GEMV_PDM_GATE_UP, GEMV_PDM_DOWN, GEMV_NROLES };
+// How one grouped GEMV launch runs: kernel kind, waves per workgroup, workgroups, and
+// the dynamic LDS each workgroup takes (staged inputs). gemv_plan chooses the kind for
+// a grouped launch and fills tile0 / ntiles / ksplit of every problem.
+struct GemvPlan {
+  int kind = 0, waves = 0, ntiles = 0;
+  int shm = 0;
+};
+GemvPlan gemv_plan(GemvProb* probs, int nprob, bool bf16);
+hipError_t launch_gemv(int role, const GemvProb* d_probs, int nprob, const GemvPlan& plan, bool bf16,
                        const float2* rope, hipStream_t st, LaunchEv ev = {});
 hipError_t launch_attention(const AttnProb* d_probs, int nprob, int ntiles, bool bf16,
                             int hq, int hkv, int hd, int max_ctx, int split_len, bool any_split,

@@ -70,10 +70,11 @@ def test_fullsize_lockstep_with_oracle(wl, T, seed):
     assert rep["steps"] >= cfg.n_stages or rep["stopped_at_near_tie"] is not None
 
 
-def _stream(name, dW, n, T, G, seed=0, speculate_from="input"):
+def _stream(name, dW, n, T, G, seed=0, speculate_from="input", lookahead=False):
     from speculative_pipeline_decoding_amd import SPD
     cfg, _, prompt = workload(name)
     gpu = SPD(cfg, dW, temperature=T, seed=seed, n=n, speculate_from=speculate_from)
+    gpu.lookahead(lookahead)
     toks = [(gpu.prefill(prompt), 0)]
     steps = []
     while len(toks) < G:
@@ -93,7 +94,8 @@ def test_fullsize_lossless_matches_autoregressive(wl):
     cfg, _, prompt = workload(name)
     print(f"[fullsize] lossless n={cfg.n_stages} vs n=1 on the {len(prompt)}-token prompt "
           f"of {name}", flush=True)
-    a, _, _ = _stream(name, dW, cfg.n_stages, 0.0, 32)
+    # the n-stage run launches each refill step's successor with it (as the benchmark does)
+    a, _, _ = _stream(name, dW, cfg.n_stages, 0.0, 32, lookahead=True)
     b, _, sb = _stream(name, dW, 1, 0.0, 32)
     assert sb.N == sb.K and abs(sb.alpha - 1.0) < 1e-12   # n=1: every step commits
     for i, ((ta, fa), (tb, fb)) in enumerate(zip(a, b)):
@@ -107,7 +109,7 @@ def test_fullsize_counting_identity_and_kv_invariants(wl):
     name, dW, _ = wl
     cfg, _, _ = workload(name)
     n = cfg.n_stages
-    toks, steps, st = _stream(name, dW, n, 1.0, 24, seed=5)
+    toks, steps, st = _stream(name, dW, n, 1.0, 24, seed=5, lookahead=True)
     rejects = [i for i, (v, acc, _, _) in enumerate(steps) if v and not acc]
     # the run ends on a verification step; a rejection there has no refill inside the run
     r_prime = len(rejects) - (1 if rejects and rejects[-1] == len(steps) - 1 else 0)

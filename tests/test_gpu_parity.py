@@ -226,6 +226,83 @@ def test_determinism_same_seed_same_bits():
     assert outs[0] == outs[1]
 
 
+def _records(name, lookahead, G, **kw):
+    """Every commit record, KV length and counter of one run through the C ABI."""
+    from speculative_pipeline_decoding_amd import SPD
+    cfg, W, prompt = workload(name)
+    g = SPD(cfg, dev_weights(name), **kw)
+    g.lookahead(lookahead)
+    toks = [g.prefill(prompt)]
+    recs = []
+    while len(toks) < G:
+        g.step()
+        c = g.verify_commit()
+        kv, pl = g.kv_lens()
+        recs.append((c.verified, c.position, c.token, c.accepted, c.draft_token, c.flags,
+                     c.committed_total, c.inflight, c.new_draft, c.newest, tuple(kv), pl))
+        if c.verified:
+            toks.append(c.token)
+    st = g.stats()
+    logits = g.debug("target_logits").tobytes()   # synchronises: no step runs ahead of it now
+    g.close()
+    return toks, recs, (st.K, st.N, st.accepted, st.rejected), logits
+
+
+def _forced(name, p, seed):
+    from oracle.spd import ar_decode
+    cfg, W, prompt = workload(name)
+    return dict(forced_p=p, forced_ref=ar_decode(cfg, W, prompt, G=cfg.gen_len + 8), seed=seed)
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("tiny", {}),
+    ("tiny", dict(temperature=1.0, seed=3)),
+    ("tiny", dict(n=4, temperature=0.7, top_p=0.875, seed=1)),
+    ("mid_bf16_L6_d384_n3", dict(temperature=1.0, seed=7)),
+    ("mid_hybrid_bf16_L8_d256_n4", {}),
+    ("mid_hybrid_bf16_L8_d256_n4", "forced"),
+])
+def test_lookahead_bit_identical(name, kw):
+    """Launching each refill step's successor with it changes when work runs, not what it
+    computes: every record, KV length, counter and the last logits match bit for bit."""
+    if kw == "forced":
+        kw = _forced(name, 0.4, 4)   # frequent rejections: lookahead stops at every verification
+    cfg, W, prompt = workload(name)
+    G = min(cfg.gen_len, 40)
+    print(f"[lookahead] {name} {sorted(k for k in kw)}", flush=True)
+    a = _records(name, False, G, **kw)
+    b = _records(name, True, G, **kw)
+    assert a[0] == b[0] and a[1] == b[1] and a[2] == b[2] and a[3] == b[3]
+    if name == "tiny" and not kw:
+        from oracle.spd import ar_decode
+        assert b[0] == ar_decode(cfg, W, prompt, G=G)   # lossless: greedy decode of the target
+
+
+def test_lookahead_reset_and_timing_guard():
+    """A step launched ahead is drained by spd_reset; timing cannot start under it."""
+    from speculative_pipeline_decoding_amd import SPD, SpdError
+    from speculative_pipeline_decoding_amd.binding import SPD_E_STATE
+    cfg, W, prompt = workload("tiny")
+    ref = _records("tiny", False, 24)[0]
+    g = SPD(cfg, dev_weights("tiny"))
+    g.lookahead(True)
+    g.prefill(prompt)
+    g.step()                 # a refill step (n = 2): its successor is enqueued with it
+    g.verify_commit()
+    with pytest.raises(SpdError) as e:
+        g.timing(True)
+    assert e.value.code == SPD_E_STATE
+    g.reset()
+    toks = [g.prefill(prompt)]
+    while len(toks) < 24:
+        g.step()
+        c = g.verify_commit()
+        if c.verified:
+            toks.append(c.token)
+    g.close()
+    assert toks == ref
+
+
 def test_call_order_and_capacity_errors():
     from speculative_pipeline_decoding_amd import SPD, SpdError
     from speculative_pipeline_decoding_amd.binding import SPD_E_STATE, SPD_E_CAPACITY, SPD_E_ARG
