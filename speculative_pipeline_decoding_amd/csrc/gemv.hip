@@ -194,13 +194,15 @@ __device__ void rows_body(const GemvProb& p, int tile, const float2* __restrict_
 #pragma unroll
   for (int j = 0; j < RR; ++j) rp[j] = row_ptr<T, RR>(p, u0, j, nunits);
   uint4 w[U][RR];
-  // iterations past the end re-read the row's first piece: every load is issued, so the
-  // compiler's count of loads in flight stays exact
+  // iterations past the end re-read the first piece of the input vector (just staged,
+  // so an L2 hit, where a row's first piece may have been streamed out already): every
+  // load is issued, so the compiler's count of loads in flight stays exact
   auto issue = [&](int s, int it) {
     const int k = it * C + lane * E;
-    const int kk = it < niter && k < K ? k : 0;
+    const bool live = it < niter && k < K;
 #pragma unroll
-    for (int j = 0; j < RR; ++j) w[s][j] = load_stream(rp[j] + kk);
+    for (int j = 0; j < RR; ++j)
+      w[s][j] = load_stream(live ? static_cast<const void*>(rp[j] + k) : static_cast<const void*>(p.x));
   };
 #pragma unroll
   for (int s = 0; s < U; ++s) issue(s, s);
