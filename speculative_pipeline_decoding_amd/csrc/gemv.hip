@@ -675,6 +675,8 @@ void launch_kind(int role, dim3 grid, const GemvProb* d_probs, int nprob, const 
 
 }  // namespace
 
+int units_host(const GemvProb& g) { return g.epi == EPI_QKV ? g.rows / 2 : g.rows; }
+
 GemvPlan gemv_plan(GemvProb* v, int n, bool bf16) {
   int mv = 1;
   bool mc = bf16 && n == 1;   // the matrix-core kernel takes one problem per launch
@@ -690,6 +692,9 @@ GemvPlan gemv_plan(GemvProb* v, int n, bool bf16) {
   int kmax = 0;
   for (int i = 0; i < n; ++i) kmax = std::max(kmax, v[i].K);
   const int kpad = bf16 ? rows_kpad<uint16_t>(kmax) : rows_kpad<float>(kmax);
+  // the matrix-core kernel stages every vector whole and then needs most of a CU's LDS:
+  // only a tall matrix (gate/up) streams enough weights per workgroup to earn it
+  for (int i = 0; i < n; ++i) mc = mc && units_host(v[i]) >= kTall;
   int kind = mv <= 1 ? K_ROWS1 : mv == 2 ? K_ROWS2 : K_SPLITK;
   // the rows kernel stages every vector whole in LDS; longer inputs take the split-K kernel
   if (kind != K_SPLITK && (size_t)mv * kpad * 4 > (size_t)kRowsLds) kind = K_SPLITK;
