@@ -591,9 +591,11 @@ enum Kind { K_ROWS1 = 0, K_ROWS2 = 1, K_SPLITK = 2, K_MFMA = 3, K_ROWS1W = 4, K_
 
 template <typename T, int KIND>
 __device__ __forceinline__ void gemv_body(const GemvProb* __restrict__ probs, int nprob,
-                                          const float2* __restrict__ rope) {
+                                          const float2* __restrict__ rope, int tpp) {
   const int b = blockIdx.x;
-  const int pi = find_problem(probs, nprob, b);
+  // tpp > 0: every problem has tpp workgroups (the stage-sliced launches), so the problem
+  // index needs no lookup in the descriptor table
+  const int pi = tpp > 0 ? b / tpp : find_problem(probs, nprob, b);
   const GemvProb& p = probs[pi];
   const int tile = b - p.tile0;
   if constexpr (KIND == K_SPLITK) {
@@ -619,9 +621,9 @@ __device__ __forceinline__ void gemv_body(const GemvProb* __restrict__ probs, in
 #define SPD_GEMV_KERNEL(name)                                                              \
   template <typename T, int KIND>                                                          \
   __global__ __launch_bounds__(KIND == 3 ? 512 : 256) void name(                           \
-      const GemvProb* __restrict__ probs, int nprob,                                       \
-                                              const float2* __restrict__ rope) {           \
-    gemv_body<T, KIND>(probs, nprob, rope);                                                \
+      const GemvProb* __restrict__ probs, int nprob, const float2* __restrict__ rope,       \
+      int tpp) {                                                                           \
+    gemv_body<T, KIND>(probs, nprob, rope, tpp);                                           \
   }
 SPD_GEMV_KERNEL(gemv_proj)
 SPD_GEMV_KERNEL(gemv_qkv)
@@ -637,7 +639,7 @@ SPD_GEMV_KERNEL(pdm_gemv_down)
 
 template <typename T, int KIND>
 void launch_kind(int role, dim3 grid, const GemvProb* d_probs, int nprob, const float2* rope,
-                 hipStream_t st, LaunchEv ev, int waves = kWaves, size_t shm = 0) {
+                 hipStream_t st, LaunchEv ev, int tpp, int waves = kWaves, size_t shm = 0) {
   const dim3 block(waves * 64);
   if constexpr (KIND == K_MFMA) {
     // more than 64 KiB of dynamic LDS: raise each role's limit once
@@ -660,16 +662,16 @@ void launch_kind(int role, dim3 grid, const GemvProb* d_probs, int nprob, const 
     }
   }
   switch (role) {
-    case GEMV_PROJ: SPD_LAUNCH(ev, (gemv_proj<T, KIND>), grid, block, shm, st, d_probs, nprob, rope); break;
-    case GEMV_QKV: SPD_LAUNCH(ev, (gemv_qkv<T, KIND>), grid, block, shm, st, d_probs, nprob, rope); break;
-    case GEMV_O: SPD_LAUNCH(ev, (gemv_o<T, KIND>), grid, block, shm, st, d_probs, nprob, rope); break;
-    case GEMV_GATE_UP: SPD_LAUNCH(ev, (gemv_gate_up<T, KIND>), grid, block, shm, st, d_probs, nprob, rope); break;
-    case GEMV_DOWN: SPD_LAUNCH(ev, (gemv_down<T, KIND>), grid, block, shm, st, d_probs, nprob, rope); break;
-    case GEMV_PDM_QKV: SPD_LAUNCH(ev, (pdm_gemv_qkv<T, KIND>), grid, block, shm, st, d_probs, nprob, rope); break;
-    case GEMV_PDM_O: SPD_LAUNCH(ev, (pdm_gemv_o<T, KIND>), grid, block, shm, st, d_probs, nprob, rope); break;
-    case GEMV_PDM_GATE_UP: SPD_LAUNCH(ev, (pdm_gemv_gate_up<T, KIND>), grid, block, shm, st, d_probs, nprob, rope); break;
-    case GEMV_PDM_DOWN: SPD_LAUNCH(ev, (pdm_gemv_down<T, KIND>), grid, block, shm, st, d_probs, nprob, rope); break;
-    default: SPD_LAUNCH(ev, (gemv_head<T, KIND>), grid, block, shm, st, d_probs, nprob, rope); break;
+    case GEMV_PROJ: SPD_LAUNCH(ev, (gemv_proj<T, KIND>), grid, block, shm, st, d_probs, nprob, rope, tpp); break;
+    case GEMV_QKV: SPD_LAUNCH(ev, (gemv_qkv<T, KIND>), grid, block, shm, st, d_probs, nprob, rope, tpp); break;
+    case GEMV_O: SPD_LAUNCH(ev, (gemv_o<T, KIND>), grid, block, shm, st, d_probs, nprob, rope, tpp); break;
+    case GEMV_GATE_UP: SPD_LAUNCH(ev, (gemv_gate_up<T, KIND>), grid, block, shm, st, d_probs, nprob, rope, tpp); break;
+    case GEMV_DOWN: SPD_LAUNCH(ev, (gemv_down<T, KIND>), grid, block, shm, st, d_probs, nprob, rope, tpp); break;
+    case GEMV_PDM_QKV: SPD_LAUNCH(ev, (pdm_gemv_qkv<T, KIND>), grid, block, shm, st, d_probs, nprob, rope, tpp); break;
+    case GEMV_PDM_O: SPD_LAUNCH(ev, (pdm_gemv_o<T, KIND>), grid, block, shm, st, d_probs, nprob, rope, tpp); break;
+    case GEMV_PDM_GATE_UP: SPD_LAUNCH(ev, (pdm_gemv_gate_up<T, KIND>), grid, block, shm, st, d_probs, nprob, rope, tpp); break;
+    case GEMV_PDM_DOWN: SPD_LAUNCH(ev, (pdm_gemv_down<T, KIND>), grid, block, shm, st, d_probs, nprob, rope, tpp); break;
+    default: SPD_LAUNCH(ev, (gemv_head<T, KIND>), grid, block, shm, st, d_probs, nprob, rope, tpp); break;
   }
 }
 
@@ -732,6 +734,9 @@ GemvPlan gemv_plan(GemvProb* v, int n, bool bf16) {
   GemvPlan out;
   out.kind = kind;
   out.ntiles = t;
+  out.tpp = v[0].ntiles;
+  for (int i = 1; i < n; ++i)
+    if (v[i].ntiles != v[0].ntiles) out.tpp = 0;
   out.waves = kind == K_MFMA ? v[0].pad * v[0].ksplit : kWaves;
   const int nvs = kind == K_ROWS2 || kind == K_ROWS2W ? 2 : 1;
   out.shm = kind == K_MFMA     ? mc_lds_bytes(v[0].nvec, v[0].K, out.waves)
@@ -746,23 +751,24 @@ hipError_t launch_gemv(int role, const GemvProb* d_probs, int nprob, const GemvP
   if (ntiles <= 0 || nprob <= 0) return hipSuccess;
   const dim3 grid(ntiles);
   const size_t shm = plan.shm;
+  const int tpp = plan.tpp;
   if (bf16) {
     switch (kind) {
-      case K_ROWS1: launch_kind<uint16_t, K_ROWS1>(role, grid, d_probs, nprob, rope, st, ev, kWaves, shm); break;
-      case K_ROWS2: launch_kind<uint16_t, K_ROWS2>(role, grid, d_probs, nprob, rope, st, ev, kWaves, shm); break;
-      case K_SPLITK: launch_kind<uint16_t, K_SPLITK>(role, grid, d_probs, nprob, rope, st, ev); break;
-      case K_MFMA: launch_kind<uint16_t, K_MFMA>(role, grid, d_probs, nprob, rope, st, ev, waves, shm); break;
-      case K_ROWS1W: launch_kind<uint16_t, K_ROWS1W>(role, grid, d_probs, nprob, rope, st, ev, kWaves, shm); break;
-      case K_ROWS2W: launch_kind<uint16_t, K_ROWS2W>(role, grid, d_probs, nprob, rope, st, ev, kWaves, shm); break;
+      case K_ROWS1: launch_kind<uint16_t, K_ROWS1>(role, grid, d_probs, nprob, rope, st, ev, tpp, kWaves, shm); break;
+      case K_ROWS2: launch_kind<uint16_t, K_ROWS2>(role, grid, d_probs, nprob, rope, st, ev, tpp, kWaves, shm); break;
+      case K_SPLITK: launch_kind<uint16_t, K_SPLITK>(role, grid, d_probs, nprob, rope, st, ev, tpp); break;
+      case K_MFMA: launch_kind<uint16_t, K_MFMA>(role, grid, d_probs, nprob, rope, st, ev, tpp, waves, shm); break;
+      case K_ROWS1W: launch_kind<uint16_t, K_ROWS1W>(role, grid, d_probs, nprob, rope, st, ev, tpp, kWaves, shm); break;
+      case K_ROWS2W: launch_kind<uint16_t, K_ROWS2W>(role, grid, d_probs, nprob, rope, st, ev, tpp, kWaves, shm); break;
       default: return hipErrorInvalidValue;
     }
   } else {
     switch (kind) {
-      case K_ROWS1: launch_kind<float, K_ROWS1>(role, grid, d_probs, nprob, rope, st, ev, kWaves, shm); break;
-      case K_ROWS2: launch_kind<float, K_ROWS2>(role, grid, d_probs, nprob, rope, st, ev, kWaves, shm); break;
-      case K_SPLITK: launch_kind<float, K_SPLITK>(role, grid, d_probs, nprob, rope, st, ev); break;
-      case K_ROWS1W: launch_kind<float, K_ROWS1W>(role, grid, d_probs, nprob, rope, st, ev, kWaves, shm); break;
-      case K_ROWS2W: launch_kind<float, K_ROWS2W>(role, grid, d_probs, nprob, rope, st, ev, kWaves, shm); break;
+      case K_ROWS1: launch_kind<float, K_ROWS1>(role, grid, d_probs, nprob, rope, st, ev, tpp, kWaves, shm); break;
+      case K_ROWS2: launch_kind<float, K_ROWS2>(role, grid, d_probs, nprob, rope, st, ev, tpp, kWaves, shm); break;
+      case K_SPLITK: launch_kind<float, K_SPLITK>(role, grid, d_probs, nprob, rope, st, ev, tpp); break;
+      case K_ROWS1W: launch_kind<float, K_ROWS1W>(role, grid, d_probs, nprob, rope, st, ev, tpp, kWaves, shm); break;
+      case K_ROWS2W: launch_kind<float, K_ROWS2W>(role, grid, d_probs, nprob, rope, st, ev, tpp, kWaves, shm); break;
       default: return hipErrorInvalidValue;
     }
   }

@@ -366,6 +366,7 @@ enum GemvRole : int { GEMV_PROJ = 0, GEMV_QKV, GEMV_O, GEMV_GATE_UP, GEMV_DOWN, 
 struct GemvPlan {
   int kind = 0, waves = 0, ntiles = 0;
   int shm = 0;
+  int tpp = 0;   // workgroups of every problem when all problems have the same count, else 0
 };
 GemvPlan gemv_plan(GemvProb* probs, int nprob, bool bf16);
 hipError_t launch_gemv(int role, const GemvProb* d_probs, int nprob, const GemvPlan& plan, bool bf16,
