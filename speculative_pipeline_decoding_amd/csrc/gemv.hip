@@ -175,17 +175,21 @@ __device__ void rows_body(const GemvProb& p, int tile, const float2* __restrict_
   const int niter = KP / C;
   const float* __restrict__ g = p.gain;
 
-  // staging loads of the first round go out before the weight ring
+  // staging loads of the first round go out before the weight ring; vector v takes its
+  // own gain (g + v * gain_stride: the shared head sweep normalises its two rows with
+  // different gains)
   const int NT = blockDim.x;
-  float4 xr[NV][kRowsStage], gr[kRowsStage];
+  float4 xr[NV][kRowsStage], gr[NV][kRowsStage];
   auto stage_load = [&](int c0) {
 #pragma unroll
     for (int u = 0; u < kRowsStage; ++u) {
       const int c = min(c0 + 4 * NT * u, K - 4);
-      gr[u] = g ? load_g4(g + c) : make_float4(1.f, 1.f, 1.f, 1.f);
 #pragma unroll
-      for (int v = 0; v < NV; ++v)
-        xr[v][u] = v < nv ? load_g4(p.x + v * p.x_stride + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int v = 0; v < NV; ++v) {
+        const bool live = v < nv;
+        xr[v][u] = live ? load_g4(p.x + v * p.x_stride + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+        gr[v][u] = g && live ? load_g4(g + v * p.gain_stride + c) : make_float4(1.f, 1.f, 1.f, 1.f);
+      }
     }
   };
   stage_load(4 * threadIdx.x);
@@ -219,7 +223,7 @@ __device__ void rows_body(const GemvProb& p, int tile, const float2* __restrict_
         float* dst = xs + rows_lds_col<T>(c);
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
-          const float4 x = xr[v][u], gg = gr[u];
+          const float4 x = xr[v][u], gg = gr[v][u];
           ss[v] += x.x * x.x; ss[v] += x.y * x.y; ss[v] += x.z * x.z; ss[v] += x.w * x.w;
           *reinterpret_cast<float4*>(dst + v * KP) =
               make_float4(x.x * gg.x, x.y * gg.y, x.z * gg.z, x.w * gg.w);

@@ -118,6 +118,48 @@ def test_mid_hybrid_planned_uneven_split(T):
     assert rep["steps"] > 0
 
 
+@pytest.mark.parametrize("T", [0.0, 1.0])
+def test_wide_ffn_down_projection_on_split_k(T):
+    """An FFN wider than the rows kernel's LDS stage (16904 fp32 inputs to the down
+    projection, 66 KiB) runs that GEMV on the split-K kernel; lockstep with the oracle."""
+    import dataclasses
+    import torch
+    from spd_inputs import get, make_prompt, make_weights
+    from speculative_pipeline_decoding_amd import upload_weights
+    cfg = dataclasses.replace(get("mid_bf16_L7_d256_n3_uneven"), name="mid_bf16_L7_d256_ffn16904",
+                              d_ffn=16904)
+    W = make_weights(cfg)
+    prompt = make_prompt(cfg)
+    _dev.clear()
+    torch.cuda.empty_cache()
+    print(f"[parity] {cfg.name} T={T}", flush=True)
+    rep = run_parity(cfg, W, upload_weights(cfg, W), prompt, T=T, seed=5)
+    print(f"[parity] -> {rep}", flush=True)
+    assert rep["steps"] > 0
+
+
+@pytest.mark.parametrize("name,T", [("tiny", 0.0), ("tiny", 1.0), ("mid_bf16_L6_d384_n3", 0.0),
+                                    ("mid_bf16_L6_d384_n3", 1.0), ("mid_hybrid_bf16_L8_d256_n4", 1.0)])
+def test_non_unit_norm_gains(name, T):
+    """Every RMSNorm gain drawn as 1 + 0.25 N(0, 1) (the synthetic weights use gains of 1,
+    under which a gain applied to the wrong row or vector goes unseen): lockstep with the
+    oracle, including the head sweep that normalises the exiting token with the target's
+    final gain and the PDM's newest row with its own."""
+    import torch
+    from speculative_pipeline_decoding_amd import upload_weights
+    cfg, W, prompt = workload(name)
+    rng = np.random.default_rng(123)
+    W2 = {k: ((1.0 + 0.25 * rng.standard_normal(v.shape)).astype(np.float32) if k.endswith("norm")
+              else v) for k, v in W.items()}
+    assert sum(1 for k in W2 if k.endswith("norm")) >= 2 * cfg.n_layers + 2
+    _dev.clear()
+    torch.cuda.empty_cache()
+    print(f"[parity] {name} random gains T={T}", flush=True)
+    rep = run_parity(cfg, W2, upload_weights(cfg, W2), prompt, T=T, seed=3)
+    print(f"[parity] -> {rep}", flush=True)
+    assert rep["steps"] > 0
+
+
 def test_layer_timing_single_token_passes():
     """At n = 1 every sub-layer launch serves one layer: each layer gets one timed pass
     per step, with a positive kernel time."""
