@@ -239,6 +239,32 @@ def test_degenerate_shapes(name, kw):
     assert rep["steps"] > 0
 
 
+@pytest.mark.parametrize("kw", [{}, {"T": 1.0, "seed": 6}, "forced"])
+def test_maximum_sizes(kw):
+    """The library's largest pipeline: n = 16 stages of one layer, k = 8 anchors, and n + 1
+    = 17 PDM window rows (past the matrix-core GEMV's 16 columns: the split-K kernel)."""
+    import dataclasses
+    import torch
+    from oracle.spd import ar_decode
+    from spd_inputs import get, make_prompt, make_weights
+    from speculative_pipeline_decoding_amd import upload_weights
+    cfg = dataclasses.replace(get("mid_bf16_L7_d256_n3_uneven"), name="max_bf16_L16_d256_n16",
+                              n_layers=16, n_stages=16, anchors=(0, 1, 2, 4, 6, 9, 12, 16),
+                              pdm_layers=2, prompt_len=40, gen_len=14, max_ctx=96)
+    W = make_weights(cfg)
+    prompt = make_prompt(cfg)
+    if kw == "forced":
+        kw = {"forced_p": 0.75, "forced_ref": ar_decode(cfg, W, prompt, G=cfg.gen_len + 20),
+              "seed": 8}
+    _dev.clear()
+    torch.cuda.empty_cache()
+    print(f"[parity] {cfg.name} {sorted(kw)}", flush=True)
+    rep = run_parity(cfg, W, upload_weights(cfg, W), prompt, **kw)
+    print(f"[parity] -> steps {rep['steps']} N {rep.get('N')} rejected {rep.get('rejected')} "
+          f"err {rep['max_logit_err']:.2e}", flush=True)
+    assert rep["steps"] >= cfg.n_stages
+
+
 def test_mid_forced_acceptance():
     from oracle.spd import ar_decode
     cfg, W, prompt = workload("mid_bf16_L6_d384_n3")
