@@ -588,10 +588,10 @@ __device__ void mfma_body(const GemvProb& p, int tile, const float2* __restrict_
   }
 }
 
-// Kernel kinds: 1 or 2 vectors (rows kernel; the W kinds give each wave 8 rows, for tall
-// matrices), 3..16 vectors on the matrix cores (bf16 weights, input staged whole in LDS),
-// else up to kMaxVec (split-K).
-enum Kind { K_ROWS1 = 0, K_ROWS2 = 1, K_SPLITK = 2, K_MFMA = 3, K_ROWS1W = 4, K_ROWS2W = 5 };
+// Kernel kinds: 1 or 2 vectors (rows kernel; K_ROWS2W gives each wave 8 rows, for the
+// two-vector head sweep), 3..16 vectors on the matrix cores (bf16 weights, input staged
+// whole in LDS: tall matrices only), else up to kMaxVec (split-K).
+enum Kind { K_ROWS1 = 0, K_ROWS2 = 1, K_SPLITK = 2, K_MFMA = 3, K_ROWS2W = 5 };
 
 template <typename T, int KIND>
 __device__ __forceinline__ void gemv_body(const GemvProb* __restrict__ probs, int nprob,
@@ -613,8 +613,8 @@ __device__ __forceinline__ void gemv_body(const GemvProb* __restrict__ probs, in
     __shared__ float red[kMcMaxWaves * kMcMaxVec];
     mfma_body(p, tile, rope, planes, red);
   } else {
-    constexpr bool wide = KIND == K_ROWS1W || KIND == K_ROWS2W;
-    constexpr int NV = KIND == K_ROWS1 || KIND == K_ROWS1W ? 1 : 2;
+    constexpr bool wide = KIND == K_ROWS2W;
+    constexpr int NV = KIND == K_ROWS1 ? 1 : 2;
     extern __shared__ float rows_xs[];
     __shared__ float red[kWaves * NV];
     rows_body<T, NV, wide ? RWIDE : RW, wide ? kRingWide : kRing>(p, tile, rope, rows_xs, red);
@@ -710,7 +710,7 @@ GemvPlan gemv_plan(GemvProb* v, int n, bool bf16) {
     bool tall = true;
     for (int i = 0; i < n; ++i)
       tall = tall && (v[i].epi == EPI_QKV ? v[i].rows / 2 : v[i].rows) >= kTall;
-    if (tall) kind = kind == K_ROWS1 ? K_ROWS1W : K_ROWS2W;
+    if (tall) kind = K_ROWS2W;
   }
   int t = 0;
   for (int i = 0; i < n; ++i) {
@@ -728,7 +728,7 @@ GemvPlan gemv_plan(GemvProb* v, int n, bool bf16) {
       g.pad = rt;
       g.ntiles = (wt + rt - 1) / rt;
     } else {
-      const int rw = kind == K_ROWS1W || kind == K_ROWS2W ? RWIDE : RW;
+      const int rw = kind == K_ROWS2W ? RWIDE : RW;
       const int upt = kind == K_SPLITK ? (pr ? RW / 2 : RW) : kWaves * (pr ? rw / 2 : rw);
       g.ntiles = (units + upt - 1) / upt;
     }
@@ -762,7 +762,6 @@ hipError_t launch_gemv(int role, const GemvProb* d_probs, int nprob, const GemvP
       case K_ROWS2: launch_kind<uint16_t, K_ROWS2>(role, grid, d_probs, nprob, rope, st, ev, tpp, kWaves, shm); break;
       case K_SPLITK: launch_kind<uint16_t, K_SPLITK>(role, grid, d_probs, nprob, rope, st, ev, tpp); break;
       case K_MFMA: launch_kind<uint16_t, K_MFMA>(role, grid, d_probs, nprob, rope, st, ev, tpp, waves, shm); break;
-      case K_ROWS1W: launch_kind<uint16_t, K_ROWS1W>(role, grid, d_probs, nprob, rope, st, ev, tpp, kWaves, shm); break;
       case K_ROWS2W: launch_kind<uint16_t, K_ROWS2W>(role, grid, d_probs, nprob, rope, st, ev, tpp, kWaves, shm); break;
       default: return hipErrorInvalidValue;
     }
@@ -771,7 +770,6 @@ hipError_t launch_gemv(int role, const GemvProb* d_probs, int nprob, const GemvP
       case K_ROWS1: launch_kind<float, K_ROWS1>(role, grid, d_probs, nprob, rope, st, ev, tpp, kWaves, shm); break;
       case K_ROWS2: launch_kind<float, K_ROWS2>(role, grid, d_probs, nprob, rope, st, ev, tpp, kWaves, shm); break;
       case K_SPLITK: launch_kind<float, K_SPLITK>(role, grid, d_probs, nprob, rope, st, ev, tpp); break;
-      case K_ROWS1W: launch_kind<float, K_ROWS1W>(role, grid, d_probs, nprob, rope, st, ev, tpp, kWaves, shm); break;
       case K_ROWS2W: launch_kind<float, K_ROWS2W>(role, grid, d_probs, nprob, rope, st, ev, tpp, kWaves, shm); break;
       default: return hipErrorInvalidValue;
     }
