@@ -313,14 +313,18 @@ int fail(spd_handle* h, int code, const std::string& m) {
   } while (0)
 
 // ---- descriptor block builder -------------------------------------------------
+// Appends descriptors to one pinned staging block. Nothing is written past the block (the
+// other block may belong to a step on the GPU): an item that does not fit is dropped,
+// `used` still counts it, and the caller rejects the step when used > kDescBytes.
 struct DescWriter {
   char* base;
   size_t used = 0;
   template <typename T> size_t put(const T* items, int count) {
     used = align_up(used, 64);
     const size_t at = used;
-    std::memcpy(base + at, items, sizeof(T) * count);
-    used += sizeof(T) * count;
+    const size_t n = sizeof(T) * (size_t)count;
+    if (at + n <= kDescBytes) std::memcpy(base + at, items, n);
+    used += n;
     return at;
   }
 };
