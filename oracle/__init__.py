@@ -32,5 +32,11 @@ KV cache, is applied explicitly.
 
 Parity pins live in tests/test_oracle_*.py. Every function here is pinned by
 at least one of them; none is "parity unpinned" except the pages' printed
-speedups, which need trained models and cannot be reproduced.
+speedups, which need trained models and cannot be reproduced. The PDM's draft
+path (anchor aggregation, projection, the speculation layers over the window,
+its own final norm and the tied head) and the PDM prefill are pinned against a
+route that steps no pipeline: one causal forward of the target for every
+position's depths, one causal forward of the PDM over the step's feature rows
+(tests/test_oracle_pdm.py, which also plants three mistakes in copies of the
+PDM pass and requires each to fail).
 """

@@ -163,6 +163,25 @@ class SPD:
                 parts.append(np.zeros(d, self.m.ft))
         return self.m.W("pdm.proj") @ np.concatenate(parts)
 
+    # -- the PDM over its window ----------------------------------------------------
+    def pdm_pass(self, newest: int):
+        """PDM over the rows pdm_len .. newest at the depths they have now.
+
+        Rows before the oldest in-flight position are at depth L (their features are
+        final and their PDM KV rows are rewritten here once more, then kept); in-flight
+        rows carry their current, partial depth. Each row runs the Ls layers at its own
+        absolute position, attending over the PDM KV at positions <= its own. The newest
+        row's final-normed state (the PDM's own final norm) goes through the tied head.
+        Returns (rows, their depths, the newest row's logits)."""
+        m, L = self.m, self.L
+        rows = list(range(self.pdm_len, newest + 1))
+        depths = [self.depth.get(x, L) for x in rows]
+        Z = {x: self.feature(x) for x in rows}
+        for r in range(self.Ls):
+            for x in rows:
+                Z[x] = m.pdm.decode_layer(r, Z[x], x)
+        return rows, depths, m.logits(Z[newest], "pdm.final_norm")
+
     # -- one pipeline step ------------------------------------------------------
     def step(self) -> StepRecord:
         m, n, L, B = self.m, self.n, self.L, self.B
@@ -174,16 +193,6 @@ class SPD:
         self.anch[newest] = {0: h0.copy()}
         self.depth[newest] = 0
         exiting = self.F[0][1] == n - 1
-
-        def pdm_pass():
-            """PDM over the rows pdm_len .. newest at the depths they have now."""
-            rows = list(range(self.pdm_len, newest + 1))
-            depths = [self.depth.get(x, L) for x in rows]
-            Z = {x: self.feature(x) for x in rows}
-            for r in range(self.Ls):
-                for x in rows:
-                    Z[x] = m.pdm.decode_layer(r, Z[x], x)
-            return rows, depths, m.logits(Z[newest], "pdm.final_norm")
 
         def target_pass():
             """Each in-flight token runs its stage's layers."""
@@ -200,12 +209,12 @@ class SPD:
         if self.output_states:
             # 3, then 2: the PDM reads the states the step produced
             target_pass()
-            rows, depths, z_q = pdm_pass()
+            rows, depths, z_q = self.pdm_pass(newest)
             # positions whose depth is L now (the exiting one included) become permanent
             self.pdm_len = max(self.pdm_len, self.F[0][0] + (1 if exiting else 0))
         else:
             # 2. PDM on the step's input states (early start)
-            rows, depths, z_q = pdm_pass()
+            rows, depths, z_q = self.pdm_pass(newest)
             # positions whose depth is already L become permanent PDM rows
             self.pdm_len = max(self.pdm_len, self.F[0][0])
             # 3. target

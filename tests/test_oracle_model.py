@@ -1,90 +1,18 @@
 """Pins for the oracle's decoder against an independent formulation built from library routines.
 
-The reference here is written from the textbook definitions with other
-primitives than the oracle uses: torch's scaled_dot_product_attention (GQA),
-torch's rms_norm and silu, RoPE in complex form, and the closed-form sum for
+The reference (tests/reference_torch.py) is written from the textbook definitions
+with other primitives than the oracle uses: torch's scaled_dot_product_attention
+(GQA), torch's rms_norm and silu, RoPE in complex form, and the closed-form sum for
 linear attention. The bf16 roundings use torch's own float->bfloat16 cast.
 """
 import numpy as np
 import pytest
-import torch
-import torch.nn.functional as F
 
 from conftest import workload
-from oracle.model import Model, lin_gammas
+from oracle.model import Model
 from oracle.spd import ar_decode
-from spd_inputs import LINEAR, SOFTMAX
-
-f64 = torch.float64
-
-
-def _t(W, name):
-    a = W[name]
-    if a.dtype == np.uint16:
-        return torch.from_numpy((a.astype(np.uint32) << 16).view(np.float32)).to(f64)
-    return torch.from_numpy(a).to(f64)
-
-
-def _bf(x):
-    return x.to(torch.float32).to(torch.bfloat16).to(f64)
-
-
-def _f32(x):
-    return x.to(torch.float32).to(f64)
-
-
-def _rope(x, pos, theta):
-    hd = x.shape[-1]
-    half = hd // 2
-    w = theta ** (-2.0 * torch.arange(half, dtype=f64) / hd)
-    ang = pos.to(f64)[:, None, None] * w
-    z = torch.complex(x[..., :half], x[..., half:]) * torch.polar(torch.ones_like(ang), ang)
-    return torch.cat([z.real, z.imag], dim=-1)
-
-
-def _linear_closed_form(q, k, v, gam):
-    """o_t = sum_{j<=t} gamma^(t-j) (qh_t . kh_j) v_j for every head (no recurrence)."""
-    P = q.shape[0]
-    qh = q / torch.sqrt((q * q).sum(-1, keepdim=True) + 1e-6)
-    kh = k / torch.sqrt((k * k).sum(-1, keepdim=True) + 1e-6)
-    t = torch.arange(P, dtype=f64)
-    decay = gam[None, None, :] ** (t[:, None, None] - t[None, :, None])       # [t, j, h]
-    decay = torch.where((t[:, None] >= t[None, :])[..., None], decay, torch.zeros_like(decay))
-    s = torch.einsum("thd,jhd->tjh", qh, kh) * decay
-    return torch.einsum("tjh,jhd->thd", s, v)
-
-
-def torch_forward(cfg, W, tokens, round_gemm=False):
-    """Whole-prompt forward; returns (final residual rows, logits of the last row)."""
-    bf16 = cfg.dtype == "bf16"
-    store = _bf if bf16 else _f32
-    gin = _bf if (bf16 and round_gemm) else (lambda x: x)
-    d, hq, hkv, hd = cfg.d_model, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
-    P = len(tokens)
-    pos = torch.arange(P)
-    H = _t(W, "embed")[torch.from_numpy(np.asarray(tokens, np.int64))]
-    for l in range(cfg.n_layers):
-        p = f"layers.{l}."
-        a = F.rms_norm(H, (d,), _t(W, p + "attn_norm"), cfg.rms_eps)
-        qkv = gin(a) @ _t(W, p + "w_qkv").T
-        if cfg.kinds[l] == SOFTMAX:
-            q = _rope(qkv[:, :hq * hd].reshape(P, hq, hd), pos, cfg.rope_theta)
-            k = store(_rope(qkv[:, hq * hd:(hq + hkv) * hd].reshape(P, hkv, hd), pos, cfg.rope_theta))
-            v = store(qkv[:, (hq + hkv) * hd:].reshape(P, hkv, hd))
-            o = F.scaled_dot_product_attention(q.transpose(0, 1)[None], k.transpose(0, 1)[None],
-                                               v.transpose(0, 1)[None], is_causal=True,
-                                               enable_gqa=True)[0].transpose(0, 1)
-        else:
-            q = qkv[:, :hq * hd].reshape(P, hq, hd)
-            k = qkv[:, hq * hd:2 * hq * hd].reshape(P, hq, hd)
-            v = qkv[:, 2 * hq * hd:].reshape(P, hq, hd)
-            o = _linear_closed_form(q, k, v, torch.from_numpy(lin_gammas(hq)))
-        H = H + gin(o.reshape(P, -1)) @ _t(W, p + "w_o").T
-        b = gin(F.rms_norm(H, (d,), _t(W, p + "ffn_norm"), cfg.rms_eps))
-        act = F.silu(b @ _t(W, p + "w_gate").T) * (b @ _t(W, p + "w_up").T)
-        H = H + gin(act) @ _t(W, p + "w_down").T
-    z = _t(W, "lm_head") @ F.rms_norm(H[-1], (d,), _t(W, "final_norm"), cfg.rms_eps)
-    return H.numpy(), z.numpy()
+from reference_torch import torch_forward
+from spd_inputs import LINEAR
 
 
 @pytest.mark.parametrize("name,plen,tol", [("tiny", 32, 1e-11), ("mid_bf16_L6_d384_n3", 40, 1e-9),
