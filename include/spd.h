@@ -134,7 +134,11 @@ typedef struct {
  * forced_mode = 1 (temperature 0 only) replaces each draft at position x by
  * forced_ref[x - P0] with probability forced_p, else by (forced_ref[x - P0] + 1) mod V,
  * where P0 is the prompt length given to spd_prefill; positions past the end
- * of forced_ref keep the PDM's draft. forced_ref [host] is copied at spd_prefill.
+ * of forced_ref keep the PDM's draft. forced_ref [host] holds ids in [0, V) (else
+ * spd_init returns SPD_E_ARG); spd_init copies it, and spd_prefill uploads it.
+ * If a rejection finds no token with p > q in floating point (the residual
+ * max(0, p - q) has no mass), the committed token is the target's argmax and the
+ * decision is flagged as a near-tie.
  */
 typedef struct {
   float temperature;
@@ -153,14 +157,16 @@ size_t spd_workspace_bytes(const spd_model_config* cfg);
  * Validate the configuration, carve the caller's workspace, bind the weight
  * pointers, and precompute the RoPE table. hip_stream is a hipStream_t (NULL:
  * the null stream). The workspace must stay valid and unused by the caller
- * until spd_destroy. Errors: SPD_E_ARG, SPD_E_CONFIG, SPD_E_CAPACITY (ws_bytes
- * too small), SPD_E_DEVICE.
+ * until spd_destroy. Errors: SPD_E_ARG (NULL pointers, bad sampling values, a
+ * forced_ref id outside [0, V)), SPD_E_CONFIG, SPD_E_CAPACITY (ws_bytes too small),
+ * SPD_E_DEVICE.
  */
 int spd_init(const spd_model_config* cfg, const spd_weights* w, const spd_sampling* s,
              void* d_workspace, size_t ws_bytes, void* hip_stream, spd_handle** out);
 
 /*
- * Run the target over the prompt [host, len token ids in [0, V)] in chunks,
+ * Run the target over the prompt [host, len token ids in [0, V), any length below
+ * max_ctx: it is uploaded through the pinned staging in 512 KiB pieces] in chunks,
  * writing the target KV cache, the anchor states of every prompt position, the
  * PDM KV cache over the verified prefix (its depth-maximised features: all
  * anchors), and the first generated token (greedy, or sampled at T > 0).

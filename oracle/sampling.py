@@ -250,7 +250,12 @@ def verify(z_t: np.ndarray, d: int, q: Optional[np.ndarray], s: Sampling, v: int
         flag = flag or not (sure_accept or sure_reject)
     if lhs < rhs:
         return int(d), True, bool(flag)
-    y, rflag = gumbel_max(np.maximum(p - q, 0.0), s.seed, STREAM_RES, v)
+    r = np.maximum(p - q, 0.0)
+    if not (r > 0).any():
+        # p <= q everywhere in floating point (the two agree to rounding), so the residual
+        # has no mass to sample from: commit the target's argmax, flagged as a near-tie
+        return argmax_lowest(z_t), False, True
+    y, rflag = gumbel_max(r, s.seed, STREAM_RES, v)
     if top_p_ranges and not rflag:
         G = gumbel(uniform(s.seed, STREAM_RES, v, np.arange(p.size)))
         with np.errstate(divide="ignore"):

@@ -831,8 +831,15 @@ int spd_init(const spd_model_config* cfg, const spd_weights* w, const spd_sampli
     if (!ptr) { g_init_error = "null PDM layer weight"; delete h; return SPD_E_ARG; }
   h->temp = s->temperature; h->top_p = s->top_p; h->seed = s->seed;
   h->forced_mode = s->forced_mode; h->forced_p = s->forced_p;
-  if (s->forced_mode && s->forced_ref_len > 0)
+  if (s->forced_mode && s->forced_ref_len > 0) {
+    for (int i = 0; i < s->forced_ref_len; ++i)
+      if (s->forced_ref[i] < 0 || s->forced_ref[i] >= p.V) {
+        g_init_error = "forced_ref id out of range [0, vocab)";
+        delete h;
+        return SPD_E_ARG;
+      }
     h->forced_ref.assign(s->forced_ref, s->forced_ref + s->forced_ref_len);
+  }
   if ((int)h->forced_ref.size() > p.max_ctx) h->forced_ref.resize(p.max_ctx);
   h->ws = static_cast<char*>(d_workspace);
   h->st = static_cast<hipStream_t>(hip_stream);
@@ -896,16 +903,23 @@ int spd_prefill(spd_handle* h, const int32_t* prompt, int32_t len, int32_t* firs
     if (prompt[i] < 0 || prompt[i] >= p.V) return fail(h, SPD_E_ARG, "token id out of range");
   hipStream_t st = h->st;
   int* toks = h->at<int>(p.o_ptok);
-  // prompt and forced reference share one staging copy
-  std::memcpy(h->h_desc, prompt, (size_t)len * 4);
-  HIPCHK(h, hipMemcpyAsync(toks, h->h_desc, (size_t)len * 4, hipMemcpyHostToDevice, st));
-  HIPCHK(h, hipStreamSynchronize(st));
-  if (!h->forced_ref.empty()) {
-    std::memcpy(h->h_desc, h->forced_ref.data(), h->forced_ref.size() * 4);
-    HIPCHK(h, hipMemcpyAsync(h->ws + p.o_forced, h->h_desc, h->forced_ref.size() * 4,
-                             hipMemcpyHostToDevice, st));
-    HIPCHK(h, hipStreamSynchronize(st));
-  }
+  // The prompt and the forced reference go to the device through the pinned staging block,
+  // one block's worth at a time (no step is in flight before a prefill, so the block is free)
+  auto upload = [&](void* dst, const int32_t* src, size_t count) -> int {
+    const size_t per = kDescBytes / sizeof(int32_t);
+    for (size_t i = 0; i < count; i += per) {
+      const size_t c = std::min(per, count - i);
+      std::memcpy(h->h_desc, src + i, c * sizeof(int32_t));
+      HIPCHK(h, hipMemcpyAsync(static_cast<char*>(dst) + i * sizeof(int32_t), h->h_desc,
+                               c * sizeof(int32_t), hipMemcpyHostToDevice, st));
+      HIPCHK(h, hipStreamSynchronize(st));
+    }
+    return SPD_OK;
+  };
+  int urc = upload(toks, prompt, (size_t)len);
+  if (urc == SPD_OK && !h->forced_ref.empty())
+    urc = upload(h->ws + p.o_forced, h->forced_ref.data(), h->forced_ref.size());
+  if (urc != SPD_OK) return urc;
   const bool bf = p.bf16;
   float* H = h->at<float>(p.o_pH);
   float* A = h->at<float>(p.o_pA);

@@ -571,11 +571,21 @@ __global__ __launch_bounds__(kVocabBlock) void residual_final_kernel(
   for (int i = threadIdx.x; i < f.nblocks; i += blockDim.x)
     m = merge(m, from_partial(part[2 * f.nblocks + i]), 1.f);
   m = block_reduce(m, 1.f, sh);
+  int y = m.garg;
+  bool flag = (m.gmax - m.gsecond) < kNearTie;
+  if (y == INT_MAX) {
+    // no token has p > q in floating point (the two distributions agree to rounding), so
+    // max(0, p - q) has no mass: commit the target's argmax instead, flagged as a near-tie
+    // (every thread sees the same reduced result, so the whole block takes this branch)
+    const Stat t = merge_row(f.part, f.nblocks, f.inv_temp, sh);
+    y = t.arg;
+    flag = true;
+  }
   if (threadIdx.x == 0) {
     Verdict* v = f.verdict;
-    v->committed = m.garg;
-    if ((m.gmax - m.gsecond) < kNearTie) v->flags |= 1;
-    f.tok_ring[f.v % f.ring] = m.garg;
+    v->committed = y;
+    if (flag) v->flags |= 1;
+    f.tok_ring[f.v % f.ring] = y;
     *f.host_verdict = *v;
   }
 }

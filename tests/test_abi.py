@@ -81,6 +81,16 @@ def test_init_rejects_bad_arguments_without_a_gpu():
     assert L.spd_init(ctypes.byref(c), ctypes.byref(w), ctypes.byref(s), fake, nb, None,
                       ctypes.byref(h)) == binding.SPD_E_CONFIG
     s.temperature, s.forced_mode = 0.0, 0
+    # forced_ref ids must lie in [0, V): checked before any device call
+    fake_layers = (ctypes.c_void_p * (7 * cfg.n_layers))(*([0x1000] * (7 * cfg.n_layers)))
+    fake_pdm = (ctypes.c_void_p * (7 * cfg.pdm_layers))(*([0x1000] * (7 * cfg.pdm_layers)))
+    wf = binding.Weights(0x1000, 0x1000, 0x1000, fake_layers, 0x1000, fake_pdm, 0x1000)
+    for bad in (-1, cfg.vocab, 1 << 30):
+        ref = (ctypes.c_int32 * 4)(1, 2, bad, 3)
+        sf = binding.Sampling(0.0, 1.0, 0, 1, 0.5, ref, 4)
+        assert L.spd_init(ctypes.byref(c), ctypes.byref(wf), ctypes.byref(sf), fake, nb, None,
+                          ctypes.byref(h)) == binding.SPD_E_ARG
+        assert b"forced_ref" in L.spd_init_error()
     # null weights
     assert L.spd_init(ctypes.byref(c), ctypes.byref(w), ctypes.byref(s), fake, nb, None,
                       ctypes.byref(h)) == binding.SPD_E_ARG

@@ -207,3 +207,22 @@ def test_top_p_unflagged_decisions_survive_logit_perturbation():
             y2, acc2, _ = S.verify(zt2, d2, q2, s, pos, zq2)
             assert (y2, acc2) == (y, acc)
     assert seen["clean"] > 500 and seen["reject"] > 100 and seen["flag"] > 0
+
+
+def test_rejection_with_an_empty_residual_commits_the_target_argmax():
+    """Degenerate rejection: q >= p everywhere (here q = 1.5 p, so the accept test
+    u q(d) < p(d) fails for u >= 2/3 and max(0, p - q) is all zero). No residual token
+    exists, so the commit falls back to the target's argmax, flagged as a near-tie."""
+    z = np.array([0.3, 1.7, -0.4, 1.1, 0.2])
+    s = S.Sampling(temperature=1.0, seed=5)
+    p = S.distribution(z, 1.0, 1.0)
+    q = 1.5 * p
+    seen = 0
+    for v in range(200):
+        y, acc, flag = S.verify(z, 3, q, s, v)
+        u = S.uniform(5, S.STREAM_ACC, v, 0)[()]
+        assert acc == (u * q[3] < p[3])
+        if not acc:
+            assert (y, flag) == (1, True)
+            seen += 1
+    assert seen > 0
