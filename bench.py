@@ -20,9 +20,11 @@ step_us is each step's full cycle as a caller sees it (enqueue, GPU execution an
 verdict read-back), taken on the host between successive verify_commit returns.
 Per-launch durations for the roofline come from HIP start/stop events that the
 library binds to each launch's dispatch packet (hipExtLaunchKernel), on the
-stream the launch runs on, over a second pass of the same warm-up and timed
-steps replayed from a fresh prefill (the events cost ~15% of step time, so the
-headline region runs without them).
+stream the launch runs on, over the timed steps of a second pass that replays
+the same warm-up and timed steps from a fresh prefill (the events cost ~15% of
+step time, so the headline region runs without them). The CPU baseline is the
+float32 oracle on the host cores: the same workload and prompt, a bounded number
+of steps, its own committed tokens over the steps' wall time.
 """
 from __future__ import annotations
 
@@ -38,7 +40,10 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-METRIC = "committed tokens/s (1 seq, 1 GPU) + step µs + % HBM roofline, n=8"
+METRIC_FMT = "committed tokens/s (1 seq, 1 GPU) + step µs + % HBM roofline, n={n}"
+# the arithmetic type of every kernel on the path: fp32 FMAs and fp32 accumulation, on bf16
+# (or fp32) weights and a bf16 (or fp32) KV cache
+ARITH_DTYPE = "f32"
 HBM_PEAK_GBS = 8000.0
 FP32_MATRIX_PEAK_TFLOPS = 157.3     # MI355X dense fp32 matrix-core peak
 BF16_MATRIX_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix-core peak
@@ -171,18 +176,22 @@ def run_spd(cfg, dW, prompt, T, seed, warmup, steps, kernel_timing, top_p=1.0,
 
     s1, out["timed"] = region()
     if kernel_timing:
-        # The same steps again from a fresh prefill, with start/stop events bound to each
-        # launch's dispatch packet (kernel durations without the command processor's gaps).
-        # They are kept out of the headline region, which runs without them.
+        # The same steps again from a fresh prefill (same seed, so the same sequence of
+        # steps), with start/stop events bound to each launch's dispatch packet (kernel
+        # durations without the command processor's gaps) over exactly the timed steps.
+        # They are kept out of the headline region, which runs without them. Lookahead is
+        # off here (the library skips it while timing anyway); results are bit-identical.
         spd.reset()
+        spd.lookahead(False)
         spd.prefill(prompt)
-        spd.timing(True)
         for _ in range(warmup):
             spd.step()
             spd.verify_commit()
+        spd.timing(True)
         _, kt = region()
         out["kernels"] = spd.timing_read()
-        out["kernel_steps"] = warmup + steps
+        out["kernel_steps"] = steps
+        out["kernel_region"] = {"N": kt["N"], "K": kt["K"]}
         spd.timing(False)
     out["alpha_total"], out["s0_total"] = s1.alpha, s1.s0
     spd.close()
@@ -207,39 +216,57 @@ def traffic_from_profile(workload: str, kernel: str):
     return value
 
 
-def cpu_baseline(cfg, W, T, seed, alpha, budget_s, top_p=1.0, speculate_from="input"):
-    """The oracle as it stands, on the host cores, over a bounded sample of the same model."""
-    import numpy as np
-    from oracle.spd import SPD as OracleSPD
-    from oracle.sampling import Sampling
-    from spd_inputs import make_prompt
+def cpu_info():
+    """CPU model, logical CPUs and BLAS threads of the host running this process."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count() or 1
-    plen = 16
-    o = OracleSPD(cfg, W, Sampling(temperature=T, top_p=top_p, seed=seed),
-                  speculate_from=speculate_from)
+    return {"cpu_model": model, "nproc": os.cpu_count(),
+            "affinity": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None,
+            "blas_threads": int(threads)}
+
+
+def cpu_baseline(cfg, W, prompt, T, seed, budget_s, top_p=1.0, speculate_from="input"):
+    """The oracle as it stands, in float32, on the host cores: the workload's own prompt,
+    then as many SPD steps as fit the budget; value = the oracle's own committed tokens
+    over the wall time of its steps (its prefill is set-up, as the GPU's is)."""
+    import numpy as np
+    from oracle.spd import SPD as OracleSPD
+    from oracle.sampling import Sampling
+    info = cpu_info()
     t = time.perf_counter()
-    o.prefill(make_prompt(cfg, length=plen))
+    o = OracleSPD(cfg, W, Sampling(temperature=T, top_p=top_p, seed=seed), ft=np.float32,
+                  speculate_from=speculate_from, record_logits=False)
+    o.prefill(np.asarray(prompt))
     setup = time.perf_counter() - t
-    log(f"cpu baseline: oracle set up in {setup:.1f}s (weights upcast to float64, untimed)")
+    log(f"cpu baseline: float32 oracle prefill of {len(prompt)} tokens in {setup:.1f}s "
+        f"(weights upcast once; untimed)")
     t0 = time.perf_counter()
-    k = 0
-    while k < 2 or (time.perf_counter() - t0 < budget_s and k < 160):
+    # bounded by the budget and by the workload's own length (G tokens, the context)
+    while (o.K < 2 or time.perf_counter() - t0 < budget_s) and 1 + o.N < cfg.gen_len \
+            and o.F[-1][0] + 1 < cfg.max_ctx:
         o.step()
-        k += 1
-        log(f"cpu baseline: oracle step {k} at {time.perf_counter() - t0:.1f}s")
+        if o.K % 8 == 0:
+            log(f"cpu baseline: oracle step {o.K} (N={o.N}) at {time.perf_counter() - t0:.1f}s")
     dt = time.perf_counter() - t0
-    steps_per_s = k / dt
-    return {"value": alpha * steps_per_s, "unit": "tokens/s", "cores": int(threads),
+    return {"value": o.N / dt, "unit": "tokens/s", "cores": info["blas_threads"],
             "kind": "oracle",
-            "sample": (f"{k} SPD steps ({dt:.1f} s) of the same n={o.n} model after a {plen}-token "
-                       f"prompt (float64 numpy oracle, weights upcast once before timing); "
-                       f"oracle steps/s {steps_per_s:.4f} scaled by the GPU run's committed "
-                       f"tokens per step alpha={alpha:.4f}"),
-            "steps_per_s": steps_per_s}
+            "sample": (f"the float32 numpy oracle on the same n={o.n} workload: prefill of its "
+                       f"{len(prompt)}-token prompt (untimed), then {o.K} SPD steps in "
+                       f"{dt:.1f} s committing N={o.N} tokens (alpha={o.alpha:.3f}); value = N "
+                       f"over the steps' wall time"),
+            "N": o.N, "K": o.K, "seconds": dt, "steps_per_s": o.K / dt, "alpha": o.alpha,
+            "prefill_s": setup, **info}
 
 
 def forced_sweep(cfg, dW, prompt, ps, warmup, steps, lookahead=True):
@@ -336,7 +363,8 @@ def main():
                     help="enqueue every step only after the previous one's verdict (no "
                          "lookahead launch of a refill step's successor)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--cpu-budget", type=float, default=20.0,
+                    help="seconds of oracle steps in the CPU baseline (its prefill is extra)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB: a kernel of "
                          "known traffic, to scale hardware byte counters")
@@ -399,8 +427,8 @@ def main():
     alpha = tm["N"] / tm["K"]
     kern = main_run["kernels"]
     ik = main_run["kernel_steps"]
+    # algorithmic bytes of the timed steps (the replay runs the same steps)
     step_bytes = sum(v["bytes"] for v in kern.values()) / ik
-    gpu_step_ms = statistics.mean(tm["step_ms"])
     dominant = max((k for k in kern if k.startswith("gemv") and kern[k]["count"]),
                    key=lambda k: kern[k]["ms"])
     d = kern[dominant]
@@ -410,7 +438,7 @@ def main():
                    "bytes_per_launch": v["bytes"] / v["count"]}
                for k, v in kern.items() if v["count"]}
     res = {
-        "metric": METRIC,
+        "metric": METRIC_FMT.format(n=cfg.n_stages),
         "value": value,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -420,14 +448,20 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": ARITH_DTYPE,
         "data": "synthetic",
         "config": {"workload": cfg.name, "n": cfg.n_stages, "Ls": cfg.pdm_layers,
                    "anchors": list(cfg.anchors), "context": cfg.prompt_len + cfg.gen_len,
                    "prompt": cfg.prompt_len, "temperature": args.temperature, "top_p": args.top_p,
                    "speculate_from": args.speculate_from, "lookahead": lookahead,
-                   "weights": "bf16 N(0,0.02) seeded", "kv_cache": "bf16",
+                   "weights": f"{cfg.dtype} N(0,{cfg.weight_std}) seeded",
+                   "kv_cache": cfg.dtype, "arithmetic": "fp32 FMA, fp32 accumulation",
                    "prompt_ids": "uniform random"},
+        "commits": tm["N"],
+        "timed_steps": tm["K"],
+        "value_note": (f"{tm['N']} commits in {tm['K']} timed steps: with random weights the "
+                       "acceptance is a random walk, so a short run's tokens/s carries alpha's "
+                       "noise; step_us and step_hbm_roofline do not depend on alpha"),
         "roofline": {"bound": "hbm", "kernel": dominant,
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
@@ -443,7 +477,10 @@ def main():
         "alpha": alpha,
         "s0": alpha * cfg.n_stages,
         "step_hbm_roofline": {"algorithmic_bytes_per_step": step_bytes,
-                              "frac": step_bytes / (gpu_step_ms * 1e-3) / (HBM_PEAK_GBS * 1e9)},
+                              "achieved_GBps": step_bytes / (ms_per_step * 1e-3) / 1e9,
+                              "frac": step_bytes / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
+                              "over": "the timed steps: their algorithmic bytes (per-launch "
+                                      "accounting of the same steps replayed) over ms_per_step"},
         "kernels": kernels,
         "t0_run": t0_run,
         "prefill_s": main_run["prefill_s"],
@@ -464,7 +501,7 @@ def main():
     if not args.no_cpu_baseline:
         del dW
         torch.cuda.empty_cache()
-        res["cpu_baseline"] = cpu_baseline(cfg, W, args.temperature, args.seed, alpha,
+        res["cpu_baseline"] = cpu_baseline(cfg, W, prompt, args.temperature, args.seed,
                                            args.cpu_budget, args.top_p, args.speculate_from)
     else:
         res["cpu_baseline"] = None

@@ -406,3 +406,34 @@ def test_call_order_and_capacity_errors():
     g.reset()
     assert g.prefill(prompt) >= 0
     g.close()
+
+
+def test_prompt_longer_than_one_staging_piece():
+    """A prompt of 132100 ids crosses the 512 KiB (131072-id) pieces in which spd_prefill
+    uploads it. The K row layer 0 stores at position p depends only on the token at p and
+    on p (RMSNorm, the K rows of W_qkv, RoPE at p), so the oracle's arithmetic gives it
+    exactly; positions on both sides of the piece boundary, and the first and last, must
+    hold the library's K rows for the right tokens."""
+    import torch
+    from oracle.model import Model
+    from oracle.numerics import apply_rope, rmsnorm
+    from speculative_pipeline_decoding_amd import SPD, upload_weights
+    cfg0, W, _ = workload("tiny")
+    P = 132100
+    cfg = cfg0.with_(max_ctx=P + 100)
+    prompt = np.random.default_rng(9).integers(0, cfg.vocab, P).astype(np.int32)
+    _dev.clear()
+    torch.cuda.empty_cache()
+    print(f"[parity] {P}-token prompt on the tiny model", flush=True)
+    gpu = SPD(cfg, upload_weights(cfg, W))
+    gpu.prefill(prompt)
+    kv = gpu.debug("target_kv").reshape(cfg.n_layers, 2, cfg.n_kv_heads, cfg.max_ctx, cfg.head_dim)
+    gpu.close()
+    m = Model(cfg, W)
+    hq, hkv, hd = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    for p in (0, 1, 131071, 131072, 131073, 131500, P - 1):
+        a = rmsnorm(m.embed(prompt[p]), m.W("layers.0.attn_norm"), cfg.rms_eps)
+        k = (m.W("layers.0.w_qkv") @ a)[hq * hd:(hq + hkv) * hd].reshape(hkv, hd)
+        k = apply_rope(k, p, cfg.rope_theta)
+        np.testing.assert_allclose(kv[0, 0, :, p, :], k, rtol=0, atol=1e-5,
+                                   err_msg=f"layer-0 K row at position {p}")
