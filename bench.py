@@ -362,6 +362,8 @@ def main():
     ap.add_argument("--no-lookahead", action="store_true",
                     help="enqueue every step only after the previous one's verdict (no "
                          "lookahead launch of a refill step's successor)")
+    ap.add_argument("--kv-f32", action="store_true",
+                    help="store the KV caches in fp32 (kv_dtype SPD_KV_F32) instead of bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0,
                     help="seconds of oracle steps in the CPU baseline (its prefill is extra)")
@@ -380,6 +382,8 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     cfg = get(args.workload)
+    if args.kv_f32:
+        cfg = cfg.with_(kv_dtype="f32")
     if args.temperature is None:
         args.temperature = float(cfg.temperatures[0])
     if args.top_p is None:
@@ -455,7 +459,8 @@ def main():
                    "prompt": cfg.prompt_len, "temperature": args.temperature, "top_p": args.top_p,
                    "speculate_from": args.speculate_from, "lookahead": lookahead,
                    "weights": f"{cfg.dtype} N(0,{cfg.weight_std}) seeded",
-                   "kv_cache": cfg.dtype, "arithmetic": "fp32 FMA, fp32 accumulation",
+                   "kv_cache": cfg.dtype if cfg.kv_dtype == "auto" else cfg.kv_dtype,
+                   "arithmetic": "fp32 FMA, fp32 accumulation",
                    "prompt_ids": "uniform random"},
         "commits": tm["N"],
         "timed_steps": tm["K"],

@@ -51,6 +51,7 @@ enum { SPD_F32 = 0, SPD_BF16 = 1 };                 /* weight (and KV cache) sto
 enum { SPD_FILL_CLAMP = 0, SPD_FILL_ZERO = 1 };      /* anchors not computed yet */
 enum { SPD_LAYER_SOFTMAX = 0, SPD_LAYER_LINEAR = 1 };
 enum { SPD_SPEC_INPUT = 0, SPD_SPEC_OUTPUT = 1 };     /* which states the PDM reads */
+enum { SPD_KV_AUTO = 0, SPD_KV_F32 = 1 };             /* KV cache storage */
 
 /*
  * Model and SPD configuration. Free parameters in the pages' notation
@@ -78,9 +79,13 @@ enum { SPD_SPEC_INPUT = 0, SPD_SPEC_OUTPUT = 1 };     /* which states the PDM re
  *     referee summary mentions): the PDM runs after the step's target layers on the
  *     states they produced, one stage deeper (the exiting token at depth L, whose PDM
  *     row becomes permanent in the same step), on the caller's stream.
+ *   kv_dtype: SPD_KV_AUTO (0) stores the target and PDM KV caches in the weight dtype
+ *     (bf16 keys and values, rounded to nearest even, for bf16 weights); SPD_KV_F32 (1)
+ *     stores them in fp32 with bf16 weights too: twice the KV bytes, and no bf16
+ *     rounding of K and V, whose one-ulp flips deep, wide models amplify in the logits.
  * Limits: d_model, d_ffn, n_q_heads*head_dim multiples of 8; head_dim in
- * {16, 32, 64, 80, 128} (bf16) or {16, 32, 64} (f32); n_q_heads a multiple of
- * n_kv_heads with at most 16 query heads per KV head; n <= 16; k <= 8; Ls <= 16.
+ * {16, 32, 64, 80, 128}; n_q_heads a multiple of n_kv_heads with at most 16 query
+ * heads per KV head; n <= 16; k <= 8; Ls <= 16.
  */
 typedef struct {
   int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, d_ffn, vocab;
@@ -95,6 +100,7 @@ typedef struct {
   int32_t anchor_fill;
   int32_t max_ctx;
   int32_t speculate_from;         /* SPD_SPEC_INPUT | SPD_SPEC_OUTPUT */
+  int32_t kv_dtype;               /* SPD_KV_AUTO | SPD_KV_F32 */
 } spd_model_config;
 
 /*
@@ -241,8 +247,8 @@ enum {
   SPD_DBG_H_RING = 3,          /* f32 [n+1][d]: residual of position p in slot p mod (n+1) */
   SPD_DBG_ANCHORS = 4,         /* f32 [n+1][k][d]: anchors of position p in slot p mod (n+1) */
   SPD_DBG_PDM_ROWS = 5,        /* f32 [n+1][d]: PDM residual rows of the last step */
-  SPD_DBG_TARGET_KV = 6,       /* dtype [softmax layers][2][hkv][max_ctx][hd] */
-  SPD_DBG_PDM_KV = 7,          /* dtype [Ls][2][hkv][max_ctx][hd] */
+  SPD_DBG_TARGET_KV = 6,       /* KV dtype [softmax layers][2][hkv][max_ctx][hd] */
+  SPD_DBG_PDM_KV = 7,          /* KV dtype [Ls][2][hkv][max_ctx][hd] */
   SPD_DBG_TOKENS = 8,          /* i32 [n+1]: token of position p in slot p mod (n+1) */
   SPD_DBG_TOP_P = 9            /* [1 + (n+1)] x {f32 zb, i32 id_cut, f32 lse, i32 0}: top-p
                                   sets (top_p < 1, T > 0) of the last target row, then of the

@@ -20,7 +20,8 @@ Linear kind (hybrid workload; a reading, since no page defines the layer):
 Precision contract (a reading; the pages give none):
     * weights are the exact stored values (bf16 or f32);
     * activations, norms, softmax and accumulations: the oracle's float type;
-    * the KV cache stores bf16 (bf16 workloads) or f32 (f32 workloads);
+    * the KV cache stores bf16 (bf16 workloads) or f32 (f32 workloads, or any workload
+      whose kv_dtype is "f32");
     * prefill and decode both keep full-precision activations at every GEMM
       input (no bf16 rounding of activations): rounding them would turn
       last-bit differences between two correct implementations into logit
@@ -75,7 +76,8 @@ class Stack:
         self.cfg, self.W, self.prefix = cfg, W, prefix
         self.kinds = list(kinds)
         self.ft = W.ft
-        self.bf16 = cfg.dtype == "bf16"
+        # the KV cache is stored in the weight dtype unless the workload asks for fp32
+        self.bf16 = cfg.dtype == "bf16" and cfg.kv_dtype != "f32"
         hkv, hd, T = cfg.n_kv_heads, cfg.head_dim, cfg.max_ctx
         self.K: List[Optional[np.ndarray]] = []
         self.V: List[Optional[np.ndarray]] = []

@@ -34,7 +34,7 @@ class ModelConfig:
     head_dim: int
     d_ffn: int
     vocab: int
-    dtype: str                      # "f32" or "bf16": weight storage; KV cache follows
+    dtype: str                      # "f32" or "bf16": weight storage
     n_stages: int                   # n
     anchors: Tuple[int, ...]        # B, ascending, anchors[0] == 0
     pdm_layers: int                 # Ls
@@ -52,6 +52,7 @@ class ModelConfig:
     top_p: float = 1.0
     weight_seed: int = 0
     prompt_seed: int = 1
+    kv_dtype: str = "auto"           # KV cache storage: "auto" (the weight dtype) or "f32"
 
     @property
     def kinds(self) -> Tuple[int, ...]:

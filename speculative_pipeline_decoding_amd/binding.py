@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(HERE, "libspd.so")
 SPD_OK, SPD_E_ARG, SPD_E_CONFIG, SPD_E_STATE, SPD_E_CAPACITY, SPD_E_DEVICE = 0, -1, -2, -3, -4, -5
 SPD_F32, SPD_BF16 = 0, 1
 SPD_FILL_CLAMP, SPD_FILL_ZERO = 0, 1
+SPD_KV_AUTO, SPD_KV_F32 = 0, 1
 DBG = {"target_logits": 1, "draft_logits": 2, "h_ring": 3, "anchors": 4, "pdm_rows": 5,
        "target_kv": 6, "pdm_kv": 7, "tokens": 8, "top_p": 9}
 # launch kinds reported by spd_timing_read
@@ -42,7 +43,7 @@ class ModelConfig(ctypes.Structure):
                 ("stage_layers", ctypes.POINTER(ctypes.c_int32)), ("n_anchors", ctypes.c_int32),
                 ("anchors", ctypes.POINTER(ctypes.c_int32)), ("pdm_layers", ctypes.c_int32),
                 ("anchor_fill", ctypes.c_int32), ("max_ctx", ctypes.c_int32),
-                ("speculate_from", ctypes.c_int32)]
+                ("speculate_from", ctypes.c_int32), ("kv_dtype", ctypes.c_int32)]
 
 
 class Weights(ctypes.Structure):
@@ -177,6 +178,7 @@ def make_config(cfg, n: Optional[int] = None, anchors: Optional[Sequence[int]] =
     c.anchor_fill = SPD_FILL_ZERO if fill == "zero" else SPD_FILL_CLAMP
     c.max_ctx = cfg.max_ctx
     c.speculate_from = {"input": 0, "output": 1}[speculate_from]
+    c.kv_dtype = {"auto": SPD_KV_AUTO, "f32": SPD_KV_F32}[getattr(cfg, "kv_dtype", "auto")]
     return c, keep
 
 
@@ -277,7 +279,8 @@ class SPD:
         code = DBG[what]
         nb = self.L.spd_debug_size(self.h, code)
         if what in ("target_kv", "pdm_kv"):
-            dt = np.uint16 if self.cfg.dtype == "bf16" else np.float32
+            kv16 = self.cfg.dtype == "bf16" and getattr(self.cfg, "kv_dtype", "auto") == "auto"
+            dt = np.uint16 if kv16 else np.float32
         elif what == "tokens":
             dt = np.int32
         elif what == "top_p":

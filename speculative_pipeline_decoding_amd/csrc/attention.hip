@@ -41,14 +41,20 @@ __device__ __forceinline__ void unpack(const uint4& u, float* f) {
 template <typename T, int HD>
 constexpr int v_words() { return (sizeof(T) == 2 ? HD / 2 : HD) + 1; }
 
-// LDS: q [GMAX][HD], p [waves][64][GMAX], V tiles [waves][64][v_words]; after the key
-// loop the V tiles are reused for the wave merge [waves][GMAX][HD + 2].
+// fp32 rows wider than 64 dims would make each wave's V tile most of the CU's LDS: there
+// the wave reads the tile's V rows straight from memory in the p V sum instead (one whole,
+// coalesced row per key, the lanes over the head dims).
+template <typename T, int HD>
+constexpr bool direct_v() { return sizeof(T) == 4 && HD > 64; }
+
+// LDS: q [GMAX][HD], p [waves][64][GMAX], V tiles [waves][64][v_words] (none when V is
+// read directly); after the key loop the same space holds the wave merge
+// [waves][GMAX][HD + 2].
 template <typename T, int HD, int GMAX>
 constexpr size_t attn_lds_floats() {
-  return (size_t)GMAX * HD + kAttnWaves * 64 * GMAX +
-         ((size_t)kAttnWaves * 64 * v_words<T, HD>() > (size_t)kAttnWaves * GMAX * (HD + 2)
-              ? (size_t)kAttnWaves * 64 * v_words<T, HD>()
-              : (size_t)kAttnWaves * GMAX * (HD + 2));
+  constexpr size_t tile = direct_v<T, HD>() ? 0 : (size_t)kAttnWaves * 64 * v_words<T, HD>();
+  constexpr size_t merge = (size_t)kAttnWaves * GMAX * (HD + 2);
+  return (size_t)GMAX * HD + kAttnWaves * 64 * GMAX + (tile > merge ? tile : merge);
 }
 
 template <typename T, int HD, int GMAX>
@@ -113,11 +119,14 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_kernel(
     const size_t rowoff = (size_t)(t0 + (valid ? lane : 0)) * HD;
     const uint4* krow = reinterpret_cast<const uint4*>(Kh + rowoff);
     const uint4* vrow = reinterpret_cast<const uint4*>(Vh + rowoff);
-    uint4 kr[NC], vr[NC];
+    constexpr bool DV = direct_v<T, HD>();
+    uint4 kr[NC], vr[DV ? 1 : NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) kr[c] = krow[c];
+    if constexpr (!DV) {
 #pragma unroll
-    for (int c = 0; c < NC; ++c) vr[c] = vrow[c];
+      for (int c = 0; c < NC; ++c) vr[c] = vrow[c];
+    }
     float sc[GMAX];
 #pragma unroll
     for (int h = 0; h < GMAX; ++h) {
@@ -139,11 +148,13 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_kernel(
       }
     }
     // the V row goes to the wave's LDS tile, to be summed by columns below
-    uint32_t* vdst = vt + lane * VW;
+    if constexpr (!DV) {
+      uint32_t* vdst = vt + lane * VW;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      vdst[4 * c] = vr[c].x; vdst[4 * c + 1] = vr[c].y;
-      vdst[4 * c + 2] = vr[c].z; vdst[4 * c + 3] = vr[c].w;
+      for (int c = 0; c < NC; ++c) {
+        vdst[4 * c] = vr[c].x; vdst[4 * c + 1] = vr[c].y;
+        vdst[4 * c + 2] = vr[c].z; vdst[4 * c + 3] = vr[c].w;
+      }
     }
 #pragma unroll
     for (int h = 0; h < GMAX; ++h) {
@@ -164,7 +175,10 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_kernel(
 #pragma unroll 4
       for (int j = 0; j < nrows; ++j) {
         float2 vv;
-        if constexpr (sizeof(T) == 2) {
+        if constexpr (DV) {
+          vv = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(Vh) +
+                                                (size_t)(t0 + j) * HD + 2 * lane);
+        } else if constexpr (sizeof(T) == 2) {
           const uint32_t wv = vt[j * VW + lane];
           vv = make_float2(bf16_lo(wv), bf16_hi(wv));
         } else {
@@ -551,6 +565,8 @@ hipError_t dispatch(bool bf16, dim3 grid, hipStream_t st, const AttnProb* probs,
   SPD_ATTN_CASE(16)
   SPD_ATTN_CASE(32)
   SPD_ATTN_CASE(64)
+  SPD_ATTN_CASE(80)
+  SPD_ATTN_CASE(128)
 #undef SPD_ATTN_CASE
   return hipErrorInvalidValue;
 }
@@ -558,7 +574,8 @@ hipError_t dispatch(bool bf16, dim3 grid, hipStream_t st, const AttnProb* probs,
 }  // namespace
 
 bool attn_supported_head_dim(int hd, bool bf16) {
-  return hd == 16 || hd == 32 || hd == 64 || (bf16 && (hd == 80 || hd == 128));
+  (void)bf16;
+  return hd == 16 || hd == 32 || hd == 64 || hd == 80 || hd == 128;
 }
 
 hipError_t launch_attention(const AttnProb* d_probs, int nprob, int ntiles, bool bf16, int hq,

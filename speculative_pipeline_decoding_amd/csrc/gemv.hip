@@ -90,9 +90,9 @@ __device__ __forceinline__ void unit_slots(const GemvProb& p, int ut, int& ja, i
   else if (p.epi == EPI_QKV) { ja = 2 * ut; jb = 2 * ut + 1; }
 }
 
-template <typename T>
-__device__ __forceinline__ void store_kv(void* base, size_t idx, float v) {
-  if constexpr (sizeof(T) == 2) static_cast<uint16_t*>(base)[idx] = f2bf(v);
+// KV cache element: bf16 (round to nearest even) or fp32, as the cache is laid out.
+__device__ __forceinline__ void store_kv(void* base, size_t idx, float v, bool b16) {
+  if (b16) static_cast<uint16_t*>(base)[idx] = f2bf(v);
   else static_cast<float*>(base)[idx] = v;
 }
 
@@ -126,13 +126,14 @@ __device__ void epilogue(const GemvProb& p, int v, int unit, float a, float b,
       } else if (head < p.hq + p.hkv) {
         const float2 cs = rope[(size_t)pos * half + i];
         const size_t base = ((size_t)(head - p.hq) * p.max_ctx + pos) * hd;
-        store_kv<T>(p.kv_k, base + i, a * cs.x - b * cs.y);
-        store_kv<T>(p.kv_k, base + i + half, a * cs.y + b * cs.x);
+        const bool b16 = sizeof(T) == 2 && !p.kv_f32;
+        store_kv(p.kv_k, base + i, a * cs.x - b * cs.y, b16);
+        store_kv(p.kv_k, base + i + half, a * cs.y + b * cs.x, b16);
       } else {
         const int g = head - p.hq - p.hkv;
-        constexpr bool blocked = sizeof(T) == 2;
-        store_kv<T>(p.kv_v, v_index(blocked, g, pos, i, hd, p.max_ctx), a);
-        store_kv<T>(p.kv_v, v_index(blocked, g, pos, i + half, hd, p.max_ctx), b);
+        const bool b16 = sizeof(T) == 2 && !p.kv_f32;   // bf16 caches are key-blocked
+        store_kv(p.kv_v, v_index(b16, g, pos, i, hd, p.max_ctx), a, b16);
+        store_kv(p.kv_v, v_index(b16, g, pos, i + half, hd, p.max_ctx), b, b16);
       }
       break;
     }

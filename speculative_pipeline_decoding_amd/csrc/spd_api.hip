@@ -71,8 +71,10 @@ struct Op {
 
 struct Plan {
   int L, d, hq, hkv, hd, F, V, n, k, Ls, max_ctx, ring, qrows, linrows, qo;
-  bool bf16;
+  bool bf16;       // weights
   int esz;
+  bool kv_bf16;    // KV caches (target and PDM): bf16, key-blocked V; else fp32, row-major
+  int kv_esz;
   float theta, eps;
   int fill;
   int spec_output;   // the PDM reads the step's output states, after the target layers
@@ -99,11 +101,15 @@ bool plan_config(const spd_model_config* c, Plan& p, std::string& err) {
   if (c->dtype != SPD_F32 && c->dtype != SPD_BF16) return bad("dtype must be SPD_F32 or SPD_BF16");
   p.bf16 = c->dtype == SPD_BF16;
   p.esz = p.bf16 ? 2 : 4;
+  if (c->kv_dtype != SPD_KV_AUTO && c->kv_dtype != SPD_KV_F32)
+    return bad("kv_dtype must be SPD_KV_AUTO or SPD_KV_F32");
+  p.kv_bf16 = p.bf16 && c->kv_dtype == SPD_KV_AUTO;
+  p.kv_esz = p.kv_bf16 ? 2 : 4;
   if (p.L < 1 || p.d < 8 || p.hq < 1 || p.hkv < 1 || p.hd < 2 || p.F < 8 || p.V < 2)
     return bad("model dimensions out of range");
   if (p.d % 8 || p.F % 8 || (p.hq * p.hd) % 8) return bad("d_model, d_ffn, n_q_heads*head_dim must be multiples of 8");
-  if (!attn_supported_head_dim(p.hd, p.bf16))
-    return bad("head_dim must be 16, 32 or 64 (f32), or 16, 32, 64, 80 or 128 (bf16)");
+  if (!attn_supported_head_dim(p.hd, p.kv_bf16))
+    return bad("head_dim must be 16, 32, 64, 80 or 128");
   if (p.hq % p.hkv || p.hq / p.hkv > 16) return bad("n_q_heads must be a multiple of n_kv_heads, group <= 16");
   if (p.n < 1 || p.n > kMaxStages || p.n > p.L) return bad("n_stages must be in [1, min(L, 16)]");
   if (p.k < 1 || p.k > kMaxAnchors || !c->anchors) return bad("need 1..8 anchors");
@@ -146,7 +152,7 @@ bool plan_config(const spd_model_config* c, Plan& p, std::string& err) {
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes); return at; };
   const size_t ctx = p.max_ctx;
-  p.kv_layer_bytes = 2 * (size_t)p.hkv * kv_ctx(p.max_ctx) * p.hd * p.esz;
+  p.kv_layer_bytes = 2 * (size_t)p.hkv * kv_ctx(p.max_ctx) * p.hd * p.kv_esz;
   p.lin_state_bytes = (size_t)p.hq * p.hd * p.hd * 4;
   p.o_kv = take(p.nsoft * p.kv_layer_bytes);
   p.o_pkv = take((size_t)p.Ls * p.kv_layer_bytes);
@@ -436,7 +442,7 @@ hipError_t run_op(spd_handle* h, const Op& op, LaunchEv ev = {}) {
                                 kLinEps, st, ev);
     case OP_ATTN: case OP_PDM_ATTN:
       return launch_attention(reinterpret_cast<const AttnProb*>(d + op.off), op.count, op.ntiles,
-                              p.bf16, p.hq, p.hkv, p.hd, p.max_ctx, op.split,
+                              p.kv_bf16, p.hq, p.hkv, p.hd, p.max_ctx, op.split,
                               op.ntiles > op.count * p.hkv, h->at<float>(p.o_apart), st, ev);
     case OP_VOCAB:
       return launch_vocab_stats(reinterpret_cast<const VocabDesc*>(d + op.off), kVocabBlocks,
@@ -623,7 +629,7 @@ int build_step(spd_handle* h, DescWriter& dw) {
           GemvProb q = gemv(h->W(l, T_QKV), p.qrows, p.d, hv, 0, 1, EPI_QKV, nullptr, 0,
                             (const float*)h->W(l, T_ATTN_NORM), 0, p.eps);
           q.aux = qbuf + (size_t)j * p.qo;
-          q.kv_k = h->kvK(l); q.kv_v = h->kvV(l);
+          q.kv_k = h->kvK(l); q.kv_v = h->kvV(l); q.kv_f32 = !p.kv_bf16;
           q.pos0 = f.pos; q.hq = p.hq; q.hkv = p.hkv; q.hd = p.hd; q.max_ctx = p.max_ctx;
           qkv.push_back(q);
           AttnProb a{};
@@ -631,7 +637,7 @@ int build_step(spd_handle* h, DescWriter& dw) {
           a.q_stride = p.qo; a.out_stride = p.qo; a.nrows = 1;
           a.K = h->kvK(l); a.V = h->kvV(l); a.len = f.pos + 1;
           at.push_back(a);
-          kvb += 2.0 * (f.pos + 1) * p.hkv * p.hd * p.esz;
+          kvb += 2.0 * (f.pos + 1) * p.hkv * p.hd * p.kv_esz;
         }
         o.push_back(gemv(h->W(l, T_O), p.d, p.qo, attn + (size_t)j * p.qo, 0, 1, EPI_ADD, hv, 0,
                          nullptr, 0, 0.f));
@@ -680,13 +686,13 @@ int build_step(spd_handle* h, DescWriter& dw) {
     GemvProb q = gemv(h->PW(r, T_QKV), p.qrows, p.d, hp, p.d, M, EPI_QKV, nullptr, 0,
                       (const float*)h->PW(r, T_ATTN_NORM), 0, p.eps);
     q.aux = qbuf + (size_t)base * p.qo; q.aux_stride = p.qo;
-    q.kv_k = h->pK(r); q.kv_v = h->pV(r);
+    q.kv_k = h->pK(r); q.kv_v = h->pV(r); q.kv_f32 = !p.kv_bf16;
     q.pos0 = h->pdm_len; q.hq = p.hq; q.hkv = p.hkv; q.hd = p.hd; q.max_ctx = p.max_ctx;
     qkv.push_back(q);
     // the last PDM layer only feeds the LM head: its attention, O and FFN run on the
     // newest row alone (its QKV still writes every row's keys and values)
     const int r0 = last ? M - 1 : 0, nr = last ? 1 : M;
-    const int rpp = attn_rows_per_problem(p.bf16, p.hq, p.hkv);
+    const int rpp = attn_rows_per_problem(p.kv_bf16, p.hq, p.hkv);
     for (int m = r0; m < M; m += rpp) {
       AttnProb a{};
       a.q = qbuf + (size_t)(base + m) * p.qo; a.out = attn + (size_t)(base + m) * p.qo;
@@ -695,7 +701,7 @@ int build_step(spd_handle* h, DescWriter& dw) {
       a.nrows = std::min(rpp, M - m);
       at.push_back(a);
     }
-    const double kvb = 2.0 * (h->pdm_len + M) * p.hkv * p.hd * p.esz;
+    const double kvb = 2.0 * (h->pdm_len + M) * p.hkv * p.hd * p.kv_esz;
     float* hrow = hp + (size_t)r0 * p.d;
     o.push_back(gemv(h->PW(r, T_O), p.d, p.qo, attn + (size_t)(base + r0) * p.qo, p.qo, nr,
                      EPI_ADD, hrow, p.d, nullptr, 0, 0.f));
@@ -945,8 +951,9 @@ int spd_prefill(spd_handle* h, const int32_t* prompt, int32_t len, int32_t* firs
                                    P, p.hq, p.hd, kLinEps, st));
     } else {
       HIPCHK(h, launch_gemm(A, p.d, wt[T_QKV], QKV, p.qrows, P, p.qrows, p.d, false, bf, st));
-      HIPCHK(h, launch_rope_kv(QKV, p.qrows, Kc, Vc, rope, pos0, P, p.hq, p.hkv, p.hd, p.max_ctx, bf, st));
-      HIPCHK(h, launch_attention_prefill(QKV, p.qrows, O, p.qo, Kc, Vc, pos0, P, bf, p.hq, p.hkv,
+      HIPCHK(h, launch_rope_kv(QKV, p.qrows, Kc, Vc, rope, pos0, P, p.hq, p.hkv, p.hd, p.max_ctx,
+                               p.kv_bf16, st));
+      HIPCHK(h, launch_attention_prefill(QKV, p.qrows, O, p.qo, Kc, Vc, pos0, P, p.kv_bf16, p.hq, p.hkv,
                                          p.hd, p.max_ctx, st));
     }
     HIPCHK(h, launch_gemm(O, p.qo, wt[T_O], Rb, p.d, P, p.d, p.qo, true, bf, st));
@@ -1249,8 +1256,8 @@ size_t spd_debug_size(const spd_handle* h, int32_t what) {
     case SPD_DBG_TARGET_LOGITS: case SPD_DBG_DRAFT_LOGITS: return (size_t)p.V * 4;
     case SPD_DBG_H_RING: case SPD_DBG_PDM_ROWS: return (size_t)p.ring * p.d * 4;
     case SPD_DBG_ANCHORS: return (size_t)p.ring * p.k * p.d * 4;
-    case SPD_DBG_TARGET_KV: return (size_t)p.nsoft * 2 * p.hkv * p.max_ctx * p.hd * p.esz;
-    case SPD_DBG_PDM_KV: return (size_t)p.Ls * 2 * p.hkv * p.max_ctx * p.hd * p.esz;
+    case SPD_DBG_TARGET_KV: return (size_t)p.nsoft * 2 * p.hkv * p.max_ctx * p.hd * p.kv_esz;
+    case SPD_DBG_PDM_KV: return (size_t)p.Ls * 2 * p.hkv * p.max_ctx * p.hd * p.kv_esz;
     case SPD_DBG_TOKENS: return (size_t)p.ring * 4;
     case SPD_DBG_TOP_P: return (size_t)(1 + p.ring) * sizeof(NucleusCut);
   }
@@ -1292,14 +1299,15 @@ int spd_debug_copy(const spd_handle* hc, int32_t what, void* dst, size_t bytes) 
     for (int l = 0; l < layers; ++l) {
       const char* kl = raw.data() + (size_t)l * p.kv_layer_bytes;
       const char* vl = kl + p.kv_layer_bytes / 2;
-      char* ok = o + (size_t)l * 2 * plane * p.esz;
-      char* ov = ok + plane * p.esz;
-      std::memcpy(ok, kl, plane * p.esz);
+      const size_t e = p.kv_esz;
+      char* ok = o + (size_t)l * 2 * plane * e;
+      char* ov = ok + plane * e;
+      std::memcpy(ok, kl, plane * e);
       for (int g = 0; g < p.hkv; ++g)
         for (int pos = 0; pos < p.max_ctx; ++pos)
           for (int d = 0; d < p.hd; ++d)
-            std::memcpy(ov + (((size_t)g * p.max_ctx + pos) * p.hd + d) * p.esz,
-                        vl + v_index(p.bf16, g, pos, d, p.hd, p.max_ctx) * p.esz, p.esz);
+            std::memcpy(ov + (((size_t)g * p.max_ctx + pos) * p.hd + d) * e,
+                        vl + v_index(p.kv_bf16, g, pos, d, p.hd, p.max_ctx) * e, e);
     }
     return SPD_OK;
   }

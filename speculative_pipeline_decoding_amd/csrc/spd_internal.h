@@ -49,6 +49,7 @@ struct GemvProb {
   int hq, hkv, hd, max_ctx;
   int ksplit;          // matrix-core kernel: waves sharing one row tile's K
   int pad;             // matrix-core kernel: row tiles per workgroup
+  int kv_f32;          // EPI_QKV: the KV cache is fp32 (row-major V) even with bf16 weights
 };
 
 // Attention over one layer's KV cache for a group of query rows that share it: row r

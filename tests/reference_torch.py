@@ -63,7 +63,7 @@ def layer(cfg, W, prefix, kind, H, round_gemm=False):
     """One pre-norm decoder layer over the whole causal sequence H (positions 0..P-1).
     Returns (new H, stored K, stored V) with K, V as [P, hkv, hd] (None for linear)."""
     bf16 = cfg.dtype == "bf16"
-    store = bf if bf16 else f32
+    store = bf if (bf16 and cfg.kv_dtype != "f32") else f32
     gin = bf if (bf16 and round_gemm) else (lambda x: x)
     d, hq, hkv, hd = cfg.d_model, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
     P = H.shape[0]

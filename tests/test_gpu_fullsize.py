@@ -81,6 +81,21 @@ def test_fullsize_lockstep_with_oracle(wl, T, seed):
     assert rep["steps"] >= cfg.n_stages or rep["stopped_at_near_tie"] is not None
 
 
+@pytest.mark.parametrize("T,seed", [(0.0, 0), (1.0, 11)])
+def test_fullsize_lockstep_fp32_kv(wl, T, seed):
+    """The fp32 KV cache option (kv_dtype "f32"): with no bf16 rounding of K and V, the
+    library and the oracle (which stores fp32 then too) agree within the fixed 5e-2 logit
+    bound on every workload, the d4096 model included."""
+    name, dW, oW = wl
+    cfg, W, prompt = workload(name)
+    cfg = cfg.with_(kv_dtype="f32")
+    print(f"[fullsize] lockstep {name} kv f32 T={T}", flush=True)
+    rep = run_parity(cfg, W, dW, prompt[:40], T=T, seed=seed, max_steps=cfg.n_stages + 6,
+                     oracle_weights=oW, tol_logits=5e-2)
+    print(f"[fullsize] -> {rep}", flush=True)
+    assert rep["steps"] >= cfg.n_stages or rep["stopped_at_near_tie"] is not None
+
+
 def _stream(name, dW, n, T, G, seed=0, speculate_from="input", lookahead=False):
     from speculative_pipeline_decoding_amd import SPD
     cfg, _, prompt = workload(name)

@@ -437,3 +437,20 @@ def test_prompt_longer_than_one_staging_piece():
         k = apply_rope(k, p, cfg.rope_theta)
         np.testing.assert_allclose(kv[0, 0, :, p, :], k, rtol=0, atol=1e-5,
                                    err_msg=f"layer-0 K row at position {p}")
+
+
+@pytest.mark.parametrize("name,T,seed", [("mid_bf16_L4_d512_hd128_n4", 0.0, 0),
+                                         ("mid_bf16_L4_d512_hd128_n4", 1.0, 6),
+                                         ("mid_bf16_L6_d384_n3", 0.0, 0),
+                                         ("mid_hybrid_bf16_L8_d256_n4", 1.0, 3)])
+def test_fp32_kv_cache(name, T, seed):
+    """kv_dtype "f32" with bf16 weights: the target and PDM KV caches hold fp32 keys and
+    values (row-major V; head dims over 64 sum p V from whole V rows), in lockstep with the
+    oracle storing fp32 too. With nothing rounded to bf16 on the way, the logits agree to
+    1e-3, twenty times tighter than the bf16-KV bound."""
+    cfg, W, prompt = workload(name)
+    cfg32 = cfg.with_(kv_dtype="f32")
+    print(f"[parity] {name} kv f32 T={T}", flush=True)
+    rep = run_parity(cfg32, W, dev_weights(name), prompt, T=T, seed=seed, tol_logits=1e-3)
+    print(f"[parity] -> {rep}", flush=True)
+    assert rep["steps"] > 0

@@ -113,3 +113,22 @@ def test_oracle_own_rounding_error_fp32_vs_fp64():
     t32, z32 = ar_decode(cfg, W, prompt, G=24, ft=np.float32, return_logits=True)
     assert t64 == t32
     assert max(np.abs(a - b).max() for a, b in zip(z64, z32)) <= 1e-5
+
+
+def test_fp32_kv_cache_option_matches_reference():
+    """kv_dtype "f32" on a bf16 model: the oracle stores K and V as fp32 (no bf16 rounding),
+    and its prefill and per-position decode both match the reference with an fp32 store."""
+    cfg, W, prompt = workload("mid_bf16_L4_d512_hd128_n4")
+    cfg = cfg.with_(kv_dtype="f32")
+    toks = prompt[:24]
+    m = Model(cfg, W)
+    H = m.embed_many(toks)
+    for l in range(cfg.n_layers):
+        H = m.target.prefill_layer(l, H, 0)
+    Href, zref = torch_forward(cfg, W, toks)
+    np.testing.assert_allclose(H, Href, rtol=0, atol=1e-9 * max(1.0, np.abs(Href).max()))
+    # the stored keys are fp32 values, not all bf16 ones
+    k = m.target.K[0][:24]
+    assert np.array_equal(k, k.astype(np.float32).astype(np.float64))
+    bits = k.astype(np.float32).view(np.uint32) & 0xFFFF
+    assert bits.any()
