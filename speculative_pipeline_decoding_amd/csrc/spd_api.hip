@@ -898,8 +898,72 @@ int spd_init(const spd_model_config* cfg, const spd_weights* w, const spd_sampli
   return SPD_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Activation buffers of the chunked prefill: CH rows each (the anchor buffer k x CH rows).
+struct PrefillBufs {
+  float *H, *A, *QKV, *O, *G, *U, *Z, *AN;
+  int CH;
+};
+
+// Floats of every chunk buffer per prompt row, each buffer rounded up to 256 bytes at CH rows.
+size_t prefill_row_floats(const Plan& p) {
+  const size_t widest = std::max({(size_t)p.d, (size_t)p.qo, (size_t)p.F, (size_t)p.k * p.d});
+  return (size_t)p.d + widest + std::max(p.qrows, p.linrows) + p.qo + 2 * (size_t)p.F + p.d +
+         (size_t)p.k * p.d;
+}
+
+// Carves the chunk buffers for CH rows out of `base`; returns the bytes used.
+size_t carve_prefill(const Plan& p, char* base, int CH, PrefillBufs& b) {
+  const size_t widest = std::max({(size_t)p.d, (size_t)p.qo, (size_t)p.F, (size_t)p.k * p.d});
+  size_t o = 0;
+  auto take = [&](size_t floats) {
+    float* at = reinterpret_cast<float*>(base + o);
+    o = align_up(o + floats * sizeof(float));
+    return at;
+  };
+  b.CH = CH;
+  b.H = take((size_t)CH * p.d);
+  b.A = take((size_t)CH * widest);
+  b.QKV = take((size_t)CH * std::max(p.qrows, p.linrows));
+  b.O = take((size_t)CH * p.qo);
+  b.G = take((size_t)CH * p.F);
+  b.U = take((size_t)CH * p.F);
+  b.Z = take((size_t)CH * p.d);
+  b.AN = take((size_t)p.k * CH * p.d);
+  return o;
+}
+
+int prefill_impl(spd_handle* h, const int32_t* prompt, int32_t len, int32_t* first_token,
+                 const PrefillBufs& bufs);
+
+}  // namespace
+
+extern "C" {
+
 int spd_prefill(spd_handle* h, const int32_t* prompt, int32_t len, int32_t* first_token) {
   if (!h) return SPD_E_ARG;
+  PrefillBufs b{};
+  b.CH = kPrefillChunk;
+  b.H = h->at<float>(h->p.o_pH);
+  b.A = h->at<float>(h->p.o_pA);
+  b.QKV = h->at<float>(h->p.o_pQKV);
+  b.O = h->at<float>(h->p.o_pO);
+  b.G = h->at<float>(h->p.o_pG);
+  b.U = h->at<float>(h->p.o_pU);
+  b.Z = h->at<float>(h->p.o_pZ);
+  b.AN = h->at<float>(h->p.o_panch);
+  return prefill_impl(h, prompt, len, first_token, b);
+}
+
+}  // extern "C"
+
+namespace {
+
+int prefill_impl(spd_handle* h, const int32_t* prompt, int32_t len, int32_t* first_token,
+                 const PrefillBufs& bufs) {
   h->err.clear();
   if (h->state != spd_handle::S_INIT) return fail(h, SPD_E_STATE, "already prefilled (spd_reset first)");
   if (!prompt || len < 1) return fail(h, SPD_E_ARG, "empty prompt");
@@ -927,16 +991,16 @@ int spd_prefill(spd_handle* h, const int32_t* prompt, int32_t len, int32_t* firs
     urc = upload(h->ws + p.o_forced, h->forced_ref.data(), h->forced_ref.size());
   if (urc != SPD_OK) return urc;
   const bool bf = p.bf16;
-  float* H = h->at<float>(p.o_pH);
-  float* A = h->at<float>(p.o_pA);
-  float* QKV = h->at<float>(p.o_pQKV);
-  float* O = h->at<float>(p.o_pO);
-  float* Gb = h->at<float>(p.o_pG);
-  float* Ub = h->at<float>(p.o_pU);
-  float* Z = h->at<float>(p.o_pZ);
-  float* AN = h->at<float>(p.o_panch);
+  float* H = bufs.H;
+  float* A = bufs.A;
+  float* QKV = bufs.QKV;
+  float* O = bufs.O;
+  float* Gb = bufs.G;
+  float* Ub = bufs.U;
+  float* Z = bufs.Z;
+  float* AN = bufs.AN;
   const float2* rope = h->at<float2>(p.o_rope);
-  const int CH = kPrefillChunk;
+  const int CH = bufs.CH;
   const int kd = p.k * p.d;
   // one decoder layer over P rows of the residual Rb (fp32 activations throughout)
   // lin_l >= 0: a linear-attention target layer (its state ring), else a softmax layer
@@ -1038,6 +1102,10 @@ int spd_prefill(spd_handle* h, const int32_t* prompt, int32_t len, int32_t* firs
   h->state = spd_handle::S_READY;
   return SPD_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 // The host issues launches one at a time, so the order of the two streams' work in the
 // op list is the order in which each stream receives it. build_step lists the whole PDM
