@@ -183,6 +183,21 @@ int spd_init(const spd_model_config* cfg, const spd_weights* w, const spd_sampli
 int spd_prefill(spd_handle* h, const int32_t* prompt, int32_t len, int32_t* first_token);
 
 /*
+ * spd_prefill for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same prefill, with
+ * the same arguments, results and errors, except that its chunk activation buffers live
+ * in a 32 MiB array of the library's own device memory instead of the caller's workspace
+ * (one array per GPU, held until the process ends), so the prompt is processed in chunks
+ * of as many rows as the array holds (at most the regular 512). It calls no allocating
+ * routine. Every call on a GPU shares that GPU's array, so calls on two handles of one GPU
+ * that overlap in time race on it. Extra errors: SPD_E_CAPACITY when even 16 prompt rows
+ * of this model do not fit the array; SPD_E_DEVICE when its address could not be obtained
+ * at spd_init.
+ */
+int spd_prefill_static_scratch(spd_handle* h, const int32_t* prompt, int32_t len,
+                               int32_t* first_token);
+
+/*
  * Enqueue one pipeline step on the stream and return at once: embed the
  * stage-0 token; the PDM drafts the next token from the step's input states;
  * every in-flight token runs its stage's layers; if the oldest token leaves the

@@ -78,7 +78,8 @@ SYMBOLS = ["spd_workspace_bytes", "spd_init", "spd_init_error", "spd_prefill", "
            "spd_verify_commit", "spd_get_stats", "spd_get_kv_lens", "spd_debug_size",
            "spd_debug_copy", "spd_reset", "spd_last_error", "spd_destroy", "spd_lookahead",
            "spd_timing_enable",
-           "spd_timing_read", "spd_timing_read_layers", "spd_balance_stages"]
+           "spd_timing_read", "spd_timing_read_layers", "spd_balance_stages",
+           "spd_prefill_static_scratch"]
 
 _lib = None
 
@@ -105,6 +106,8 @@ def load() -> ctypes.CDLL:
     L.spd_init.argtypes = [P(ModelConfig), P(Weights), P(Sampling), VP, ctypes.c_size_t, VP, P(VP)]
     L.spd_init_error.restype = ctypes.c_char_p
     L.spd_prefill.argtypes = [VP, P(ctypes.c_int32), ctypes.c_int32, P(ctypes.c_int32)]
+    L.spd_prefill_static_scratch.argtypes = [VP, P(ctypes.c_int32), ctypes.c_int32,
+                                             P(ctypes.c_int32)]
     L.spd_step.argtypes = [VP]
     L.spd_verify_commit.argtypes = [VP, P(Commit)]
     L.spd_get_stats.argtypes = [VP, P(Stats)]
@@ -254,6 +257,13 @@ class SPD:
         arr = _i32(prompt)
         first = ctypes.c_int32()
         self._chk(self.L.spd_prefill(self.h, arr, len(prompt), ctypes.byref(first)))
+        return first.value
+
+    def prefill_static_scratch(self, prompt) -> int:
+        """spd_prefill with its chunk buffers in the library's static device array."""
+        arr = _i32(prompt)
+        first = ctypes.c_int32()
+        self._chk(self.L.spd_prefill_static_scratch(self.h, arr, len(prompt), ctypes.byref(first)))
         return first.value
 
     def step(self) -> None:

@@ -14,6 +14,7 @@
 #include <cstdio>
 #include <cstring>
 #include <deque>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -26,6 +27,40 @@ namespace spd {
 int attn_max_split();
 bool attn_supported_head_dim(int hd, bool bf16);
 }
+
+// Device memory for spd_prefill_static_scratch, the prefill entry point for callers that
+// cannot allocate: its chunk buffers live in this array. Each GPU the library runs on holds
+// its own copy until the process ends. In host code the name is only a stand-in: the
+// device address comes from hipGetSymbolAddress, looked up once per device at spd_init.
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kScratchDevices] = {};
+std::string g_scratch_err[kScratchDevices];
+
+// The current device's copy of `scratch` (looked up on its first use), or nullptr with a
+// message in err.
+char* scratch_of_current_device(std::string& err) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) { err = std::string("hipGetDevice: ") + hipGetErrorString(e); return nullptr; }
+  if (dev < 0 || dev >= kScratchDevices) { err = "device index beyond the static scratch table"; return nullptr; }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev] && g_scratch_err[dev].empty()) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      g_scratch_err[dev] = std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e);
+    else
+      g_scratch_ptr[dev] = static_cast<char*>(ptr);
+  }
+  err = g_scratch_err[dev];
+  return g_scratch_ptr[dev];
+}
+}  // namespace
 
 namespace {
 
@@ -213,6 +248,8 @@ struct spd_handle {
   std::vector<int> forced_ref;
   // device
   char* ws;
+  char* scratch = nullptr;         // this device's copy of the static scratch array
+  std::string scratch_err;
   hipStream_t st;                 // the caller's stream: target chain, head, verify
   hipStream_t st2 = nullptr;      // library-owned stream for the PDM chain
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
@@ -882,6 +919,9 @@ int spd_init(const spd_model_config* cfg, const spd_weights* w, const spd_sampli
     return dev_fail(e, "hipEventCreateWithFlags");
   if ((e = hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming)) != hipSuccess)
     return dev_fail(e, "hipEventCreateWithFlags");
+  // the static scratch of this device (spd_prefill_static_scratch); a failed lookup only
+  // disables that entry point
+  h->scratch = scratch_of_current_device(h->scratch_err);
   std::vector<float2> rope;
   fill_rope(p, rope);
   if ((e = hipMemcpyAsync(h->ws + p.o_rope, rope.data(), rope.size() * sizeof(float2),
@@ -908,14 +948,8 @@ struct PrefillBufs {
   int CH;
 };
 
-// Floats of every chunk buffer per prompt row, each buffer rounded up to 256 bytes at CH rows.
-size_t prefill_row_floats(const Plan& p) {
-  const size_t widest = std::max({(size_t)p.d, (size_t)p.qo, (size_t)p.F, (size_t)p.k * p.d});
-  return (size_t)p.d + widest + std::max(p.qrows, p.linrows) + p.qo + 2 * (size_t)p.F + p.d +
-         (size_t)p.k * p.d;
-}
-
-// Carves the chunk buffers for CH rows out of `base`; returns the bytes used.
+// Carves the chunk buffers for CH rows out of `base` (nullptr: only sizes them); returns
+// the bytes used.
 size_t carve_prefill(const Plan& p, char* base, int CH, PrefillBufs& b) {
   const size_t widest = std::max({(size_t)p.d, (size_t)p.qo, (size_t)p.F, (size_t)p.k * p.d});
   size_t o = 0;
@@ -955,6 +989,26 @@ int spd_prefill(spd_handle* h, const int32_t* prompt, int32_t len, int32_t* firs
   b.U = h->at<float>(h->p.o_pU);
   b.Z = h->at<float>(h->p.o_pZ);
   b.AN = h->at<float>(h->p.o_panch);
+  return prefill_impl(h, prompt, len, first_token, b);
+}
+
+int spd_prefill_static_scratch(spd_handle* h, const int32_t* prompt, int32_t len,
+                               int32_t* first_token) {
+  if (!h) return SPD_E_ARG;
+  h->err.clear();
+  if (!h->scratch) return fail(h, SPD_E_DEVICE, "static scratch unavailable: " + h->scratch_err);
+  // as many prompt rows per chunk as the array holds (at most the regular chunk)
+  PrefillBufs b{};
+  int CH = kPrefillChunk;
+  while (CH > 0 && carve_prefill(h->p, nullptr, CH, b) > kStaticScratchBytes) CH -= 16;
+  if (CH <= 0) {
+    const size_t need = carve_prefill(h->p, nullptr, 16, b);
+    return fail(h, SPD_E_CAPACITY,
+                "the model is too wide for the static prefill scratch: 16 prompt rows need " +
+                    std::to_string(need) + " bytes, the array holds " +
+                    std::to_string(kStaticScratchBytes));
+  }
+  carve_prefill(h->p, h->scratch, CH, b);
   return prefill_impl(h, prompt, len, first_token, b);
 }
 

@@ -102,6 +102,7 @@ def test_null_handle_calls():
     assert L.spd_step(None) == binding.SPD_E_ARG
     assert L.spd_verify_commit(None, None) == binding.SPD_E_ARG
     assert L.spd_prefill(None, None, 0, None) == binding.SPD_E_ARG
+    assert L.spd_prefill_static_scratch(None, None, 0, None) == binding.SPD_E_ARG
     assert L.spd_lookahead(None, 1) == binding.SPD_E_ARG
     assert L.spd_reset(None) == binding.SPD_E_ARG
     L.spd_destroy(None)
