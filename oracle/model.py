@@ -94,6 +94,8 @@ class Stack:
                 self.S.append(np.zeros((cfg.n_q_heads, hd, hd), self.ft))
             self.snap.append({})
         self.gam = lin_gammas(cfg.n_q_heads).astype(self.ft)
+        # keys and values of sibling candidates: (layer, position, branch) -> (k, v)
+        self.side: Dict[tuple, tuple] = {}
 
     # -- precision contract ------------------------------------------------
     def store(self, x: np.ndarray) -> np.ndarray:
@@ -107,20 +109,24 @@ class Stack:
         return self.W(f"{self.prefix}.{i}.{t}")
 
     # -- one position ------------------------------------------------------
-    def decode_layer(self, i: int, h: np.ndarray, pos: int) -> np.ndarray:
+    def decode_layer(self, i: int, h: np.ndarray, pos: int, branch: int = 0) -> np.ndarray:
+        """Layer i on residual h at position pos. branch > 0: a sibling candidate of the
+        token at pos (draft tree): its key and value go to a side entry, and it attends over
+        the cached positions before pos and its own key, not the main token's."""
         c = self.cfg
         a = rmsnorm(h, self.w(i, "attn_norm"), c.rms_eps)
         qkv = self.w(i, "w_qkv") @ a
         if self.kinds[i] == SOFTMAX:
-            o = self._attend_one(i, qkv, pos)
+            o = self._attend_one(i, qkv, pos, branch)
         else:
+            assert branch == 0, "sibling candidates need softmax layers"
             o = self._linear_one(i, qkv, pos)
         h = h + self.w(i, "w_o") @ o
         b = rmsnorm(h, self.w(i, "ffn_norm"), c.rms_eps)
         act = silu(self.w(i, "w_gate") @ b) * (self.w(i, "w_up") @ b)
         return h + self.w(i, "w_down") @ act
 
-    def _attend_one(self, i: int, qkv: np.ndarray, pos: int) -> np.ndarray:
+    def _attend_one(self, i: int, qkv: np.ndarray, pos: int, branch: int = 0) -> np.ndarray:
         c = self.cfg
         hq, hkv, hd = c.n_q_heads, c.n_kv_heads, c.head_dim
         q = qkv[: hq * hd].reshape(hq, hd)
@@ -128,9 +134,15 @@ class Stack:
         v = qkv[(hq + hkv) * hd:].reshape(hkv, hd)
         q = apply_rope(q, pos, c.rope_theta)
         k = apply_rope(k, pos, c.rope_theta)
-        self.K[i][pos] = self.store(k)
-        self.V[i][pos] = self.store(v)
-        Ks, Vs = self.K[i][: pos + 1], self.V[i][: pos + 1]
+        if branch == 0:
+            self.K[i][pos] = self.store(k)
+            self.V[i][pos] = self.store(v)
+            Ks, Vs = self.K[i][: pos + 1], self.V[i][: pos + 1]
+        else:
+            ks, vs = self.store(k), self.store(v)
+            self.side[(i, pos, branch)] = (ks, vs)
+            Ks = np.concatenate([self.K[i][:pos], ks[None]])
+            Vs = np.concatenate([self.V[i][:pos], vs[None]])
         group = hq // hkv
         o = np.empty((hq, hd), self.ft)
         for head in range(hq):
@@ -204,6 +216,18 @@ class Stack:
         self.S[i] = S
         self.snap[i][pos0 + P - 1] = S.copy()
         return O.reshape(P, -1)
+
+    # -- draft tree -----------------------------------------------------------------
+    def adopt(self, pos: int, branch: int, layers: Sequence[int]) -> None:
+        """The sibling `branch` at pos becomes the main token there: its keys and values of
+        the given layers move into the cache at pos."""
+        for i in layers:
+            self.K[i][pos], self.V[i][pos] = self.side[(i, pos, branch)]
+
+    def drop_side(self, keep) -> None:
+        """Forget the sibling entries whose position fails keep(pos)."""
+        for key in [k for k in self.side if not keep(k[1])]:
+            del self.side[key]
 
     # -- rejection ---------------------------------------------------------------
     def truncate(self, length: int) -> None:

@@ -21,6 +21,20 @@ Readings (the pages are silent):
   * forced mode (acceptance sweep): the draft at position x becomes the
     reference greedy token r[x] when u_FORCE(x) < p_force, else (r[x] + 1) mod V.
 
+Draft trees of width W (the review's "Assumptions & free parameters" lists W = 1 and 4; a
+reading, since the pages describe no mechanism): the PDM proposes W distinct candidates
+for a position, best first. At T = 0 they are the W largest logits (ties: lower id first);
+at T > 0 the W largest Gumbel-perturbed scores log q_i + G_i, which draws W tokens from q
+without replacement (Gumbel-top-k: Kool, van Hoof & Welling 2019); W = 1 is the plain
+draft. Verification tests them in rank order (recursive rejection sampling, Jeon et al.
+2024): round i proposes c_i from q_i, q renormalised without c_0 .. c_{i-1}, against the
+target r_i (r_0 = p); accept iff u_i q_i(c_i) < r_i(c_i), else
+r_{i+1} = max(0, r_i - q_i) / sum(max(0, r_i - q_i)). Each round is one speculative
+sampling step whose proposal is, given the earlier rounds, distributed as q_i and
+independent of u_i, so by induction the committed token is distributed as p. If every
+candidate is rejected, y ~ r_W. At T = 0 the committed token is argmax p, accepted when it
+is a candidate.
+
 Near-ties at top_p < 1. Another implementation computes the same decisions from
 logits that differ from these by at most Sampling.logit_slack (delta) each, and
 sums masses with a relative rounding of at most TOP_P_EPS. Every probability it
@@ -275,3 +289,72 @@ def residual_distribution(p: np.ndarray, q: np.ndarray) -> np.ndarray:
     r = np.maximum(p - q, 0.0)
     tot = r.sum()
     return r / tot if tot > 0 else r
+
+
+def select_drafts(z_q: np.ndarray, s: Sampling, pos: int, W: int):
+    """The PDM's W candidates for position pos, best first: (candidates, q or None, flag).
+    W = 1 is select_draft. Otherwise (top_p >= 1, no forced mode): the W largest logits at
+    T = 0, the W largest log q_i + G_i at T > 0 (lower id first on ties); flag marks a gap
+    below NEAR_TIE between two of the W + 1 largest scores, whose order decides the
+    candidates and their ranks."""
+    if W == 1:
+        d, q, flag = select_draft(z_q, s, pos)
+        return [d], q, flag
+    assert s.forced_p is None and s.top_p >= 1.0
+    V = z_q.size
+    if s.temperature == 0.0:
+        q, sc = None, z_q
+    else:
+        q = distribution(z_q, s.temperature, s.top_p)
+        G = gumbel(uniform(s.seed, STREAM_DRAFT, pos, np.arange(V)))
+        with np.errstate(divide="ignore"):
+            sc = np.where(q > 0, np.log(q) + G, -np.inf)
+    order = np.lexsort((np.arange(V), -sc))        # descending score, lower id first
+    top = order[: W + 1]
+    vals = sc[top]
+    flag = any(vals[j] - vals[j + 1] < NEAR_TIE for j in range(len(top) - 1))
+    return [int(t) for t in top[:W]], q, bool(flag)
+
+
+def tree_rounds(p: np.ndarray, q: np.ndarray, cands):
+    """The rounds of recursive rejection sampling of candidates cands (best first) against
+    target p with draft distribution q, without any randomness: per round i the pair
+    (q_i(c_i), r_i(c_i)), so that c_i is accepted iff u_i q_i(c_i) < r_i(c_i), and the
+    unnormalised residual max(0, r_{W-1} - q_{W-1}) that y is drawn from when every round
+    rejects. Stops early (residual None) if a residual has no mass in floating point."""
+    r, left, rounds = p, q.copy(), []
+    res = None
+    for i, c in enumerate(cands):
+        qi = q if i == 0 else left / left.sum()
+        rounds.append((qi[c], r[c]))
+        res = np.maximum(r - qi, 0.0)
+        if not (res > 0).any():
+            return rounds, None
+        r = res / res.sum()
+        left[c] = 0.0
+    return rounds, res
+
+
+def verify_tree(z_t: np.ndarray, cands, q: Optional[np.ndarray], s: Sampling, v: int):
+    """Verify the candidates for position v (best first) against target logits z_t.
+    Returns (y, index of the accepted candidate or -1, near-tie flag)."""
+    if len(cands) == 1:
+        y, acc, flag = verify(z_t, cands[0], q, s, v)
+        return y, (0 if acc else -1), flag
+    assert s.top_p >= 1.0
+    if s.temperature == 0.0:
+        y = argmax_lowest(z_t)
+        return y, (cands.index(y) if y in cands else -1), top2_gap(z_t) < NEAR_TIE
+    p = distribution(z_t, s.temperature, s.top_p)
+    rounds, res = tree_rounds(p, q, cands)
+    flag = False
+    for i, (qc, rc) in enumerate(rounds):
+        u = uniform(s.seed, STREAM_ACC, v, i)[()]
+        flag = flag or abs(u * qc - rc) < NEAR_TIE * qc
+        if u * qc < rc:
+            return int(cands[i]), i, bool(flag)
+    if res is None:
+        # a residual without mass (see verify): the target's argmax, flagged
+        return argmax_lowest(z_t), -1, True
+    y, rflag = gumbel_max(res, s.seed, STREAM_RES, v)
+    return int(y), -1, bool(flag or rflag)

@@ -28,6 +28,20 @@ Readings, where the pages leave a step open (each also listed in the design doc):
   the embedding of the stage-0 token is part of the step's input state, so
   the newest PDM row sees it (depth 0).
 
+Draft trees of width W (the review's "Assumptions & free parameters": W = 1 and 4; a
+reading, since the pages describe no mechanism): each draft position carries W candidates
+(sampling.select_drafts), best first. The first is the spine: the PDM's next draft
+continues from it. The others are siblings: they enter the pipeline with the spine and
+run the same stages at the same position, each attending over the cached positions before
+it (the committed prefix and the spine's in-flight positions: its ancestors) and its own
+key. When the token before them leaves the pipeline, all W are verified
+(sampling.verify_tree). The spine accepted: as with W = 1. A sibling accepted: it is
+adopted as the token at v (its keys and values move into the cache, its states become the
+position's), every position after v (the spine's descendants) and this step's draft are
+flushed, and the adopted token finishes its last stage in the next step. None accepted: the
+usual reject and reseed. Positions whose token is already verified (a reseed, an adopted
+sibling, a draft verified in the step that made it) carry one candidate.
+
 Output-state speculation, the ablation the pith.science review mentions against the
 input-state ("early start") schedule of its "Core claim": with speculate_from="output"
 the PDM runs after the step's target layers and reads each position's states at its
@@ -44,7 +58,7 @@ import numpy as np
 
 from spd_inputs.configs import ModelConfig
 from .model import Model
-from .sampling import Sampling, first_token, select_draft, verify, argmax_lowest
+from .sampling import Sampling, first_token, select_drafts, verify_tree, argmax_lowest
 
 
 def stage_sizes(L: int, n: int, explicit: Sequence[int] = ()) -> List[int]:
@@ -76,6 +90,10 @@ class StepRecord:
     inflight: List[Tuple[int, int]] = field(default_factory=list)
     pdm_rows: Tuple[int, int] = (0, 0)   # window [first, last] of PDM rows this step
     pdm_row_depths: List[int] = field(default_factory=list)
+    drafts: List[int] = field(default_factory=list)        # the W candidates drafted this step
+    verified_cands: List[int] = field(default_factory=list)  # candidates tested at v
+    accepted_index: int = -1     # which candidate was accepted (-1: none)
+    single: bool = False         # the exiting token was alone: v held this step's drafts
 
 
 class SPD:
@@ -85,8 +103,13 @@ class SPD:
                  n: Optional[int] = None, anchors: Optional[Sequence[int]] = None,
                  Ls: Optional[int] = None, fill: str = "clamp", ft=np.float64,
                  model: Optional[Model] = None, record_logits: bool = True,
-                 speculate_from: str = "input"):
+                 speculate_from: str = "input", W: int = 1):
         assert speculate_from in ("input", "output")
+        assert W >= 1
+        self.W = W
+        if W > 1:
+            assert speculate_from == "input" and sampling.forced_p is None
+            assert sampling.top_p >= 1.0 and all(k == 0 for k in cfg.kinds)
         self.output_states = speculate_from == "output"
         self.cfg = cfg
         self.n = cfg.n_stages if n is None else n
@@ -116,6 +139,11 @@ class SPD:
         self.N = self.K = self.accepted = self.rejected = 0
         self.committed: List[int] = []         # generated stream incl. the first token
         self.P0 = 0
+        # draft tree: sibling candidates (ranks 1 .. W-1) of in-flight positions, their
+        # residuals and anchor states
+        self.sib: Dict[int, List[int]] = {}
+        self.sib_h: Dict[Tuple[int, int], np.ndarray] = {}
+        self.sib_anch: Dict[Tuple[int, int], Dict[int, np.ndarray]] = {}
 
     # -- prefill -------------------------------------------------------------
     def prefill(self, prompt: np.ndarray) -> int:
@@ -186,25 +214,40 @@ class SPD:
     def step(self) -> StepRecord:
         m, n, L, B = self.m, self.n, self.L, self.B
         newest = self.F[-1][0]
-        assert self.F[-1][1] == 0
-        # 1. the stage-0 token enters: embedding = anchor 0
-        h0 = m.embed(self.tok[newest])
-        self.h[newest] = h0
-        self.anch[newest] = {0: h0.copy()}
-        self.depth[newest] = 0
+        # 1. the stage-0 token enters: embedding = anchor 0 (every step except the one after a
+        #    sibling was adopted, whose newest token is the adopted one, in its last stage)
+        if self.F[-1][1] == 0:
+            h0 = m.embed(self.tok[newest])
+            self.h[newest] = h0
+            self.anch[newest] = {0: h0.copy()}
+            self.depth[newest] = 0
+            for b, t in enumerate(self.sib.get(newest, []), start=1):
+                hs = m.embed(t)
+                self.sib_h[(newest, b)] = hs
+                self.sib_anch[(newest, b)] = {0: hs.copy()}
+        else:
+            assert self.W > 1 and len(self.F) == 1 and self.F[0][1] == n - 1
         exiting = self.F[0][1] == n - 1
 
         def target_pass():
-            """Each in-flight token runs its stage's layers."""
+            """Each in-flight token (and its sibling candidates) runs its stage's layers."""
             for pos, st in self.F:
+                layers = range(self.starts[st], self.starts[st] + self.sizes[st])
                 h = self.h[pos]
-                for l in range(self.starts[st], self.starts[st] + self.sizes[st]):
+                for l in layers:
                     h = m.target.decode_layer(l, h, pos)
                     if (l + 1) in B:
                         self.anch[pos][B.index(l + 1)] = h.copy()
                     self.kv_len[l] = pos + 1
                 self.h[pos] = h
                 self.depth[pos] += self.sizes[st]
+                for b in range(1, len(self.sib.get(pos, [])) + 1):
+                    hs = self.sib_h[(pos, b)]
+                    for l in layers:
+                        hs = m.target.decode_layer(l, hs, pos, branch=b)
+                        if (l + 1) in B:
+                            self.sib_anch[(pos, b)][B.index(l + 1)] = hs.copy()
+                    self.sib_h[(pos, b)] = hs
 
         if self.output_states:
             # 3, then 2: the PDM reads the states the step produced
@@ -220,46 +263,72 @@ class SPD:
             # 3. target
             target_pass()
         dpos = newest + 1
-        d, q, dflag = select_draft(z_q, self.s, dpos)
+        drafts, q, dflag = select_drafts(z_q, self.s, dpos, self.W)
+        d = drafts[0]
         if q is not None:
             self.q[dpos] = q
             self.zq[dpos] = z_q
         self.K += 1
         rec = StepRecord(K=self.K, newest=newest, draft=d, draft_flag=dflag, exited=False,
                          draft_logits=z_q if self.record_logits else None,
-                         pdm_rows=(rows[0], rows[-1]), pdm_row_depths=depths)
+                         pdm_rows=(rows[0], rows[-1]), pdm_row_depths=depths, drafts=drafts)
         # 4. streaming verification of the position after the exiting token
         if self.F[0][1] == n - 1:
             p = self.F[0][0]
             v = p + 1
             z_t = m.logits(self.h[p])
-            dv = self.tok[v] if len(self.F) > 1 else d
-            y, acc, vflag = verify(z_t, dv, self.q.get(v), self.s, v, self.zq.get(v))
+            single = len(self.F) == 1
+            cands = drafts if single else [self.tok[v]] + self.sib.get(v, [])
+            y, idx, vflag = verify_tree(z_t, cands, self.q.get(v), self.s, v)
+            acc = idx >= 0
             self.N += 1
             self.committed.append(y)
             rec.exited, rec.exit_pos, rec.verified_pos = True, p, v
-            rec.verified_draft, rec.committed, rec.accepted, rec.verify_flag = dv, y, acc, vflag
+            rec.verified_draft, rec.committed, rec.accepted, rec.verify_flag = cands[0], y, acc, vflag
+            rec.verified_cands, rec.accepted_index, rec.single = list(cands), idx, single
             rec.target_logits = z_t if self.record_logits else None
-            if acc:
+            if acc and (idx == 0 or single):
+                # the spine (or, when v is this step's draft, any candidate: none of them has
+                # entered the pipeline yet) is the token at v; the pipeline shifts
                 self.accepted += 1
-                self.F = [[pos, st + 1] for pos, st in self.F[1:]] + [[dpos, 0]]
-                self.tok[dpos] = d
+                self._drop_siblings(lambda x: x != v)
+                if single:
+                    self.F = [[dpos, 0]]
+                    self.tok[dpos] = y
+                else:
+                    self.F = [[pos, st + 1] for pos, st in self.F[1:]] + [[dpos, 0]]
+                    self.tok[dpos] = d
+                    if len(drafts) > 1:
+                        self.sib[dpos] = drafts[1:]
+            elif acc:
+                # a sibling at v: it becomes the token at v, and the spine's descendants go
+                self.accepted += 1
+                st_v = self.F[1][1]
+                ran = list(range(self.starts[st_v] + self.sizes[st_v]))
+                m.target.adopt(v, idx, ran)
+                self.h[v] = self.sib_h[(v, idx)]
+                self.anch[v] = self.sib_anch[(v, idx)]
+                self.kv_len = [min(k, v + 1 if l < len(ran) else v) for l, k in enumerate(self.kv_len)]
+                m.target.truncate(v + 1)
+                self._forget_from(v + 1)
+                self._drop_siblings(lambda x: x < v)
+                self.tok[v] = y
+                self.F = [[v, st_v + 1]]
             else:
                 # 5. reject: truncate, flush, reseed (v, y) at stage 0
                 self.rejected += 1
                 self.kv_len = [min(k, v) for k in self.kv_len]
                 m.target.truncate(v)
-                for dead in [x for x in self.h if x >= v]:
-                    self.h.pop(dead, None)
-                    self.anch.pop(dead, None)
-                    self.depth.pop(dead, None)
-                self.tok = {x: t for x, t in self.tok.items() if x < v}
+                self._forget_from(v)
+                self._drop_siblings(lambda x: x < v)
                 self.tok[v] = y
                 self.F = [[v, 0]]
         else:
             # refill step: nothing leaves the pipeline
             self.F = [[pos, st + 1] for pos, st in self.F] + [[dpos, 0]]
             self.tok[dpos] = d
+            if len(drafts) > 1:
+                self.sib[dpos] = drafts[1:]
         # forget states nobody reads again
         for old in [x for x in self.h if x < self.pdm_len]:
             self.h.pop(old, None)
@@ -268,10 +337,32 @@ class SPD:
         for old in [x for x in self.q if x < self.pdm_len]:
             self.q.pop(old, None)
             self.zq.pop(old, None)
+        self._drop_siblings(lambda x: x >= self.pdm_len)
         rec.kv_len = list(self.kv_len)
         rec.pdm_len = self.pdm_len
         rec.inflight = [tuple(f) for f in self.F]
         return rec
+
+    # -- draft-tree bookkeeping ----------------------------------------------------
+    def _forget_from(self, x0: int) -> None:
+        """Drop every state and token of positions >= x0 (a flush)."""
+        for dead in [x for x in self.h if x >= x0]:
+            self.h.pop(dead, None)
+            self.anch.pop(dead, None)
+            self.depth.pop(dead, None)
+        self.tok = {x: t for x, t in self.tok.items() if x < x0}
+        for dead in [x for x in self.q if x >= x0]:
+            self.q.pop(dead, None)
+            self.zq.pop(dead, None)
+
+    def _drop_siblings(self, keep) -> None:
+        """Forget the sibling candidates (and their side keys) of positions failing keep."""
+        for x in [x for x in self.sib if not keep(x)]:
+            for b in range(1, len(self.sib[x]) + 1):
+                self.sib_h.pop((x, b), None)
+                self.sib_anch.pop((x, b), None)
+            del self.sib[x]
+        self.m.target.drop_side(keep)
 
     # -- statistics (Eq. 9) --------------------------------------------------------
     @property
