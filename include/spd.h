@@ -83,6 +83,17 @@ enum { SPD_KV_AUTO = 0, SPD_KV_F32 = 1 };             /* KV cache storage */
  *     (bf16 keys and values, rounded to nearest even, for bf16 weights); SPD_KV_F32 (1)
  *     stores them in fp32 with bf16 weights too: twice the KV bytes, and no bf16
  *     rounding of K and V, whose one-ulp flips deep, wide models amplify in the logits.
+ *   draft_width: W, candidates the PDM proposes per draft position (0 or 1: a chain;
+ *     at most 4). The pith.science review lists W = 1 and 4 among the paper's free
+ *     parameters ("Assumptions & free parameters"). With W > 1 each draft position
+ *     carries the PDM's W best candidates (largest logits at T = 0; at T > 0 the W
+ *     largest log q + Gumbel scores, a draw without replacement from q), ranked best
+ *     first; rank 0 (the spine) is the token the next positions build on, ranks 1..W-1
+ *     (siblings) run through the same layers at the same position, each attending to
+ *     the cache plus its own key. Verification tests them in rank order (see
+ *     spd_sampling); an accepted sibling becomes the token at its position, keeping
+ *     the layers it has run, and the positions after it are flushed. Needs softmax
+ *     layers only, SPD_SPEC_INPUT, top_p >= 1 and forced_mode 0.
  * Limits: d_model, d_ffn, n_q_heads*head_dim multiples of 8; head_dim in
  * {16, 32, 64, 80, 128}; n_q_heads a multiple of n_kv_heads with at most 16 query
  * heads per KV head; n <= 16; k <= 8; Ls <= 16.
@@ -101,6 +112,7 @@ typedef struct {
   int32_t max_ctx;
   int32_t speculate_from;         /* SPD_SPEC_INPUT | SPD_SPEC_OUTPUT */
   int32_t kv_dtype;               /* SPD_KV_AUTO | SPD_KV_F32 */
+  int32_t draft_width;            /* W: candidates per draft position, 1..4 (0 means 1) */
 } spd_model_config;
 
 /*
@@ -145,6 +157,13 @@ typedef struct {
  * If a rejection finds no token with p > q in floating point (the residual
  * max(0, p - q) has no mass), the committed token is the target's argmax and the
  * decision is flagged as a near-tie.
+ * Draft trees (draft_width W > 1): at T = 0 the committed token is the target's argmax
+ * and the accepted candidate is the one equal to it, if any. At T > 0 the candidates
+ * c_0..c_{W-1} are tested in rank order by recursive rejection sampling: round i
+ * proposes from q_i, q with c_0..c_{i-1} removed and renormalised, against r_i, where
+ * r_0 = p and r_{i+1} = max(0, r_i - q_i) normalised; c_i is accepted iff
+ * u_i q_i(c_i) < r_i(c_i) with u_i the stream-2 number of (v, i); if every round rejects,
+ * y is drawn from r_W. A residual without mass ends the rounds as above.
  */
 typedef struct {
   float temperature;
@@ -238,10 +257,13 @@ int spd_lookahead(spd_handle* h, int on);
  *   flags: bit 0 near-tie in the verify decision (top-2 gap < 1e-3, or
  *     |u q(d) - p(d)| < 1e-3 q(d)); bit 1 near-tie in the draft selection
  *   committed_total: N after this step; inflight: tokens in flight now
+ *   accepted_index: rank of the accepted candidate at v (0: the spine; > 0 a sibling,
+ *     with draft_width > 1), -1 when nothing was accepted or nothing verified
  */
 typedef struct {
   int32_t verified, position, token, accepted, draft_token, flags;
   int32_t committed_total, inflight, new_draft, newest;
+  int32_t accepted_index;
 } spd_commit;
 int spd_verify_commit(spd_handle* h, spd_commit* out);
 
@@ -259,12 +281,14 @@ int spd_get_kv_lens(const spd_handle* h, int32_t* per_layer, int32_t* pdm_len);
 enum {
   SPD_DBG_TARGET_LOGITS = 1,   /* f32 [V]: last target head output (prefill row or exit) */
   SPD_DBG_DRAFT_LOGITS = 2,    /* f32 [V]: last PDM head output (raw logits) */
-  SPD_DBG_H_RING = 3,          /* f32 [n+1][d]: residual of position p in slot p mod (n+1) */
-  SPD_DBG_ANCHORS = 4,         /* f32 [n+1][k][d]: anchors of position p in slot p mod (n+1) */
+  SPD_DBG_H_RING = 3,          /* f32 [n+1][W][d]: residual of position p's candidate b in
+                                  row (p mod (n+1)) W + b (b = 0: the token) */
+  SPD_DBG_ANCHORS = 4,         /* f32 [n+1][W][k][d]: anchors, rows as SPD_DBG_H_RING */
   SPD_DBG_PDM_ROWS = 5,        /* f32 [n+1][d]: PDM residual rows of the last step */
   SPD_DBG_TARGET_KV = 6,       /* KV dtype [softmax layers][2][hkv][max_ctx][hd] */
   SPD_DBG_PDM_KV = 7,          /* KV dtype [Ls][2][hkv][max_ctx][hd] */
-  SPD_DBG_TOKENS = 8,          /* i32 [n+1]: token of position p in slot p mod (n+1) */
+  SPD_DBG_TOKENS = 8,          /* i32 [n+1][W]: candidate b of position p in row
+                                  (p mod (n+1)) W + b */
   SPD_DBG_TOP_P = 9            /* [1 + (n+1)] x {f32 zb, i32 id_cut, f32 lse, i32 0}: top-p
                                   sets (top_p < 1, T > 0) of the last target row, then of the
                                   draft of position p in entry 1 + p mod (n+1); a set is the

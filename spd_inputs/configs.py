@@ -53,6 +53,7 @@ class ModelConfig:
     weight_seed: int = 0
     prompt_seed: int = 1
     kv_dtype: str = "auto"           # KV cache storage: "auto" (the weight dtype) or "f32"
+    draft_width: int = 1             # W: draft candidates per position (1: a chain)
 
     @property
     def kinds(self) -> Tuple[int, ...]:

@@ -43,7 +43,8 @@ class ModelConfig(ctypes.Structure):
                 ("stage_layers", ctypes.POINTER(ctypes.c_int32)), ("n_anchors", ctypes.c_int32),
                 ("anchors", ctypes.POINTER(ctypes.c_int32)), ("pdm_layers", ctypes.c_int32),
                 ("anchor_fill", ctypes.c_int32), ("max_ctx", ctypes.c_int32),
-                ("speculate_from", ctypes.c_int32), ("kv_dtype", ctypes.c_int32)]
+                ("speculate_from", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+                ("draft_width", ctypes.c_int32)]
 
 
 class Weights(ctypes.Structure):
@@ -63,7 +64,8 @@ class Sampling(ctypes.Structure):
 class Commit(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("verified", "position", "token", "accepted",
                                               "draft_token", "flags", "committed_total",
-                                              "inflight", "new_draft", "newest")]
+                                              "inflight", "new_draft", "newest",
+                                              "accepted_index")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -153,7 +155,8 @@ def _i32(vals) -> ctypes.Array:
 
 
 def make_config(cfg, n: Optional[int] = None, anchors: Optional[Sequence[int]] = None,
-                Ls: Optional[int] = None, fill: str = "clamp", speculate_from: str = "input"):
+                Ls: Optional[int] = None, fill: str = "clamp", speculate_from: str = "input",
+                draft_width: Optional[int] = None):
     """spd_model_config from a workload description; returns (struct, keep-alive list)."""
     n = cfg.n_stages if n is None else n
     anchors = list(cfg.anchors if anchors is None else anchors)
@@ -182,6 +185,7 @@ def make_config(cfg, n: Optional[int] = None, anchors: Optional[Sequence[int]] =
     c.max_ctx = cfg.max_ctx
     c.speculate_from = {"input": 0, "output": 1}[speculate_from]
     c.kv_dtype = {"auto": SPD_KV_AUTO, "f32": SPD_KV_F32}[getattr(cfg, "kv_dtype", "auto")]
+    c.draft_width = getattr(cfg, "draft_width", 1) if draft_width is None else draft_width
     return c, keep
 
 
@@ -205,12 +209,13 @@ class SPD:
                  forced_p: Optional[float] = None, forced_ref: Optional[Sequence[int]] = None,
                  n: Optional[int] = None, anchors: Optional[Sequence[int]] = None,
                  Ls: Optional[int] = None, fill: str = "clamp", stream=None,
-                 speculate_from: str = "input"):
+                 speculate_from: str = "input", draft_width: Optional[int] = None):
         import torch
         self.L = load()
         self.cfg = cfg
         self._keep = []
-        self.c, keep = make_config(cfg, n, anchors, Ls, fill, speculate_from)
+        self.c, keep = make_config(cfg, n, anchors, Ls, fill, speculate_from, draft_width)
+        self.W = self.c.draft_width
         self._keep += keep
         self.n = self.c.n_stages
         self.Ls = self.c.pdm_layers

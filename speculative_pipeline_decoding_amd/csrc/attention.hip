@@ -80,6 +80,9 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_kernel(
   const T* Kb;
   const T* Vb;
   int len, nsplit, s, g, slot;
+  int self_key = -1;             // a sibling candidate's own key: read from its side row
+  const T* sk_row = nullptr;
+  const T* sv_row = nullptr;
   if (probs) {
     const int pi = find_problem(probs, nprob, b);
     const AttnProb& P = probs[pi];
@@ -90,6 +93,11 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_kernel(
     q = P.q; out = P.out; len = P.len; slot = P.slot;
     Kb = static_cast<const T*>(P.K);
     Vb = static_cast<const T*>(P.V);
+    if (P.side_k && P.self_row >= 0) {
+      self_key = P.len - 1;
+      sk_row = static_cast<const T*>(P.side_k) + ((size_t)g * P.side_rows + P.self_row) * HD;
+      sv_row = static_cast<const T*>(P.side_v) + ((size_t)g * P.side_rows + P.self_row) * HD;
+    }
   } else {
     const int r = b / hkv;
     g = b % hkv;
@@ -116,9 +124,11 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_kernel(
     const int nrows = min(64, k_hi - t0);
     const bool valid = lane < nrows;
     // this lane's key: K and V rows, both requested before either is used
-    const size_t rowoff = (size_t)(t0 + (valid ? lane : 0)) * HD;
-    const uint4* krow = reinterpret_cast<const uint4*>(Kh + rowoff);
-    const uint4* vrow = reinterpret_cast<const uint4*>(Vh + rowoff);
+    const int key = t0 + (valid ? lane : 0);
+    const size_t rowoff = (size_t)key * HD;
+    const bool own = key == self_key;
+    const uint4* krow = reinterpret_cast<const uint4*>(own ? sk_row : Kh + rowoff);
+    const uint4* vrow = reinterpret_cast<const uint4*>(own ? sv_row : Vh + rowoff);
     constexpr bool DV = direct_v<T, HD>();
     uint4 kr[NC], vr[DV ? 1 : NC];
 #pragma unroll
@@ -176,8 +186,9 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_kernel(
       for (int j = 0; j < nrows; ++j) {
         float2 vv;
         if constexpr (DV) {
-          vv = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(Vh) +
-                                                (size_t)(t0 + j) * HD + 2 * lane);
+          const float* vr0 = t0 + j == self_key ? reinterpret_cast<const float*>(sv_row)
+                                                : reinterpret_cast<const float*>(Vh) + (size_t)(t0 + j) * HD;
+          vv = *reinterpret_cast<const float2*>(vr0 + 2 * lane);
         } else if constexpr (sizeof(T) == 2) {
           const uint32_t wv = vt[j * VW + lane];
           vv = make_float2(bf16_lo(wv), bf16_hi(wv));
@@ -324,6 +335,9 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_mfma_kernel(
   const uint16_t* Kb;
   const uint16_t* Vb;
   int len, nrows, qs, os, nsplit, s, g, slot;
+  int self_key = -1;             // a sibling candidate's own key: read from its side row
+  const uint16_t* sk_row = nullptr;
+  const uint16_t* sv_row = nullptr;
   if (probs) {
     const int pi = find_problem(probs, nprob, blockIdx.x);
     const AttnProb& P = probs[pi];
@@ -332,6 +346,11 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_mfma_kernel(
     q = P.q; out = P.out; len = P.len; nrows = P.nrows; qs = P.q_stride; os = P.out_stride;
     Kb = static_cast<const uint16_t*>(P.K);
     Vb = static_cast<const uint16_t*>(P.V);
+    if (P.side_k && P.self_row >= 0) {
+      self_key = P.len - 1;
+      sk_row = static_cast<const uint16_t*>(P.side_k) + ((size_t)g * P.side_rows + P.self_row) * HD;
+      sv_row = static_cast<const uint16_t*>(P.side_v) + ((size_t)g * P.side_rows + P.self_row) * HD;
+    }
   } else {
     const int R = 16 / G;
     const int r0 = (blockIdx.x / hkv) * R;
@@ -362,18 +381,30 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_mfma_kernel(
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       const int key = min(kb + 16 * kt + c, max_ctx - 1);
+      const uint16_t* krow = key == self_key ? sk_row : Kg + (size_t)key * HD;
 #pragma unroll
       for (int st = 0; st < KST; ++st) {
         const int d0 = 32 * st + 8 * gq;
-        kf[buf][kt][st] = load_g16(Kg + (size_t)key * HD + (d0 < HD ? d0 : 0));
+        kf[buf][kt][st] = load_g16(krow + (d0 < HD ? d0 : 0));
       }
     }
     const uint16_t* vb = Vg + (size_t)(min(kb, max_ctx - 1) / 32) * HD * 32;
+    // a sibling's own key sits in this block: the lane holding it (keys 4 gq .. 4 gq + 3,
+    // and 16 + 4 gq .. of the block, dim 16 dt + c) swaps in the side row's value
+    const int off = self_key - kb;
+    const bool own = self_key >= 0 && off >= 0 && off < 32 && ((off & 15) >> 2) == gq;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const uint16_t* vp = vb + (size_t)(16 * dt + c) * 32 + 4 * gq;
-      const uint2 a = load_g8(vp);
-      const uint2 b = load_g8(vp + 16);
+      uint2 a = load_g8(vp);
+      uint2 b = load_g8(vp + 16);
+      if (own) {
+        const uint32_t val = sv_row[16 * dt + c];
+        uint2& w = off < 16 ? a : b;
+        const int e = off & 3;
+        uint32_t& word = (e >> 1) ? w.y : w.x;
+        word = (e & 1) ? ((word & 0xffffu) | (val << 16)) : ((word & 0xffff0000u) | val);
+      }
       vf[buf][dt] = make_uint4(a.x, a.y, b.x, b.y);
     }
   };

@@ -117,7 +117,8 @@ __device__ void epilogue(const GemvProb& p, int v, int unit, float a, float b,
     case EPI_QKV: {
       const int hd = p.hd, half = hd >> 1;
       const int head = unit / half, i = unit % half;
-      const int pos = p.pos0 + v;
+      const int pos = p.same_pos ? p.pos0 : p.pos0 + v;
+      const bool side = p.same_pos && v > 0;   // a sibling candidate: its own side row
       if (head < p.hq) {
         const float2 cs = rope[(size_t)pos * half + i];
         float* q = p.aux + v * p.aux_stride + head * hd;
@@ -125,15 +126,24 @@ __device__ void epilogue(const GemvProb& p, int v, int unit, float a, float b,
         q[i + half] = a * cs.y + b * cs.x;
       } else if (head < p.hq + p.hkv) {
         const float2 cs = rope[(size_t)pos * half + i];
-        const size_t base = ((size_t)(head - p.hq) * p.max_ctx + pos) * hd;
         const bool b16 = sizeof(T) == 2 && !p.kv_f32;
-        store_kv(p.kv_k, base + i, a * cs.x - b * cs.y, b16);
-        store_kv(p.kv_k, base + i + half, a * cs.y + b * cs.x, b16);
+        const int g = head - p.hq;
+        void* dst = side ? p.side_k : p.kv_k;
+        const size_t base = side ? ((size_t)g * p.side_rows + p.side_row0 + v - 1) * hd
+                                 : ((size_t)g * p.max_ctx + pos) * hd;
+        store_kv(dst, base + i, a * cs.x - b * cs.y, b16);
+        store_kv(dst, base + i + half, a * cs.y + b * cs.x, b16);
       } else {
         const int g = head - p.hq - p.hkv;
         const bool b16 = sizeof(T) == 2 && !p.kv_f32;   // bf16 caches are key-blocked
-        store_kv(p.kv_v, v_index(b16, g, pos, i, hd, p.max_ctx), a, b16);
-        store_kv(p.kv_v, v_index(b16, g, pos, i + half, hd, p.max_ctx), b, b16);
+        if (side) {                                       // side rows are row-major
+          const size_t base = ((size_t)g * p.side_rows + p.side_row0 + v - 1) * hd;
+          store_kv(p.side_v, base + i, a, b16);
+          store_kv(p.side_v, base + i + half, b, b16);
+        } else {
+          store_kv(p.kv_v, v_index(b16, g, pos, i, hd, p.max_ctx), a, b16);
+          store_kv(p.kv_v, v_index(b16, g, pos, i + half, hd, p.max_ctx), b, b16);
+        }
       }
       break;
     }
@@ -592,7 +602,7 @@ __device__ void mfma_body(const GemvProb& p, int tile, const float2* __restrict_
 // Kernel kinds: 1 or 2 vectors (rows kernel; K_ROWS2W gives each wave 8 rows, for the
 // two-vector head sweep), 3..16 vectors on the matrix cores (bf16 weights, input staged
 // whole in LDS: tall matrices only), else up to kMaxVec (split-K).
-enum Kind { K_ROWS1 = 0, K_ROWS2 = 1, K_SPLITK = 2, K_MFMA = 3, K_ROWS2W = 5 };
+enum Kind { K_ROWS1 = 0, K_ROWS2 = 1, K_SPLITK = 2, K_MFMA = 3, K_ROWS2W = 5, K_ROWS4 = 6 };
 
 template <typename T, int KIND>
 __device__ __forceinline__ void gemv_body(const GemvProb* __restrict__ probs, int nprob,
@@ -615,7 +625,7 @@ __device__ __forceinline__ void gemv_body(const GemvProb* __restrict__ probs, in
     mfma_body(p, tile, rope, planes, red);
   } else {
     constexpr bool wide = KIND == K_ROWS2W;
-    constexpr int NV = KIND == K_ROWS1 ? 1 : 2;
+    constexpr int NV = KIND == K_ROWS1 ? 1 : KIND == K_ROWS4 ? 4 : 2;
     extern __shared__ float rows_xs[];
     __shared__ float red[kWaves * NV];
     rows_body<T, NV, wide ? RWIDE : RW, wide ? kRingWide : kRing>(p, tile, rope, rows_xs, red);
@@ -702,7 +712,8 @@ GemvPlan gemv_plan(GemvProb* v, int n, bool bf16) {
   // the matrix-core kernel stages every vector whole and then needs most of a CU's LDS:
   // only a tall matrix (gate/up) streams enough weights per workgroup to earn it
   for (int i = 0; i < n; ++i) mc = mc && units_host(v[i]) >= kTall;
-  int kind = mv <= 1 ? K_ROWS1 : mv == 2 ? K_ROWS2 : K_SPLITK;
+  // 3 or 4 vectors: the candidates of a draft tree's positions (stage problems)
+  int kind = mv <= 1 ? K_ROWS1 : mv == 2 ? K_ROWS2 : mv <= 4 ? K_ROWS4 : K_SPLITK;
   // the rows kernel stages every vector whole in LDS; longer inputs take the split-K kernel
   if (kind != K_SPLITK && (size_t)mv * kpad * 4 > (size_t)kRowsLds) kind = K_SPLITK;
   if (mc && mv > 2) kind = K_MFMA;
@@ -743,7 +754,7 @@ GemvPlan gemv_plan(GemvProb* v, int n, bool bf16) {
   for (int i = 1; i < n; ++i)
     if (v[i].ntiles != v[0].ntiles) out.tpp = 0;
   out.waves = kind == K_MFMA ? v[0].pad * v[0].ksplit : kWaves;
-  const int nvs = kind == K_ROWS2 || kind == K_ROWS2W ? 2 : 1;
+  const int nvs = kind == K_ROWS2 || kind == K_ROWS2W ? 2 : kind == K_ROWS4 ? 4 : 1;
   out.shm = kind == K_MFMA     ? mc_lds_bytes(v[0].nvec, v[0].K, out.waves)
             : kind == K_SPLITK ? 0
                                : nvs * kpad * (int)sizeof(float);
@@ -764,6 +775,7 @@ hipError_t launch_gemv(int role, const GemvProb* d_probs, int nprob, const GemvP
       case K_SPLITK: launch_kind<uint16_t, K_SPLITK>(role, grid, d_probs, nprob, rope, st, ev, tpp); break;
       case K_MFMA: launch_kind<uint16_t, K_MFMA>(role, grid, d_probs, nprob, rope, st, ev, tpp, waves, shm); break;
       case K_ROWS2W: launch_kind<uint16_t, K_ROWS2W>(role, grid, d_probs, nprob, rope, st, ev, tpp, kWaves, shm); break;
+      case K_ROWS4: launch_kind<uint16_t, K_ROWS4>(role, grid, d_probs, nprob, rope, st, ev, tpp, kWaves, shm); break;
       default: return hipErrorInvalidValue;
     }
   } else {
@@ -772,6 +784,7 @@ hipError_t launch_gemv(int role, const GemvProb* d_probs, int nprob, const GemvP
       case K_ROWS2: launch_kind<float, K_ROWS2>(role, grid, d_probs, nprob, rope, st, ev, tpp, kWaves, shm); break;
       case K_SPLITK: launch_kind<float, K_SPLITK>(role, grid, d_probs, nprob, rope, st, ev, tpp); break;
       case K_ROWS2W: launch_kind<float, K_ROWS2W>(role, grid, d_probs, nprob, rope, st, ev, tpp, kWaves, shm); break;
+      case K_ROWS4: launch_kind<float, K_ROWS4>(role, grid, d_probs, nprob, rope, st, ev, tpp, kWaves, shm); break;
       default: return hipErrorInvalidValue;
     }
   }

@@ -38,12 +38,51 @@ __global__ __launch_bounds__(256) void embed_gather_kernel(const EmbedGather* __
   const T* __restrict__ erow = E + (size_t)tok * d;
   if (blockIdx.x == 0) {
     if (!e.embed_new) return;
-    float* __restrict__ h = e.h_ring + (size_t)e.newest_slot * d;
-    float* __restrict__ a0 = e.anchors + (size_t)e.newest_slot * e.k * d;
-    for (int i = threadIdx.x; i < d; i += blockDim.x) {
-      const float v = ld(erow, i);
-      h[i] = v;
-      a0[i] = v;
+    // the newest token and its sibling candidates (ring rows newest_slot + b)
+    for (int b = 0; b < e.embed_w; ++b) {
+      const T* __restrict__ er = E + (size_t)e.tok_ring[e.newest_slot + b] * d;
+      float* __restrict__ h = e.h_ring + (size_t)(e.newest_slot + b) * d;
+      float* __restrict__ a0 = e.anchors + (size_t)(e.newest_slot + b) * e.k * d;
+      for (int i = threadIdx.x; i < d; i += blockDim.x) {
+        const float v = ld(er, i);
+        h[i] = v;
+        a0[i] = v;
+      }
+    }
+    return;
+  }
+  if (blockIdx.x > e.M * e.k) {
+    // adoption of a sibling candidate: block 1 + M k moves its residual and anchors, each
+    // block after it one target layer's key and value rows (side row -> cache at the
+    // position). The gather above reads the sibling's own row, so nothing here races it.
+    const int a = blockIdx.x - 1 - e.M * e.k;
+    if (a == 0) {
+      const float* __restrict__ hs = e.h_ring + (size_t)e.adopt_from * d;
+      float* __restrict__ hd = e.h_ring + (size_t)e.adopt_to * d;
+      for (int i = threadIdx.x; i < d; i += blockDim.x) hd[i] = hs[i];
+      const float* __restrict__ as = e.anchors + (size_t)e.adopt_from * e.k * d;
+      float* __restrict__ ad = e.anchors + (size_t)e.adopt_to * e.k * d;
+      for (int i = threadIdx.x; i < e.k * d; i += blockDim.x) ad[i] = as[i];
+      return;
+    }
+    const int l = a - 1;
+    const int hd = e.hd, esz = e.kv_bf16 ? 2 : 4;
+    char* K = e.kv_base + (size_t)l * e.kv_layer_bytes;
+    char* Vc = K + e.kv_layer_bytes / 2;
+    const char* SK = e.side_base + (size_t)l * e.side_layer_bytes;
+    const char* SV = SK + e.side_layer_bytes / 2;
+    for (int t = threadIdx.x; t < e.hkv * hd; t += blockDim.x) {
+      const int g = t / hd, dd2 = t % hd;
+      const size_t src = ((size_t)g * e.side_rows + e.adopt_side_row) * hd + dd2;
+      const size_t kdst = ((size_t)g * e.max_ctx + e.adopt_pos) * hd + dd2;
+      const size_t vdst = v_index(e.kv_bf16 != 0, g, e.adopt_pos, dd2, hd, e.max_ctx);
+      if (esz == 2) {
+        reinterpret_cast<uint16_t*>(K)[kdst] = reinterpret_cast<const uint16_t*>(SK)[src];
+        reinterpret_cast<uint16_t*>(Vc)[vdst] = reinterpret_cast<const uint16_t*>(SV)[src];
+      } else {
+        reinterpret_cast<float*>(K)[kdst] = reinterpret_cast<const float*>(SK)[src];
+        reinterpret_cast<float*>(Vc)[vdst] = reinterpret_cast<const float*>(SV)[src];
+      }
     }
     return;
   }
@@ -157,9 +196,9 @@ __global__ void copy_rows_kernel(const float* __restrict__ s, int ss, float* __r
 
 hipError_t launch_embed_gather(const EmbedGather* desc, const void* blk_src, void* blk_dst,
                                size_t blk_bytes, int M, int k, int d, bool bf16, hipStream_t s,
-                               LaunchEv ev) {
+                               LaunchEv ev, int adopt_layers) {
   (void)d;
-  const dim3 grid(1 + M * k);
+  const dim3 grid(1 + M * k + (adopt_layers > 0 ? 1 + adopt_layers : 0));
   const int n16 = (int)((blk_bytes + 15) / 16);
   const uint4* src = static_cast<const uint4*>(blk_src);
   uint4* dst = static_cast<uint4*>(blk_dst);

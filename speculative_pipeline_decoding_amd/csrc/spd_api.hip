@@ -82,6 +82,7 @@ long long float_gap(const float* to, const float* from) {
 struct Inflight {
   int pos;
   int stage;
+  int w = 1;       // candidates at this position: the token and w - 1 siblings (draft trees)
 };
 
 // Launch kinds of a step (and their timing buckets). The PDM's launches run on a
@@ -102,6 +103,7 @@ struct Op {
   int stream = 0;  // 0: the caller's stream, 1: the PDM stream
   GemvPlan plan;   // GEMV: kernel kind, workgroups and LDS (gemv_plan)
   int layer = -1;  // the one target layer this launch serves, when only one token is in it
+  int adopt = 0;   // OP_EMBED: target layers of a sibling's keys to adopt (extra workgroups)
 };
 
 struct Plan {
@@ -113,10 +115,13 @@ struct Plan {
   float theta, eps;
   int fill;
   int spec_output;   // the PDM reads the step's output states, after the target layers
+  int W;             // draft candidates per position; ring rows are slot * W + candidate
+  int side_rows;     // rows of each layer's sibling side cache per kv head: ring * (W - 1)
+  size_t side_layer_bytes;
   std::vector<int> kind, sizes, starts, anchors, ord;   // ord: index among softmax / linear layers
   int nsoft = 0, nlin = 0;
   // workspace offsets
-  size_t o_kv, o_pkv, o_lin, o_h, o_anch, o_tok, o_qring, o_qlse, o_cut, o_nuc, o_X, o_hp, o_qbuf, o_attn,
+  size_t o_kv, o_pkv, o_side, o_top, o_lin, o_h, o_anch, o_tok, o_qring, o_qlse, o_cut, o_nuc, o_X, o_hp, o_qbuf, o_attn,
       o_act, o_lqkv, o_logits, o_part, o_verdict, o_desc, o_apart, o_rope,
       o_forced, o_ptok, o_pH, o_pA, o_pQKV, o_pO, o_pG, o_pU, o_pZ, o_panch, total;
   size_t kv_layer_bytes;     // K and V of one layer
@@ -133,6 +138,9 @@ bool plan_config(const spd_model_config* c, Plan& p, std::string& err) {
   if (c->speculate_from != SPD_SPEC_INPUT && c->speculate_from != SPD_SPEC_OUTPUT)
     return bad("speculate_from must be SPD_SPEC_INPUT or SPD_SPEC_OUTPUT");
   p.spec_output = c->speculate_from == SPD_SPEC_OUTPUT;
+  p.W = c->draft_width < 1 ? 1 : c->draft_width;
+  if (p.W > kMaxWidth) return bad("draft_width must be in [1, 4]");
+  if (p.W > 1 && p.spec_output) return bad("draft trees (draft_width > 1) need SPD_SPEC_INPUT");
   if (c->dtype != SPD_F32 && c->dtype != SPD_BF16) return bad("dtype must be SPD_F32 or SPD_BF16");
   p.bf16 = c->dtype == SPD_BF16;
   p.esz = p.bf16 ? 2 : 4;
@@ -162,6 +170,8 @@ bool plan_config(const spd_model_config* c, Plan& p, std::string& err) {
     for (int l = 0; l < p.L; ++l) p.kind[l] = c->layer_kind[l];
   for (int l = 0; l < p.L; ++l) {
     if (p.kind[l] != SPD_LAYER_SOFTMAX && p.kind[l] != SPD_LAYER_LINEAR) return bad("bad layer_kind");
+    if (p.W > 1 && p.kind[l] == SPD_LAYER_LINEAR)
+      return bad("draft trees (draft_width > 1) need softmax layers only");
   }
   p.sizes.resize(p.n);
   if (c->stage_layers) {
@@ -191,15 +201,18 @@ bool plan_config(const spd_model_config* c, Plan& p, std::string& err) {
   p.lin_state_bytes = (size_t)p.hq * p.hd * p.hd * 4;
   p.o_kv = take(p.nsoft * p.kv_layer_bytes);
   p.o_pkv = take((size_t)p.Ls * p.kv_layer_bytes);
+  p.side_rows = p.ring * (p.W - 1);
+  p.side_layer_bytes = 2 * (size_t)p.hkv * p.side_rows * p.hd * p.kv_esz;
+  p.o_side = take(p.nsoft * p.side_layer_bytes);
   p.o_lin = take((size_t)p.nlin * p.ring * p.lin_state_bytes);
-  p.o_h = take((size_t)p.ring * p.d * 4);
-  p.o_anch = take((size_t)p.ring * p.k * p.d * 4);
-  p.o_tok = take((size_t)p.ring * 4);
+  p.o_h = take((size_t)p.ring * p.W * p.d * 4);
+  p.o_anch = take((size_t)p.ring * p.W * p.k * p.d * 4);
+  p.o_tok = take((size_t)p.ring * p.W * 4);
   p.o_qring = take((size_t)p.ring * p.V * 4);
   p.o_qlse = take((size_t)p.ring * 4);
   p.o_cut = take((size_t)(1 + p.ring) * sizeof(NucleusCut));   // target row, then draft ring
   p.o_nuc = take(kNucPartBytes + kNucHistBytes + kNucCntBytes + (size_t)2 * p.V * sizeof(int2));
-  const int T = p.n + p.ring;   // decode rows: target tokens + PDM rows
+  const int T = p.n * p.W + p.ring;   // decode rows: target candidates + PDM rows
   p.o_X = take((size_t)p.ring * p.k * p.d * 4);
   p.o_hp = take((size_t)p.ring * p.d * 4);
   p.o_qbuf = take((size_t)T * p.qo * 4);
@@ -208,6 +221,7 @@ bool plan_config(const spd_model_config* c, Plan& p, std::string& err) {
   p.o_lqkv = take((size_t)p.n * p.linrows * 4);
   p.o_logits = take((size_t)p.V * 4);
   p.o_part = take((size_t)3 * kVocabBlocks * sizeof(VocabPartial));
+  p.o_top = take((size_t)kVocabBlocks * sizeof(VocabTop));
   p.o_verdict = take(sizeof(Verdict));
   p.o_desc = take(kDescBytes);
   const int G = p.hq / p.hkv;
@@ -290,6 +304,10 @@ struct spd_handle {
   int pdm_len = 0;
   std::vector<int> kv_len;
   long long N = 0, K = 0, acc = 0, rej = 0;
+  // a sibling candidate accepted at adopt_pos: the next step adopts it (its states and
+  // keys move to the position's main rows) before anything reads them
+  bool adopt = false;
+  int adopt_pos = 0, adopt_idx = 0, adopt_layers = 0;
   // the pending step
   bool pend_exit = false;
   int pend_v = 0, pend_dpos = 0, pend_newest = 0;
@@ -316,6 +334,11 @@ struct spd_handle {
   void* kvK(int l) const { return ws + p.o_kv + (size_t)p.ord[l] * p.kv_layer_bytes; }
   void* kvV(int l) const { return (char*)kvK(l) + p.kv_layer_bytes / 2; }
   void* pK(int r) const { return ws + p.o_pkv + (size_t)r * p.kv_layer_bytes; }
+  // sibling candidates' keys and values of softmax layer l: [hkv][side_rows][hd] each
+  void* sideK(int l) const { return ws + p.o_side + (size_t)p.ord[l] * p.side_layer_bytes; }
+  void* sideV(int l) const { return (char*)sideK(l) + p.side_layer_bytes / 2; }
+  // ring row of the token (candidate 0) at a position
+  int row(int pos) const { return slot(pos) * p.W; }
   // state of linear layer l after the position whose ring slot is `slot`
   float* lin(int l, int slot) const {
     return reinterpret_cast<float*>(ws + p.o_lin +
@@ -465,7 +488,8 @@ hipError_t run_op(spd_handle* h, const Op& op, LaunchEv ev = {}) {
       // the step's first launch: it reads its own descriptor from the pinned staging and
       // copies the whole block to the device for the launches that follow
       return launch_embed_gather(reinterpret_cast<const EmbedGather*>(h->d_hdesc + op.off),
-                                 h->d_hdesc, d, h->desc_used, op.count, p.k, p.d, p.bf16, st, ev);
+                                 h->d_hdesc, d, h->desc_used, op.count, p.k, p.d, p.bf16, st, ev,
+                                 op.adopt);
     case OP_GATHER:
       // gather-only (output states): the descriptor block is on the device by now
       return launch_embed_gather(reinterpret_cast<const EmbedGather*>(d + op.off), nullptr,
@@ -490,6 +514,9 @@ hipError_t run_op(spd_handle* h, const Op& op, LaunchEv ev = {}) {
     case OP_FINAL:
       return launch_finalize(reinterpret_cast<const FinalizeDesc*>(d + op.off), st, ev);
     case OP_RESID:
+      // after a rejection at T > 0: the residual draw, or with draft trees the later rounds
+      if (p.W > 1)
+        return launch_tree_rounds(reinterpret_cast<const FinalizeDesc*>(d + op.off), st, ev);
       return launch_residual_impl(reinterpret_cast<const FinalizeDesc*>(d + op.off),
                                   h->at<VocabPartial>(p.o_part), kVocabBlocks, st, ev);
   }
@@ -583,19 +610,37 @@ int build_step(spd_handle* h, DescWriter& dw) {
 
   // 1. embedding + PDM feature gather, on the caller's stream (it must precede the
   //    target's first writes to the residual and anchor rings)
+  // a token enters stage 0 every step, except right after a sibling's adoption (then the
+  // newest token is the adopted one, in its last stage)
+  const bool fresh = h->F.back().stage == 0;
   EmbedGather eg{};
   eg.embed = h->embed;
   eg.tok_ring = h->at<int>(p.o_tok);
   eg.h_ring = hring;
   eg.anchors = anch;
   eg.X = X;
-  eg.newest_slot = h->slot(newest);
-  eg.embed_new = 1;
+  eg.newest_slot = h->row(newest);
+  eg.embed_new = fresh ? 1 : 0;
+  eg.embed_w = h->F.back().w;
   eg.d = p.d; eg.k = p.k; eg.M = M;
+  if (h->adopt) {
+    // the adopted sibling's rows move in this launch; the gather reads them where they are
+    eg.adopt_layers = h->adopt_layers;
+    eg.adopt_from = h->row(h->adopt_pos) + h->adopt_idx;
+    eg.adopt_to = h->row(h->adopt_pos);
+    eg.adopt_pos = h->adopt_pos;
+    eg.adopt_side_row = h->slot(h->adopt_pos) * (p.W - 1) + h->adopt_idx - 1;
+    eg.kv_base = h->ws + p.o_kv;
+    eg.side_base = h->ws + p.o_side;
+    eg.kv_layer_bytes = p.kv_layer_bytes;
+    eg.side_layer_bytes = p.side_layer_bytes;
+    eg.hkv = p.hkv; eg.hd = p.hd; eg.max_ctx = p.max_ctx; eg.side_rows = p.side_rows;
+    eg.kv_bf16 = p.kv_bf16 ? 1 : 0;
+  }
   const bool out_states = p.spec_output != 0;
   for (int r = 0; r < M; ++r) {
     const int x = h->pdm_len + r;
-    eg.row_slot[r] = h->slot(x);
+    eg.row_slot[r] = h->row(x) + (h->adopt && x == h->adopt_pos ? h->adopt_idx : 0);
     // the row's depth when the PDM reads it: at the step's start, or (output states)
     // after its stage's layers
     int depth = p.L;
@@ -612,7 +657,7 @@ int build_step(spd_handle* h, DescWriter& dw) {
       else src = p.fill == SPD_FILL_CLAMP ? deepest : -1;
       // the newest g0 is embedded in this launch (input states); after the target layers
       // it is read from its anchor slot like any other
-      if (!out_states && x == newest && src == 0) src = -2;
+      if (!out_states && fresh && x == newest && src == 0) src = -2;
       eg.src[r][i] = (signed char)src;
     }
   }
@@ -627,7 +672,9 @@ int build_step(spd_handle* h, DescWriter& dw) {
     eg.embed_new = 0;
     gather_off = dw.put(&eg, 1);
   } else {
-    h->ops.push_back({OP_EMBED, dw.put(&eg, 1), M, 0, 0, 0.0});
+    Op op{OP_EMBED, dw.put(&eg, 1), M, 0, 0, 0.0};
+    op.adopt = eg.adopt_layers;
+    h->ops.push_back(op);
     h->ops.push_back({OP_FORK, 0, 0, 0, 0, 0.0});
   }
   // 3. target sub-layers on the caller's stream: every in-flight token at layer
@@ -647,7 +694,9 @@ int build_step(spd_handle* h, DescWriter& dw) {
         const Inflight f = h->F[j];
         if (p.sizes[f.stage] <= r) continue;
         const int l = p.starts[f.stage] + r;
-        const int s = h->slot(f.pos);
+        const int s = h->row(f.pos);       // ring row of the position's token
+        const int w = f.w;                 // its candidates: rows s .. s + w - 1
+        const int jr = j * p.W;            // their decode rows
         float* hv = hring + (size_t)s * p.d;
         round_layer = l;
         ++round_tokens;
@@ -658,34 +707,51 @@ int build_step(spd_handle* h, DescWriter& dw) {
           qkv.push_back(gemv(h->W(l, T_QKV), p.linrows, p.d, hv, 0, 1, EPI_STORE, lrow, 0,
                              (const float*)h->W(l, T_ATTN_NORM), 0, p.eps));
           LinProb lp{};
-          lp.qkv = lrow; lp.out = attn + (size_t)j * p.qo;
+          lp.qkv = lrow; lp.out = attn + (size_t)jr * p.qo;
           lp.s_prev = h->lin(l, h->slot(f.pos - 1)); lp.s_next = h->lin(l, h->slot(f.pos));
           lin.push_back(lp);
           linb += 2.0 * p.lin_state_bytes;
         } else {
-          GemvProb q = gemv(h->W(l, T_QKV), p.qrows, p.d, hv, 0, 1, EPI_QKV, nullptr, 0,
+          // the candidates of one position: one problem of w vectors at the same position;
+          // the siblings' keys and values go to their side rows
+          GemvProb q = gemv(h->W(l, T_QKV), p.qrows, p.d, hv, p.d, w, EPI_QKV, nullptr, 0,
                             (const float*)h->W(l, T_ATTN_NORM), 0, p.eps);
-          q.aux = qbuf + (size_t)j * p.qo;
+          q.aux = qbuf + (size_t)jr * p.qo; q.aux_stride = p.qo;
           q.kv_k = h->kvK(l); q.kv_v = h->kvV(l); q.kv_f32 = !p.kv_bf16;
           q.pos0 = f.pos; q.hq = p.hq; q.hkv = p.hkv; q.hd = p.hd; q.max_ctx = p.max_ctx;
+          q.same_pos = 1;
+          if (w > 1) {
+            q.side_k = h->sideK(l); q.side_v = h->sideV(l);
+            q.side_row0 = h->slot(f.pos) * (p.W - 1); q.side_rows = p.side_rows;
+          }
           qkv.push_back(q);
-          AttnProb a{};
-          a.q = qbuf + (size_t)j * p.qo; a.out = attn + (size_t)j * p.qo;
-          a.q_stride = p.qo; a.out_stride = p.qo; a.nrows = 1;
-          a.K = h->kvK(l); a.V = h->kvV(l); a.len = f.pos + 1;
-          at.push_back(a);
+          for (int b = 0; b < w; ++b) {
+            AttnProb a{};
+            a.q = qbuf + (size_t)(jr + b) * p.qo; a.out = attn + (size_t)(jr + b) * p.qo;
+            a.q_stride = p.qo; a.out_stride = p.qo; a.nrows = 1;
+            a.K = h->kvK(l); a.V = h->kvV(l); a.len = f.pos + 1;
+            a.self_row = -1;
+            if (b > 0) {   // a sibling: its own key from its side row
+              a.self_row = h->slot(f.pos) * (p.W - 1) + b - 1;
+              a.side_k = h->sideK(l); a.side_v = h->sideV(l); a.side_rows = p.side_rows;
+            }
+            at.push_back(a);
+          }
           kvb += 2.0 * (f.pos + 1) * p.hkv * p.hd * p.kv_esz;
         }
-        o.push_back(gemv(h->W(l, T_O), p.d, p.qo, attn + (size_t)j * p.qo, 0, 1, EPI_ADD, hv, 0,
-                         nullptr, 0, 0.f));
-        GemvProb g = gemv(h->W(l, T_GATE), p.F, p.d, hv, 0, 1, EPI_SWIGLU, act + (size_t)j * p.F, 0,
-                          (const float*)h->W(l, T_FFN_NORM), 0, p.eps);
+        o.push_back(gemv(h->W(l, T_O), p.d, p.qo, attn + (size_t)jr * p.qo, p.qo, w, EPI_ADD, hv,
+                         p.d, nullptr, 0, 0.f));
+        GemvProb g = gemv(h->W(l, T_GATE), p.F, p.d, hv, p.d, w, EPI_SWIGLU, act + (size_t)jr * p.F,
+                          p.F, (const float*)h->W(l, T_FFN_NORM), 0, p.eps);
         g.W2 = h->W(l, T_UP);
         gu.push_back(g);
-        GemvProb dn = gemv(h->W(l, T_DOWN), p.d, p.F, act + (size_t)j * p.F, 0, 1, EPI_ADD, hv, 0,
-                           nullptr, 0, 0.f);
+        GemvProb dn = gemv(h->W(l, T_DOWN), p.d, p.F, act + (size_t)jr * p.F, p.F, w, EPI_ADD, hv,
+                           p.d, nullptr, 0, 0.f);
         for (int i = 0; i < p.k; ++i)
-          if (p.anchors[i] == l + 1) dn.aux = anch + ((size_t)s * p.k + i) * p.d;
+          if (p.anchors[i] == l + 1) {
+            dn.aux = anch + ((size_t)s * p.k + i) * p.d;
+            dn.aux_stride = kd;
+          }
         down.push_back(dn);
         h->pend_layers.push_back({l, f.pos});
       }
@@ -715,7 +781,7 @@ int build_step(spd_handle* h, DescWriter& dw) {
     std::vector<GemvProb> g{gemv(h->proj, p.d, kd, X, kd, M, EPI_STORE, hp, p.d, nullptr, 0, 0.f)};
     push_gemv(OP_GEMV_PROJ, g, pdm_stream);
   }
-  const int base = p.n;
+  const int base = p.n * p.W;
   for (int r = 0; r < p.Ls; ++r) {
     const bool last = r == p.Ls - 1;
     std::vector<GemvProb> qkv, o, gu, down;
@@ -750,7 +816,7 @@ int build_step(spd_handle* h, DescWriter& dw) {
     down.push_back(gemv(h->PW(r, T_DOWN), p.d, p.F, act + (size_t)(base + r0) * p.F, p.F, nr,
                         EPI_ADD, hrow, p.d, nullptr, 0, 0.f));
     push_gemv(OP_PDM_QKV, qkv, pdm_stream);
-    push_attn(OP_PDM_ATTN, at, pdm_stream, p.n, kvb);
+    push_attn(OP_PDM_ATTN, at, pdm_stream, base, kvb);
     push_gemv(OP_PDM_O, o, pdm_stream);
     push_gemv(OP_PDM_GU, gu, pdm_stream);
     push_gemv(OP_PDM_DOWN, down, pdm_stream);
@@ -767,7 +833,7 @@ int build_step(spd_handle* h, DescWriter& dw) {
   {
     GemvProb g;
     if (exited) {
-      float* hx = hring + (size_t)h->slot(ex_pos) * p.d;
+      float* hx = hring + (size_t)h->row(ex_pos) * p.d;
       g = gemv(h->head, p.V, p.d, hx, float_gap(hnew, hx), 2, EPI_STORE, logits,
                float_gap(qnew, logits), h->final_norm, float_gap(h->pdm_final_norm, h->final_norm),
                p.eps);
@@ -791,6 +857,8 @@ int build_step(spd_handle* h, DescWriter& dw) {
   vd.nucleus = nucleus; vd.top_p = h->top_p;
   vd.cut[0] = cuts; vd.cut[1] = cuts + 1 + h->slot(dpos);
   h->nucleus_scratch(vd);
+  vd.topw = p.W;
+  vd.top = h->at<VocabTop>(p.o_top);
   const size_t voff = dw.put(&vd, 1);
   h->ops.push_back({OP_VOCAB, voff, 1, kVocabBlocks, 0, 0.0});
   if (nucleus) h->ops.push_back({OP_NUCLEUS, voff, 1, kVocabBlocks, 0, 0.0});
@@ -810,6 +878,8 @@ int build_step(spd_handle* h, DescWriter& dw) {
   fd.part = h->at<VocabPartial>(p.o_part);
   fd.nucleus = nucleus;
   fd.cut_t = cuts; fd.cut_q = cuts + 1 + h->slot(dpos); fd.cut_q_v = cuts + 1 + h->slot(v);
+  fd.W = p.W;
+  fd.top = h->at<VocabTop>(p.o_top);
   const size_t foff = dw.put(&fd, 1);
   h->ops.push_back({OP_FINAL, foff, 1, 1, 0, 0.0});
   if (sampled && exited) h->ops.push_back({OP_RESID, foff, 1, kVocabBlocks, 0, 0.0});
@@ -851,6 +921,10 @@ int spd_init(const spd_model_config* cfg, const spd_weights* w, const spd_sampli
   if (!(s->top_p > 0.f)) { g_init_error = "top_p must be > 0"; return SPD_E_ARG; }
   if (s->forced_mode && s->temperature != 0.f) {
     g_init_error = "forced mode needs temperature 0";
+    return SPD_E_CONFIG;
+  }
+  if (p.W > 1 && (s->forced_mode || s->top_p < 1.f)) {
+    g_init_error = "draft trees (draft_width > 1) need top_p >= 1 and forced_mode 0";
     return SPD_E_CONFIG;
   }
   if (s->forced_mode && (s->forced_ref_len < 0 || (s->forced_ref_len > 0 && !s->forced_ref))) {
@@ -1124,6 +1198,7 @@ int prefill_impl(spd_handle* h, const int32_t* prompt, int32_t len, int32_t* fir
       const size_t vo = dw.put(&vd, 1);
       FinalizeDesc fd{};
       fd.mode = 1; fd.dpos = len; fd.ring = p.ring; fd.V = p.V; fd.nblocks = kVocabBlocks;
+      fd.W = p.W;
       fd.temp = h->temp; fd.inv_temp = vd.inv_temp; fd.seed = h->seed;
       fd.tok_ring = h->at<int>(p.o_tok); fd.verdict = h->at<Verdict>(p.o_verdict);
       fd.host_verdict = h->d_hverdict;
@@ -1141,7 +1216,7 @@ int prefill_impl(spd_handle* h, const int32_t* prompt, int32_t len, int32_t* fir
       HIPCHK(h, launch_finalize(reinterpret_cast<const FinalizeDesc*>(d + fo), st));
       // the exiting-row residual of the last prompt position (debug view)
       HIPCHK(h, launch_copy_rows(H + (size_t)(P - 1) * p.d, p.d, h->at<float>(p.o_h) +
-                                 (size_t)h->slot(len - 1) * p.d, p.d, 1, p.d, st));
+                                 (size_t)h->row(len - 1) * p.d, p.d, 1, p.d, st));
     }
   }
   HIPCHK(h, hipStreamSynchronize(st));
@@ -1149,7 +1224,8 @@ int prefill_impl(spd_handle* h, const int32_t* prompt, int32_t len, int32_t* fir
   if (first_token) *first_token = t0;
   h->P0 = len;
   h->F.clear();
-  h->F.push_back({len, 0});
+  h->F.push_back({len, 0, 1});
+  h->adopt = false;
   h->pdm_len = len;
   std::fill(h->kv_len.begin(), h->kv_len.end(), len);
   h->N = h->K = h->acc = h->rej = 0;
@@ -1182,7 +1258,7 @@ void interleave_streams(std::vector<Op>& ops) {
 bool same_inflight(const std::deque<Inflight>& a, const std::deque<Inflight>& b) {
   if (a.size() != b.size()) return false;
   for (size_t i = 0; i < a.size(); ++i)
-    if (a[i].pos != b[i].pos || a[i].stage != b[i].stage) return false;
+    if (a[i].pos != b[i].pos || a[i].stage != b[i].stage || a[i].w != b[i].w) return false;
   return true;
 }
 
@@ -1195,7 +1271,7 @@ void prebuild_next(spd_handle* h) {
   if (h->pend_exit) return;
   std::deque<Inflight> F2 = h->F;
   for (auto& f : F2) f.stage += 1;
-  F2.push_back({h->pend_dpos, 0});
+  F2.push_back({h->pend_dpos, 0, p.W});
   if (F2.back().pos >= p.max_ctx || F2.front().stage >= p.n) return;
   const int pdm2 = std::max(h->pdm_len, h->F.front().pos);
   // save the pending step's state
@@ -1254,7 +1330,8 @@ int spd_step(spd_handle* h) {
     return fail(h, SPD_E_STATE, h->state == spd_handle::S_INIT ? "no prefill" : "a step is pending");
   const int newest = h->F.back().pos;
   if (newest >= h->p.max_ctx) return fail(h, SPD_E_CAPACITY, "newest position reached max_ctx");
-  const bool pre_ok = h->pre_valid && h->pre_pdm_len == h->pdm_len && same_inflight(h->pre_F, h->F);
+  const bool pre_ok = h->pre_valid && !h->adopt && h->pre_pdm_len == h->pdm_len &&
+                      same_inflight(h->pre_F, h->F);
   if (h->ahead) {
     // launched while the previous step ran (that step verified nothing, so this state was
     // fixed at its launch)
@@ -1272,6 +1349,7 @@ int spd_step(spd_handle* h) {
       DescWriter dw{h->h_desc};
       int rc = build_step(h, dw);
       if (rc != SPD_OK) return rc;
+      h->adopt = false;   // the embedding launch of this step moves the adopted sibling
       interleave_streams(h->ops);
       if (dw.used > kDescBytes) return fail(h, SPD_E_CAPACITY, "internal: descriptor block overflow");
       if (h->ops.empty() || h->ops.front().kind != OP_EMBED)
@@ -1326,28 +1404,48 @@ int spd_verify_commit(spd_handle* h, spd_commit* out) {
   c.newest = h->pend_newest;
   c.new_draft = vd.draft;
   c.flags = vd.flags;
+  c.accepted_index = -1;
   if (h->pend_exit) {
     const int v = h->pend_v;
+    // the exiting token alone: the candidates at v were this step's drafts, none of which
+    // has entered the pipeline
+    const bool single = h->F.size() == 1;
     h->N += 1;
     c.verified = 1;
     c.position = v;
     c.token = vd.committed;
     c.accepted = vd.accepted;
+    c.accepted_index = vd.accepted ? vd.accepted_index : -1;
     c.draft_token = vd.verified_draft;
-    if (vd.accepted) {
+    if (vd.accepted && (vd.accepted_index <= 0 || single)) {
+      // the first candidate at v is the token there (or v holds this step's drafts): the
+      // pipeline shifts, and v's other candidates are dropped
       h->acc += 1;
       h->F.pop_front();
-      h->F.push_back({h->pend_dpos, 0});
+      if (!h->F.empty()) h->F.front().w = 1;
+      h->F.push_back({h->pend_dpos, 0, single ? 1 : p.W});
+    } else if (vd.accepted) {
+      // a sibling at v: it becomes the token there, with the layers it has run; every
+      // token after v goes. The next step's embedding launch moves its rows.
+      h->acc += 1;
+      const int st = h->F[1].stage;
+      const int depth = p.starts[st];
+      for (int l = 0; l < p.L; ++l) h->kv_len[l] = std::min(h->kv_len[l], l < depth ? v + 1 : v);
+      h->F.clear();
+      h->F.push_back({v, st, 1});
+      h->adopt = true;
+      h->adopt_pos = v;
+      h->adopt_idx = vd.accepted_index;
+      h->adopt_layers = depth;
     } else {
       h->rej += 1;
       for (auto& k : h->kv_len) k = std::min(k, v);
       h->F.clear();
-      h->F.push_back({v, 0});
+      h->F.push_back({v, 0, 1});
     }
   } else {
-    h->F.push_back({h->pend_dpos, 0});
+    h->F.push_back({h->pend_dpos, 0, p.W});
   }
-  (void)p;
   c.committed_total = (int)h->N;
   c.inflight = (int)h->F.size();
   if (out) *out = c;
@@ -1376,11 +1474,12 @@ size_t spd_debug_size(const spd_handle* h, int32_t what) {
   const Plan& p = h->p;
   switch (what) {
     case SPD_DBG_TARGET_LOGITS: case SPD_DBG_DRAFT_LOGITS: return (size_t)p.V * 4;
-    case SPD_DBG_H_RING: case SPD_DBG_PDM_ROWS: return (size_t)p.ring * p.d * 4;
-    case SPD_DBG_ANCHORS: return (size_t)p.ring * p.k * p.d * 4;
+    case SPD_DBG_H_RING: return (size_t)p.ring * p.W * p.d * 4;
+    case SPD_DBG_PDM_ROWS: return (size_t)p.ring * p.d * 4;
+    case SPD_DBG_ANCHORS: return (size_t)p.ring * p.W * p.k * p.d * 4;
     case SPD_DBG_TARGET_KV: return (size_t)p.nsoft * 2 * p.hkv * p.max_ctx * p.hd * p.kv_esz;
     case SPD_DBG_PDM_KV: return (size_t)p.Ls * 2 * p.hkv * p.max_ctx * p.hd * p.kv_esz;
-    case SPD_DBG_TOKENS: return (size_t)p.ring * 4;
+    case SPD_DBG_TOKENS: return (size_t)p.ring * p.W * 4;
     case SPD_DBG_TOP_P: return (size_t)(1 + p.ring) * sizeof(NucleusCut);
   }
   return 0;
@@ -1449,6 +1548,7 @@ int spd_reset(spd_handle* h) {
   h->P0 = 0;
   h->pend_dpos = 0;
   h->pre_valid = false;
+  h->adopt = false;
   return SPD_OK;
 }
 

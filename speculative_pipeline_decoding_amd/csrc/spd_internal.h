@@ -12,6 +12,7 @@ namespace spd {
 constexpr int kMaxStages = 16;          // n
 constexpr int kMaxRows = kMaxStages + 1;  // PDM rows per step: n + 1
 constexpr int kMaxAnchors = 8;          // k
+constexpr int kMaxWidth = 4;            // W: draft candidates per position
 constexpr int kWaves = 4;               // waves per GEMV workgroup
 constexpr int kMaxVec = kMaxRows;       // input vectors of one GEMV problem
 constexpr int kAttnTile = 64;           // keys per attention tile
@@ -24,7 +25,9 @@ enum Epi : int {
   EPI_STORE = 0,   // y[v][row] = acc
   EPI_ADD = 1,     // y[v][row] += acc; aux (if set): aux[v][row] = new y (anchor capture)
   EPI_SWIGLU = 2,  // y[v][row] = silu(W row) * (W2 row)
-  EPI_QKV = 3,     // rotate q,k pairs (RoPE at pos0 + v); q -> aux, k,v -> KV cache
+  EPI_QKV = 3,     // rotate q,k pairs (RoPE at pos0 + v, or pos0 for every vector when
+                   // same_pos); q -> aux, k,v -> KV cache (vectors v >= 1 of a same_pos
+                   // problem, sibling candidates, -> their side rows)
 };
 
 // One matrix times nvec vectors, y = epilogue(W * (x ⊙ gain) * rms_scale(x)).
@@ -50,6 +53,11 @@ struct GemvProb {
   int ksplit;          // matrix-core kernel: waves sharing one row tile's K
   int pad;             // matrix-core kernel: row tiles per workgroup
   int kv_f32;          // EPI_QKV: the KV cache is fp32 (row-major V) even with bf16 weights
+  int same_pos;        // EPI_QKV: every vector is a candidate for position pos0
+  int side_row0;       // EPI_QKV, same_pos: side row of vector 1 (vector v: side_row0 + v - 1)
+  int side_rows;       // rows of the side caches per kv head
+  void* side_k;        // EPI_QKV, same_pos: side K [hkv][side_rows][hd], row-major
+  void* side_v;        // side V, same layout
 };
 
 // Attention over one layer's KV cache for a group of query rows that share it: row r
@@ -67,7 +75,11 @@ struct AttnProb {
   int slot;            // index of this problem's partial area
   int nrows;           // query rows
   int q_stride, out_stride;
-  int pad;
+  int self_row;        // with side_k set: a sibling candidate (nrows 1), whose own key,
+                       // position len - 1, is side row self_row, not the cache's row
+  int side_rows;
+  const void* side_k;  // [hkv][side_rows][hd] row-major, in the cache's dtype
+  const void* side_v;
 };
 
 // Rows of a layer's K or V cache, padded to whole 32-key blocks.
@@ -99,11 +111,21 @@ struct EmbedGather {
   float* h_ring;              // [ring][d]
   float* anchors;             // [ring][k][d]
   float* X;                   // [M][k * d] gathered PDM features
-  int newest_slot;
+  int newest_slot;             // ring row of the newest token (rows: slot * W + candidate)
   int embed_new;              // 1: block 0 embeds the newest token (0: a gather-only launch)
+  int embed_w;                // candidates of the newest position embedded (rows newest_slot ..)
   int d, k, M;
-  int row_slot[kMaxRows];     // ring slot of PDM row r
+  int row_slot[kMaxRows];     // ring row of PDM row r
   signed char src[kMaxRows][kMaxAnchors];  // anchor index feeding segment i; -1: zeros; -2: newest g0
+  // adoption of a sibling candidate as the token at position adopt_pos: its residual and
+  // anchors move from ring row adopt_from to adopt_to, and its keys and values of the
+  // first adopt_layers target layers from its side row into the cache at adopt_pos
+  int adopt_layers;           // 0: nothing to adopt
+  int adopt_from, adopt_to, adopt_pos, adopt_side_row;
+  char* kv_base;              // target KV region: softmax layer l at kv_base + l * kv_layer_bytes
+  char* side_base;            // side caches: layer l at side_base + l * side_layer_bytes
+  size_t kv_layer_bytes, side_layer_bytes;
+  int hkv, hd, max_ctx, side_rows, kv_bf16;
 };
 
 // The vocabulary pass: statistics of up to two logit rows (target, draft).
@@ -133,6 +155,8 @@ struct VocabDesc {
   int nucleus;                // T > 0 and top_p < 1: the Gumbel draw runs over the top-p set
   float top_p;
   NucleusCut* cut[2];         // where each active row's top-p set is written
+  int topw;                   // > 1: the draft row's topw + 1 best (score, id) per block
+  struct VocabTop* top;       // [nblocks] (scores: the logit at T = 0, z / T + G at T > 0)
   unsigned long long* nuc_part;   // scratch: per-slice histograms [2][64][4096]
   unsigned long long* nuc_hist;   // scratch: merged histograms [2][4096]
   int2* nuc_cand;                 // scratch: listed (logit bits, id) [2][V]
@@ -144,6 +168,12 @@ struct VocabDesc {
 constexpr size_t kNucPartBytes = (size_t)2 * 64 * 4096 * 8;
 constexpr size_t kNucHistBytes = (size_t)2 * 4096 * 8;
 constexpr size_t kNucCntBytes = (size_t)2 * 64 * 4 + 16;   // counts, then the two maxima
+
+// The best scores of one slice of the draft row, highest first, lower id first on ties.
+struct VocabTop {
+  float s[kMaxWidth + 1];
+  int id[kMaxWidth + 1];
+};
 
 struct VocabPartial {
   float max, second;          // raw logit max and runner-up
@@ -165,6 +195,10 @@ struct Verdict {
   int need_residual;
   int first_token;      // prefill: first generated token
   float lse_t, lse_q, p_d, q_d;
+  int accepted_index;   // which candidate at v was accepted (-1: none)
+  int need_rrs;         // T > 0, W > 1, the first candidate rejected: the later rounds run
+  int target_arg;       // argmax of the target row (lowest id on ties)
+  int pad;
 };
 
 struct FinalizeDesc {
@@ -197,6 +231,8 @@ struct FinalizeDesc {
   const NucleusCut* cut_t;   // the target row's set (this step)
   const NucleusCut* cut_q;   // this step's draft row's set
   const NucleusCut* cut_q_v; // the set of the draft at v
+  int W;                     // candidates per draft position (token ring rows: slot * W + b)
+  const VocabTop* top;       // [nblocks] the draft row's best scores (W > 1)
 };
 
 enum RngStream : int { RNG_DRAFT = 1, RNG_ACC = 2, RNG_RES = 3, RNG_FORCE = 4, RNG_FIRST = 5 };
@@ -390,7 +426,7 @@ hipError_t launch_linear_scan(const float* qkv, int qkv_stride, float* out, int 
 // blk_src / blk_dst / blk_bytes: the step's descriptor block, copied to the device first.
 hipError_t launch_embed_gather(const EmbedGather* desc, const void* blk_src, void* blk_dst,
                                size_t blk_bytes, int M, int k, int d, bool bf16, hipStream_t st,
-                               LaunchEv ev = {});
+                               LaunchEv ev = {}, int adopt_layers = 0);
 hipError_t launch_vocab_stats(const VocabDesc* d_desc, int nblocks, VocabPartial* part,
                               hipStream_t st, LaunchEv ev = {});
 hipError_t launch_nucleus(const VocabDesc* d_desc, int nblocks, VocabPartial* part,
@@ -398,6 +434,8 @@ hipError_t launch_nucleus(const VocabDesc* d_desc, int nblocks, VocabPartial* pa
 hipError_t launch_finalize(const FinalizeDesc* d_desc, hipStream_t st, LaunchEv ev = {});
 hipError_t launch_residual_impl(const FinalizeDesc* d_desc, VocabPartial* part, int nblocks,
                                 hipStream_t st, LaunchEv ev = {});
+// Draft trees at T > 0: the verification rounds after the first candidate's rejection.
+hipError_t launch_tree_rounds(const FinalizeDesc* d_desc, hipStream_t st, LaunchEv ev = {});
 // prefill helpers
 hipError_t launch_embed_rows(const void* embed, const int* toks, float* H, int P, int d,
                              bool bf16, hipStream_t st);

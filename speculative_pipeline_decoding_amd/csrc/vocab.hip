@@ -77,6 +77,56 @@ __device__ Stat block_reduce(Stat s, float invT, Stat* sh) {
   return r;
 }
 
+// ---- the best W + 1 scores of a row (draft trees) ---------------------------------
+// A list holds kTopL (score, id) pairs, best first: higher score, lower id on ties.
+constexpr int kTopL = kMaxWidth + 1;
+__device__ __forceinline__ bool better(float a, int ia, float b, int ib) {
+  return a > b || (a == b && ia < ib);
+}
+__device__ __forceinline__ void top_clear(float* s, int* id) {
+#pragma unroll
+  for (int j = 0; j < kTopL; ++j) { s[j] = -INFINITY; id[j] = INT_MAX; }
+}
+__device__ __forceinline__ void top_insert(float* s, int* id, float v, int i) {
+#pragma unroll
+  for (int j = 0; j < kTopL; ++j) {
+    if (better(v, i, s[j], id[j])) {
+      const float tv = s[j]; const int ti = id[j];
+      s[j] = v; id[j] = i; v = tv; i = ti;
+    }
+  }
+}
+// The block's best kTopL of every thread's list (each thread passes its own, best first):
+// each wave pops its best head kTopL times (butterfly reductions, the same order in every
+// wave), then thread 0 merges the waves' lists. The result lands in os / oid (thread 0).
+__device__ __forceinline__ void top_block(const float* s, const int* id, float* ws, int* wid,
+                                          float* os, int* oid) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int head = 0;
+  for (int k = 0; k < kTopL; ++k) {
+    float bs = head < kTopL ? s[0] : -INFINITY;
+    int bi = head < kTopL ? id[0] : INT_MAX;
+#pragma unroll
+    for (int j = 1; j < kTopL; ++j)
+      if (j == head) { bs = s[j]; bi = id[j]; }
+    float ms = bs;
+    int mi = bi;
+    for (int o = 32; o > 0; o >>= 1) {
+      const float s2 = __shfl_xor(ms, o);
+      const int i2 = __shfl_xor(mi, o);
+      if (better(s2, i2, ms, mi)) { ms = s2; mi = i2; }
+    }
+    if (bi == mi && bs == ms && mi != INT_MAX) ++head;   // ids are distinct: one lane pops
+    if (lane == 0) { ws[w * kTopL + k] = ms; wid[w * kTopL + k] = mi; }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    top_clear(os, oid);
+    for (int j = 0; j < (int)(blockDim.x >> 6) * kTopL; ++j) top_insert(os, oid, ws[j], wid[j]);
+  }
+  __syncthreads();
+}
+
 __global__ __launch_bounds__(kVocabBlock) void vocab_stats_kernel(const VocabDesc* __restrict__ dd,
                                                                    VocabPartial* __restrict__ part) {
   __shared__ Stat sh[kVocabBlock];
@@ -88,6 +138,11 @@ __global__ __launch_bounds__(kVocabBlock) void vocab_stats_kernel(const VocabDes
     const float* z = d.logits[r];
     Stat s = stat_empty();
     const bool gum = d.gumbel_stream[r] != 0 && !d.nucleus;
+    // draft trees: the draft row's best scores (logits at T = 0, Gumbel scores at T > 0)
+    const bool tops = r == 1 && d.topw > 1;
+    float ts[kTopL];
+    int ti[kTopL];
+    top_clear(ts, ti);
     for (int i = lo + threadIdx.x; i < hi; i += blockDim.x) {
       const float v = z[i];
       if (d.sampled) {
@@ -96,15 +151,27 @@ __global__ __launch_bounds__(kVocabBlock) void vocab_stats_kernel(const VocabDes
       }
       if (v > s.max) { s.second = s.max; s.max = v; s.arg = i; }
       else if (v > s.second) { s.second = v; }
+      float g = v;
       if (gum) {
         const float u = rng_uniform(d.seed, d.gumbel_stream[r], d.gumbel_pos[r], (unsigned long long)i);
-        const float g = v * d.inv_temp + gumbel_of(u);
+        g = v * d.inv_temp + gumbel_of(u);
         if (g > s.gmax) { s.gsecond = s.gmax; s.gmax = g; s.garg = i; }
         else if (g > s.gsecond) { s.gsecond = g; }
       }
+      if (tops) top_insert(ts, ti, g, i);
     }
     const Stat b = block_reduce(s, d.inv_temp, sh);
     if (threadIdx.x == 0) part[r * d.nblocks + blockIdx.x] = to_partial(b);
+    if (tops) {
+      __shared__ float tws[kVocabBlock / 64 * kTopL], tos[kTopL];
+      __shared__ int twi[kVocabBlock / 64 * kTopL], toi[kTopL];
+      top_block(ts, ti, tws, twi, tos, toi);
+      if (threadIdx.x == 0) {
+        VocabTop& o = d.top[blockIdx.x];
+#pragma unroll
+        for (int j = 0; j < kTopL; ++j) { o.s[j] = tos[j]; o.id[j] = toi[j]; }
+      }
+    }
   }
 }
 
@@ -460,9 +527,22 @@ __global__ __launch_bounds__(kVocabBlock) void finalize_kernel(const FinalizeDes
   __shared__ Stat sh[kVocabBlock];
   const FinalizeDesc& f = *fd;
   const bool sampled = f.temp > 0.f;
+  const int W = f.W > 0 ? f.W : 1;           // token ring rows: slot * W + candidate
   Stat t = stat_empty(), q = stat_empty();
   if (f.mode == 1 || f.exited) t = merge_row(f.part, f.nblocks, f.inv_temp, sh);
   if (f.mode == 0) q = merge_row(f.part + f.nblocks, f.nblocks, f.inv_temp, sh);
+  // draft trees: the draft row's best W + 1 scores over every slice's list
+  __shared__ float tws[kVocabBlock / 64 * kTopL], tos[kTopL];
+  __shared__ int twi[kVocabBlock / 64 * kTopL], toi[kTopL];
+  if (f.mode == 0 && W > 1) {
+    float ls[kTopL];
+    int li[kTopL];
+    top_clear(ls, li);
+    for (int b = threadIdx.x; b < f.nblocks; b += blockDim.x)
+#pragma unroll
+      for (int j = 0; j < kTopL; ++j) top_insert(ls, li, f.top[b].s[j], f.top[b].id[j]);
+    top_block(ls, li, tws, twi, tos, toi);
+  }
   if (threadIdx.x != 0) return;
   Verdict v{};
   v.committed = -1;
@@ -476,15 +556,19 @@ __global__ __launch_bounds__(kVocabBlock) void finalize_kernel(const FinalizeDes
     else { y = t.arg; flag = (t.max - t.second) < kNearTie; }
     v.first_token = y;
     v.flags = flag ? 1 : 0;
-    f.tok_ring[f.dpos % f.ring] = y;
+    f.tok_ring[(f.dpos % f.ring) * W] = y;
     *f.verdict = v;
     *f.host_verdict = v;
     return;
   }
-  // draft for position dpos
+  // draft for position dpos: the best candidate (the only one when W = 1)
   int d;
   bool dflag;
-  if (sampled) { d = q.garg; dflag = (q.gmax - q.gsecond) < kNearTie; }
+  if (W > 1) {
+    d = toi[0];
+    dflag = false;
+    for (int j = 0; j < W; ++j) dflag = dflag || (tos[j] - tos[j + 1]) < kNearTie;
+  } else if (sampled) { d = q.garg; dflag = (q.gmax - q.gsecond) < kNearTie; }
   else { d = q.arg; dflag = (q.max - q.second) < kNearTie; }
   v.lse_q = f.nucleus ? f.cut_q->lse : q.max * f.inv_temp + logf(q.sum);
   *f.lse_q_new = v.lse_q;
@@ -499,17 +583,28 @@ __global__ __launch_bounds__(kVocabBlock) void finalize_kernel(const FinalizeDes
   }
   v.draft = d;
   v.flags = dflag ? 2 : 0;
-  f.tok_ring[f.dpos % f.ring] = d;
+  v.accepted_index = -1;
+  const int drow = (f.dpos % f.ring) * W;
+  f.tok_ring[drow] = d;
+  for (int j = 1; j < W; ++j) f.tok_ring[drow + j] = toi[j];
   if (f.exited) {
     v.exited = 1;
-    const int dv = f.tok_ring[f.v % f.ring];
+    // the candidates at v: this step's drafts when the exiting token was alone (then v is
+    // dpos and their ring rows were just written)
+    const int vrow = (f.v % f.ring) * W;
+    const int dv = f.tok_ring[vrow];
     v.verified_draft = dv;
+    v.target_arg = t.arg;
     if (!sampled) {
       const int y = t.arg;
+      int idx = -1;
+      for (int j = 0; j < W; ++j)
+        if (idx < 0 && f.tok_ring[vrow + j] == y) idx = j;
       v.committed = y;
-      v.accepted = (y == dv);
+      v.accepted = idx >= 0;
+      v.accepted_index = idx;
       if ((t.max - t.second) < kNearTie) v.flags |= 1;
-      if (!v.accepted) f.tok_ring[f.v % f.ring] = y;
+      f.tok_ring[vrow] = y;
     } else {
       float pd = expf(f.zt[dv] * f.inv_temp - v.lse_t);
       float qd = expf(f.zq_v[dv] * f.inv_temp - *f.lse_q_v);
@@ -522,7 +617,8 @@ __global__ __launch_bounds__(kVocabBlock) void finalize_kernel(const FinalizeDes
       v.q_d = qd;
       v.accepted = (u * qd < pd);
       if (fabsf(u * qd - pd) < kNearTie * qd) v.flags |= 1;
-      if (v.accepted) v.committed = dv;
+      if (v.accepted) { v.committed = dv; v.accepted_index = 0; }
+      else if (W > 1) v.need_rrs = 1;       // the later candidates' rounds (tree_rounds_kernel)
       else v.need_residual = 1;
     }
   }
@@ -585,8 +681,98 @@ __global__ __launch_bounds__(kVocabBlock) void residual_final_kernel(
     Verdict* v = f.verdict;
     v->committed = y;
     if (flag) v->flags |= 1;
-    f.tok_ring[f.v % f.ring] = y;
+    f.tok_ring[(f.v % f.ring) * (f.W > 0 ? f.W : 1)] = y;
     *f.host_verdict = *v;
+  }
+}
+
+// Draft trees at T > 0, after finalize rejected the first candidate: the remaining rounds of
+// recursive rejection sampling, in one block. Round i tests candidate c_i, proposed from q_i
+// (q without c_0 .. c_{i-1}, renormalised), against r_i = R_i / Z_i, where R_1 = max(0, p - q)
+// and R_{i+1} = max(0, R_i / Z_i - q_i) (R_0 = p, Z_0 = 1): accept iff u_i q_i(c_i) < r_i(c_i).
+// Every Z_i is a block sum over the vocabulary (R_i(x) evaluated from p(x), q(x) and the
+// earlier rounds' constants); if all rounds reject, y = argmax over R_W > 0 of
+// log R_W(x) + G(x) (RES stream), which draws from r_W. A residual without mass commits the
+// target's argmax, flagged.
+__global__ __launch_bounds__(kVocabBlock) void tree_rounds_kernel(const FinalizeDesc* __restrict__ fd) {
+  __shared__ Stat sh[kVocabBlock];
+  __shared__ float red[kVocabBlock / 64];
+  const FinalizeDesc& f = *fd;
+  Verdict* vd = f.verdict;
+  if (!vd->need_rrs) return;
+  const int W = f.W;
+  const int vrow = (f.v % f.ring) * W;
+  int cand[kMaxWidth];
+  for (int j = 0; j < W; ++j) cand[j] = f.tok_ring[vrow + j];
+  const float lse_t = vd->lse_t, lse_q = *f.lse_q_v, invT = f.inv_temp;
+  float Z[kMaxWidth + 1], E[kMaxWidth + 1];   // normalisers, excluded q mass before round i
+  Z[0] = 1.f;
+  E[0] = 0.f;
+  // R_i(x) for i >= 1 from p(x) = px, q(x) = qx
+  auto R = [&](int i, int x, float px, float qx) {
+    float r = px;
+    for (int j = 0; j < i; ++j) {
+      bool out = false;
+      for (int m = 0; m < j; ++m) out = out || cand[m] == x;
+      const float qj = out ? 0.f : (j == 0 ? qx : qx / (1.f - E[j]));
+      r = fmaxf(0.f, r / Z[j] - qj);
+    }
+    return r;
+  };
+  int y = -1, idx = -1;
+  bool flag = (vd->flags & 1) != 0;
+  for (int i = 1; i < W && y < 0; ++i) {
+    // Z_i: a block sum in a fixed order
+    float part = 0.f;
+    for (int x = threadIdx.x; x < f.V; x += blockDim.x)
+      part += R(i, x, expf(f.zt[x] * invT - lse_t), expf(f.zq_v[x] * invT - lse_q));
+    for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = part;
+    __syncthreads();
+    float Zi = 0.f;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) Zi += red[w];
+    __syncthreads();
+    if (!(Zi > 0.f)) { y = vd->target_arg; flag = true; break; }
+    Z[i] = Zi;
+    E[i] = E[i - 1] + expf(f.zq_v[cand[i - 1]] * invT - lse_q);
+    const int c = cand[i];
+    const float qc = expf(f.zq_v[c] * invT - lse_q) / (1.f - E[i]);
+    const float rc = R(i, c, expf(f.zt[c] * invT - lse_t), expf(f.zq_v[c] * invT - lse_q)) / Zi;
+    const float u = rng_uniform(f.seed, RNG_ACC, f.v, (unsigned long long)i);
+    if (fabsf(u * qc - rc) < kNearTie * qc) flag = true;
+    if (u * qc < rc) { y = c; idx = i; }
+  }
+  if (y < 0) {
+    // every round rejected: draw from r_W. Its unnormalised R_W needs Z_{W-1} (already in Z)
+    // and the excluded mass E_{W-1}
+    const int Wl = W;
+    Stat m = stat_empty();
+    for (int x = threadIdx.x; x < f.V; x += blockDim.x) {
+      float px = expf(f.zt[x] * invT - lse_t), qx = expf(f.zq_v[x] * invT - lse_q);
+      float r = px;
+      for (int j = 0; j < Wl; ++j) {
+        bool out = false;
+        for (int mm = 0; mm < j; ++mm) out = out || cand[mm] == x;
+        const float qj = out ? 0.f : (j == 0 ? qx : qx / (1.f - E[j]));
+        r = fmaxf(0.f, r / Z[j] - qj);
+      }
+      if (r > 0.f) {
+        const float g = logf(r) + gumbel_of(rng_uniform(f.seed, RNG_RES, f.v, (unsigned long long)x));
+        if (g > m.gmax || (g == m.gmax && x < m.garg)) { m.gsecond = m.gmax; m.gmax = g; m.garg = x; }
+        else if (g > m.gsecond) m.gsecond = g;
+      }
+    }
+    m = block_reduce(m, 1.f, sh);
+    if (m.garg == INT_MAX) { y = vd->target_arg; flag = true; }
+    else { y = m.garg; if ((m.gmax - m.gsecond) < kNearTie) flag = true; }
+  }
+  if (threadIdx.x == 0) {
+    vd->committed = y;
+    vd->accepted = idx >= 0;
+    vd->accepted_index = idx;
+    if (flag) vd->flags |= 1;
+    f.tok_ring[vrow] = y;
+    *f.host_verdict = *vd;
   }
 }
 
@@ -612,6 +798,11 @@ hipError_t launch_nucleus(const VocabDesc* d_desc, int nblocks, VocabPartial* pa
 
 hipError_t launch_finalize(const FinalizeDesc* d_desc, hipStream_t st, LaunchEv ev) {
   SPD_LAUNCH(ev, finalize_kernel, dim3(1), dim3(kVocabBlock), 0, st, d_desc);
+  return hipGetLastError();
+}
+
+hipError_t launch_tree_rounds(const FinalizeDesc* d_desc, hipStream_t st, LaunchEv ev) {
+  SPD_LAUNCH(ev, tree_rounds_kernel, dim3(1), dim3(kVocabBlock), 0, st, d_desc);
   return hipGetLastError();
 }
 

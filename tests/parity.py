@@ -5,6 +5,8 @@ Comparison rule:
     committed token, accept flag, KV length of every layer, PDM length;
   * floats: logits max-abs <= 1e-4 (f32 weights) / 5e-2 (bf16 weights);
     residual and anchor states relative L2 <= 1e-5 (f32) / 2e-2 (bf16);
+  * draft trees (width > 1): every candidate of every draft position, the accepted
+    candidate's rank, and the states of sibling candidates as above;
   * a token decision may differ only where the oracle flags a near-tie
     (top-2 gap < 1e-3, or |u q(d) - p(d)| < 1e-3 q(d)); the comparison stops there;
   * top_p < 1: every logit row must lie within `slack` of the oracle's (the envelope its
@@ -66,7 +68,7 @@ def rel(a, b):
 def run_parity(cfg, W, dW, prompt, G=None, T=0.0, seed=0, n=None, fill="clamp",
                forced_p=None, forced_ref=None, check_states=True, max_steps=None,
                oracle_weights=None, tol_logits=None, top_p=1.0, slack=None,
-               speculate_from="input", anchors=None, Ls=None, progress_every=0):
+               speculate_from="input", anchors=None, Ls=None, progress_every=0, width=1):
     from speculative_pipeline_decoding_amd import SPD
     G = cfg.gen_len if G is None else G
     tol_l, tol_h = tolerances(cfg)
@@ -76,7 +78,8 @@ def run_parity(cfg, W, dW, prompt, G=None, T=0.0, seed=0, n=None, fill="clamp",
     nucleus = T > 0 and top_p < 1.0
     if nucleus:
         tol_l = min(tol_l, s.slack())
-    kw = {"top_p": top_p, "speculate_from": speculate_from, "anchors": anchors, "Ls": Ls}
+    kw = {"top_p": top_p, "speculate_from": speculate_from, "anchors": anchors, "Ls": Ls,
+          "draft_width": width}
     if forced_p is not None:
         s.forced_p, s.forced_ref, s.forced_base = forced_p, np.asarray(forced_ref), len(prompt)
         kw.update(forced_p=forced_p, forced_ref=list(forced_ref))
@@ -86,9 +89,9 @@ def run_parity(cfg, W, dW, prompt, G=None, T=0.0, seed=0, n=None, fill="clamp",
         from oracle.model import Model
         model = Model(cfg, W, weights=oracle_weights)
     orc = OracleSPD(cfg, W, s, n=n, fill=fill, model=model, speculate_from=speculate_from,
-                    anchors=anchors, Ls=Ls)
+                    anchors=anchors, Ls=Ls, W=width)
     rep = {"steps": 0, "max_logit_err": 0.0, "max_state_rel": 0.0, "stopped_at_near_tie": None,
-           "flagged": 0}
+           "flagged": 0, "sibling_accepts": 0, "adoptions": 0}
     t0o = orc.prefill(prompt)
     t0g = gpu.prefill(prompt)
     zt = gpu.debug("target_logits")
@@ -135,8 +138,12 @@ def run_parity(cfg, W, dW, prompt, G=None, T=0.0, seed=0, n=None, fill="clamp",
                 check_against_envelope(keep, rec.target_logits, s, f"step {k} target")
                 rep["top_p_sets"] += 1
                 rep["top_p_split_ties"] += int(split)
-        if c.new_draft != rec.draft:
-            assert rec.draft_flag, f"step {k}: draft {c.new_draft} != {rec.draft} without a near tie"
+        drafts = [c.new_draft]
+        if width > 1:
+            toks = gpu.debug("tokens").reshape(ring, width)
+            drafts += [int(t) for t in toks[(rec.newest + 1) % ring, 1:]]
+        if drafts != list(rec.drafts):
+            assert rec.draft_flag, f"step {k}: drafts {drafts} != {rec.drafts} without a near tie"
             rep["stopped_at_near_tie"] = k
             break
         assert bool(c.verified) == rec.exited, (k, c.verified, rec.exited)
@@ -147,27 +154,38 @@ def run_parity(cfg, W, dW, prompt, G=None, T=0.0, seed=0, n=None, fill="clamp",
             assert e <= tol_l, f"step {k}: target logits err {e}"
             assert c.position == rec.verified_pos
             assert c.draft_token == rec.verified_draft, (k, c.draft_token, rec.verified_draft)
-            if c.token != rec.committed or bool(c.accepted) != rec.accepted:
-                assert rec.verify_flag, (f"step {k}: commit ({c.token}, {c.accepted}) != "
-                                         f"({rec.committed}, {rec.accepted}) without a near tie")
+            if (c.token != rec.committed or bool(c.accepted) != rec.accepted
+                    or c.accepted_index != rec.accepted_index):
+                assert rec.verify_flag, (f"step {k}: commit ({c.token}, {c.accepted_index}) != "
+                                         f"({rec.committed}, {rec.accepted_index}) without a near tie")
                 rep["stopped_at_near_tie"] = k
                 break
+            if c.accepted_index > 0:
+                rep["sibling_accepts"] += 1
+                if not rec.single:
+                    rep["adoptions"] += 1
         kv, pl = gpu.kv_lens()
         assert kv == rec.kv_len, (k, kv, rec.kv_len)
         assert pl == rec.pdm_len, (k, pl, rec.pdm_len)
         assert c.committed_total == orc.N and c.inflight == len(orc.F)
+        # a sibling adopted by this commit still sits in its own row: the next step moves it
+        moved = {}
+        if rec.exited and c.accepted_index > 0 and not rec.single:
+            moved = {rec.verified_pos: c.accepted_index}
         if check_states:
-            hr = gpu.debug("h_ring").reshape(ring, cfg.d_model)
-            an = gpu.debug("anchors").reshape(ring, len(orc.B), cfg.d_model)
-            for x, hv in orc.h.items():
-                r = rel(hr[x % ring], hv)
+            hr = gpu.debug("h_ring").reshape(ring, width, cfg.d_model)
+            an = gpu.debug("anchors").reshape(ring, width, len(orc.B), cfg.d_model)
+            # the oracle's token at x, and its sibling b, against ring row (x mod ring) W + b
+            states = [((x, moved.get(x, 0)), hv, orc.anch.get(x, {})) for x, hv in orc.h.items()]
+            states += [((x, b), hv, orc.sib_anch.get((x, b), {})) for (x, b), hv in orc.sib_h.items()]
+            for (x, b), hv, amap in states:
+                r = rel(hr[x % ring, b], hv)
                 rep["max_state_rel"] = max(rep["max_state_rel"], r)
-                assert r <= tol_h, f"step {k}: residual of position {x} rel err {r}"
-            for x, amap in orc.anch.items():
+                assert r <= tol_h, f"step {k}: residual of position {x} candidate {b} rel err {r}"
                 for i, av in amap.items():
-                    r = rel(an[x % ring, i], av)
+                    r = rel(an[x % ring, b, i], av)
                     rep["max_state_rel"] = max(rep["max_state_rel"], r)
-                    assert r <= tol_h, f"step {k}: anchor {i} of position {x} rel err {r}"
+                    assert r <= tol_h, f"step {k}: anchor {i} of position {x}.{b} rel err {r}"
     st = gpu.stats()
     if rep["stopped_at_near_tie"] is None:
         assert (st.N, st.K, st.accepted, st.rejected) == (orc.N, orc.K, orc.accepted, orc.rejected)

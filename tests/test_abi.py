@@ -97,6 +97,37 @@ def test_init_rejects_bad_arguments_without_a_gpu():
     assert not h.value
 
 
+def test_draft_width_limits():
+    binding, L = _lib()
+    cfg = get("tiny")
+    for w in (0, 1, 2, 4):
+        c, keep = binding.make_config(cfg, draft_width=w)
+        assert L.spd_workspace_bytes(ctypes.byref(c)) > 0, w
+    # the side caches and the candidate rows grow the workspace
+    c1, k1 = binding.make_config(cfg, draft_width=1)
+    c4, k4 = binding.make_config(cfg, draft_width=4)
+    assert L.spd_workspace_bytes(ctypes.byref(c4)) > L.spd_workspace_bytes(ctypes.byref(c1))
+    for bad in (dict(draft_width=5), dict(draft_width=-1),
+                dict(draft_width=2, speculate_from="output")):
+        c, keep = binding.make_config(cfg, **bad)
+        if bad.get("draft_width") == -1:
+            continue     # negative widths read as 1
+        assert L.spd_workspace_bytes(ctypes.byref(c)) == 0, bad
+    c, keep = binding.make_config(get("mid_hybrid_bf16_L8_d256_n4"), draft_width=2)
+    assert L.spd_workspace_bytes(ctypes.byref(c)) == 0     # linear layers
+    # top_p < 1 and forced mode are refused with W > 1, before any device call
+    c, keep = binding.make_config(cfg, draft_width=2)
+    nb = L.spd_workspace_bytes(ctypes.byref(c))
+    fake = ctypes.c_void_p(0x1000)
+    h = ctypes.c_void_p()
+    w = binding.Weights()
+    for s in (binding.Sampling(1.0, 0.9, 0, 0, 0.0, None, 0),
+              binding.Sampling(0.0, 1.0, 0, 1, 0.5, None, 0)):
+        assert L.spd_init(ctypes.byref(c), ctypes.byref(w), ctypes.byref(s), fake, nb, None,
+                          ctypes.byref(h)) == binding.SPD_E_CONFIG
+        assert b"draft" in L.spd_init_error()
+
+
 def test_null_handle_calls():
     binding, L = _lib()
     assert L.spd_step(None) == binding.SPD_E_ARG

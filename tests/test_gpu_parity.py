@@ -454,3 +454,37 @@ def test_fp32_kv_cache(name, T, seed):
     rep = run_parity(cfg32, W, dev_weights(name), prompt, T=T, seed=seed, tol_logits=1e-3)
     print(f"[parity] -> {rep}", flush=True)
     assert rep["steps"] > 0
+
+
+@pytest.mark.parametrize("name,w,kw", [
+    ("tiny", 2, {}), ("tiny", 4, {}), ("tiny", 4, {"T": 1.0, "seed": 3}),
+    ("tiny", 2, {"T": 1.0, "seed": 5}),
+    ("mid_bf16_L6_d384_n3", 4, {"T": 1.0, "seed": 7, "G": 24}),
+    ("mid_bf16_L4_d512_hd128_n4", 2, {"T": 1.0, "seed": 7, "G": 24})])
+def test_draft_tree(name, w, kw):
+    """W candidates per draft position: every candidate, the accepted rank, the siblings'
+    states, and the adoption of accepted siblings (their rows and keys) in lockstep."""
+    rep = _run(name, width=w, **kw)
+    assert rep["steps"] > 0
+    if rep["stopped_at_near_tie"] is None:
+        assert rep["sibling_accepts"] > 0 and rep["adoptions"] > 0
+
+
+def test_draft_tree_lookahead_bit_identical():
+    import torch
+    from speculative_pipeline_decoding_amd import SPD
+    cfg, W, prompt = workload("tiny")
+    runs = []
+    for la in (False, True):
+        g = SPD(cfg, dev_weights("tiny"), temperature=1.0, seed=3, draft_width=4)
+        g.lookahead(la)
+        out = [g.prefill(prompt)]
+        while len(out) < cfg.gen_len:
+            g.step()
+            c = g.verify_commit()
+            if c.verified:
+                out.append((c.token, c.accepted_index))
+        runs.append(out)
+        g.close()
+    torch.cuda.synchronize()
+    assert runs[0] == runs[1]
