@@ -136,7 +136,7 @@ def run_spd(cfg, dW, prompt, T, seed, warmup, steps, kernel_timing, top_p=1.0,
     from speculative_pipeline_decoding_amd import SPD
     stream = torch.cuda.current_stream()
     spd = SPD(cfg, dW, temperature=T, top_p=top_p, seed=seed, stream=stream,
-              speculate_from=speculate_from)
+              speculate_from=speculate_from, draft_width=cfg.draft_width)
     # a refill step's successor is enqueued together with it (the library skips this while
     # per-launch timing is on)
     spd.lookahead(lookahead)
@@ -246,7 +246,7 @@ def cpu_baseline(cfg, W, prompt, T, seed, budget_s, top_p=1.0, speculate_from="i
     info = cpu_info()
     t = time.perf_counter()
     o = OracleSPD(cfg, W, Sampling(temperature=T, top_p=top_p, seed=seed), ft=np.float32,
-                  speculate_from=speculate_from, record_logits=False)
+                  speculate_from=speculate_from, record_logits=False, W=cfg.draft_width)
     o.prefill(np.asarray(prompt))
     setup = time.perf_counter() - t
     log(f"cpu baseline: float32 oracle prefill of {len(prompt)} tokens in {setup:.1f}s "
@@ -364,6 +364,12 @@ def main():
                          "lookahead launch of a refill step's successor)")
     ap.add_argument("--kv-f32", action="store_true",
                     help="store the KV caches in fp32 (kv_dtype SPD_KV_F32) instead of bf16")
+    ap.add_argument("--draft-width", type=int, default=None,
+                    help="draft candidates per position for the headline run (default: the "
+                         "workload's, 1)")
+    ap.add_argument("--tree-width", type=int, default=4,
+                    help="also time the same steps with draft trees of this width (the "
+                         "paper's W = 4; 0 or 1 skips it; softmax-only models)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0,
                     help="seconds of oracle steps in the CPU baseline (its prefill is extra)")
@@ -384,6 +390,8 @@ def main():
     cfg = get(args.workload)
     if args.kv_f32:
         cfg = cfg.with_(kv_dtype="f32")
+    if args.draft_width is not None:
+        cfg = cfg.with_(draft_width=args.draft_width)
     if args.temperature is None:
         args.temperature = float(cfg.temperatures[0])
     if args.top_p is None:
@@ -425,6 +433,23 @@ def main():
                   "ms_per_step": rt["wall_s"] * 1e3 / rt["K"],
                   "step_us_median": 1e3 * statistics.median(rt["step_ms"])}
         log(f"T=0: timed {rt['K']} steps, N={rt['N']}")
+    tree_run = None
+    tree_ok = (args.tree_width > 1 and cfg.draft_width == 1 and not any(cfg.kinds)
+               and args.speculate_from == "input" and args.top_p >= 1.0)
+    if tree_ok:
+        # the same workload with draft trees (W candidates per draft position), same seed
+        r = run_spd(cfg.with_(draft_width=args.tree_width), dW, prompt, args.temperature,
+                    args.seed, args.warmup, args.steps, False, lookahead=lookahead)
+        rt = r["timed"]
+        tree_run = {"draft_width": args.tree_width, "temperature": args.temperature,
+                    "tokens_per_s": rt["N"] / rt["wall_s"], "N": rt["N"], "K": rt["K"],
+                    "alpha": rt["N"] / rt["K"], "s0": rt["N"] / rt["K"] * cfg.n_stages,
+                    "ms_per_step": rt["wall_s"] * 1e3 / rt["K"],
+                    "step_us_median": 1e3 * statistics.median(rt["step_ms"]),
+                    "full_median_us": 1e3 * statistics.median(rt["full"]) if rt["full"] else None,
+                    "refill_median_us": (1e3 * statistics.median(rt["refill"])
+                                         if rt["refill"] else None)}
+        log(f"W={args.tree_width}: timed {rt['K']} steps, N={rt['N']}")
 
     value = tm["N"] / tm["wall_s"]
     ms_per_step = tm["wall_s"] * 1e3 / tm["K"]
@@ -458,6 +483,7 @@ def main():
                    "anchors": list(cfg.anchors), "context": cfg.prompt_len + cfg.gen_len,
                    "prompt": cfg.prompt_len, "temperature": args.temperature, "top_p": args.top_p,
                    "speculate_from": args.speculate_from, "lookahead": lookahead,
+                   "draft_width": cfg.draft_width,
                    "weights": f"{cfg.dtype} N(0,{cfg.weight_std}) seeded",
                    "kv_cache": cfg.dtype if cfg.kv_dtype == "auto" else cfg.kv_dtype,
                    "arithmetic": "fp32 FMA, fp32 accumulation",
@@ -488,6 +514,7 @@ def main():
                                       "accounting of the same steps replayed) over ms_per_step"},
         "kernels": kernels,
         "t0_run": t0_run,
+        "tree_run": tree_run,
         "prefill_s": main_run["prefill_s"],
         "device": torch.cuda.get_device_name(0),
     }

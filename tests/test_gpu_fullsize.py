@@ -96,10 +96,11 @@ def test_fullsize_lockstep_fp32_kv(wl, T, seed):
     assert rep["steps"] >= cfg.n_stages or rep["stopped_at_near_tie"] is not None
 
 
-def _stream(name, dW, n, T, G, seed=0, speculate_from="input", lookahead=False):
+def _stream(name, dW, n, T, G, seed=0, speculate_from="input", lookahead=False, draft_width=1):
     from speculative_pipeline_decoding_amd import SPD
     cfg, _, prompt = workload(name)
-    gpu = SPD(cfg, dW, temperature=T, seed=seed, n=n, speculate_from=speculate_from)
+    gpu = SPD(cfg, dW, temperature=T, seed=seed, n=n, speculate_from=speculate_from,
+              draft_width=draft_width)
     gpu.lookahead(lookahead)
     toks = [(gpu.prefill(prompt), 0)]
     steps = []
@@ -234,3 +235,37 @@ def test_fullsize_lockstep_at_full_context(wl, mode):
         assert rep["N"] == G - 1
     if mode == "forced" and rep["stopped_at_near_tie"] is None:
         assert rep["rejected"] > 0 and rep["N"] > rep["rejected"]
+
+
+@pytest.mark.parametrize("T,seed", [(1.0, 1), (1.0, 10)])
+def test_fullsize_draft_tree_lockstep(wl, T, seed):
+    """Draft trees (W = 4) on the benchmark's n=8 model in lockstep with the oracle: every
+    candidate, the accepted rank, the siblings' states and their adoption, at the
+    benchmark's launch shapes on a short prompt."""
+    name, dW, oW = wl
+    if name != "dense_bf16_L32_d2560_n8_ctx2048":
+        pytest.skip("run on the benchmark's model only (the oracle runs every candidate)")
+    cfg, W, prompt = workload(name)
+    print(f"[fullsize] draft tree lockstep {name} W=4 T={T}", flush=True)
+    rep = run_parity(cfg, W, dW, prompt[:40], T=T, seed=seed, max_steps=cfg.n_stages + 12,
+                     oracle_weights=oW, tol_logits=logit_tolerance(name, T), width=4)
+    print(f"[fullsize] -> {rep}", flush=True)
+    # both seeds reach an accepted sibling (adopted) within these steps in the oracle
+    assert rep["stopped_at_near_tie"] is not None or rep["adoptions"] > 0
+
+
+def test_fullsize_draft_tree_lossless(wl):
+    """At T = 0 a draft tree changes only which positions are accepted: the committed
+    stream still equals autoregressive decoding (the library at n = 1)."""
+    name, dW, _ = wl
+    cfg, _, _ = workload(name)
+    if any(cfg.kinds):
+        pytest.skip("draft trees need softmax layers only")
+    G = 24
+    ref, _, _ = _stream(name, dW, 1, 0.0, G)
+    got, steps, st = _stream(name, dW, cfg.n_stages, 0.0, G, draft_width=4)
+    for (a, fa), (b, fb) in zip(ref, got):
+        if fa or fb:
+            break
+        assert a == b
+    assert st.N == G - 1
