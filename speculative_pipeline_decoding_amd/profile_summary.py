@@ -8,6 +8,10 @@
       counter reads for a plain device-to-device copy of known size (the largest
       copy dispatch in the run, of --calib-mib MiB), as HBM bytes per launch.
 
+  python -m speculative_pipeline_decoding_amd.profile_summary mfma COUNTER_DIR TRACE_DIR
+      per kernel with matrix-core work: bf16 MFMA flops per dispatch (MfmaFlopsBF16),
+      their rate over the kernel-trace mean duration, and MfmaUtil.
+
 Every summary records the SHA-256 of the GEMV source it measured, so a later
 reader can tell whether the numbers still describe the current kernel.
 """
@@ -98,6 +102,29 @@ def cmd_traffic(a):
             print(f"traffic_bytes_per_launch {k} {tb:.0f}")
 
 
+def cmd_mfma(a):
+    """Matrix-core use per kernel: MfmaFlopsBF16 (bf16 MFMA operations x 512) and MfmaUtil
+    (percent of SIMD cycles with the MFMA unit busy, over the dispatch's active cycles) from
+    one counter run, and the mean duration from a kernel trace of the same command."""
+    flops = counter_values(a.counter_dir, "MfmaFlopsBF16")
+    util = counter_values(a.counter_dir, "MfmaUtil")
+    dur = kernel_durations(a.trace_dir)
+    print(f"gemv source sha256[:16]: {source_hash()}")
+    print(f"{'kernel':44s} {'calls':>6s} {'avg_us':>8s} {'MFMA_GFLOP':>11s} {'TFLOP/s':>8s} "
+          f"{'of_2.5P':>7s} {'MfmaUtil%':>9s}")
+    for k in sorted(flops, key=lambda k: -sum(flops[k])):
+        fv = flops[k]
+        if sum(fv) == 0:
+            continue
+        uv = util.get(k, [0.0])
+        d = dur.get(k)
+        avg_us = sum(d) / len(d) if d else float("nan")
+        f_avg = sum(fv) / len(fv)
+        tf = f_avg / (avg_us * 1e-6) / 1e12 if d else float("nan")
+        print(f"{k:44s} {len(fv):6d} {avg_us:8.2f} {f_avg / 1e9:11.3f} {tf:8.1f} "
+              f"{tf / 2500.0:7.3f} {sum(uv) / len(uv):9.2f}")
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -108,8 +135,11 @@ def main(argv=None):
     t.add_argument("write_dir")
     t.add_argument("--calib-mib", type=int, required=True)
     t.add_argument("--kernel", default="gemv_gate_up")
+    m = sub.add_parser("mfma")
+    m.add_argument("counter_dir")
+    m.add_argument("trace_dir")
     a = ap.parse_args(argv)
-    {"stats": cmd_stats, "traffic": cmd_traffic}[a.cmd](a)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "mfma": cmd_mfma}[a.cmd](a)
 
 
 if __name__ == "__main__":
