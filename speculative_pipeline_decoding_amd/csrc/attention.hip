@@ -316,7 +316,9 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_merge_kernel(
 // 16-key half; the PV step takes exactly those keys as its k slots, so p goes from
 // the softmax to the next MFMA without leaving the lane. The softmax is the usual
 // running max / sum per column, reduced over the four lane groups with shuffles.
-template <int HD>
+// SIB: the launch holds sibling candidates (draft trees), whose own key and value come
+// from side rows; without it the kernel carries none of that code.
+template <int HD, bool SIB>
 __global__ __launch_bounds__(kAttnWaves * 64) void attn_mfma_kernel(
     const AttnProb* __restrict__ probs, int nprob,
     // prefill mode (probs == nullptr): workgroup b covers prompt rows R (b / hkv) .. of kv
@@ -346,7 +348,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_mfma_kernel(
     q = P.q; out = P.out; len = P.len; nrows = P.nrows; qs = P.q_stride; os = P.out_stride;
     Kb = static_cast<const uint16_t*>(P.K);
     Vb = static_cast<const uint16_t*>(P.V);
-    if (P.side_k && P.self_row >= 0) {
+    if (SIB && P.side_k && P.self_row >= 0) {
       self_key = P.len - 1;
       sk_row = static_cast<const uint16_t*>(P.side_k) + ((size_t)g * P.side_rows + P.self_row) * HD;
       sv_row = static_cast<const uint16_t*>(P.side_v) + ((size_t)g * P.side_rows + P.self_row) * HD;
@@ -373,6 +375,11 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_mfma_kernel(
   const uint16_t* Kg = Kb + (size_t)g * max_ctx * HD;
   const uint16_t* Vg = Vb + (size_t)g * (kv_ctx(max_ctx) / 32) * HD * 32;
 
+  // a sibling's own value row, the DT dims this lane takes in the PV step, read once
+  uint32_t svv[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) svv[dt] = SIB && self_key >= 0 ? sv_row[16 * dt + c] : 0u;
+
   // K and V pieces of block j; rows past the cache end are clamped (their scores are
   // masked, and the cache is zero-filled at set-up, so every value is finite)
   uint4 kf[2][2][KST], vf[2][DT];
@@ -381,7 +388,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_mfma_kernel(
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       const int key = min(kb + 16 * kt + c, max_ctx - 1);
-      const uint16_t* krow = key == self_key ? sk_row : Kg + (size_t)key * HD;
+      const uint16_t* krow = SIB && key == self_key ? sk_row : Kg + (size_t)key * HD;
 #pragma unroll
       for (int st = 0; st < KST; ++st) {
         const int d0 = 32 * st + 8 * gq;
@@ -389,22 +396,11 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_mfma_kernel(
       }
     }
     const uint16_t* vb = Vg + (size_t)(min(kb, max_ctx - 1) / 32) * HD * 32;
-    // a sibling's own key sits in this block: the lane holding it (keys 4 gq .. 4 gq + 3,
-    // and 16 + 4 gq .. of the block, dim 16 dt + c) swaps in the side row's value
-    const int off = self_key - kb;
-    const bool own = self_key >= 0 && off >= 0 && off < 32 && ((off & 15) >> 2) == gq;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const uint16_t* vp = vb + (size_t)(16 * dt + c) * 32 + 4 * gq;
-      uint2 a = load_g8(vp);
-      uint2 b = load_g8(vp + 16);
-      if (own) {
-        const uint32_t val = sv_row[16 * dt + c];
-        uint2& w = off < 16 ? a : b;
-        const int e = off & 3;
-        uint32_t& word = (e >> 1) ? w.y : w.x;
-        word = (e & 1) ? ((word & 0xffffu) | (val << 16)) : ((word & 0xffff0000u) | val);
-      }
+      const uint2 a = load_g8(vp);
+      const uint2 b = load_g8(vp + 16);
       vf[buf][dt] = make_uint4(a.x, a.y, b.x, b.y);
     }
   };
@@ -439,6 +435,25 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_mfma_kernel(
 
   auto block = [&](int buf, int j) {
     const int kb = k_lo + 32 * j;
+    // a sibling's own key sits in this block: the lane holding it (keys 4 gq .. 4 gq + 3,
+    // and 16 + 4 gq .. of the block, dim 16 dt + c) swaps in the side row's value. Done
+    // here, where the values are consumed anyway, with selects only (a swap at load time
+    // would make every load wait at once), and only in a sibling's workgroups.
+    if (SIB && self_key >= 0) {
+      const int off = self_key - kb;
+      const bool own = self_key >= 0 && off >= 0 && off < 32 && ((off & 15) >> 2) == gq;
+      const int word = ((off >> 4) & 1) * 2 + ((off >> 1) & 1);
+      const uint32_t mask = own ? (0xffffu << (16 * (off & 1))) : 0u;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const uint32_t ins = (off & 1) ? (svv[dt] << 16) : svv[dt];
+        uint4& v = vf[buf][dt];
+        v.x = word == 0 ? ((v.x & ~mask) | (ins & mask)) : v.x;
+        v.y = word == 1 ? ((v.y & ~mask) | (ins & mask)) : v.y;
+        v.z = word == 2 ? ((v.z & ~mask) | (ins & mask)) : v.z;
+        v.w = word == 3 ? ((v.w & ~mask) | (ins & mask)) : v.w;
+      }
+    }
     f32x4_t sc[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -550,13 +565,17 @@ void launch_valu(dim3 grid, hipStream_t st, const AttnProb* probs, int nprob, co
 }
 
 template <int HD>
-void launch_mfma(dim3 grid, hipStream_t st, const AttnProb* probs, int nprob, const float* pq,
+void launch_mfma(bool sib, dim3 grid, hipStream_t st, const AttnProb* probs, int nprob, const float* pq,
                  int q_stride, float* pout, int out_stride, const void* pK, const void* pV,
                  int pos0, int prows, int G, int hkv, int max_ctx, int split, float* part,
                  bool merge, LaunchEv ev) {
   LaunchEv e1{ev.start, merge ? nullptr : ev.stop}, e2{nullptr, ev.stop};
-  SPD_LAUNCH(e1, (attn_mfma_kernel<HD>), grid, dim3(kAttnWaves * 64), 0, st, probs, nprob, pq,
-             q_stride, pout, out_stride, pK, pV, pos0, prows, G, hkv, max_ctx, split, part);
+  if (sib)
+    SPD_LAUNCH(e1, (attn_mfma_kernel<HD, true>), grid, dim3(kAttnWaves * 64), 0, st, probs, nprob,
+               pq, q_stride, pout, out_stride, pK, pV, pos0, prows, G, hkv, max_ctx, split, part);
+  else
+    SPD_LAUNCH(e1, (attn_mfma_kernel<HD, false>), grid, dim3(kAttnWaves * 64), 0, st, probs, nprob,
+               pq, q_stride, pout, out_stride, pK, pV, pos0, prows, G, hkv, max_ctx, split, part);
   if (merge)
     SPD_LAUNCH(e2, (attn_merge_kernel<HD>), dim3(nprob * hkv * merge_parts(HD)),
                dim3(kAttnWaves * 64), 0, st, probs, G, hkv, 16, part);
@@ -566,13 +585,13 @@ void launch_mfma(dim3 grid, hipStream_t st, const AttnProb* probs, int nprob, co
 hipError_t dispatch(bool bf16, dim3 grid, hipStream_t st, const AttnProb* probs, int nprob,
                     const float* pq, int q_stride, float* pout, int out_stride, const void* pK,
                     const void* pV, int pos0, int prows, int hq, int hkv, int hd, int max_ctx,
-                    int split, float* part, bool merge, LaunchEv ev = {}) {
+                    int split, float* part, bool merge, LaunchEv ev = {}, bool sib = false) {
   const int G = hq / hkv;
   if (bf16) {
 #define SPD_ATTN_CASE(HDV)                                                                    \
     if (hd == HDV) {                                                                          \
-      launch_mfma<HDV>(grid, st, probs, nprob, pq, q_stride, pout, out_stride, pK, pV, pos0,  \
-                       prows, G, hkv, max_ctx, split, part, merge, ev);                       \
+      launch_mfma<HDV>(sib, grid, st, probs, nprob, pq, q_stride, pout, out_stride, pK, pV,   \
+                       pos0, prows, G, hkv, max_ctx, split, part, merge, ev);                 \
       return hipGetLastError();                                                               \
     }
     SPD_ATTN_CASE(16)
@@ -611,10 +630,10 @@ bool attn_supported_head_dim(int hd, bool bf16) {
 
 hipError_t launch_attention(const AttnProb* d_probs, int nprob, int ntiles, bool bf16, int hq,
                             int hkv, int hd, int max_ctx, int split_len, bool any_split,
-                            float* partials, hipStream_t st, LaunchEv ev) {
+                            float* partials, hipStream_t st, LaunchEv ev, bool siblings) {
   if (ntiles <= 0) return hipSuccess;
   return dispatch(bf16, dim3(ntiles), st, d_probs, nprob, nullptr, 0, nullptr, 0, nullptr, nullptr,
-                  0, 0, hq, hkv, hd, max_ctx, split_len, partials, any_split, ev);
+                  0, 0, hq, hkv, hd, max_ctx, split_len, partials, any_split, ev, siblings);
 }
 
 hipError_t launch_attention_prefill(const float* q, int q_stride, float* out, int out_stride,

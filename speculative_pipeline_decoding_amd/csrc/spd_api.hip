@@ -103,7 +103,8 @@ struct Op {
   int stream = 0;  // 0: the caller's stream, 1: the PDM stream
   GemvPlan plan;   // GEMV: kernel kind, workgroups and LDS (gemv_plan)
   int layer = -1;  // the one target layer this launch serves, when only one token is in it
-  int adopt = 0;   // OP_EMBED: target layers of a sibling's keys to adopt (extra workgroups)
+  int adopt = 0;   // OP_EMBED: target layers of a sibling's keys to adopt (extra workgroups);
+                   // OP_ATTN: 1 if a problem is a sibling candidate (its own key in a side row)
 };
 
 struct Plan {
@@ -504,7 +505,8 @@ hipError_t run_op(spd_handle* h, const Op& op, LaunchEv ev = {}) {
     case OP_ATTN: case OP_PDM_ATTN:
       return launch_attention(reinterpret_cast<const AttnProb*>(d + op.off), op.count, op.ntiles,
                               p.kv_bf16, p.hq, p.hkv, p.hd, p.max_ctx, op.split,
-                              op.ntiles > op.count * p.hkv, h->at<float>(p.o_apart), st, ev);
+                              op.ntiles > op.count * p.hkv, h->at<float>(p.o_apart), st, ev,
+                              op.adopt != 0);
     case OP_VOCAB:
       return launch_vocab_stats(reinterpret_cast<const VocabDesc*>(d + op.off), kVocabBlocks,
                                 h->at<VocabPartial>(p.o_part), st, ev);
@@ -605,6 +607,8 @@ int build_step(spd_handle* h, DescWriter& dw) {
     const int nt = finish_attn(p, a, split, slot0);
     Op op{kind, dw.put(a.data(), (int)a.size()), (int)a.size(), nt, split, kvb};
     op.stream = stream;
+    for (const AttnProb& x : a)
+      if (x.side_k && x.self_row >= 0) op.adopt = 1;
     h->ops.push_back(op);
   };
 

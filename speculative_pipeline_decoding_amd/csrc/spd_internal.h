@@ -410,7 +410,8 @@ hipError_t launch_gemv(int role, const GemvProb* d_probs, int nprob, const GemvP
                        const float2* rope, hipStream_t st, LaunchEv ev = {});
 hipError_t launch_attention(const AttnProb* d_probs, int nprob, int ntiles, bool bf16,
                             int hq, int hkv, int hd, int max_ctx, int split_len, bool any_split,
-                            float* partials, hipStream_t st, LaunchEv ev = {});
+                            float* partials, hipStream_t st, LaunchEv ev = {},
+                            bool siblings = false);   // siblings: some problem has self_row >= 0
 hipError_t launch_attention_prefill(const float* q, int q_stride, float* out, int out_stride,
                                     const void* K, const void* V, int pos0, int P, bool bf16,
                                     int hq, int hkv, int hd, int max_ctx, hipStream_t st);

@@ -88,6 +88,7 @@ __device__ __forceinline__ void top_clear(float* s, int* id) {
   for (int j = 0; j < kTopL; ++j) { s[j] = -INFINITY; id[j] = INT_MAX; }
 }
 __device__ __forceinline__ void top_insert(float* s, int* id, float v, int i) {
+  if (!better(v, i, s[kTopL - 1], id[kTopL - 1])) return;   // the common case: not in the list
 #pragma unroll
   for (int j = 0; j < kTopL; ++j) {
     if (better(v, i, s[j], id[j])) {
