@@ -691,10 +691,15 @@ __global__ __launch_bounds__(kVocabBlock) void residual_final_kernel(
 // recursive rejection sampling, in one block. Round i tests candidate c_i, proposed from q_i
 // (q without c_0 .. c_{i-1}, renormalised), against r_i = R_i / Z_i, where R_1 = max(0, p - q)
 // and R_{i+1} = max(0, R_i / Z_i - q_i) (R_0 = p, Z_0 = 1): accept iff u_i q_i(c_i) < r_i(c_i).
-// Every Z_i is a block sum over the vocabulary (R_i(x) evaluated from p(x), q(x) and the
-// earlier rounds' constants); if all rounds reject, y = argmax over R_W > 0 of
-// log R_W(x) + G(x) (RES stream), which draws from r_W. A residual without mass commits the
-// target's argmax, flagged.
+// If all rounds reject, y = argmax over R_W > 0 of log R_W(x) + G(x) (RES stream), which draws
+// from r_W; a residual without mass commits the target's argmax, flagged.
+//
+// Off the candidates, q_j(x) = q(x) s_j with s_0 = 1, s_j = 1 / (1 - E_j) (E_j: the mass of
+// c_0 .. c_{j-1}), and since max(0, max(0, a) / Z - b) = max(0, a / Z - b) for b >= 0, Z > 0,
+// every R_i there is one clamp: R_i(x) = max(0, A_i p(x) - B_i q(x)), A_{i+1} = A_i / Z_i,
+// B_{i+1} = B_i / Z_i + s_i (A_0 = 1, B_0 = 0). The W candidates follow the recursion itself.
+// So a pass over the vocabulary costs two exponentials and a clamp per token; Z_i is the
+// block's sum in a fixed order.
 __global__ __launch_bounds__(kVocabBlock) void tree_rounds_kernel(const FinalizeDesc* __restrict__ fd) {
   __shared__ Stat sh[kVocabBlock];
   __shared__ float red[kVocabBlock / 64];
@@ -704,58 +709,83 @@ __global__ __launch_bounds__(kVocabBlock) void tree_rounds_kernel(const Finalize
   const int W = f.W;
   const int vrow = (f.v % f.ring) * W;
   int cand[kMaxWidth];
-  for (int j = 0; j < W; ++j) cand[j] = f.tok_ring[vrow + j];
+  float qcand[kMaxWidth], pcand[kMaxWidth];
   const float lse_t = vd->lse_t, lse_q = *f.lse_q_v, invT = f.inv_temp;
-  float Z[kMaxWidth + 1], E[kMaxWidth + 1];   // normalisers, excluded q mass before round i
-  Z[0] = 1.f;
-  E[0] = 0.f;
-  // R_i(x) for i >= 1 from p(x) = px, q(x) = qx
-  auto R = [&](int i, int x, float px, float qx) {
-    float r = px;
-    for (int j = 0; j < i; ++j) {
-      bool out = false;
-      for (int m = 0; m < j; ++m) out = out || cand[m] == x;
-      const float qj = out ? 0.f : (j == 0 ? qx : qx / (1.f - E[j]));
-      r = fmaxf(0.f, r / Z[j] - qj);
-    }
-    return r;
-  };
+#pragma unroll
+  for (int j = 0; j < kMaxWidth; ++j) {
+    cand[j] = j < W ? f.tok_ring[vrow + j] : -1;
+    pcand[j] = j < W ? expf(f.zt[cand[j]] * invT - lse_t) : 0.f;
+    qcand[j] = j < W ? expf(f.zq_v[cand[j]] * invT - lse_q) : 0.f;
+  }
+  float Z[kMaxWidth + 1], S[kMaxWidth + 1], A[kMaxWidth + 1], B[kMaxWidth + 1];
+  float Rc[kMaxWidth];                 // R_i at each candidate for the current round i
+  Z[0] = 1.f; S[0] = 1.f; A[0] = 1.f; B[0] = 0.f;
+#pragma unroll
+  for (int k = 0; k < kMaxWidth; ++k) Rc[k] = pcand[k];   // R_0 = p
+  float E = 0.f;                                          // mass of the candidates so far
   int y = -1, idx = -1;
   bool flag = (vd->flags & 1) != 0;
+  // R_i at the candidates from R_{i-1}: candidate k is out of q_{i-1} once k < i - 1
+  auto step_cands = [&](int i) {
+#pragma unroll
+    for (int k = 0; k < kMaxWidth; ++k) {
+      const float qj = k < i - 1 ? 0.f : qcand[k] * S[i - 1];
+      Rc[k] = fmaxf(0.f, Rc[k] / Z[i - 1] - qj);
+    }
+  };
+  auto is_cand = [&](int x, int& k) {
+    k = -1;
+#pragma unroll
+    for (int j = 0; j < kMaxWidth; ++j)
+      if (j < W && cand[j] == x) k = j;
+    return k >= 0;
+  };
   for (int i = 1; i < W && y < 0; ++i) {
-    // Z_i: a block sum in a fixed order
+    A[i] = A[i - 1] / Z[i - 1];
+    B[i] = B[i - 1] / Z[i - 1] + S[i - 1];
+    step_cands(i);
     float part = 0.f;
-    for (int x = threadIdx.x; x < f.V; x += blockDim.x)
-      part += R(i, x, expf(f.zt[x] * invT - lse_t), expf(f.zq_v[x] * invT - lse_q));
+    for (int x = threadIdx.x; x < f.V; x += blockDim.x) {
+      int k;
+      if (is_cand(x, k)) continue;       // added below, once
+      const float px = expf(f.zt[x] * invT - lse_t), qx = expf(f.zq_v[x] * invT - lse_q);
+      part += fmaxf(0.f, A[i] * px - B[i] * qx);
+    }
     for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = part;
     __syncthreads();
     float Zi = 0.f;
     for (int w = 0; w < (int)(blockDim.x >> 6); ++w) Zi += red[w];
+#pragma unroll
+    for (int k = 0; k < kMaxWidth; ++k)
+      if (k < W) Zi += Rc[k];
     __syncthreads();
     if (!(Zi > 0.f)) { y = vd->target_arg; flag = true; break; }
     Z[i] = Zi;
-    E[i] = E[i - 1] + expf(f.zq_v[cand[i - 1]] * invT - lse_q);
-    const int c = cand[i];
-    const float qc = expf(f.zq_v[c] * invT - lse_q) / (1.f - E[i]);
-    const float rc = R(i, c, expf(f.zt[c] * invT - lse_t), expf(f.zq_v[c] * invT - lse_q)) / Zi;
+    E += qcand[i - 1];
+    S[i] = 1.f / (1.f - E);
+    const float qc = qcand[i] * S[i];
+    const float rc = Rc[i] / Zi;
     const float u = rng_uniform(f.seed, RNG_ACC, f.v, (unsigned long long)i);
     if (fabsf(u * qc - rc) < kNearTie * qc) flag = true;
-    if (u * qc < rc) { y = c; idx = i; }
+    if (u * qc < rc) { y = cand[i]; idx = i; }
   }
   if (y < 0) {
-    // every round rejected: draw from r_W. Its unnormalised R_W needs Z_{W-1} (already in Z)
-    // and the excluded mass E_{W-1}
-    const int Wl = W;
+    // every round rejected: draw from r_W (R_W from Z_{W-1}, s_{W-1})
+    const float AW = A[W - 1] / Z[W - 1], BW = B[W - 1] / Z[W - 1] + S[W - 1];
+    step_cands(W);
     Stat m = stat_empty();
     for (int x = threadIdx.x; x < f.V; x += blockDim.x) {
-      float px = expf(f.zt[x] * invT - lse_t), qx = expf(f.zq_v[x] * invT - lse_q);
-      float r = px;
-      for (int j = 0; j < Wl; ++j) {
-        bool out = false;
-        for (int mm = 0; mm < j; ++mm) out = out || cand[mm] == x;
-        const float qj = out ? 0.f : (j == 0 ? qx : qx / (1.f - E[j]));
-        r = fmaxf(0.f, r / Z[j] - qj);
+      int k;
+      float r;
+      if (is_cand(x, k)) {
+        r = 0.f;
+#pragma unroll
+        for (int j = 0; j < kMaxWidth; ++j)
+          if (j == k) r = Rc[j];
+      } else {
+        const float px = expf(f.zt[x] * invT - lse_t), qx = expf(f.zq_v[x] * invT - lse_q);
+        r = fmaxf(0.f, AW * px - BW * qx);
       }
       if (r > 0.f) {
         const float g = logf(r) + gumbel_of(rng_uniform(f.seed, RNG_RES, f.v, (unsigned long long)x));
