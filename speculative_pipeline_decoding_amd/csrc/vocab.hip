@@ -99,7 +99,8 @@ __device__ __forceinline__ void top_insert(float* s, int* id, float v, int i) {
 }
 // The block's best kTopL of every thread's list (each thread passes its own, best first):
 // each wave pops its best head kTopL times (butterfly reductions, the same order in every
-// wave), then thread 0 merges the waves' lists. The result lands in os / oid (thread 0).
+// wave), then wave 0 pops the best of the waves' lists the same way. The result lands in
+// os / oid (written by thread 0).
 __device__ __forceinline__ void top_block(const float* s, const int* id, float* ws, int* wid,
                                           float* os, int* oid) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -121,9 +122,26 @@ __device__ __forceinline__ void top_block(const float* s, const int* id, float* 
     if (lane == 0) { ws[w * kTopL + k] = ms; wid[w * kTopL + k] = mi; }
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    top_clear(os, oid);
-    for (int j = 0; j < (int)(blockDim.x >> 6) * kTopL; ++j) top_insert(os, oid, ws[j], wid[j]);
+  // wave 0 merges the waves' lists (at most 128 entries, two per lane) by the same pops
+  if (w == 0) {
+    const int n = (int)(blockDim.x >> 6) * kTopL;
+    float h0 = lane < n ? ws[lane] : -INFINITY, h1 = lane + 64 < n ? ws[lane + 64] : -INFINITY;
+    int j0 = lane < n ? wid[lane] : INT_MAX, j1 = lane + 64 < n ? wid[lane + 64] : INT_MAX;
+    if (better(h1, j1, h0, j0)) {
+      const float t = h0; h0 = h1; h1 = t;
+      const int ti = j0; j0 = j1; j1 = ti;
+    }
+    for (int k = 0; k < kTopL; ++k) {
+      float ms = h0;
+      int mi = j0;
+      for (int o = 32; o > 0; o >>= 1) {
+        const float s2 = __shfl_xor(ms, o);
+        const int i2 = __shfl_xor(mi, o);
+        if (better(s2, i2, ms, mi)) { ms = s2; mi = i2; }
+      }
+      if (mi == j0 && ms == h0 && mi != INT_MAX) { h0 = h1; j0 = j1; h1 = -INFINITY; j1 = INT_MAX; }
+      if (lane == 0) { os[k] = ms; oid[k] = mi; }
+    }
   }
   __syncthreads();
 }
