@@ -185,15 +185,18 @@ __device__ void rows_body(const GemvProb& p, int tile, const float2* __restrict_
   const int K = p.K, KP = rows_kpad<T>(K);
   const int niter = KP / C;
   const float* __restrict__ g = p.gain;
+  // float4 of each input per thread per staging round: fewer with four vectors, whose
+  // staging registers would otherwise halve the waves a SIMD can hold
+  constexpr int ST = NV >= 4 ? 1 : kRowsStage;
 
   // staging loads of the first round go out before the weight ring; vector v takes its
   // own gain (g + v * gain_stride: the shared head sweep normalises its two rows with
   // different gains)
   const int NT = blockDim.x;
-  float4 xr[NV][kRowsStage], gr[NV][kRowsStage];
+  float4 xr[NV][ST], gr[NV][ST];
   auto stage_load = [&](int c0) {
 #pragma unroll
-    for (int u = 0; u < kRowsStage; ++u) {
+    for (int u = 0; u < ST; ++u) {
       const int c = min(c0 + 4 * NT * u, K - 4);
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
@@ -225,10 +228,10 @@ __device__ void rows_body(const GemvProb& p, int tile, const float2* __restrict_
   float ss[NV];
 #pragma unroll
   for (int v = 0; v < NV; ++v) ss[v] = 0.f;
-  for (int c0 = 4 * threadIdx.x; c0 < K; c0 += 4 * NT * kRowsStage) {
+  for (int c0 = 4 * threadIdx.x; c0 < K; c0 += 4 * NT * ST) {
     if (c0 != 4 * (int)threadIdx.x) stage_load(c0);
 #pragma unroll
-    for (int u = 0; u < kRowsStage; ++u) {
+    for (int u = 0; u < ST; ++u) {
       const int c = c0 + 4 * NT * u;
       if (c < K) {
         float* dst = xs + rows_lds_col<T>(c);
