@@ -13,6 +13,9 @@ constexpr int kMaxStages = 16;          // n
 constexpr int kMaxRows = kMaxStages + 1;  // PDM rows per step: n + 1
 constexpr int kMaxAnchors = 8;          // k
 constexpr int kMaxWidth = 4;            // W: draft candidates per position
+// a launch finds its problem with one load per lane of a wave: at most 64 problems, and a
+// target attention launch holds one per candidate of every in-flight position
+static_assert(kMaxStages * kMaxWidth <= 64, "attention problems per launch exceed a wave");
 constexpr int kWaves = 4;               // waves per GEMV workgroup
 constexpr int kMaxVec = kMaxRows;       // input vectors of one GEMV problem
 constexpr int kAttnTile = 64;           // keys per attention tile

@@ -488,3 +488,58 @@ def test_draft_tree_lookahead_bit_identical():
         g.close()
     torch.cuda.synchronize()
     assert runs[0] == runs[1]
+
+
+@pytest.mark.parametrize("kw", [{}, {"T": 1.0, "seed": 6}])
+def test_draft_tree_maximum_sizes(kw):
+    """Draft trees at the largest pipeline: n = 16 stages of one layer with W = 4 candidates
+    per position, so a target attention launch holds 64 problems (the most one launch takes),
+    k = 8 anchors and 17 PDM window rows."""
+    import dataclasses
+    import torch
+    from spd_inputs import get, make_prompt, make_weights
+    from speculative_pipeline_decoding_amd import upload_weights
+    cfg = dataclasses.replace(get("mid_bf16_L7_d256_n3_uneven"), name="max_bf16_L16_d256_n16",
+                              n_layers=16, n_stages=16, anchors=(0, 1, 2, 4, 6, 9, 12, 16),
+                              pdm_layers=2, prompt_len=40, gen_len=14, max_ctx=96)
+    W = make_weights(cfg)
+    prompt = make_prompt(cfg)
+    _dev.clear()
+    torch.cuda.empty_cache()
+    print(f"[parity] {cfg.name} W=4 {sorted(kw)}", flush=True)
+    rep = run_parity(cfg, W, upload_weights(cfg, W), prompt, width=4, **kw)
+    print(f"[parity] -> steps {rep['steps']} N {rep.get('N')} sibling accepts "
+          f"{rep['sibling_accepts']} adoptions {rep['adoptions']} err {rep['max_logit_err']:.2e}",
+          flush=True)
+    assert rep["steps"] >= cfg.n_stages or rep["stopped_at_near_tie"] is not None
+
+
+@pytest.mark.parametrize("name,w,kw", [
+    ("tiny", 4, {"prompt_len": 1}),                    # a one-token prompt
+    ("tiny", 3, {"prompt_len": 1, "T": 1.0, "seed": 2}),
+    ("tiny", 2, {"n": 1, "G": 30}),                    # n = 1: every exit verifies its own drafts
+    ("tiny", 4, {"n": 1, "T": 1.0, "seed": 4, "G": 30}),
+    ("tiny", 2, {"anchors": (0,)}),                    # k = 1
+    ("mid_bf16_L7_d256_n3_uneven", 3, {"T": 1.0, "seed": 3, "G": 24}),
+])
+def test_draft_tree_degenerate_shapes(name, w, kw):
+    import dataclasses
+    import torch
+    from spd_inputs import make_weights
+    from speculative_pipeline_decoding_amd import upload_weights
+    cfg, W, prompt = workload(name)
+    kw = dict(kw)
+    P = kw.pop("prompt_len", len(prompt))
+    if "anchors" in kw:
+        # another anchor count changes the projection's width: a model of its own
+        cfg = dataclasses.replace(cfg, anchors=kw.pop("anchors"))
+        W = make_weights(cfg)
+        _dev.clear()
+        torch.cuda.empty_cache()
+        dW = upload_weights(cfg, W)
+    else:
+        dW = dev_weights(name)
+    print(f"[parity] {name} W={w} anchors {cfg.anchors} prompt {P} {kw}", flush=True)
+    rep = run_parity(cfg, W, dW, prompt[:P], width=w, **kw)
+    print(f"[parity] -> {rep['steps']} steps, {rep['sibling_accepts']} sibling accepts", flush=True)
+    assert rep["steps"] > 0
