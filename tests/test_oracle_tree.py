@@ -155,3 +155,37 @@ def test_tree_step_count_identity(name, w, T):
     for rec in r.records:
         kv = rec.kv_len
         assert all(a >= b for a, b in zip(kv, kv[1:]))
+
+
+def test_tree_residuals_off_the_candidates_are_one_clamp():
+    """The rounds' residuals, off the candidates, are one clamp of a linear combination:
+    R_i(x) = max(0, A_i p(x) - B_i q(x)) with A_{i+1} = A_i / Z_i, B_{i+1} = B_i / Z_i + s_i
+    (A_0 = 1, B_0 = 0, Z_0 = 1, s_0 = 1, s_i = 1 / (1 - E_i), E_i the q-mass of c_0..c_{i-1}),
+    because max(0, max(0, a) / Z - b) = max(0, a / Z - b) for b >= 0 and Z > 0. Checked
+    against the oracle's own rounds (sampling.tree_rounds) to rounding, so a pass over the
+    vocabulary needs two exponentials and a clamp per token."""
+    rng = np.random.default_rng(5)
+    for trial in range(40):
+        V, W = int(rng.integers(6, 40)), int(rng.integers(2, 5))
+        p = rng.dirichlet(np.ones(V) * rng.choice([0.2, 1.0, 3.0]))
+        q = rng.dirichlet(np.ones(V) * rng.choice([0.2, 1.0, 3.0]))
+        cands = [int(c) for c in rng.choice(V, size=W, replace=False)]
+        # the oracle's unnormalised residuals R_1 .. R_W, round by round
+        r, left, Rs, Zs = p, q.copy(), [], [1.0]
+        for i, c in enumerate(cands):
+            qi = q if i == 0 else left / left.sum()
+            res = np.maximum(r - qi, 0.0)
+            Rs.append(res)
+            if not (res > 0).any():
+                break
+            Zs.append(res.sum())
+            r = res / res.sum()
+            left[c] = 0.0
+        off = np.setdiff1d(np.arange(V), cands)
+        A, B, E = 1.0, 0.0, 0.0
+        for i, R in enumerate(Rs):
+            s = 1.0 if i == 0 else 1.0 / (1.0 - E)
+            A, B = A / Zs[i], B / Zs[i] + s
+            np.testing.assert_allclose(np.maximum(0.0, A * p[off] - B * q[off]), R[off],
+                                       rtol=1e-12, atol=1e-15)
+            E += q[cands[i]]
