@@ -172,7 +172,11 @@ __device__ __forceinline__ int rows_lds_col(int c) {   // c: a multiple of 4
 }
 constexpr int kRowsStage = 4;   // float4 of each input per thread per staging round
 
-template <typename T, int NV, int RR, int U>
+// CH: the staged input does not fit the LDS whole (four vectors over a long K): it is
+// staged p.kchunk columns at a time (a multiple of U iterations), each chunk consumed before
+// the next replaces it; the weight ring runs on across chunks and sum(x^2) accumulates over
+// them (the norm scale is applied to the finished sums).
+template <typename T, int NV, int RR, int U, bool CH = false>
 __device__ void rows_body(const GemvProb& p, int tile, const float2* __restrict__ rope,
                           float* __restrict__ xs, float* __restrict__ red) {
   constexpr int E = Elt<T>::N;
@@ -228,6 +232,86 @@ __device__ void rows_body(const GemvProb& p, int tile, const float2* __restrict_
   float ss[NV];
 #pragma unroll
   for (int v = 0; v < NV; ++v) ss[v] = 0.f;
+  float acc[RR][NV];
+#pragma unroll
+  for (int j = 0; j < RR; ++j)
+#pragma unroll
+    for (int v = 0; v < NV; ++v) acc[j][v] = 0.f;
+  float sc[NV];
+  if constexpr (CH) {
+    const int KCH = p.kchunk;          // a multiple of U * C
+    for (int ch0 = 0; ch0 < KP; ch0 += KCH) {
+      const int ch1 = min(KP, ch0 + KCH), kend = min(ch1, K);
+      if (ch0 > 0) {
+        __syncthreads();               // every wave is done with the previous chunk
+        stage_load(ch0 + 4 * threadIdx.x);
+      }
+      for (int c0 = ch0 + 4 * threadIdx.x; c0 < kend; c0 += 4 * NT * ST) {
+        if (c0 != ch0 + 4 * (int)threadIdx.x) stage_load(c0);
+#pragma unroll
+        for (int u = 0; u < ST; ++u) {
+          const int c = c0 + 4 * NT * u;
+          if (c < kend) {
+            float* dst = xs + rows_lds_col<T>(c - ch0);
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+              const float4 x = xr[v][u], gg = gr[v][u];
+              ss[v] += x.x * x.x; ss[v] += x.y * x.y; ss[v] += x.z * x.z; ss[v] += x.w * x.w;
+              *reinterpret_cast<float4*>(dst + v * KCH) =
+                  make_float4(x.x * gg.x, x.y * gg.y, x.z * gg.z, x.w * gg.w);
+            }
+          }
+        }
+      }
+      __syncthreads();
+      const int ie = ch1 / C;
+      for (int i0 = ch0 / C; i0 < ie; i0 += U) {
+#pragma unroll
+        for (int s = 0; s < U; ++s) {
+          const int it = i0 + s;
+          const int k = it * C + lane * E;
+          if (it < ie && k < K) {
+            float xv[NV][E];
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+#pragma unroll
+              for (int h = 0; h < E / 4; ++h) {
+                const float4 t = *reinterpret_cast<const float4*>(xs + v * KCH + (it * C - ch0) +
+                                                                  256 * h + 4 * lane);
+                xv[v][4 * h] = t.x; xv[v][4 * h + 1] = t.y; xv[v][4 * h + 2] = t.z; xv[v][4 * h + 3] = t.w;
+              }
+#pragma unroll
+            for (int j = 0; j < RR; ++j) {
+              float wf[E];
+              to_f32(w[s][j], wf, (const T*)nullptr);
+#pragma unroll
+              for (int v = 0; v < NV; ++v)
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[j][v] += wf[e] * xv[v][e];
+            }
+          }
+          issue(s, it + U);
+        }
+      }
+    }
+    if (g) {
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        const float t = wave_sum(ss[v]);
+        if (lane == 0) red[wave * NV + v] = t;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      sc[v] = 1.f;
+      if (g) {
+        float t = 0.f;
+        for (int q = 0; q < kWaves; ++q) t += red[q * NV + v];
+        sc[v] = rsqrtf(t / (float)K + p.eps);
+      }
+    }
+  } else {
   for (int c0 = 4 * threadIdx.x; c0 < K; c0 += 4 * NT * ST) {
     if (c0 != 4 * (int)threadIdx.x) stage_load(c0);
 #pragma unroll
@@ -253,7 +337,6 @@ __device__ void rows_body(const GemvProb& p, int tile, const float2* __restrict_
     }
   }
   __syncthreads();
-  float sc[NV];
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
     sc[v] = 1.f;
@@ -264,11 +347,6 @@ __device__ void rows_body(const GemvProb& p, int tile, const float2* __restrict_
     }
   }
 
-  float acc[RR][NV];
-#pragma unroll
-  for (int j = 0; j < RR; ++j)
-#pragma unroll
-    for (int v = 0; v < NV; ++v) acc[j][v] = 0.f;
   for (int i0 = 0; i0 < niter; i0 += U) {
 #pragma unroll
     for (int s = 0; s < U; ++s) {
@@ -296,6 +374,7 @@ __device__ void rows_body(const GemvProb& p, int tile, const float2* __restrict_
       issue(s, it + U);
     }
   }
+  }   // staged whole
 #pragma unroll
   for (int v = 0; v < NV; ++v)
 #pragma unroll
@@ -603,9 +682,11 @@ __device__ void mfma_body(const GemvProb& p, int tile, const float2* __restrict_
 }
 
 // Kernel kinds: 1 or 2 vectors (rows kernel; K_ROWS2W gives each wave 8 rows, for the
-// two-vector head sweep), 3..16 vectors on the matrix cores (bf16 weights, input staged
-// whole in LDS: tall matrices only), else up to kMaxVec (split-K).
-enum Kind { K_ROWS1 = 0, K_ROWS2 = 1, K_SPLITK = 2, K_MFMA = 3, K_ROWS2W = 5, K_ROWS4 = 6 };
+// two-vector head sweep), 3 or 4 (K_ROWS4; K_ROWS4C stages a long input in chunks), 3..16
+// vectors on the matrix cores (bf16 weights, input staged whole in LDS: tall matrices
+// only), else up to kMaxVec (split-K).
+enum Kind { K_ROWS1 = 0, K_ROWS2 = 1, K_SPLITK = 2, K_MFMA = 3, K_ROWS2W = 5, K_ROWS4 = 6,
+            K_ROWS4C = 7 };
 
 template <typename T, int KIND>
 __device__ __forceinline__ void gemv_body(const GemvProb* __restrict__ probs, int nprob,
@@ -628,10 +709,11 @@ __device__ __forceinline__ void gemv_body(const GemvProb* __restrict__ probs, in
     mfma_body(p, tile, rope, planes, red);
   } else {
     constexpr bool wide = KIND == K_ROWS2W;
-    constexpr int NV = KIND == K_ROWS1 ? 1 : KIND == K_ROWS4 ? 4 : 2;
+    constexpr int NV = KIND == K_ROWS1 ? 1 : (KIND == K_ROWS4 || KIND == K_ROWS4C) ? 4 : 2;
     extern __shared__ float rows_xs[];
     __shared__ float red[kWaves * NV];
-    rows_body<T, NV, wide ? RWIDE : RW, wide ? kRingWide : kRing>(p, tile, rope, rows_xs, red);
+    rows_body<T, NV, wide ? RWIDE : RW, wide ? kRingWide : kRing, KIND == K_ROWS4C>(
+        p, tile, rope, rows_xs, red);
   }
 }
 
@@ -717,8 +799,18 @@ GemvPlan gemv_plan(GemvProb* v, int n, bool bf16) {
   for (int i = 0; i < n; ++i) mc = mc && units_host(v[i]) >= kTall;
   // 3 or 4 vectors: the candidates of a draft tree's positions (stage problems)
   int kind = mv <= 1 ? K_ROWS1 : mv == 2 ? K_ROWS2 : mv <= 4 ? K_ROWS4 : K_SPLITK;
-  // the rows kernel stages every vector whole in LDS; longer inputs take the split-K kernel
-  if (kind != K_SPLITK && (size_t)mv * kpad * 4 > (size_t)kRowsLds) kind = K_SPLITK;
+  // the rows kernel stages every vector whole in LDS; longer inputs take the split-K kernel,
+  // or with four vectors the rows kernel staging them in chunks of whole ring rounds
+  int kchunk = 0;
+  if (kind != K_SPLITK && (size_t)mv * kpad * 4 > (size_t)kRowsLds) {
+    if (kind == K_ROWS4) {
+      const int unit = kRing * 64 * (bf16 ? 8 : 4);          // K elements per ring round
+      kchunk = (int)(kRowsLds / (4 * 4) / unit) * unit;
+      kind = kchunk > 0 ? K_ROWS4C : K_SPLITK;
+    } else {
+      kind = K_SPLITK;
+    }
+  }
   if (mc && mv > 2) kind = K_MFMA;
   // two vectors over a tall matrix (the shared head sweep): eight rows per wave
   if (kind == K_ROWS2) {
@@ -757,9 +849,12 @@ GemvPlan gemv_plan(GemvProb* v, int n, bool bf16) {
   for (int i = 1; i < n; ++i)
     if (v[i].ntiles != v[0].ntiles) out.tpp = 0;
   out.waves = kind == K_MFMA ? v[0].pad * v[0].ksplit : kWaves;
-  const int nvs = kind == K_ROWS2 || kind == K_ROWS2W ? 2 : kind == K_ROWS4 ? 4 : 1;
+  const int nvs = kind == K_ROWS2 || kind == K_ROWS2W ? 2
+                  : kind == K_ROWS4 || kind == K_ROWS4C ? 4 : 1;
+  for (int i = 0; i < n; ++i) v[i].kchunk = kind == K_ROWS4C ? kchunk : 0;
   out.shm = kind == K_MFMA     ? mc_lds_bytes(v[0].nvec, v[0].K, out.waves)
             : kind == K_SPLITK ? 0
+            : kind == K_ROWS4C ? nvs * kchunk * (int)sizeof(float)
                                : nvs * kpad * (int)sizeof(float);
   return out;
 }
@@ -779,6 +874,7 @@ hipError_t launch_gemv(int role, const GemvProb* d_probs, int nprob, const GemvP
       case K_MFMA: launch_kind<uint16_t, K_MFMA>(role, grid, d_probs, nprob, rope, st, ev, tpp, waves, shm); break;
       case K_ROWS2W: launch_kind<uint16_t, K_ROWS2W>(role, grid, d_probs, nprob, rope, st, ev, tpp, kWaves, shm); break;
       case K_ROWS4: launch_kind<uint16_t, K_ROWS4>(role, grid, d_probs, nprob, rope, st, ev, tpp, kWaves, shm); break;
+      case K_ROWS4C: launch_kind<uint16_t, K_ROWS4C>(role, grid, d_probs, nprob, rope, st, ev, tpp, kWaves, shm); break;
       default: return hipErrorInvalidValue;
     }
   } else {
@@ -788,6 +884,7 @@ hipError_t launch_gemv(int role, const GemvProb* d_probs, int nprob, const GemvP
       case K_SPLITK: launch_kind<float, K_SPLITK>(role, grid, d_probs, nprob, rope, st, ev, tpp); break;
       case K_ROWS2W: launch_kind<float, K_ROWS2W>(role, grid, d_probs, nprob, rope, st, ev, tpp, kWaves, shm); break;
       case K_ROWS4: launch_kind<float, K_ROWS4>(role, grid, d_probs, nprob, rope, st, ev, tpp, kWaves, shm); break;
+      case K_ROWS4C: launch_kind<float, K_ROWS4C>(role, grid, d_probs, nprob, rope, st, ev, tpp, kWaves, shm); break;
       default: return hipErrorInvalidValue;
     }
   }

@@ -61,6 +61,8 @@ struct GemvProb {
   int side_rows;       // rows of the side caches per kv head
   void* side_k;        // EPI_QKV, same_pos: side K [hkv][side_rows][hd], row-major
   void* side_v;        // side V, same layout
+  int kchunk;          // rows kernel, chunked: K columns staged at a time (0: all of K)
+  int pad2;
 };
 
 // Attention over one layer's KV cache for a group of query rows that share it: row r

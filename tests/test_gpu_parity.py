@@ -543,3 +543,26 @@ def test_draft_tree_degenerate_shapes(name, w, kw):
     rep = run_parity(cfg, W, dW, prompt[:P], width=w, **kw)
     print(f"[parity] -> {rep['steps']} steps, {rep['sibling_accepts']} sibling accepts", flush=True)
     assert rep["steps"] > 0
+
+
+@pytest.mark.parametrize("w,T,d_ffn", [(3, 1.0, 16904), (4, 0.0, 4160), (4, 1.0, 9728)])
+def test_draft_tree_long_down_projection_staged_in_chunks(w, T, d_ffn):
+    """With 3 or 4 candidates per position the down projection's inputs (w x d_ffn fp32)
+    exceed the rows kernel's LDS stage: it stages them in chunks of whole ring rounds
+    (the last chunk partial, the boundary inside a pair of rounds with 4160). Lockstep with
+    the oracle, siblings' states included."""
+    import dataclasses
+    import torch
+    from spd_inputs import get, make_prompt, make_weights
+    from speculative_pipeline_decoding_amd import upload_weights
+    cfg = dataclasses.replace(get("mid_bf16_L7_d256_n3_uneven"),
+                              name=f"mid_bf16_L7_d256_ffn{d_ffn}", d_ffn=d_ffn)
+    W = make_weights(cfg)
+    prompt = make_prompt(cfg)
+    _dev.clear()
+    torch.cuda.empty_cache()
+    print(f"[parity] {cfg.name} W={w} T={T}", flush=True)
+    rep = run_parity(cfg, W, upload_weights(cfg, W), prompt, T=T, seed=5, width=w, G=20)
+    print(f"[parity] -> steps {rep['steps']} sibling accepts {rep['sibling_accepts']} "
+          f"err {rep['max_logit_err']:.2e} state {rep['max_state_rel']:.2e}", flush=True)
+    assert rep["steps"] > 0
