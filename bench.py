@@ -305,6 +305,36 @@ def forced_sweep(cfg, dW, prompt, ps, warmup, steps, lookahead=True):
     return out
 
 
+def ar_reference(cfg, dW, prompt, T, seed, warmup, steps):
+    """Context: the same library at n = 1 with a one-layer PDM, i.e. autoregressive decoding
+    on the same kernels. Each step runs all L layers for one token and the head sweep and
+    commits exactly one token (the draft it makes is verified in the same step). On one GPU
+    SPD cannot beat this: every commit costs at least one sweep of the weights; the paper's
+    speedup needs a GPU per stage."""
+    import torch
+    from speculative_pipeline_decoding_amd import SPD
+    stream = torch.cuda.current_stream()
+    spd = SPD(cfg, dW, temperature=T, seed=seed, n=1, Ls=1, stream=stream)
+    spd.lookahead(True)
+    spd.prefill(prompt)
+    for _ in range(warmup):
+        spd.step()
+        spd.verify_commit()
+    s0 = spd.stats()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        spd.step()
+        spd.verify_commit()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    s1 = spd.stats()
+    spd.close()
+    N = s1.N - s0.N
+    return {"n": 1, "pdm_layers": 1, "temperature": T, "tokens_per_s": N / wall,
+            "ms_per_token": 1e3 * wall / max(N, 1), "N": N}
+
+
 def stage_plan_report(cfg, dW, prompt, steps):
     """Per-layer cost of one token through each target layer (the library at n = 1, where
     every sub-layer launch serves one layer), and the stage split balanced on it against
@@ -518,6 +548,9 @@ def main():
         "prefill_s": main_run["prefill_s"],
         "device": torch.cuda.get_device_name(0),
     }
+    res["ar_reference"] = ar_reference(cfg, dW, prompt, args.temperature, args.seed, 8,
+                                       min(64, cfg.gen_len - 8))
+    log(f"AR reference (n=1): {res['ar_reference']['tokens_per_s']:.1f} tokens/s")
     res["hbm_ceiling"] = hbm_ceiling()
     res["prefill"] = prefill_rate(cfg, dW, prompt)
     log(f"HBM copy {res['hbm_ceiling']['copy_GBps']:.0f} GB/s, read {res['hbm_ceiling']['read_GBps']:.0f}"

@@ -566,3 +566,17 @@ def test_draft_tree_long_down_projection_staged_in_chunks(w, T, d_ffn):
     print(f"[parity] -> steps {rep['steps']} sibling accepts {rep['sibling_accepts']} "
           f"err {rep['max_logit_err']:.2e} state {rep['max_state_rel']:.2e}", flush=True)
     assert rep["steps"] > 0
+
+
+@pytest.mark.parametrize("T,seed", [(0.0, 0), (1.0, 7)])
+def test_draft_tree_with_fp32_kv_cache(T, seed):
+    """Draft trees over fp32 KV caches with bf16 weights: the siblings' side rows are fp32
+    too and their attention runs on the fp32 kernel (row-major V)."""
+    cfg, W, prompt = workload("mid_bf16_L6_d384_n3")
+    cfg32 = cfg.with_(kv_dtype="f32")
+    print(f"[parity] mid_bf16_L6_d384_n3 kv f32 W=4 T={T}", flush=True)
+    rep = run_parity(cfg32, W, dev_weights("mid_bf16_L6_d384_n3"), prompt, T=T, seed=seed,
+                     width=4, tol_logits=1e-3, G=24)
+    print(f"[parity] -> steps {rep['steps']} sibling accepts {rep['sibling_accepts']} "
+          f"err {rep['max_logit_err']:.2e}", flush=True)
+    assert rep["steps"] > 0
