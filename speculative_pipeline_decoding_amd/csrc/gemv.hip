@@ -90,10 +90,16 @@ __device__ __forceinline__ void unit_slots(const GemvProb& p, int ut, int& ja, i
   else if (p.epi == EPI_QKV) { ja = 2 * ut; jb = 2 * ut + 1; }
 }
 
+// Epilogue memory accesses go through global-address-space pointers: the pointers come
+// from the problem descriptor, and as generic (FLAT) accesses they would make every
+// later wait for an in-flight weight load a wait for all of them.
+__device__ __forceinline__ void gst(float* p, float v) { *(SPD_GLOBAL float*)p = v; }
+__device__ __forceinline__ float gld(const float* p) { return *(const SPD_GLOBAL float*)p; }
+
 // KV cache element: bf16 (round to nearest even) or fp32, as the cache is laid out.
 __device__ __forceinline__ void store_kv(void* base, size_t idx, float v, bool b16) {
-  if (b16) static_cast<uint16_t*>(base)[idx] = f2bf(v);
-  else static_cast<float*>(base)[idx] = v;
+  if (b16) ((SPD_GLOBAL uint16_t*)base)[idx] = f2bf(v);
+  else ((SPD_GLOBAL float*)base)[idx] = v;
 }
 
 // Epilogue of one output unit of vector v; a (and b for paired kinds) are scaled sums.
@@ -102,17 +108,17 @@ __device__ void epilogue(const GemvProb& p, int v, int unit, float a, float b,
                          const float2* __restrict__ rope) {
   switch (p.epi) {
     case EPI_STORE:
-      p.y[v * p.y_stride + unit] = a;
+      gst(p.y + v * p.y_stride + unit, a);
       break;
     case EPI_ADD: {
       float* yp = p.y + v * p.y_stride + unit;
-      const float nv = *yp + a;
-      *yp = nv;
-      if (p.aux) p.aux[v * p.aux_stride + unit] = nv;
+      const float nv = gld(yp) + a;
+      gst(yp, nv);
+      if (p.aux) gst(p.aux + v * p.aux_stride + unit, nv);
       break;
     }
     case EPI_SWIGLU:
-      p.y[v * p.y_stride + unit] = a / (1.0f + expf(-a)) * b;
+      gst(p.y + v * p.y_stride + unit, a / (1.0f + expf(-a)) * b);
       break;
     case EPI_QKV: {
       const int hd = p.hd, half = hd >> 1;
@@ -122,8 +128,8 @@ __device__ void epilogue(const GemvProb& p, int v, int unit, float a, float b,
       if (head < p.hq) {
         const float2 cs = rope[(size_t)pos * half + i];
         float* q = p.aux + v * p.aux_stride + head * hd;
-        q[i] = a * cs.x - b * cs.y;
-        q[i + half] = a * cs.y + b * cs.x;
+        gst(q + i, a * cs.x - b * cs.y);
+        gst(q + i + half, a * cs.y + b * cs.x);
       } else if (head < p.hq + p.hkv) {
         const float2 cs = rope[(size_t)pos * half + i];
         const bool b16 = sizeof(T) == 2 && !p.kv_f32;
