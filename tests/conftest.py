@@ -18,6 +18,14 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
+    # a test module may declare deselect(item): parameter combinations it does not run
+    kept, dropped = [], []
+    for it in items:
+        fn = getattr(it.module, "deselect", None) if getattr(it, "module", None) else None
+        (dropped if fn is not None and fn(it) else kept).append(it)
+    if dropped:
+        config.hook.pytest_deselected(items=dropped)
+        items[:] = kept
     if os.environ.get("SPD_SLOW") == "1":
         return
     skip = pytest.mark.skip(reason="slow CPU test; set SPD_SLOW=1")

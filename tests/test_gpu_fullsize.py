@@ -41,6 +41,26 @@ DEFAULT_FULL_CONTEXT = {("dense_bf16_L32_d2560_n4", "T0"), ("dense_bf16_L32_d256
 _state = {}
 
 
+def deselect(item) -> bool:
+    """Cases this module does not run (conftest deselects them at collection): the
+    full-context lockstep beyond its defaults (minutes of fp64 oracle work each; set
+    SPD_FULL_CONTEXT_LOCKSTEP=1 to run every case), the draft-tree lockstep on any model but
+    the benchmark's (the oracle runs every candidate), and draft trees on the hybrid model
+    (trees need softmax layers only)."""
+    cs = getattr(item, "callspec", None)
+    if cs is None or "wl" not in cs.params:
+        return False
+    name, fn = cs.params["wl"], item.originalname
+    if fn == "test_fullsize_lockstep_at_full_context":
+        return (os.environ.get("SPD_FULL_CONTEXT_LOCKSTEP") != "1"
+                and (name, cs.params["mode"]) not in DEFAULT_FULL_CONTEXT)
+    if fn == "test_fullsize_draft_tree_lockstep":
+        return name != "dense_bf16_L32_d2560_n8_ctx2048"
+    if fn == "test_fullsize_draft_tree_lossless":
+        return name.startswith("hybrid")
+    return False
+
+
 @pytest.fixture(scope="module", params=NAMES)
 def wl(request):
     """(name, device weights, oracle weights) of one workload; the previous one is dropped."""
@@ -214,8 +234,6 @@ def test_fullsize_lockstep_at_full_context(wl, mode):
     from oracle.spd import ar_decode
     name, dW, oW = wl
     everything = os.environ.get("SPD_FULL_CONTEXT_LOCKSTEP") == "1"
-    if not everything and (name, mode) not in DEFAULT_FULL_CONTEXT:
-        pytest.skip("minutes of fp64 oracle work; set SPD_FULL_CONTEXT_LOCKSTEP=1")
     cfg, W, prompt = workload(name)
     G = 33 if everything else 9
     T, seed = (1.0, 11) if mode == "T1" else (0.0, 0)
@@ -243,8 +261,6 @@ def test_fullsize_draft_tree_lockstep(wl, T, seed):
     candidate, the accepted rank, the siblings' states and their adoption, at the
     benchmark's launch shapes on a short prompt."""
     name, dW, oW = wl
-    if name != "dense_bf16_L32_d2560_n8_ctx2048":
-        pytest.skip("run on the benchmark's model only (the oracle runs every candidate)")
     cfg, W, prompt = workload(name)
     print(f"[fullsize] draft tree lockstep {name} W=4 T={T}", flush=True)
     rep = run_parity(cfg, W, dW, prompt[:40], T=T, seed=seed, max_steps=cfg.n_stages + 12,
@@ -259,8 +275,7 @@ def test_fullsize_draft_tree_lossless(wl):
     stream still equals autoregressive decoding (the library at n = 1)."""
     name, dW, _ = wl
     cfg, _, _ = workload(name)
-    if any(cfg.kinds):
-        pytest.skip("draft trees need softmax layers only")
+    assert not any(cfg.kinds)
     G = 24
     ref, _, _ = _stream(name, dW, 1, 0.0, G)
     got, steps, st = _stream(name, dW, cfg.n_stages, 0.0, G, draft_width=4)
