@@ -1,12 +1,21 @@
 """Summarise rocprofv3 CSV output into the short text kept under profiles/.
 
-  python -m speculative_pipeline_decoding_amd.profile_summary stats DIR
-      per-kernel dispatch count, total and average duration (kernel trace)
+  python -m speculative_pipeline_decoding_amd.profile_summary stats DIR \
+         [--kernel K --group G --skip S]
+      per-kernel dispatch count, total and average duration (kernel trace); with
+      --kernel, also K's average over one phase of the run (below)
   python -m speculative_pipeline_decoding_amd.profile_summary traffic FETCH_DIR WRITE_DIR \
-         --calib-mib 1024 [--kernel gemv_gate_up]
+         --calib-mib 1024 [--kernel gemv_gate_up --group G --skip S]
       FETCH_SIZE and WRITE_SIZE per dispatch (KiB), each scaled by what the same
       counter reads for a plain device-to-device copy of known size (the largest
-      copy dispatch in the run, of --calib-mib MiB), as HBM bytes per launch.
+      copy dispatch in the run, of --calib-mib MiB), as HBM bytes per launch; the
+      kernel's bytes per launch are taken over one phase.
+
+A phase of a kernel is the run of its dispatches between two prefills (any prefill
+GEMM dispatch ends one): in bench.py's default run, phase 0 holds the headline steps,
+phase 1 the same steps replayed with per-launch events (what its kernel table and
+roofline time), phase 2 the autoregressive reference. --skip drops the phase's
+warm-up dispatches.
 
   python -m speculative_pipeline_decoding_amd.profile_summary mfma COUNTER_DIR TRACE_DIR
       per kernel with matrix-core work: bf16 MFMA flops per dispatch (MfmaFlopsBF16),
@@ -57,6 +66,47 @@ def kernel_durations(trace_dir: str):
     return agg
 
 
+def _phase(values, names, kernel, group, skip, sep="gemm_x3_kernel"):
+    """Values of one kernel's dispatches in one phase of a run, in dispatch order: phases
+    are the runs of that kernel's dispatches between prefills (any `sep` dispatch ends a
+    phase); `skip` leading dispatches of the phase are dropped (the warm-up steps)."""
+    phases, cur = [], []
+    for n, v in zip(names, values):
+        if n == sep:
+            if cur:
+                phases.append(cur)
+                cur = []
+        elif n == kernel:
+            cur.append(v)
+    if cur:
+        phases.append(cur)
+    if group >= len(phases):
+        raise SystemExit(f"{kernel}: {len(phases)} phases, no phase {group}")
+    return phases[group][skip:]
+
+
+def trace_sequence(trace_dir: str):
+    """(kernel names, durations in us) of every dispatch, in dispatch order."""
+    rows = sorted(csv.DictReader(open(_find(trace_dir, "kernel_trace.csv"))),
+                  key=lambda r: int(r["Dispatch_Id"]))
+    return ([short_name(r["Kernel_Name"]) for r in rows],
+            [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows])
+
+
+def counter_sequence(d: str, counter: str):
+    """(kernel names, values) of one counter over every dispatch, in dispatch order."""
+    rows = sorted((r for r in csv.DictReader(open(_find(d, "counter_collection.csv")))
+                   if r["Counter_Name"] == counter), key=lambda r: int(r["Dispatch_Id"]))
+    return [short_name(r["Kernel_Name"]) for r in rows], [float(r["Counter_Value"]) for r in rows]
+
+
+def _full_name(names, kernel):
+    hits = sorted({n for n in names if n.startswith(kernel)}, key=lambda n: -names.count(n))
+    if not hits:
+        raise SystemExit(f"no dispatch of {kernel}")
+    return hits[0]
+
+
 def counter_values(d: str, counter: str):
     rows = list(csv.DictReader(open(_find(d, "counter_collection.csv"))))
     agg = collections.defaultdict(list)
@@ -73,6 +123,12 @@ def cmd_stats(a):
     print(f"{'kernel':62s} {'calls':>7s} {'total_ms':>10s} {'avg_us':>9s} {'share':>6s}")
     for k, v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
         print(f"{k:62s} {len(v):7d} {sum(v) / 1e3:10.3f} {sum(v) / len(v):9.2f} {100 * sum(v) / tot:5.1f}%")
+    if a.kernel:
+        names, durs = trace_sequence(a.dir)
+        k = _full_name(names, a.kernel)
+        v = _phase(durs, names, k, a.group, a.skip)
+        print(f"phase {a.group} of {k} (dispatches after {a.skip} warm-up ones): "
+              f"{len(v)} calls, avg_us {sum(v) / len(v):.2f}")
 
 
 def cmd_traffic(a):
@@ -94,12 +150,16 @@ def cmd_traffic(a):
         wb = sum(wv) / len(wv) * 1024 * wscale
         print(f"{k:62s} {len(fv):6d} {fb / 1e6:10.2f} {wb / 1e6:9.2f}")
     if a.kernel:
-        keys = [k for k in f if k.startswith(a.kernel)]
-        if keys:
-            k = max(keys, key=lambda k: sum(f[k]))
-            fv, wv = f[k], w.get(k, [0.0])
-            tb = (sum(fv) / len(fv)) * 1024 * fscale + (sum(wv) / len(wv)) * 1024 * wscale
-            print(f"traffic_bytes_per_launch {k} {tb:.0f}")
+        fn, fv = counter_sequence(a.fetch_dir, "FETCH_SIZE")
+        wn, wv = counter_sequence(a.write_dir, "WRITE_SIZE")
+        k = _full_name(fn, a.kernel)
+        fp = _phase(fv, fn, k, a.group, a.skip)
+        wp = _phase(wv, wn, k, a.group, a.skip)
+        fb = sum(fp) / len(fp) * 1024 * fscale
+        wb = sum(wp) / len(wp) * 1024 * wscale
+        print(f"phase {a.group} of {k} (dispatches after {a.skip} warm-up ones): {len(fp)} calls, "
+              f"fetch_MB {fb / 1e6:.2f}, write_MB {wb / 1e6:.2f}")
+        print(f"traffic_bytes_per_launch {k} {fb + wb:.0f}")
 
 
 def cmd_mfma(a):
@@ -130,11 +190,18 @@ def main(argv=None):
     sub = ap.add_subparsers(dest="cmd", required=True)
     s = sub.add_parser("stats")
     s.add_argument("dir")
+    s.add_argument("--kernel", default=None)
     t = sub.add_parser("traffic")
     t.add_argument("fetch_dir")
     t.add_argument("write_dir")
     t.add_argument("--calib-mib", type=int, required=True)
     t.add_argument("--kernel", default="gemv_gate_up")
+    for q in (s, t):
+        q.add_argument("--group", type=int, default=0,
+                       help="phase of --kernel: its dispatches between the run's n-th and "
+                            "next prefill (0 = before the second prefill)")
+        q.add_argument("--skip", type=int, default=0,
+                       help="leading dispatches of the phase to drop (warm-up steps)")
     m = sub.add_parser("mfma")
     m.add_argument("counter_dir")
     m.add_argument("trace_dir")
