@@ -139,8 +139,9 @@ bool plan_config(const spd_model_config* c, Plan& p, std::string& err) {
   if (c->speculate_from != SPD_SPEC_INPUT && c->speculate_from != SPD_SPEC_OUTPUT)
     return bad("speculate_from must be SPD_SPEC_INPUT or SPD_SPEC_OUTPUT");
   p.spec_output = c->speculate_from == SPD_SPEC_OUTPUT;
+  if (c->draft_width < 0 || c->draft_width > kMaxWidth)
+    return bad("draft_width must be in [1, 4] (0 means 1)");
   p.W = c->draft_width < 1 ? 1 : c->draft_width;
-  if (p.W > kMaxWidth) return bad("draft_width must be in [1, 4]");
   if (p.W > 1 && p.spec_output) return bad("draft trees (draft_width > 1) need SPD_SPEC_INPUT");
   if (c->dtype != SPD_F32 && c->dtype != SPD_BF16) return bad("dtype must be SPD_F32 or SPD_BF16");
   p.bf16 = c->dtype == SPD_BF16;

@@ -110,8 +110,6 @@ def test_draft_width_limits():
     for bad in (dict(draft_width=5), dict(draft_width=-1),
                 dict(draft_width=2, speculate_from="output")):
         c, keep = binding.make_config(cfg, **bad)
-        if bad.get("draft_width") == -1:
-            continue     # negative widths read as 1
         assert L.spd_workspace_bytes(ctypes.byref(c)) == 0, bad
     c, keep = binding.make_config(get("mid_hybrid_bf16_L8_d256_n4"), draft_width=2)
     assert L.spd_workspace_bytes(ctypes.byref(c)) == 0     # linear layers
