@@ -14,7 +14,7 @@ circularity check, "Assumptions & free parameters") and the aiqbench abstract:
     and reseeds it;
   * alpha = N/K (committed tokens per pipeline step) and S0 = alpha * n (Eq. 9).
 
-Readings, where the pages leave a step open (each also listed in the design doc):
+Readings, where the pages leave a step open:
   R1  anchor b = residual after b target layers (b = 0: embedding; b = L: last
       layer output before the final norm);
   R3  anchors not yet computed for a position are filled by the deepest one

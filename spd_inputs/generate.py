@@ -4,7 +4,7 @@ Both the CPU oracle and the GPU path load their inputs from here, so they see
 identical bits. Nothing here is part of the method: it draws numbers, and
 stores them in the workload's weight format.
 
-Recipe (stated again in the design doc):
+Recipe:
   * every matrix ~ N(0, weight_std^2), drawn in float32 and stored as bfloat16
     (round to nearest even) for bf16 workloads, as float32 otherwise;
   * RMSNorm gains are 1.0, stored as float32;
