@@ -84,7 +84,7 @@ enum { SPD_KV_AUTO = 0, SPD_KV_F32 = 1 };             /* KV cache storage */
  *     stores them in fp32 with bf16 weights too: twice the KV bytes, and no bf16
  *     rounding of K and V, whose one-ulp flips deep, wide models amplify in the logits.
  *   draft_width: W, candidates the PDM proposes per draft position (0 or 1: a chain;
- *     at most 4). The pith.science review lists W = 1 and 4 among the paper's free
+ *     at most 4; any other value is SPD_E_CONFIG). The pith.science review lists W = 1 and 4 among the paper's free
  *     parameters ("Assumptions & free parameters"). With W > 1 each draft position
  *     carries the PDM's W best candidates (largest logits at T = 0; at T > 0 the W
  *     largest log q + Gumbel scores, a draw without replacement from q), ranked best
@@ -112,7 +112,8 @@ typedef struct {
   int32_t max_ctx;
   int32_t speculate_from;         /* SPD_SPEC_INPUT | SPD_SPEC_OUTPUT */
   int32_t kv_dtype;               /* SPD_KV_AUTO | SPD_KV_F32 */
-  int32_t draft_width;            /* W: candidates per draft position, 1..4 (0 means 1) */
+  int32_t draft_width;            /* W: candidates per draft position, 1..4 (0 means 1;
+                                     other values: SPD_E_CONFIG) */
 } spd_model_config;
 
 /*
