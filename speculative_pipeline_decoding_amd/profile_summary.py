@@ -66,6 +66,12 @@ def kernel_durations(trace_dir: str):
     return agg
 
 
+def _matches(name: str, kernel: str) -> bool:
+    """A kernel given by its full short name, or by its base name: every instantiation
+    (a GEMV role's launches take different kernel kinds as their vector counts change)."""
+    return name == kernel or ("<" not in kernel and name.startswith(kernel + "<"))
+
+
 def _phase(values, names, kernel, group, skip, sep="gemm_x3_kernel"):
     """Values of one kernel's dispatches in one phase of a run, in dispatch order: phases
     are the runs of that kernel's dispatches between prefills (any `sep` dispatch ends a
@@ -76,7 +82,7 @@ def _phase(values, names, kernel, group, skip, sep="gemm_x3_kernel"):
             if cur:
                 phases.append(cur)
                 cur = []
-        elif n == kernel:
+        elif _matches(n, kernel):
             cur.append(v)
     if cur:
         phases.append(cur)
@@ -100,11 +106,11 @@ def counter_sequence(d: str, counter: str):
     return [short_name(r["Kernel_Name"]) for r in rows], [float(r["Counter_Value"]) for r in rows]
 
 
-def _full_name(names, kernel):
-    hits = sorted({n for n in names if n.startswith(kernel)}, key=lambda n: -names.count(n))
+def _kernel_label(names, kernel):
+    hits = sorted({n for n in names if _matches(n, kernel)})
     if not hits:
         raise SystemExit(f"no dispatch of {kernel}")
-    return hits[0]
+    return hits[0] if len(hits) == 1 else f"{kernel} ({', '.join(hits)})"
 
 
 def counter_values(d: str, counter: str):
@@ -125,8 +131,8 @@ def cmd_stats(a):
         print(f"{k:62s} {len(v):7d} {sum(v) / 1e3:10.3f} {sum(v) / len(v):9.2f} {100 * sum(v) / tot:5.1f}%")
     if a.kernel:
         names, durs = trace_sequence(a.dir)
-        k = _full_name(names, a.kernel)
-        v = _phase(durs, names, k, a.group, a.skip)
+        k = _kernel_label(names, a.kernel)
+        v = _phase(durs, names, a.kernel, a.group, a.skip)
         print(f"phase {a.group} of {k} (dispatches after {a.skip} warm-up ones): "
               f"{len(v)} calls, avg_us {sum(v) / len(v):.2f}")
 
@@ -152,9 +158,9 @@ def cmd_traffic(a):
     if a.kernel:
         fn, fv = counter_sequence(a.fetch_dir, "FETCH_SIZE")
         wn, wv = counter_sequence(a.write_dir, "WRITE_SIZE")
-        k = _full_name(fn, a.kernel)
-        fp = _phase(fv, fn, k, a.group, a.skip)
-        wp = _phase(wv, wn, k, a.group, a.skip)
+        k = _kernel_label(fn, a.kernel)
+        fp = _phase(fv, fn, a.kernel, a.group, a.skip)
+        wp = _phase(wv, wn, a.kernel, a.group, a.skip)
         fb = sum(fp) / len(fp) * 1024 * fscale
         wb = sum(wp) / len(wp) * 1024 * wscale
         print(f"phase {a.group} of {k} (dispatches after {a.skip} warm-up ones): {len(fp)} calls, "

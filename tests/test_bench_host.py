@@ -53,6 +53,17 @@ def test_profile_phases_pick_the_timed_replay(tmp_path, capsys):
     assert "phase 1" in last and "2 calls" in last and "avg_us 0.03" in last   # (20 + 30) / 2 ns
     ps.main(["stats", str(tmp_path / "t"), "--kernel", "gemv_gate_up", "--group", "0"])
     assert "2 calls, avg_us 0.10" in capsys.readouterr().out.strip().splitlines()[-1]
+    # a base name covers every kind of the kernel (launches change kind with their vector
+    # counts); a full name, one kind
+    gu4 = "spd::(anonymous namespace)::gemv_gate_up<unsigned short, 6>(x)"
+    rows = [["KERNEL_DISPATCH", d, gu4 if d == 8 else k, 1000, 1000 + (40 if d == 8 else ns)]
+            for d, k, ns in seq]
+    _write_csv(str(tmp_path / "t2" / "run_kernel_trace.csv"),
+               ["Kind", "Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"], rows)
+    ps.main(["stats", str(tmp_path / "t2"), "--kernel", "gemv_gate_up", "--group", "1"])
+    assert "4 calls, avg_us 0.03" in capsys.readouterr().out.strip().splitlines()[-1]   # 100/4 ns
+    ps.main(["stats", str(tmp_path / "t2"), "--kernel", "gemv_gate_up<bf16, 6>", "--group", "0"])
+    assert "1 calls, avg_us 0.04" in capsys.readouterr().out.strip().splitlines()[-1]
     # counters: FETCH_SIZE / WRITE_SIZE per dispatch, scaled by a calibration copy
     copy = "__amd_rocclr_copyBuffer"
     cseq = seq + [(13, copy, 0)]
