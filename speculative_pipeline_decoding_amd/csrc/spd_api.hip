@@ -885,6 +885,9 @@ int build_step(spd_handle* h, DescWriter& dw) {
   fd.cut_t = cuts; fd.cut_q = cuts + 1 + h->slot(dpos); fd.cut_q_v = cuts + 1 + h->slot(v);
   fd.W = p.W;
   fd.top = h->at<VocabTop>(p.o_top);
+  // the rejection rounds keep p and q of the verified position in the top-p scratch, which
+  // draft trees leave unused (they refuse top_p < 1)
+  fd.pq = p.W > 1 ? h->at<float>(p.o_nuc) : nullptr;
   const size_t foff = dw.put(&fd, 1);
   h->ops.push_back({OP_FINAL, foff, 1, 1, 0, 0.0});
   if (sampled && exited) h->ops.push_back({OP_RESID, foff, 1, kVocabBlocks, 0, 0.0});

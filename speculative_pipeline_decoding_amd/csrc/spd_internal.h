@@ -238,6 +238,7 @@ struct FinalizeDesc {
   const NucleusCut* cut_q_v; // the set of the draft at v
   int W;                     // candidates per draft position (token ring rows: slot * W + b)
   const VocabTop* top;       // [nblocks] the draft row's best scores (W > 1)
+  float* pq;                 // W > 1: [2][V] scratch, p(x) then q(x) of the verified position
 };
 
 enum RngStream : int { RNG_DRAFT = 1, RNG_ACC = 2, RNG_RES = 3, RNG_FORCE = 4, RNG_FIRST = 5 };

@@ -763,11 +763,23 @@ __global__ __launch_bounds__(kVocabBlock) void tree_rounds_kernel(const Finalize
     B[i] = B[i - 1] / Z[i - 1] + S[i - 1];
     step_cands(i);
     float part = 0.f;
-    for (int x = threadIdx.x; x < f.V; x += blockDim.x) {
-      int k;
-      if (is_cand(x, k)) continue;       // added below, once
-      const float px = expf(f.zt[x] * invT - lse_t), qx = expf(f.zq_v[x] * invT - lse_q);
-      part += fmaxf(0.f, A[i] * px - B[i] * qx);
+    // the first round evaluates p(x) and q(x) and keeps them; later passes read them back
+    // (each thread reads only what it stored itself)
+    if (i == 1) {
+      for (int x = threadIdx.x; x < f.V; x += blockDim.x) {
+        int k;
+        if (is_cand(x, k)) continue;     // added below, once
+        const float px = expf(f.zt[x] * invT - lse_t), qx = expf(f.zq_v[x] * invT - lse_q);
+        f.pq[x] = px;
+        f.pq[f.V + x] = qx;
+        part += fmaxf(0.f, A[i] * px - B[i] * qx);
+      }
+    } else {
+      for (int x = threadIdx.x; x < f.V; x += blockDim.x) {
+        int k;
+        if (is_cand(x, k)) continue;
+        part += fmaxf(0.f, A[i] * f.pq[x] - B[i] * f.pq[f.V + x]);
+      }
     }
     for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = part;
@@ -802,8 +814,7 @@ __global__ __launch_bounds__(kVocabBlock) void tree_rounds_kernel(const Finalize
         for (int j = 0; j < kMaxWidth; ++j)
           if (j == k) r = Rc[j];
       } else {
-        const float px = expf(f.zt[x] * invT - lse_t), qx = expf(f.zq_v[x] * invT - lse_q);
-        r = fmaxf(0.f, AW * px - BW * qx);
+        r = fmaxf(0.f, AW * f.pq[x] - BW * f.pq[f.V + x]);   // stored by the first round
       }
       if (r > 0.f) {
         const float g = logf(r) + gumbel_of(rng_uniform(f.seed, RNG_RES, f.v, (unsigned long long)x));
