@@ -519,7 +519,8 @@ hipError_t run_op(spd_handle* h, const Op& op, LaunchEv ev = {}) {
     case OP_RESID:
       // after a rejection at T > 0: the residual draw, or with draft trees the later rounds
       if (p.W > 1)
-        return launch_tree_rounds(reinterpret_cast<const FinalizeDesc*>(d + op.off), st, ev);
+        return launch_tree_rounds(reinterpret_cast<const FinalizeDesc*>(d + op.off),
+                                  h->at<VocabPartial>(p.o_part), kVocabBlocks, st, ev);
       return launch_residual_impl(reinterpret_cast<const FinalizeDesc*>(d + op.off),
                                   h->at<VocabPartial>(p.o_part), kVocabBlocks, st, ev);
   }

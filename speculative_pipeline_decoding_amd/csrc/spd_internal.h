@@ -442,7 +442,8 @@ hipError_t launch_finalize(const FinalizeDesc* d_desc, hipStream_t st, LaunchEv 
 hipError_t launch_residual_impl(const FinalizeDesc* d_desc, VocabPartial* part, int nblocks,
                                 hipStream_t st, LaunchEv ev = {});
 // Draft trees at T > 0: the verification rounds after the first candidate's rejection.
-hipError_t launch_tree_rounds(const FinalizeDesc* d_desc, hipStream_t st, LaunchEv ev = {});
+hipError_t launch_tree_rounds(const FinalizeDesc* d_desc, VocabPartial* part, int nblocks,
+                              hipStream_t st, LaunchEv ev = {});
 // prefill helpers
 hipError_t launch_embed_rows(const void* embed, const int* toks, float* H, int P, int d,
                              bool bf16, hipStream_t st);

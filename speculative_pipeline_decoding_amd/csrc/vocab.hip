@@ -705,12 +705,29 @@ __global__ __launch_bounds__(kVocabBlock) void residual_final_kernel(
   }
 }
 
+// The final draw of the tree rounds when every candidate was rejected, handed from the
+// rounds kernel (one block) to a pass over the vocabulary on many blocks: R_W(x) =
+// max(0, A_W p(x) - B_W q(x)) off the candidates, Rc at the candidates; p and q are the ones
+// the first round stored (pq). It sits in the scratch right after pq ([2][V] floats).
+struct TreeRes {
+  float AW, BW;
+  int cand[kMaxWidth];
+  float Rc[kMaxWidth];
+  int W;
+  int flag;       // a near-tie already met in the rounds
+  int pending;    // 1: the draw is still to be made
+};
+__device__ __forceinline__ TreeRes* tree_res_of(const FinalizeDesc& f) {
+  return reinterpret_cast<TreeRes*>(f.pq + 2 * (size_t)f.V);
+}
+
 // Draft trees at T > 0, after finalize rejected the first candidate: the remaining rounds of
 // recursive rejection sampling, in one block. Round i tests candidate c_i, proposed from q_i
 // (q without c_0 .. c_{i-1}, renormalised), against r_i = R_i / Z_i, where R_1 = max(0, p - q)
 // and R_{i+1} = max(0, R_i / Z_i - q_i) (R_0 = p, Z_0 = 1): accept iff u_i q_i(c_i) < r_i(c_i).
 // If all rounds reject, y = argmax over R_W > 0 of log R_W(x) + G(x) (RES stream), which draws
-// from r_W; a residual without mass commits the target's argmax, flagged.
+// from r_W; a residual without mass commits the target's argmax, flagged. That draw, a pass of
+// three logarithms per token, runs on many blocks (tree_res_kernel, tree_res_final_kernel).
 //
 // Off the candidates, q_j(x) = q(x) s_j with s_0 = 1, s_j = 1 / (1 - E_j) (E_j: the mass of
 // c_0 .. c_{j-1}), and since max(0, max(0, a) / Z - b) = max(0, a / Z - b) for b >= 0, Z > 0,
@@ -800,38 +817,89 @@ __global__ __launch_bounds__(kVocabBlock) void tree_rounds_kernel(const Finalize
     if (fabsf(u * qc - rc) < kNearTie * qc) flag = true;
     if (u * qc < rc) { y = cand[i]; idx = i; }
   }
+  TreeRes* tr = tree_res_of(f);
   if (y < 0) {
-    // every round rejected: draw from r_W (R_W from Z_{W-1}, s_{W-1})
+    // every round rejected: y ~ r_W (R_W from Z_{W-1}, s_{W-1}), drawn by tree_res_kernel
+    // and committed by tree_res_final_kernel
     const float AW = A[W - 1] / Z[W - 1], BW = B[W - 1] / Z[W - 1] + S[W - 1];
     step_cands(W);
-    Stat m = stat_empty();
-    for (int x = threadIdx.x; x < f.V; x += blockDim.x) {
-      int k;
-      float r;
-      if (is_cand(x, k)) {
-        r = 0.f;
+    if (threadIdx.x == 0) {
+      tr->AW = AW; tr->BW = BW; tr->W = W; tr->flag = flag;
 #pragma unroll
-        for (int j = 0; j < kMaxWidth; ++j)
-          if (j == k) r = Rc[j];
-      } else {
-        r = fmaxf(0.f, AW * f.pq[x] - BW * f.pq[f.V + x]);   // stored by the first round
-      }
-      if (r > 0.f) {
-        const float g = logf(r) + gumbel_of(rng_uniform(f.seed, RNG_RES, f.v, (unsigned long long)x));
-        if (g > m.gmax || (g == m.gmax && x < m.garg)) { m.gsecond = m.gmax; m.gmax = g; m.garg = x; }
-        else if (g > m.gsecond) m.gsecond = g;
-      }
+      for (int k = 0; k < kMaxWidth; ++k) { tr->cand[k] = cand[k]; tr->Rc[k] = Rc[k]; }
+      tr->pending = 1;
     }
-    m = block_reduce(m, 1.f, sh);
-    if (m.garg == INT_MAX) { y = vd->target_arg; flag = true; }
-    else { y = m.garg; if ((m.gmax - m.gsecond) < kNearTie) flag = true; }
+    return;
   }
   if (threadIdx.x == 0) {
+    tr->pending = 0;
     vd->committed = y;
     vd->accepted = idx >= 0;
     vd->accepted_index = idx;
     if (flag) vd->flags |= 1;
     f.tok_ring[vrow] = y;
+    *f.host_verdict = *vd;
+  }
+}
+
+// The final draw over the vocabulary, one slice per block: the largest log R_W(x) + G(x)
+// (RES stream at (v, x)) of each slice, ties to the lower id, with the runner-up score.
+__global__ __launch_bounds__(kVocabBlock) void tree_res_kernel(const FinalizeDesc* __restrict__ fd,
+                                                               VocabPartial* __restrict__ part) {
+  __shared__ Stat sh[kVocabBlock];
+  const FinalizeDesc& f = *fd;
+  const TreeRes& tr = *tree_res_of(f);
+  if (!f.verdict->need_rrs || !tr.pending) return;
+  const int chunk = (f.V + f.nblocks - 1) / f.nblocks;
+  const int lo = blockIdx.x * chunk, hi = min(f.V, lo + chunk);
+  Stat s = stat_empty();
+  for (int x = lo + threadIdx.x; x < hi; x += blockDim.x) {
+    int k = -1;
+#pragma unroll
+    for (int j = 0; j < kMaxWidth; ++j)
+      if (j < tr.W && tr.cand[j] == x) k = j;
+    float r = 0.f;
+    if (k >= 0) {
+#pragma unroll
+      for (int j = 0; j < kMaxWidth; ++j)
+        if (j == k) r = tr.Rc[j];
+    } else {
+      r = fmaxf(0.f, tr.AW * f.pq[x] - tr.BW * f.pq[f.V + x]);   // stored by the first round
+    }
+    if (r > 0.f) {
+      const float g = logf(r) + gumbel_of(rng_uniform(f.seed, RNG_RES, f.v, (unsigned long long)x));
+      if (g > s.gmax) { s.gsecond = s.gmax; s.gmax = g; s.garg = x; }
+      else if (g > s.gsecond) { s.gsecond = g; }
+    }
+  }
+  const Stat b = block_reduce(s, 1.f, sh);
+  if (threadIdx.x == 0) part[2 * f.nblocks + blockIdx.x] = to_partial(b);
+}
+
+// ... one block merges the slices in block order and commits the draw (a residual without
+// mass commits the target's argmax, flagged).
+__global__ __launch_bounds__(kVocabBlock) void tree_res_final_kernel(
+    const FinalizeDesc* __restrict__ fd, const VocabPartial* __restrict__ part) {
+  __shared__ Stat sh[kVocabBlock];
+  const FinalizeDesc& f = *fd;
+  TreeRes* tr = tree_res_of(f);
+  Verdict* vd = f.verdict;
+  if (!vd->need_rrs || !tr->pending) return;
+  Stat m = stat_empty();
+  for (int i = threadIdx.x; i < f.nblocks; i += blockDim.x)
+    m = merge(m, from_partial(part[2 * f.nblocks + i]), 1.f);
+  m = block_reduce(m, 1.f, sh);
+  int y;
+  bool flag = tr->flag != 0;
+  if (m.garg == INT_MAX) { y = vd->target_arg; flag = true; }
+  else { y = m.garg; if ((m.gmax - m.gsecond) < kNearTie) flag = true; }
+  if (threadIdx.x == 0) {
+    tr->pending = 0;
+    vd->committed = y;
+    vd->accepted = 0;
+    vd->accepted_index = -1;
+    if (flag) vd->flags |= 1;
+    f.tok_ring[(f.v % f.ring) * f.W] = y;
     *f.host_verdict = *vd;
   }
 }
@@ -861,8 +929,12 @@ hipError_t launch_finalize(const FinalizeDesc* d_desc, hipStream_t st, LaunchEv 
   return hipGetLastError();
 }
 
-hipError_t launch_tree_rounds(const FinalizeDesc* d_desc, hipStream_t st, LaunchEv ev) {
-  SPD_LAUNCH(ev, tree_rounds_kernel, dim3(1), dim3(kVocabBlock), 0, st, d_desc);
+hipError_t launch_tree_rounds(const FinalizeDesc* d_desc, VocabPartial* part, int nblocks,
+                              hipStream_t st, LaunchEv ev) {
+  const LaunchEv e1{ev.start, nullptr}, e0{nullptr, nullptr}, e2{nullptr, ev.stop};
+  SPD_LAUNCH(e1, tree_rounds_kernel, dim3(1), dim3(kVocabBlock), 0, st, d_desc);
+  SPD_LAUNCH(e0, tree_res_kernel, dim3(nblocks), dim3(kVocabBlock), 0, st, d_desc, part);
+  SPD_LAUNCH(e2, tree_res_final_kernel, dim3(1), dim3(kVocabBlock), 0, st, d_desc, part);
   return hipGetLastError();
 }
 
